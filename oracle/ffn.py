@@ -1,0 +1,138 @@
+"""Routed-expert FFN of b12x ``moe.fused_moe`` in fp64 (oracle).
+
+TEST INFRASTRUCTURE ONLY.
+
+What the pages fix (b12x README "What's in here" / "Using it"; vLLM b12x page
+"Supported Configurations" and "ModelOpt block codecs"):
+
+* the op is a routed-expert FFN over caller-supplied ``topk_ids`` /
+  ``topk_weights``, with expert weights kept packed in MXFP4 or NVFP4;
+* activations are BF16 (W4A16: inline weight dequant, no activation-scale
+  math) or dynamically quantized MXFP8 (W4A8);
+* experts are bias-free, SiLU-gated or non-gated ReLU^2;
+* the output is the top-k-weighted combine of the experts' outputs.
+
+Readings where the pages are silent:
+
+* gated weights ``w13[E, 2I, H]``: rows ``[0, I)`` are the gate projection,
+  rows ``[I, 2I)`` the up projection; ``h = silu(gate) * up`` with
+  ``silu(z) = z / (1 + exp(-z))``; no clamp, no bias.
+* non-gated weights ``w1[E, I, H]``: ``h = max(w1 x, 0)^2``.
+* the expert's intermediate ``h`` is rounded to the precision of the down
+  projection's operand before it: bf16 (round to nearest even) for BF16
+  activations, MXFP8 (per 32 along I, the same rule as the activations) for
+  MXFP8 activations.
+* combine: ``out[t] = sum_j w[t, j] * y[t, j]`` in ascending slot order, with
+  the weights used as given (no renormalization); a pair whose id lies outside
+  ``[0, E)`` contributes nothing; a repeated id counts once per slot.
+* ``topk_ids`` are int32 ``[T, k]``, ``topk_weights`` float32 ``[T, k]``.
+"""
+from dataclasses import dataclass
+from typing import Optional
+
+import numpy as np
+
+from .formats import (bf16_decode, dequant_mxfp4, dequant_nvfp4, dequant_mxfp8,
+                      quantize_mxfp8, round_to_bf16)
+
+
+@dataclass
+class Weights:
+    """Source-format expert weights (the layout a checkpoint provides).
+
+    ``w13_codes`` uint8 [E, N1, H/2] with N1 = 2I (gated) or I (ReLU^2);
+    ``w13_scales`` uint8 [E, N1, H/G]; ``w2_codes`` uint8 [E, H, I/2];
+    ``w2_scales`` uint8 [E, H, I/G]; G = 32 (MXFP4, E8M0) or 16 (NVFP4,
+    E4M3); ``w13_global`` / ``w2_global`` float32 [E] for NVFP4, else None.
+    Each array may also be a mapping expert -> per-expert array (then
+    ``num_experts`` is required); only the experts a call touches are read.
+    """
+    weight_format: str
+    gated: bool
+    w13_codes: np.ndarray
+    w13_scales: np.ndarray
+    w2_codes: np.ndarray
+    w2_scales: np.ndarray
+    w13_global: Optional[np.ndarray] = None
+    w2_global: Optional[np.ndarray] = None
+    num_experts: Optional[int] = None   # required when the arrays are per-expert mappings
+
+    @property
+    def E(self):
+        return self.num_experts if self.num_experts is not None else len(self.w13_codes)
+
+    def _dequant(self, codes, scales, g):
+        if self.weight_format == "mxfp4":
+            return dequant_mxfp4(codes, scales)
+        if self.weight_format == "nvfp4":
+            return dequant_nvfp4(codes, scales, g)
+        raise ValueError(f"unknown weight format {self.weight_format!r}")
+
+    def w13(self, e):
+        g = None if self.w13_global is None else self.w13_global[e]
+        return self._dequant(np.asarray(self.w13_codes[e]), np.asarray(self.w13_scales[e]), g)
+
+    def w2(self, e):
+        g = None if self.w2_global is None else self.w2_global[e]
+        return self._dequant(np.asarray(self.w2_codes[e]), np.asarray(self.w2_scales[e]), g)
+
+
+def _silu(z):
+    with np.errstate(over="ignore"):
+        return z / (1.0 + np.exp(-z))
+
+
+def expert_ffn(xa, w13, w2, gated, intermediate):
+    """One expert on the rows ``xa`` [m, H]: returns y [m, H] (fp64)."""
+    z = xa @ w13.T
+    if gated:
+        inter = w13.shape[0] // 2
+        h = _silu(z[:, :inter]) * z[:, inter:]
+    else:
+        h = np.maximum(z, 0.0) ** 2
+    if intermediate == "bf16":
+        h = round_to_bf16(h)
+    elif intermediate == "mxfp8":
+        h = dequant_mxfp8(*quantize_mxfp8(h))
+    elif intermediate != "none":
+        raise ValueError(f"unknown intermediate rounding {intermediate!r}")
+    return h @ w2.T
+
+
+def fused_moe(x_bits, topk_ids, topk_weights, weights, act_format="bf16",
+              intermediate=None):
+    """Reference fused MoE.  Returns the fp64 output [T, H] before the final
+    bf16 rounding.
+
+    x_bits: uint16 bf16 patterns [T, H]; topk_ids int32 [T, k];
+    topk_weights float32 [T, k]; weights: ``Weights``.
+    act_format: "bf16" (W4A16) or "mxfp8" (W4A8: each row of x is MXFP8
+    quantized per 32 along H and the GEMMs see the dequantized values).
+    intermediate: rounding of h before the down projection; defaults to "bf16"
+    for W4A16 and "mxfp8" for W4A8 ("none" keeps fp64).
+    """
+    x = bf16_decode(x_bits)
+    ids = np.asarray(topk_ids).astype(np.int64)
+    wts = np.asarray(topk_weights, dtype=np.float32).astype(np.float64)
+    T, k = ids.shape
+    E = weights.E
+    if act_format == "bf16":
+        xa = x
+    elif act_format == "mxfp8":
+        xa = dequant_mxfp8(*quantize_mxfp8(x))
+    else:
+        raise ValueError(f"unknown activation format {act_format!r}")
+    if intermediate is None:
+        intermediate = "bf16" if act_format == "bf16" else "mxfp8"
+
+    # y[t, j] for every valid pair, expert by expert (each expert dequantized once)
+    y = np.zeros((T, k, x.shape[1]), dtype=np.float64)
+    valid = (ids >= 0) & (ids < E)
+    for e in np.unique(ids[valid]):
+        tt, jj = np.nonzero(ids == e)
+        y[tt, jj] = expert_ffn(xa[tt], weights.w13(e), weights.w2(e), weights.gated, intermediate)
+
+    out = np.zeros((T, x.shape[1]), dtype=np.float64)
+    for j in range(k):
+        out += np.where(valid[:, j:j + 1], wts[:, j:j + 1] * y[:, j], 0.0)
+    return out

@@ -1,0 +1,85 @@
+"""Pins of the oracle's routing against a brute force built differently
+(per-expert filtering instead of one counting pass) and against the
+invariants any correct stable routing must satisfy."""
+import numpy as np
+import pytest
+
+from oracle.routing import route
+
+
+def brute_force(ids, E, row_pad, tile_rows):
+    flat = [int(v) for v in np.asarray(ids).reshape(-1)]
+    per_expert = [[p for p, v in enumerate(flat) if v == e] for e in range(E)]
+    rows, pos, tiles = [], [-1] * len(flat), []
+    for e, pairs in enumerate(per_expert):
+        start = len(rows)
+        for p in pairs:
+            pos[p] = len(rows)
+            rows.append(p)
+        while len(rows) % row_pad:
+            rows.append(-1)
+        for r in range(start, len(rows), tile_rows):
+            tiles.append((e, r, min(tile_rows, len(rows) - r)))
+    counts = [len(p) for p in per_expert]
+    return counts, rows, pos, tiles
+
+
+CASES = [
+    ("uniform", 16, 2, 8),
+    ("one_hot_expert", 20, 4, 8),
+    ("duplicates", 12, 3, 5),
+    ("bad_ids", 10, 4, 6),
+    ("empty", 0, 4, 8),
+    ("many_experts_few_tokens", 3, 8, 128),
+]
+
+
+def _ids(kind, T, k, E, rng):
+    if kind == "uniform" or kind == "many_experts_few_tokens":
+        return np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32).reshape(T, k)
+    if kind == "one_hot_expert":
+        return np.full((T, k), 3, dtype=np.int32)
+    if kind == "duplicates":
+        return rng.integers(0, 2, size=(T, k)).astype(np.int32)
+    if kind == "bad_ids":
+        ids = rng.integers(0, E, size=(T, k)).astype(np.int32)
+        ids[0, 0], ids[1, 1], ids[2, 2], ids[3, 3] = -1, E, 1000, -(2 ** 31)
+        return ids
+    return np.zeros((T, k), dtype=np.int32)
+
+
+@pytest.mark.parametrize("kind,T,k,E", CASES)
+@pytest.mark.parametrize("row_pad,tile_rows", [(1, 4), (16, 32), (16, 16), (4, 128)])
+def test_route_matches_brute_force(kind, T, k, E, row_pad, tile_rows):
+    rng = np.random.default_rng([sum(map(ord, kind)), row_pad, T, k])
+    ids = _ids(kind, T, k, E, rng)
+    r = route(ids, E, row_pad, tile_rows)
+    counts, rows, pos, tiles = brute_force(ids, E, row_pad, tile_rows)
+    assert r.counts.tolist() == counts
+    assert r.sorted_ids.tolist() == rows
+    assert r.pos.tolist() == pos
+    assert [tuple(t) for t in r.tiles.tolist()] == tiles
+    assert r.offsets.tolist() == [0] + list(np.cumsum(counts))
+
+
+@pytest.mark.parametrize("seed", range(5))
+def test_route_invariants(seed):
+    rng = np.random.default_rng(seed)
+    E, T, k = 13, 37, 3
+    ids = rng.integers(-2, E + 2, size=(T, k)).astype(np.int32)
+    r = route(ids, E, 8, 24)
+    flat = ids.reshape(-1)
+    valid = (flat >= 0) & (flat < E)
+    assert r.counts.sum() == valid.sum()
+    live = r.sorted_ids[r.sorted_ids >= 0]
+    assert sorted(live.tolist()) == np.nonzero(valid)[0].tolist()      # a permutation of the valid pairs
+    for i, p in enumerate(r.sorted_ids):
+        if p >= 0:
+            assert r.pos[p] == i and flat[p] == np.searchsorted(r.padded_offsets, i, side="right") - 1
+    assert np.all(r.pos[~valid] == -1)
+    assert np.all(np.diff(r.padded_offsets) % 8 == 0)
+    for e in range(E):                                                 # stable: ascending p in each expert
+        seg = r.sorted_ids[r.padded_offsets[e]:r.padded_offsets[e + 1]]
+        seg = seg[seg >= 0]
+        assert np.all(np.diff(seg) > 0)
+    assert r.tiles[:, 2].sum() == r.padded_offsets[-1] and np.all(r.tiles[:, 2] <= 24)
