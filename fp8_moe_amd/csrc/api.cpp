@@ -1,0 +1,395 @@
+// Host runtime and C ABI of the fused MoE: weight planning, op planning,
+// scratch layout, binding validation and launch sequencing.  Plan, scratch
+// and bind logic touch no device; only prepare_weights, run, run_stage and
+// quantize_rows enqueue kernels.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <new>
+
+#include "internal.h"
+
+using namespace b12x;
+
+namespace {
+
+thread_local char g_err[512];
+
+b12x_status fail(b12x_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+b12x_status fail(b12x_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+b12x_status hip_fail(int err, const char* what) {
+  return fail(B12X_ERR_HIP, "%s: HIP error %d (%s)", what, err, hip_error_name(err));
+}
+
+uint64_t align_up(uint64_t v, uint64_t a) { return (v + a - 1) / a * a; }
+
+bool aligned(const void* p, uint64_t a) { return ((uintptr_t)p % a) == 0; }
+
+b12x_status check_desc(const b12x_moe_weight_desc* d) {
+  if (!d) return fail(B12X_ERR_INVALID_ARGUMENT, "weight desc is NULL");
+  if (d->struct_size != sizeof(b12x_moe_weight_desc))
+    return fail(B12X_ERR_INVALID_ARGUMENT, "weight desc struct_size %u != %zu", d->struct_size,
+                sizeof(b12x_moe_weight_desc));
+  if (d->weight_format != B12X_WEIGHT_MXFP4 && d->weight_format != B12X_WEIGHT_NVFP4)
+    return fail(B12X_ERR_INVALID_ARGUMENT, "unknown weight format %d", d->weight_format);
+  if (d->gated != 0 && d->gated != 1) return fail(B12X_ERR_INVALID_ARGUMENT, "gated must be 0 or 1");
+  if (d->num_experts < 1 || d->hidden < 1 || d->inter < 1)
+    return fail(B12X_ERR_INVALID_ARGUMENT, "E, H and I must be positive");
+  if (d->num_experts > kMaxExperts)
+    return fail(B12X_ERR_UNSUPPORTED, "E = %d exceeds %d experts", d->num_experts, kMaxExperts);
+  // whole scale blocks along both contractions, whole 16-row fragments along both outputs
+  if (d->hidden % 32 || d->inter % 32)
+    return fail(B12X_ERR_UNSUPPORTED, "H (%d) and I (%d) must be multiples of 32", d->hidden, d->inter);
+  if ((int64_t)d->hidden * d->inter * d->num_experts > (int64_t)1 << 40)
+    return fail(B12X_ERR_UNSUPPORTED, "weights larger than 2^40 elements");
+  return B12X_OK;
+}
+
+b12x_status check_caps(const b12x_moe_caps* c) {
+  if (!c) return fail(B12X_ERR_INVALID_ARGUMENT, "caps is NULL");
+  if (c->struct_size != sizeof(b12x_moe_caps))
+    return fail(B12X_ERR_INVALID_ARGUMENT, "caps struct_size %u != %zu", c->struct_size, sizeof(b12x_moe_caps));
+  if (c->weights.struct_size != sizeof(b12x_moe_weight_plan) || c->weights.layout_id != kLayoutId)
+    return fail(B12X_ERR_INVALID_ARGUMENT, "caps.weights is not a plan from b12x_moe_plan_weights");
+  b12x_status st = check_desc(&c->weights.desc);
+  if (st) return st;
+  if (c->top_k < 1 || c->top_k > 64) return fail(B12X_ERR_UNSUPPORTED, "top_k %d outside [1, 64]", c->top_k);
+  if (c->max_tokens < 1) return fail(B12X_ERR_INVALID_ARGUMENT, "max_tokens must be >= 1");
+  if (c->max_tokens * c->top_k > ((int64_t)1 << 30))
+    return fail(B12X_ERR_UNSUPPORTED, "max_tokens * top_k exceeds 2^30 pairs");
+  if (c->act_format != B12X_ACT_BF16 && c->act_format != B12X_ACT_MXFP8)
+    return fail(B12X_ERR_INVALID_ARGUMENT, "unknown activation format %d", c->act_format);
+  if (c->activation != B12X_ACTIVATION_SILU_GATED && c->activation != B12X_ACTIVATION_RELU2)
+    return fail(B12X_ERR_INVALID_ARGUMENT, "unknown activation %d", c->activation);
+  if ((c->activation == B12X_ACTIVATION_SILU_GATED) != (c->weights.desc.gated == 1))
+    return fail(B12X_ERR_UNSUPPORTED, "SiLU-gated experts need gated weights and ReLU^2 needs non-gated ones");
+  if (c->act_format == B12X_ACT_MXFP8 && c->weights.desc.weight_format != B12X_WEIGHT_MXFP4)
+    return fail(B12X_ERR_UNSUPPORTED, "MXFP8 activations run with MXFP4 weights only");
+  return B12X_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* b12x_status_string(b12x_status s) {
+  switch (s) {
+    case B12X_OK: return "ok";
+    case B12X_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case B12X_ERR_UNSUPPORTED: return "unsupported";
+    case B12X_ERR_CAPACITY: return "capacity exceeded";
+    case B12X_ERR_SCRATCH_TOO_SMALL: return "scratch too small";
+    case B12X_ERR_MISALIGNED: return "misaligned";
+    case B12X_ERR_LAYOUT_MISMATCH: return "layout mismatch";
+    case B12X_ERR_HIP: return "HIP error";
+    default: return "unknown status";
+  }
+}
+
+const char* b12x_last_error(void) { return g_err; }
+
+b12x_status b12x_moe_plan_weights(const b12x_moe_weight_desc* d, b12x_moe_weight_plan* out) {
+  b12x_status st = check_desc(d);
+  if (st) return st;
+  if (!out) return fail(B12X_ERR_INVALID_ARGUMENT, "out is NULL");
+  MatrixLayout l13 = make_matrix_layout((int64_t)(d->gated ? 2 : 1) * d->inter, d->hidden, d->weight_format);
+  MatrixLayout l2 = make_matrix_layout(d->hidden, d->inter, d->weight_format);
+  const uint64_t E = (uint64_t)d->num_experts;
+  memset(out, 0, sizeof(*out));
+  out->struct_size = sizeof(b12x_moe_weight_plan);
+  out->layout_id = kLayoutId;
+  out->desc = *d;
+  out->alignment = 256;
+  uint64_t off = 0;
+  out->w13_codes_off = off;  off = align_up(off + E * l13.codes_per_expert, 256);
+  out->w13_scales_off = off; off = align_up(off + E * l13.scales_per_expert, 256);
+  out->w2_codes_off = off;   off = align_up(off + E * l2.codes_per_expert, 256);
+  out->w2_scales_off = off;  off = align_up(off + E * l2.scales_per_expert, 256);
+  out->w13_global_off = off; off = align_up(off + E * 4, 256);
+  out->w2_global_off = off;  off = align_up(off + E * 4, 256);
+  out->prepared_bytes = off;
+  return B12X_OK;
+}
+
+b12x_status b12x_moe_prepare_weights(const b12x_moe_weight_plan* wp, const b12x_moe_weight_src* src, void* dst,
+                                     uint64_t dst_bytes, void* stream, b12x_moe_experts* out) {
+  if (!wp || !src || !dst || !out) return fail(B12X_ERR_INVALID_ARGUMENT, "NULL argument");
+  if (wp->struct_size != sizeof(b12x_moe_weight_plan) || wp->layout_id != kLayoutId)
+    return fail(B12X_ERR_INVALID_ARGUMENT, "not a weight plan from b12x_moe_plan_weights");
+  b12x_status st = check_desc(&wp->desc);
+  if (st) return st;
+  if (dst_bytes < wp->prepared_bytes)
+    return fail(B12X_ERR_SCRATCH_TOO_SMALL, "prepared buffer %llu < %llu bytes", (unsigned long long)dst_bytes,
+                (unsigned long long)wp->prepared_bytes);
+  if (!aligned(dst, wp->alignment)) return fail(B12X_ERR_MISALIGNED, "prepared buffer not %llu-byte aligned",
+                                                (unsigned long long)wp->alignment);
+  const b12x_moe_weight_desc& d = wp->desc;
+  const bool nv = d.weight_format == B12X_WEIGHT_NVFP4;
+  if (!src->w13_codes || !src->w13_scales || !src->w2_codes || !src->w2_scales)
+    return fail(B12X_ERR_INVALID_ARGUMENT, "NULL source weight pointer");
+  if (nv && (!src->w13_global || !src->w2_global))
+    return fail(B12X_ERR_INVALID_ARGUMENT, "NVFP4 weights need both per-expert fp32 scales");
+  if (!aligned(src->w13_codes, 16) || !aligned(src->w2_codes, 16))
+    return fail(B12X_ERR_MISALIGNED, "source codes must be 16-byte aligned");
+  hipStream_t s = (hipStream_t)stream;
+  uint8_t* base = (uint8_t*)dst;
+  PackArgs a;
+  a.wfmt = d.weight_format;
+  a.E = d.num_experts;
+  a.l = make_matrix_layout((int64_t)(d.gated ? 2 : 1) * d.inter, d.hidden, d.weight_format);
+  a.src_codes = (const uint8_t*)src->w13_codes;
+  a.src_scales = (const uint8_t*)src->w13_scales;
+  a.dst_codes = base + wp->w13_codes_off;
+  a.dst_scales = base + wp->w13_scales_off;
+  a.gated_interleave = d.gated;
+  int err = launch_pack(a, s);
+  if (err) return hip_fail(err, "pack w13");
+  a.l = make_matrix_layout(d.hidden, d.inter, d.weight_format);
+  a.src_codes = (const uint8_t*)src->w2_codes;
+  a.src_scales = (const uint8_t*)src->w2_scales;
+  a.dst_codes = base + wp->w2_codes_off;
+  a.dst_scales = base + wp->w2_scales_off;
+  a.gated_interleave = 0;
+  err = launch_pack(a, s);
+  if (err) return hip_fail(err, "pack w2");
+  if (nv) {
+    err = launch_copy_f32(src->w13_global, (float*)(base + wp->w13_global_off), d.num_experts, s);
+    if (!err) err = launch_copy_f32(src->w2_global, (float*)(base + wp->w2_global_off), d.num_experts, s);
+    if (err) return hip_fail(err, "copy global scales");
+  }
+  out->plan = *wp;
+  out->base = dst;
+  out->bytes = dst_bytes;
+  return B12X_OK;
+}
+
+int32_t b12x_moe_is_supported(const b12x_moe_caps* caps) { return check_caps(caps) == B12X_OK ? 1 : 0; }
+
+b12x_status b12x_moe_plan(const b12x_moe_caps* caps, b12x_moe_plan_t* out) {
+  b12x_status st = check_caps(caps);
+  if (st) return st;
+  if (!out) return fail(B12X_ERR_INVALID_ARGUMENT, "out is NULL");
+  b12x_moe_plan_impl* p = new (std::nothrow) b12x_moe_plan_impl();
+  if (!p) return fail(B12X_ERR_INVALID_ARGUMENT, "host allocation failed");
+  const b12x_moe_weight_desc& d = caps->weights.desc;
+  p->caps = *caps;
+  p->E = d.num_experts;
+  p->H = d.hidden;
+  p->I = d.inter;
+  p->k = caps->top_k;
+  p->gated = d.gated;
+  p->wfmt = d.weight_format;
+  p->afmt = caps->act_format;
+  p->act = caps->activation;
+  p->max_tokens = caps->max_tokens;
+  p->l13 = make_matrix_layout((int64_t)(d.gated ? 2 : 1) * d.inter, d.hidden, d.weight_format);
+  p->l2 = make_matrix_layout(d.hidden, d.inter, d.weight_format);
+  p->Hp = align_up(p->H, kFragK);
+  p->Ip = align_up(p->I, kFragK);
+  p->max_pairs = p->max_tokens * p->k;
+  p->max_rows = p->max_pairs + (int64_t)p->E * (kRowPad - 1);
+  p->max_rows = (int64_t)align_up(p->max_rows, kRowPad);
+  p->max_tiles = (p->max_rows + kTileRows - 1) / kTileRows + p->E;
+  p->max_chunks = (p->max_pairs + kRouteChunk - 1) / kRouteChunk;
+  const bool a8 = p->afmt == B12X_ACT_MXFP8;
+  uint64_t len[R_COUNT_] = {0};
+  len[R_COUNTS] = 4ull * p->E;
+  len[R_OFFSETS] = 4ull * (p->E + 1);
+  len[R_POFF] = 4ull * (p->E + 1);
+  len[R_SORTED] = 4ull * p->max_rows;
+  len[R_POS] = 4ull * p->max_pairs;
+  len[R_TILES] = 16ull * p->max_tiles;
+  len[R_NTILES] = 16;
+  len[R_CHUNK] = 4ull * p->max_chunks * p->E;
+  len[R_XQ] = a8 ? (uint64_t)p->max_tokens * p->Hp : 0;
+  len[R_XS] = a8 ? (uint64_t)p->max_tokens * (p->Hp / 32) : 0;
+  len[R_H] = (uint64_t)p->max_rows * p->Ip * (a8 ? 1 : 2);
+  len[R_HS] = a8 ? (uint64_t)p->max_rows * (p->Ip / 32) : 0;
+  len[R_Y] = 4ull * p->max_rows * p->H;
+  uint64_t off = 0;
+  for (int r = 1; r < R_COUNT_; ++r) {
+    p->off[r] = off;
+    p->len[r] = len[r];
+    off = align_up(off + len[r], 256);
+  }
+  p->scratch_bytes = off;
+  *out = p;
+  return B12X_OK;
+}
+
+void b12x_moe_plan_destroy(b12x_moe_plan_t plan) { delete plan; }
+
+b12x_status b12x_moe_scratch_specs(b12x_moe_plan_t p, b12x_scratch_spec* specs, int32_t cap, int32_t* n) {
+  if (!p || !n) return fail(B12X_ERR_INVALID_ARGUMENT, "NULL argument");
+  if (cap > 0 && !specs) return fail(B12X_ERR_INVALID_ARGUMENT, "specs is NULL");
+  *n = 1;
+  if (cap >= 1) {
+    specs[0].bytes = p->scratch_bytes;
+    specs[0].alignment = 256;
+    specs[0].dtype = 0;
+    specs[0].reserved = 0;
+  }
+  return B12X_OK;
+}
+
+b12x_status b12x_moe_scratch_region(b12x_moe_plan_t p, int32_t region, uint64_t* offset, uint64_t* bytes) {
+  if (!p || !offset || !bytes) return fail(B12X_ERR_INVALID_ARGUMENT, "NULL argument");
+  if (region < R_COUNTS || region > R_NTILES) return fail(B12X_ERR_INVALID_ARGUMENT, "unknown region %d", region);
+  *offset = p->off[region];
+  *bytes = p->len[region];
+  return B12X_OK;
+}
+
+b12x_status b12x_moe_bind(b12x_moe_plan_t p, void* scratch, uint64_t scratch_bytes, const b12x_moe_experts* ex,
+                          const void* a, int64_t T, int64_t a_stride, const int32_t* ids, const float* tw, void* out,
+                          int64_t out_stride, b12x_moe_binding* binding) {
+  if (!p || !binding || !ex) return fail(B12X_ERR_INVALID_ARGUMENT, "NULL plan, experts or binding");
+  if (T < 0) return fail(B12X_ERR_INVALID_ARGUMENT, "T < 0");
+  if (T > p->max_tokens)
+    return fail(B12X_ERR_CAPACITY, "T = %lld exceeds max_tokens = %lld", (long long)T, (long long)p->max_tokens);
+  if (memcmp(&ex->plan, &p->caps.weights, sizeof(b12x_moe_weight_plan)) != 0)
+    return fail(B12X_ERR_LAYOUT_MISMATCH, "prepared weights follow a different weight plan");
+  if (!ex->base || ex->bytes < ex->plan.prepared_bytes)
+    return fail(B12X_ERR_LAYOUT_MISMATCH, "prepared weight buffer missing or too small");
+  if (T > 0) {
+    if (!a || !ids || !tw || !out || !scratch) return fail(B12X_ERR_INVALID_ARGUMENT, "NULL device pointer");
+    if (a_stride < p->H || out_stride < p->H) return fail(B12X_ERR_INVALID_ARGUMENT, "row stride smaller than H");
+    if (a_stride % 8 || out_stride % 8) return fail(B12X_ERR_MISALIGNED, "row strides must be multiples of 8");
+    if (!aligned(a, 16) || !aligned(out, 16) || !aligned(ids, 16) || !aligned(tw, 16))
+      return fail(B12X_ERR_MISALIGNED, "a, out, topk_ids and topk_weights must be 16-byte aligned");
+    if (!aligned(scratch, 256)) return fail(B12X_ERR_MISALIGNED, "scratch must be 256-byte aligned");
+    if (scratch_bytes < p->scratch_bytes)
+      return fail(B12X_ERR_SCRATCH_TOO_SMALL, "scratch %llu < %llu bytes", (unsigned long long)scratch_bytes,
+                  (unsigned long long)p->scratch_bytes);
+    const char* ab = (const char*)a;
+    const char* ob = (const char*)out;
+    const int64_t abytes = ((T - 1) * a_stride + p->H) * 2, obytes = ((T - 1) * out_stride + p->H) * 2;
+    if (ab < ob + obytes && ob < ab + abytes) return fail(B12X_ERR_INVALID_ARGUMENT, "out aliases a");
+  }
+  BindingImpl b;
+  memset(&b, 0, sizeof(b));
+  b.magic = kBindingMagic;
+  b.path = 1;
+  b.E = p->E; b.H = p->H; b.I = p->I; b.k = p->k;
+  b.gated = p->gated; b.wfmt = p->wfmt; b.afmt = p->afmt; b.act = p->act;
+  b.T = T; b.a_stride = a_stride; b.out_stride = out_stride;
+  b.Hp = p->Hp; b.Ip = p->Ip; b.max_rows = p->max_rows; b.max_tiles = p->max_tiles;
+  b.nf13 = p->l13.nf; b.kf13 = p->l13.kf; b.kfs13 = p->l13.kfs;
+  b.nf2 = p->l2.nf; b.kf2 = p->l2.kf; b.kfs2 = p->l2.kfs;
+  b.a = (const uint16_t*)a; b.ids = ids; b.tw = tw; b.out = (uint16_t*)out;
+  const uint8_t* wb = (const uint8_t*)ex->base;
+  const b12x_moe_weight_plan& wp = ex->plan;
+  b.w13_codes = wb + wp.w13_codes_off;
+  b.w13_scales = wb + wp.w13_scales_off;
+  b.w2_codes = wb + wp.w2_codes_off;
+  b.w2_scales = wb + wp.w2_scales_off;
+  const bool nv = p->wfmt == B12X_WEIGHT_NVFP4;
+  b.w13_global = nv ? (const float*)(wb + wp.w13_global_off) : nullptr;
+  b.w2_global = nv ? (const float*)(wb + wp.w2_global_off) : nullptr;
+  uint8_t* sb = (uint8_t*)scratch;
+  b.counts = (int32_t*)(sb + p->off[R_COUNTS]);
+  b.offsets = (int32_t*)(sb + p->off[R_OFFSETS]);
+  b.poff = (int32_t*)(sb + p->off[R_POFF]);
+  b.sorted = (int32_t*)(sb + p->off[R_SORTED]);
+  b.pos = (int32_t*)(sb + p->off[R_POS]);
+  b.tiles = (int32_t*)(sb + p->off[R_TILES]);
+  b.ntiles = (int32_t*)(sb + p->off[R_NTILES]);
+  b.chunk = (int32_t*)(sb + p->off[R_CHUNK]);
+  b.xq = p->len[R_XQ] ? sb + p->off[R_XQ] : nullptr;
+  b.xs = p->len[R_XS] ? sb + p->off[R_XS] : nullptr;
+  b.h = sb + p->off[R_H];
+  b.hs = p->len[R_HS] ? sb + p->off[R_HS] : nullptr;
+  b.y = (float*)(sb + p->off[R_Y]);
+  memset(binding, 0, sizeof(*binding));
+  memcpy(binding, &b, sizeof(b));
+  return B12X_OK;
+}
+
+static b12x_status get_binding(const b12x_moe_binding* binding, BindingImpl* b) {
+  if (!binding) return fail(B12X_ERR_INVALID_ARGUMENT, "binding is NULL");
+  memcpy(b, binding, sizeof(*b));
+  if (b->magic != kBindingMagic) return fail(B12X_ERR_INVALID_ARGUMENT, "not a binding from b12x_moe_bind");
+  return B12X_OK;
+}
+
+static b12x_status run_stage(const BindingImpl& b, int stage, hipStream_t s) {
+  int err = 0;
+  switch (stage) {
+    case B12X_STAGE_ROUTE: err = launch_route(b, s); break;
+    case B12X_STAGE_QUANT_X:
+      if (b.afmt != B12X_ACT_MXFP8) return fail(B12X_ERR_UNSUPPORTED, "QUANT_X runs only with MXFP8 activations");
+      err = launch_quant_rows(b.a, b.T, b.H, b.a_stride, b.xq, b.Hp, b.xs, b.Hp / 32, s);
+      break;
+    case B12X_STAGE_GEMM1: err = launch_gemm1(b, s); break;
+    case B12X_STAGE_GEMM2: err = launch_gemm2(b, s); break;
+    case B12X_STAGE_COMBINE: err = launch_combine(b, s); break;
+    default: return fail(B12X_ERR_INVALID_ARGUMENT, "unknown stage %d", stage);
+  }
+  if (err) return hip_fail(err, "kernel launch");
+  return B12X_OK;
+}
+
+b12x_status b12x_moe_run_stage(const b12x_moe_binding* binding, int32_t stage, void* stream) {
+  BindingImpl b;
+  b12x_status st = get_binding(binding, &b);
+  if (st) return st;
+  if (b.T == 0) return B12X_OK;
+  return run_stage(b, stage, (hipStream_t)stream);
+}
+
+b12x_status b12x_moe_run(const b12x_moe_binding* binding, void* stream) {
+  BindingImpl b;
+  b12x_status st = get_binding(binding, &b);
+  if (st) return st;
+  if (b.T == 0) return B12X_OK;
+  hipStream_t s = (hipStream_t)stream;
+  const int stages[5] = {B12X_STAGE_ROUTE, B12X_STAGE_QUANT_X, B12X_STAGE_GEMM1, B12X_STAGE_GEMM2,
+                         B12X_STAGE_COMBINE};
+  for (int i = 0; i < 5; ++i) {
+    if (stages[i] == B12X_STAGE_QUANT_X && b.afmt != B12X_ACT_MXFP8) continue;
+    st = run_stage(b, stages[i], s);
+    if (st) return st;
+  }
+  return B12X_OK;
+}
+
+b12x_status b12x_moe_binding_query(const b12x_moe_binding* binding, int32_t what, int64_t* value) {
+  BindingImpl b;
+  b12x_status st = get_binding(binding, &b);
+  if (st) return st;
+  if (!value) return fail(B12X_ERR_INVALID_ARGUMENT, "value is NULL");
+  switch (what) {
+    case B12X_QUERY_PATH: *value = b.path; break;
+    case B12X_QUERY_TILE_ROWS: *value = kTileRows; break;
+    case B12X_QUERY_ROW_PAD: *value = kRowPad; break;
+    case B12X_QUERY_T: *value = b.T; break;
+    case B12X_QUERY_NUM_STAGES: *value = b.afmt == B12X_ACT_MXFP8 ? 5 : 4; break;
+    default: return fail(B12X_ERR_INVALID_ARGUMENT, "unknown query %d", what);
+  }
+  return B12X_OK;
+}
+
+b12x_status b12x_mxfp8_quantize_rows(const void* x, int64_t rows, int64_t cols, int64_t stride, uint8_t* codes,
+                                     uint8_t* scales, void* stream) {
+  if (rows < 0 || cols < 0) return fail(B12X_ERR_INVALID_ARGUMENT, "negative size");
+  if (cols % 32) return fail(B12X_ERR_UNSUPPORTED, "cols (%lld) must be a multiple of 32", (long long)cols);
+  if (rows == 0 || cols == 0) return B12X_OK;
+  if (!x || !codes || !scales) return fail(B12X_ERR_INVALID_ARGUMENT, "NULL device pointer");
+  if (stride < cols) return fail(B12X_ERR_INVALID_ARGUMENT, "stride smaller than cols");
+  if (stride % 8 || !aligned(x, 16) || !aligned(codes, 16))
+    return fail(B12X_ERR_MISALIGNED, "x, codes and the row stride must be 16-byte aligned");
+  int err = launch_quant_rows((const uint16_t*)x, rows, cols, stride, codes, cols, scales, cols / 32,
+                              (hipStream_t)stream);
+  if (err) return hip_fail(err, "quantize rows");
+  return B12X_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,93 @@
+// Device helpers shared by the gfx950 kernels: vector types, bf16 and
+// E4M3 / E8M0 encoders written with integer operations (so that results do
+// not depend on denormal modes), and the MXFP8 block-scale rule.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "internal.h"
+
+namespace b12x {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t f32_bits(float f) { return __builtin_bit_cast(uint32_t, f); }
+__device__ __forceinline__ float bits_f32(uint32_t u) { return __builtin_bit_cast(float, u); }
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t bf16_rne(float f) {
+  uint32_t u = f32_bits(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t h) { return bits_f32(h << 16); }
+
+// floor(log2 m) for a non-zero fp32 magnitude given by its bits.
+__device__ __forceinline__ int ilog2_mag(uint32_t mag) {
+  const uint32_t e = mag >> 23;
+  if (e) return (int)e - 127;
+  return (31 - __builtin_clz(mag)) - 149;  // subnormal: m * 2^-149
+}
+
+// MXFP8 shared exponent of a 32-block from its largest magnitude (fp32 bits):
+// clamp(floor(log2 amax) - 8, -127, 127), or -127 for an all-zero block.
+__device__ __forceinline__ int mx_scale_exp(uint32_t amax_mag) {
+  if (amax_mag == 0) return -127;
+  int s = ilog2_mag(amax_mag) - 8;
+  return s < -127 ? -127 : (s > 127 ? 127 : s);
+}
+
+// Round sig / 2^sh to the nearest integer, ties to even (sig < 2^24, sh >= 1).
+__device__ __forceinline__ uint32_t rne_shift(uint32_t sig, int sh) {
+  if (sh >= 25) return 0;  // sig < 2^24 <= half: below one half
+  const uint32_t r = sig >> sh, rem = sig & ((1u << sh) - 1u), half = 1u << (sh - 1);
+  return r + ((rem > half || (rem == half && (r & 1u))) ? 1u : 0u);
+}
+
+// E4M3 (FN) code of v * 2^-s (v given as fp32 bits, s the block exponent):
+// round half to even onto the E4M3 grid, subnormals kept, saturating at
+// +-448, sign of zero kept.
+__device__ __forceinline__ uint32_t e4m3_encode_scaled(uint32_t vbits, int s) {
+  const uint32_t sign = (vbits >> 24) & 0x80u;
+  const uint32_t mag = vbits & 0x7FFFFFFFu;
+  if (mag == 0) return sign;
+  uint32_t sig;
+  int ev;
+  if (mag >> 23) {
+    sig = (mag & 0x7FFFFFu) | 0x800000u;
+    ev = (int)(mag >> 23) - 127;
+  } else {
+    const int lz = __builtin_clz(mag) - 8;
+    sig = mag << lz;
+    ev = -126 - lz;
+  }
+  const int eq = ev - s;  // value = sig * 2^(eq - 23)
+  int code;
+  if (eq >= -6) {
+    code = ((eq + 7) << 3) + (int)rne_shift(sig, 20) - 8;  // a carry into 16 bumps the exponent
+    if (code > 0x7E) code = 0x7E;
+  } else {
+    code = (int)rne_shift(sig, 14 - eq);  // units of 2^-9; 8 is the smallest normal
+  }
+  return sign | (uint32_t)code;
+}
+
+// Value of an E4M3 (FN) code as fp32 (finite codes).
+__device__ __forceinline__ float e4m3_value(uint32_t c) {
+  const uint32_t e = (c >> 3) & 15u, m = c & 7u;
+  const float mag = e ? bits_f32(((e + 120u) << 23) | (m << 20)) : (float)m * 0.001953125f;
+  return (c & 0x80u) ? -mag : mag;
+}
+
+// E8M0 scale code as the fp32 whose exponent field is the code; the gfx950
+// scaled FP4 conversions read exactly that field.
+__device__ __forceinline__ float e8m0_as_scale(uint32_t c) { return bits_f32(c << 23); }
+
+}  // namespace b12x

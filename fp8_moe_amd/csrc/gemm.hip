@@ -1,0 +1,449 @@
+// Grouped expert GEMMs of the fused MoE on gfx950 MFMA (b12x README "What's in
+// here": the unified dynamic path runs routed experts on a persistent grid;
+// W4A16 dequantizes the FP4 weights inline with no activation-scale math;
+// w4a8_mx multiplies FP4 weights with dynamically quantized MXFP8
+// activations).  One kernel template serves
+//   GEMM1: h[row] = act(x[token(row)] . W13_e^T)   (SiLU-gated or ReLU^2)
+//   GEMM2: y[row] = h[row] . W2_e^T
+// over the routing tiles (expert, first row, rows).  A workgroup of 4 waves
+// owns 128 rows x 8 weight fragments (128 output columns); wave (wm, wn)
+// computes rows [64 wm, 64 wm + 64) x fragments [4 wn, 4 wn + 4).  The A rows
+// (bf16 or MXFP8 codes) go through double-buffered LDS; the packed FP4
+// fragments stream from global memory straight into registers.
+//   W4A16: each 1 KB fragment is four 16x16x32 bf16 MFMA operands; FP4 is
+//          turned into bf16 in registers (v_cvt_scalef32_pk_bf16_fp4 with the
+//          E8M0 scale, or fp32 conversion times the E4M3 scale for NVFP4; both
+//          products are exact in bf16).
+//   W4A8:  each fragment is one 16x16x128 scaled MFMA operand (fp8 A x fp4 B,
+//          one E8M0 scale per lane on each side).
+// The NVFP4 per-expert fp32 scale multiplies the fp32 accumulators.
+#include "device_common.h"
+
+namespace b12x {
+
+constexpr int kGemmThreads = 256;
+
+struct GemmParams {
+  const int32_t* tiles;
+  const int32_t* ntiles;
+  int n_ntiles;
+  int max_tiles;  // bounds that make a stale tile list harmless
+  int max_rows;
+  int E;
+  // A operand: bf16 rows (a16) or MXFP8 codes + scales (a8, as); GEMM1 maps
+  // a row to its token through sorted / k_top, GEMM2 reads rows directly.
+  const uint16_t* a16;
+  const uint8_t* a8;
+  const uint8_t* as;
+  int64_t a_stride;   // elements (bf16) or bytes (codes)
+  int64_t as_stride;  // bytes
+  const int32_t* sorted;
+  int k_top;
+  int64_t n_pairs;
+  int64_t K;
+  int KF;
+  // B operand (prepared weights)
+  const uint8_t* bcodes;
+  const uint8_t* bscales;
+  const float* bglobal;
+  int64_t b_codes_expert;
+  int64_t b_scales_expert;
+  int NF;
+  int KFS;
+  // outputs
+  uint16_t* h16;
+  uint8_t* h8;
+  uint8_t* hs;
+  int64_t h_stride;
+  int64_t hs_stride;
+  float* y;
+  int64_t y_stride;
+};
+
+enum { MODE_SILU = 1, MODE_RELU2 = 2, MODE_DOWN = 3 };
+
+__device__ __forceinline__ bf16x8 u32x4_as_bf16x8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  i32x4 v = {(int)a, (int)b, (int)c, (int)d};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// Eight FP4 codes (one dword, low nibble first) -> eight bf16 (as 4 dwords).
+template <int WF>
+__device__ __forceinline__ bf16x8 dequant8(uint32_t codes, float scale) {
+  if constexpr (WF == B12X_WEIGHT_MXFP4) {
+    const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 0);
+    const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 1);
+    const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 2);
+    const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 3);
+    return u32x4_as_bf16x8(__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1),
+                           __builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, p3));
+  } else {
+    uint32_t out[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      f32x2 v;
+      if (b == 0) v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 0);
+      if (b == 1) v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 1);
+      if (b == 2) v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 2);
+      if (b == 3) v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 3);
+      const uint32_t lo = f32_bits(v.x * scale), hi = f32_bits(v.y * scale);
+      out[b] = __builtin_amdgcn_perm(hi, lo, 0x07060302u);  // exact: <= 6 significant bits
+    }
+    return u32x4_as_bf16x8(out[0], out[1], out[2], out[3]);
+  }
+}
+
+template <int WF, int AF, int MODE>
+__global__ __launch_bounds__(kGemmThreads, 2) void moe_gemm_kernel(const GemmParams p) {
+  constexpr bool A8 = AF == B12X_ACT_MXFP8;
+  constexpr int ROWB = A8 ? 144 : 272;  // LDS bytes per A row: 128 K elements + 16 bytes of skew
+  __shared__ __attribute__((aligned(16))) uint8_t lds_a[2][kTileRows * ROWB];
+  __shared__ uint32_t lds_s[2][A8 ? kTileRows : 1];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int g = lane >> 4, r16 = lane & 15;
+  const int total = min(max(p.ntiles[0], 0), p.max_tiles) * p.n_ntiles;
+
+  for (int w = blockIdx.x; w < total; w += gridDim.x) {
+    const int tile = w / p.n_ntiles;
+    const int nt = w - tile * p.n_ntiles;
+    const int e = p.tiles[4 * tile], row0 = p.tiles[4 * tile + 1], nrows = p.tiles[4 * tile + 2];
+    if (e < 0 || e >= p.E || row0 < 0 || nrows <= 0 || nrows > kTileRows || row0 + nrows > p.max_rows) continue;
+    const int nmf = max(0, min(4, (nrows - 64 * wm + 15) / 16));
+    const int f0 = nt * kTileFrags + wn * 4;
+    const int nnf = max(0, min(4, p.NF - f0));
+    const uint8_t* bcodes = p.bcodes + (int64_t)e * p.b_codes_expert;
+    const uint8_t* bscales = p.bscales + (int64_t)e * p.b_scales_expert;
+    const float gsc = p.bglobal ? p.bglobal[e] : 1.0f;
+
+    // ---- A-row sources for this thread's loads
+    constexpr int LOADS = A8 ? 4 : 8;           // rows loaded per thread per K fragment
+    constexpr int CHUNKS = A8 ? 8 : 16;         // 16-byte chunks per 128-element row
+    const int c = tid % CHUNKS;
+    int64_t src_row[LOADS];
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int rr = tid / CHUNKS + (kGemmThreads / CHUNKS) * i;
+      int64_t sr = -1;
+      if (rr < nrows) {
+        if (p.sorted) {
+          const int pair = p.sorted[row0 + rr];
+          sr = (pair >= 0 && pair < p.n_pairs) ? pair / p.k_top : -1;
+        } else {
+          sr = row0 + rr;
+        }
+      }
+      src_row[i] = sr;
+    }
+    int64_t s_row = -1;  // A8: scale row loaded by threads 0..127
+    if (A8 && tid < kTileRows && tid < nrows) {
+      if (p.sorted) {
+        const int pair = p.sorted[row0 + tid];
+        s_row = (pair >= 0 && pair < p.n_pairs) ? pair / p.k_top : -1;
+      } else {
+        s_row = row0 + tid;
+      }
+    }
+    const int kblocks = (int)(p.K / 32);
+
+    uint4 ra[LOADS];
+    uint32_t rs = 0;
+    auto load_a = [&](int kf) {
+      const int64_t k0 = (int64_t)kf * kFragK + (A8 ? 16 : 8) * c;
+#pragma unroll
+      for (int i = 0; i < LOADS; ++i) {
+        ra[i] = make_uint4(0, 0, 0, 0);
+        if (src_row[i] >= 0 && k0 < p.K) {
+          if constexpr (A8) ra[i] = *(const uint4*)(p.a8 + src_row[i] * p.a_stride + k0);
+          else ra[i] = *(const uint4*)(p.a16 + src_row[i] * p.a_stride + k0);
+        }
+      }
+      if constexpr (A8) {
+        rs = 0x7F7F7F7Fu;
+        if (s_row >= 0) {
+          uint32_t word = 0;
+#pragma unroll
+          for (int b = 0; b < 4; ++b) {
+            const int blk = kf * 4 + b;
+            const uint32_t v = blk < kblocks ? p.as[s_row * p.as_stride + blk] : 127u;
+            word |= v << (8 * b);
+          }
+          rs = word;
+        }
+      }
+    };
+    auto store_a = [&](int buf) {
+#pragma unroll
+      for (int i = 0; i < LOADS; ++i) {
+        const int rr = tid / CHUNKS + (kGemmThreads / CHUNKS) * i;
+        *(uint4*)(&lds_a[buf][rr * ROWB + 16 * c]) = ra[i];
+      }
+      if constexpr (A8) {
+        if (tid < kTileRows) lds_s[buf][tid] = rs;
+      }
+    };
+    uint4 bq[4], bq_next[4];
+    uint32_t bs[4], bs_next[4];
+    auto load_b = [&](int kf, uint4* q, uint32_t* sc) {
+      const int sgrp = WF == B12X_WEIGHT_MXFP4 ? kf >> 2 : kf >> 1;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (j < nnf) {
+          const int f = f0 + j;
+          q[j] = *(const uint4*)(bcodes + ((int64_t)f * p.KF + kf) * kFragBytes + lane * 16);
+          sc[j] = *(const uint32_t*)(bscales + ((int64_t)f * p.KFS + sgrp) * kScaleGroupBytes + lane * 4);
+        }
+      }
+    };
+
+    f32x4 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    __syncthreads();  // the previous work item is done with LDS
+    load_a(0);
+    store_a(0);
+    load_b(0, bq, bs);
+
+    for (int kf = 0; kf < p.KF; ++kf) {
+      __syncthreads();
+      const int buf = kf & 1;
+      const bool more = kf + 1 < p.KF;
+      if (more) {
+        load_a(kf + 1);
+        load_b(kf + 1, bq_next, bs_next);
+      }
+      const uint8_t* la = lds_a[buf];
+      if constexpr (!A8) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          bf16x8 bfr[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            if (j < nnf) {
+              const uint32_t dw = s == 0 ? bq[j].x : s == 1 ? bq[j].y : s == 2 ? bq[j].z : bq[j].w;
+              float sc;
+              if constexpr (WF == B12X_WEIGHT_MXFP4) sc = e8m0_as_scale((bs[j] >> (8 * (kf & 3))) & 0xFFu);
+              else sc = e4m3_value((bs[j] >> (8 * (2 * (kf & 1) + (s >> 1)))) & 0xFFu);
+              bfr[j] = dequant8<WF>(dw, sc);
+            }
+          }
+#pragma unroll
+          for (int mf = 0; mf < 4; ++mf) {
+            if (mf < nmf) {
+              const int row = 64 * wm + 16 * mf + r16;
+              const uint4 av = *(const uint4*)(la + row * ROWB + 64 * g + 16 * s);
+              const bf16x8 afr = u32x4_as_bf16x8(av.x, av.y, av.z, av.w);
+#pragma unroll
+              for (int j = 0; j < 4; ++j)
+                if (j < nnf) acc[mf][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr, bfr[j], acc[mf][j], 0, 0, 0);
+            }
+          }
+        }
+      } else {
+        i32x8 bfr[4];
+        int sb[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          bfr[j] = i32x8{(int)bq[j].x, (int)bq[j].y, (int)bq[j].z, (int)bq[j].w, 0, 0, 0, 0};
+          sb[j] = (int)((bs[j] >> (8 * (kf & 3))) & 0xFFu);
+        }
+#pragma unroll
+        for (int mf = 0; mf < 4; ++mf) {
+          if (mf < nmf) {
+            const int row = 64 * wm + 16 * mf + r16;
+            const uint4 a0 = *(const uint4*)(la + row * ROWB + 16 * g);
+            const uint4 a1 = *(const uint4*)(la + row * ROWB + 64 + 16 * g);
+            const i32x8 afr = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w,
+                               (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+            const int sa = (int)((lds_s[buf][row] >> (8 * g)) & 0xFFu);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              if (j < nnf)
+                acc[mf][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(afr, bfr[j], acc[mf][j], 0, 4, 0, sa,
+                                                                               0, sb[j]);
+          }
+        }
+      }
+      if (more) {
+        store_a(buf ^ 1);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          bq[j] = bq_next[j];
+          bs[j] = bs_next[j];
+        }
+      }
+    }
+
+    // ---- epilogue: lane holds column r16 of each fragment, rows 4 g + i of each 16-row block
+    if constexpr (MODE == MODE_DOWN) {
+#pragma unroll
+      for (int mf = 0; mf < 4; ++mf) {
+        if (mf < nmf) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            if (j < nnf) {
+              const int col = 16 * (f0 + j) + r16;
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const int64_t row = row0 + 64 * wm + 16 * mf + 4 * g + i;
+                p.y[row * p.y_stride + col] = acc[mf][j][i] * gsc;
+              }
+            }
+          }
+        }
+      }
+    } else {
+      // activation values: gated -> 2 columns (pairs 0, 1); relu2 -> 4 columns
+      constexpr int NH = MODE == MODE_SILU ? 2 : 4;
+      const int nh = MODE == MODE_SILU ? nnf / 2 : nnf;
+      const int hcol0 = MODE == MODE_SILU ? 16 * (f0 / 2) : 16 * f0;
+#pragma unroll
+      for (int mf = 0; mf < 4; ++mf) {
+        if (mf < nmf) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int64_t row = row0 + 64 * wm + 16 * mf + 4 * g + i;
+            float hv[NH];
+#pragma unroll
+            for (int q = 0; q < NH; ++q) {
+              if constexpr (MODE == MODE_SILU) {
+                const float gt = acc[mf][2 * q][i] * gsc, up = acc[mf][2 * q + 1][i] * gsc;
+                hv[q] = gt / (1.0f + __expf(-gt)) * up;
+              } else {
+                const float z = acc[mf][q][i] * gsc;
+                hv[q] = z > 0.f ? z * z : 0.f;
+              }
+            }
+            if constexpr (!A8) {
+#pragma unroll
+              for (int q = 0; q < NH; ++q)
+                if (q < nh) p.h16[row * p.h_stride + hcol0 + 16 * q + r16] = (uint16_t)bf16_rne(hv[q]);
+            } else {
+              // MXFP8 blocks of 32 columns = column groups (0, 1) and (2, 3)
+#pragma unroll
+              for (int blk = 0; blk < NH / 2; ++blk) {
+                if (2 * blk < nh) {
+                  float m = fmaxf(fabsf(hv[2 * blk]), fabsf(hv[2 * blk + 1]));
+                  m = fmaxf(m, __shfl_xor(m, 1));
+                  m = fmaxf(m, __shfl_xor(m, 2));
+                  m = fmaxf(m, __shfl_xor(m, 4));
+                  m = fmaxf(m, __shfl_xor(m, 8));
+                  const int s = mx_scale_exp(f32_bits(m));
+                  const int64_t col = hcol0 + 32 * blk + r16;
+                  p.h8[row * p.h_stride + col] = (uint8_t)e4m3_encode_scaled(f32_bits(hv[2 * blk]), s);
+                  p.h8[row * p.h_stride + col + 16] = (uint8_t)e4m3_encode_scaled(f32_bits(hv[2 * blk + 1]), s);
+                  if (r16 == 0) p.hs[row * p.hs_stride + (hcol0 + 32 * blk) / 32] = (uint8_t)(s + 127);
+                }
+              }
+            }
+          }
+        }
+      }
+    }
+  }
+}
+
+static int g_cu_count[64];
+
+static int cu_count() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!g_cu_count[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    g_cu_count[dev] = n;
+  }
+  return g_cu_count[dev];
+}
+
+template <int WF, int AF, int MODE>
+static int launch_gemm_t(const GemmParams& p, int64_t max_work, hipStream_t s) {
+  const int64_t cap = (int64_t)cu_count() * 2;
+  const int64_t grid = max_work < cap ? max_work : cap;
+  if (grid <= 0) return 0;
+  hipLaunchKernelGGL((moe_gemm_kernel<WF, AF, MODE>), dim3((unsigned)grid), dim3(kGemmThreads), 0, s, p);
+  return (int)hipGetLastError();
+}
+
+template <int MODE>
+static int dispatch(const BindingImpl& b, const GemmParams& p, int64_t max_work, hipStream_t s) {
+  const bool nv = b.wfmt == B12X_WEIGHT_NVFP4, a8 = b.afmt == B12X_ACT_MXFP8;
+  if (a8) return launch_gemm_t<B12X_WEIGHT_MXFP4, B12X_ACT_MXFP8, MODE>(p, max_work, s);
+  if (nv) return launch_gemm_t<B12X_WEIGHT_NVFP4, B12X_ACT_BF16, MODE>(p, max_work, s);
+  return launch_gemm_t<B12X_WEIGHT_MXFP4, B12X_ACT_BF16, MODE>(p, max_work, s);
+}
+
+int launch_gemm1(const BindingImpl& b, hipStream_t s) {
+  GemmParams p = {};
+  const bool a8 = b.afmt == B12X_ACT_MXFP8;
+  p.tiles = b.tiles;
+  p.ntiles = b.ntiles;
+  p.max_tiles = (int)b.max_tiles;
+  p.max_rows = (int)b.max_rows;
+  p.E = b.E;
+  p.n_ntiles = (int)((b.nf13 + kTileFrags - 1) / kTileFrags);
+  p.a16 = b.a;
+  p.a8 = b.xq;
+  p.as = b.xs;
+  p.a_stride = a8 ? b.Hp : b.a_stride;
+  p.as_stride = b.Hp / 32;
+  p.sorted = b.sorted;
+  p.k_top = b.k;
+  p.n_pairs = b.T * b.k;
+  p.K = b.H;
+  p.KF = (int)b.kf13;
+  p.bcodes = b.w13_codes;
+  p.bscales = b.w13_scales;
+  p.bglobal = b.w13_global;
+  p.b_codes_expert = b.nf13 * b.kf13 * kFragBytes;
+  p.b_scales_expert = b.nf13 * b.kfs13 * kScaleGroupBytes;
+  p.NF = (int)b.nf13;
+  p.KFS = (int)b.kfs13;
+  p.h16 = (uint16_t*)b.h;
+  p.h8 = (uint8_t*)b.h;
+  p.hs = b.hs;
+  p.h_stride = b.Ip;
+  p.hs_stride = b.Ip / 32;
+  const int64_t max_work = b.max_tiles * p.n_ntiles;
+  return b.gated ? dispatch<MODE_SILU>(b, p, max_work, s) : dispatch<MODE_RELU2>(b, p, max_work, s);
+}
+
+int launch_gemm2(const BindingImpl& b, hipStream_t s) {
+  GemmParams p = {};
+  const bool a8 = b.afmt == B12X_ACT_MXFP8;
+  p.tiles = b.tiles;
+  p.ntiles = b.ntiles;
+  p.max_tiles = (int)b.max_tiles;
+  p.max_rows = (int)b.max_rows;
+  p.E = b.E;
+  p.n_ntiles = (int)((b.nf2 + kTileFrags - 1) / kTileFrags);
+  p.a16 = (const uint16_t*)b.h;
+  p.a8 = (const uint8_t*)b.h;
+  p.as = b.hs;
+  p.a_stride = b.Ip;
+  p.as_stride = b.Ip / 32;
+  p.sorted = nullptr;
+  p.k_top = b.k;
+  p.K = b.I;
+  p.KF = (int)b.kf2;
+  p.bcodes = b.w2_codes;
+  p.bscales = b.w2_scales;
+  p.bglobal = b.w2_global;
+  p.b_codes_expert = b.nf2 * b.kf2 * kFragBytes;
+  p.b_scales_expert = b.nf2 * b.kfs2 * kScaleGroupBytes;
+  p.NF = (int)b.nf2;
+  p.KFS = (int)b.kfs2;
+  p.y = b.y;
+  p.y_stride = b.H;
+  (void)a8;
+  const int64_t max_work = b.max_tiles * p.n_ntiles;
+  return dispatch<MODE_DOWN>(b, p, max_work, s);
+}
+
+}  // namespace b12x

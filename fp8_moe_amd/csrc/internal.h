@@ -1,0 +1,137 @@
+// Internal structures shared by the host runtime (api.cpp) and the kernels.
+// Not part of the C ABI.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/b12x_moe.h"
+
+typedef struct ihipStream_t* hipStream_t;
+
+namespace b12x {
+
+// ---- prepared weight layout -------------------------------------------------
+// A matrix with N output rows and K contraction elements is stored as
+// fragments of 16 rows x 128 K.  Fragment (f, kf) is 1024 bytes: lane l
+// (0..63) owns 16 bytes = the 32 FP4 codes of row (f*16 + l%16) at
+// K = 128*kf + 32*(l/16) + [0, 32), low nibble first.  That is exactly the
+// fp4 operand of one 16x16x128 scaled MFMA, and, read as four dwords, four
+// bf16 MFMA (16x16x32) operands once the K order inside a fragment is taken
+// as (lane group, dword) on both operands.  K beyond the matrix is zero.
+// Scales: one dword per lane and fragment group; MXFP4 packs the E8M0 codes
+// of 4 consecutive fragments (byte j = fragment 4q+j), NVFP4 the two E4M3
+// codes (the lane's two 16-element halves) of 2 consecutive fragments
+// (bytes 2j, 2j+1 = fragment 2q+j).  Gated w13 interleaves 16-row blocks:
+// fragment 2j = gate rows [16j, 16j+16), fragment 2j+1 = up rows of the same
+// h columns, so a gate/up pair always sits in one lane.
+constexpr int kFragK = 128;
+constexpr int kFragN = 16;
+constexpr int kFragBytes = 1024;
+constexpr int kScaleGroupBytes = 256;
+constexpr uint32_t kLayoutId = 0x4d4f4501u;  // "MOE", version 1
+
+// ---- grouped path ------------------------------------------------------------
+constexpr int kTileRows = 128;   // rows per GEMM tile (multiple of kRowPad)
+constexpr int kRowPad = 16;      // per-expert row padding = MFMA row block
+constexpr int kTileFrags = 8;    // 16-row weight fragments per GEMM tile (N = 128)
+constexpr int kRouteChunk = 1024;  // routing pairs per workgroup
+constexpr int kMaxExperts = 1024;
+
+struct MatrixLayout {
+  int64_t n = 0, k = 0;     // logical rows / contraction length
+  int64_t nf = 0, kf = 0;   // n/16, ceil(k/128)
+  int64_t kfs = 0;          // scale dword groups per fragment row
+  uint64_t codes_per_expert = 0, scales_per_expert = 0;  // bytes
+};
+
+inline MatrixLayout make_matrix_layout(int64_t n, int64_t k, int wfmt) {
+  MatrixLayout m;
+  m.n = n;
+  m.k = k;
+  m.nf = n / kFragN;
+  m.kf = (k + kFragK - 1) / kFragK;
+  m.kfs = wfmt == B12X_WEIGHT_MXFP4 ? (m.kf + 3) / 4 : (m.kf + 1) / 2;
+  m.codes_per_expert = (uint64_t)(m.nf * m.kf) * kFragBytes;
+  m.scales_per_expert = (uint64_t)(m.nf * m.kfs) * kScaleGroupBytes;
+  return m;
+}
+
+struct PlanImpl {
+  b12x_moe_caps caps;
+  int E = 0, H = 0, I = 0, k = 0;
+  int gated = 0, wfmt = 0, afmt = 0, act = 0;
+  int64_t max_tokens = 0;
+  MatrixLayout l13, l2;
+  int64_t Hp = 0, Ip = 0;  // H, I rounded up to 128
+  int64_t max_pairs = 0, max_rows = 0, max_tiles = 0, max_chunks = 0;
+  uint64_t off[16] = {0};   // scratch region offsets, indexed by Region
+  uint64_t len[16] = {0};   // scratch region sizes
+  uint64_t scratch_bytes = 0;
+};
+
+enum Region {
+  R_COUNTS = 1, R_OFFSETS = 2, R_POFF = 3, R_SORTED = 4, R_POS = 5, R_TILES = 6, R_NTILES = 7,
+  R_CHUNK = 8, R_XQ = 9, R_XS = 10, R_H = 11, R_HS = 12, R_Y = 13, R_COUNT_ = 14
+};
+
+// Everything a run needs, resolved at bind time (trivially copyable).
+struct BindingImpl {
+  uint32_t magic;
+  int32_t path;
+  int32_t E, H, I, k, gated, wfmt, afmt, act;
+  int64_t T, a_stride, out_stride;
+  int64_t Hp, Ip, max_rows, max_tiles;
+  int64_t nf13, kf13, kfs13, nf2, kf2, kfs2;
+  const uint16_t* a;
+  const int32_t* ids;
+  const float* tw;
+  uint16_t* out;
+  const uint8_t* w13_codes;
+  const uint8_t* w13_scales;
+  const float* w13_global;
+  const uint8_t* w2_codes;
+  const uint8_t* w2_scales;
+  const float* w2_global;
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* poff;
+  int32_t* sorted;
+  int32_t* pos;
+  int32_t* tiles;
+  int32_t* ntiles;
+  int32_t* chunk;
+  uint8_t* xq;
+  uint8_t* xs;
+  void* h;
+  uint8_t* hs;
+  float* y;
+};
+constexpr uint32_t kBindingMagic = 0xb12b1d01u;
+static_assert(sizeof(BindingImpl) <= sizeof(b12x_moe_binding), "binding does not fit the ABI struct");
+
+// ---- kernel launchers (kernels/*.hip); return hipError_t as int ----------------
+struct PackArgs {
+  const uint8_t* src_codes;
+  const uint8_t* src_scales;
+  uint8_t* dst_codes;
+  uint8_t* dst_scales;
+  int E;
+  MatrixLayout l;
+  int wfmt;
+  int gated_interleave;  // 1: rows are [gate; up] halves to interleave per 16
+};
+int launch_pack(const PackArgs& a, hipStream_t s);
+int launch_copy_f32(const float* src, float* dst, int n, hipStream_t s);
+int launch_route(const BindingImpl& b, hipStream_t s);
+int launch_quant_rows(const uint16_t* x, int64_t rows, int64_t cols, int64_t stride, uint8_t* codes,
+                      int64_t code_stride, uint8_t* scales, int64_t scale_stride, hipStream_t s);
+int launch_gemm1(const BindingImpl& b, hipStream_t s);
+int launch_gemm2(const BindingImpl& b, hipStream_t s);
+int launch_combine(const BindingImpl& b, hipStream_t s);
+const char* hip_error_name(int err);
+
+}  // namespace b12x
+
+// The opaque plan handle of the C ABI.
+struct b12x_moe_plan_impl : b12x::PlanImpl {};

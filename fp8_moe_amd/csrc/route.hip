@@ -1,0 +1,159 @@
+// Integer routing stage of the grouped path (b12x README "Using it": the op
+// binds caller-supplied topk_ids / topk_weights; "What's in here": routed
+// experts run on a persistent grid).  Produces, for pair p = t*k + j:
+// per-expert counts, exclusive offsets, offsets of rows padded per expert to
+// kRowPad, the stable expert-major permutation of the pairs (padding rows -1),
+// each pair's row and the list of (expert, first row, rows) GEMM tiles.
+// Three launches: per-chunk histograms, one scan workgroup, per-chunk scatter.
+// Integer atomics only touch LDS counters whose final values are
+// order-independent; every written position is deterministic.
+#include "device_common.h"
+
+namespace b12x {
+
+constexpr int kRouteThreads = 256;
+constexpr int kPairsPerThread = kRouteChunk / kRouteThreads;
+
+__device__ __forceinline__ int valid_expert(int e, int E) { return e >= 0 && e < E; }
+
+// chunk[c * E + e] = number of valid pairs of chunk c routed to e.
+__global__ __launch_bounds__(kRouteThreads) void route_count_kernel(const int32_t* __restrict__ ids, int64_t P,
+                                                                     int E, int32_t* __restrict__ chunk) {
+  __shared__ int hist[kMaxExperts];
+  for (int e = threadIdx.x; e < E; e += kRouteThreads) hist[e] = 0;
+  __syncthreads();
+  const int64_t base = (int64_t)blockIdx.x * kRouteChunk;
+  for (int i = 0; i < kPairsPerThread; ++i) {
+    const int64_t p = base + i * kRouteThreads + threadIdx.x;
+    if (p < P) {
+      const int e = ids[p];
+      if (valid_expert(e, E)) atomicAdd(&hist[e], 1);
+    }
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += kRouteThreads) chunk[(int64_t)blockIdx.x * E + e] = hist[e];
+}
+
+// Block-wide exclusive scan of one int per thread (blockDim.x = 1024).
+__device__ int block_exclusive_scan(int v, int* lds, int* total) {
+  const int tid = threadIdx.x;
+  lds[tid] = v;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int add = tid >= off ? lds[tid - off] : 0;
+    __syncthreads();
+    lds[tid] += add;
+    __syncthreads();
+  }
+  const int incl = lds[tid];
+  *total = lds[1023];
+  __syncthreads();
+  return incl - v;
+}
+
+// One workgroup of 1024 threads, thread e = expert e.
+__global__ __launch_bounds__(1024) void route_scan_kernel(int E, int n_chunks, int32_t* __restrict__ chunk,
+                                                          int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                                                          int32_t* __restrict__ poff, int32_t* __restrict__ sorted,
+                                                          int32_t* __restrict__ tiles, int32_t* __restrict__ ntiles) {
+  __shared__ int lds[1024];
+  const int e = threadIdx.x;
+  int cnt = 0;
+  if (e < E) {
+    for (int c = 0; c < n_chunks; ++c) {  // chunk counts -> exclusive per-chunk bases
+      const int h = chunk[(int64_t)c * E + e];
+      chunk[(int64_t)c * E + e] = cnt;
+      cnt += h;
+    }
+  }
+  const int padded = (cnt + kRowPad - 1) / kRowPad * kRowPad;
+  const int n_t = (padded + kTileRows - 1) / kTileRows;
+  int tot_cnt, tot_pad, tot_tiles;
+  const int off = block_exclusive_scan(cnt, lds, &tot_cnt);
+  const int poffe = block_exclusive_scan(padded, lds, &tot_pad);
+  const int toff = block_exclusive_scan(n_t, lds, &tot_tiles);
+  if (e < E) {
+    counts[e] = cnt;
+    offsets[e] = off;
+    poff[e] = poffe;
+    for (int r = poffe + cnt; r < poffe + padded; ++r) sorted[r] = -1;
+    for (int i = 0; i < n_t; ++i) {
+      const int r0 = poffe + i * kTileRows;
+      const int rows = min(kTileRows, padded - i * kTileRows);
+      *(int4*)(tiles + 4 * (toff + i)) = make_int4(e, r0, rows, 0);
+    }
+  }
+  if (e == 0) {
+    offsets[E] = tot_cnt;
+    poff[E] = tot_pad;
+    *(int4*)ntiles = make_int4(tot_tiles, tot_pad, 0, 0);
+  }
+}
+
+// Stable scatter: each wave takes 256 consecutive pairs of the chunk in four
+// rounds of 64; a lane's rank among equal experts of its round comes from
+// ballots (lanes below it with the same expert), and LDS counters carry the
+// count across rounds.  Waves are then ordered by a prefix over their counts.
+__global__ __launch_bounds__(kRouteThreads) void route_scatter_kernel(const int32_t* __restrict__ ids, int64_t P,
+                                                                       int E, const int32_t* __restrict__ chunk,
+                                                                       const int32_t* __restrict__ poff,
+                                                                       int32_t* __restrict__ sorted,
+                                                                       int32_t* __restrict__ pos) {
+  __shared__ int cnt[4][kMaxExperts];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  for (int i = threadIdx.x; i < 4 * kMaxExperts; i += kRouteThreads) (&cnt[0][0])[i] = 0;
+  __syncthreads();
+  const int64_t base = (int64_t)blockIdx.x * kRouteChunk + wave * 256;
+  int my_e[4], my_rank[4];
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int r = 0; r < 4; ++r) {
+    const int64_t p = base + r * 64 + lane;
+    int e = p < P ? ids[p] : -1;
+    const bool v = valid_expert(e, E);
+    if (!v) e = -1;
+    my_e[r] = e;
+    my_rank[r] = -1;
+    uint64_t pending = __ballot(v);
+    while (pending) {
+      const int leader = __builtin_ctzll(pending);
+      const int le = __shfl(e, leader);
+      const uint64_t same = __ballot(e == le);
+      const int before = cnt[wave][le];
+      if (e == le) my_rank[r] = before + __builtin_popcountll(same & below);
+      if (lane == leader) cnt[wave][le] = before + __builtin_popcountll(same);
+      pending &= ~same;
+    }
+  }
+  __syncthreads();
+  for (int r = 0; r < 4; ++r) {
+    const int64_t p = base + r * 64 + lane;
+    if (p >= P) continue;
+    const int e = my_e[r];
+    if (e < 0) {
+      pos[p] = -1;
+      continue;
+    }
+    int wbase = 0;
+    for (int w = 0; w < wave; ++w) wbase += cnt[w][e];
+    const int row = poff[e] + chunk[(int64_t)blockIdx.x * E + e] + wbase + my_rank[r];
+    sorted[row] = (int32_t)p;
+    pos[p] = row;
+  }
+}
+
+int launch_route(const BindingImpl& b, hipStream_t s) {
+  const int64_t P = b.T * b.k;
+  const int n_chunks = (int)((P + kRouteChunk - 1) / kRouteChunk);
+  hipLaunchKernelGGL(route_count_kernel, dim3(n_chunks), dim3(kRouteThreads), 0, s, b.ids, P, b.E, b.chunk);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return (int)e;
+  hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(1024), 0, s, b.E, n_chunks, b.chunk, b.counts, b.offsets,
+                     b.poff, b.sorted, b.tiles, b.ntiles);
+  e = hipGetLastError();
+  if (e != hipSuccess) return (int)e;
+  hipLaunchKernelGGL(route_scatter_kernel, dim3(n_chunks), dim3(kRouteThreads), 0, s, b.ids, P, b.E, b.chunk,
+                     b.poff, b.sorted, b.pos);
+  return (int)hipGetLastError();
+}
+
+}  // namespace b12x

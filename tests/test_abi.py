@@ -1,0 +1,132 @@
+"""The C-ABI library on the CPU: it loads, exports every function the header
+declares, and its host-side planning and binding validation behave as the
+header documents (no device work is launched by these calls)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    text = open(os.path.join(ROOT, "include", "b12x_moe.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(b12x_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    import fp8_moe_amd as fm
+    names = _declared_functions()
+    assert len(names) >= 14
+    lib = ctypes.CDLL(fm.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(fm.EXPORTED)
+
+
+def test_weight_plan_sizes():
+    import fp8_moe_amd as fm
+    wp = fm.plan_weights(128, 2048, 768, True, "mxfp4")
+    codes13 = 128 * 1536 * 2048 // 2
+    codes2 = 128 * 2048 * 768 // 2
+    assert wp.w13_scales_off - wp.w13_codes_off == codes13
+    assert wp.w2_scales_off - wp.w2_codes_off == codes2
+    assert wp.prepared_bytes >= codes13 + codes2 + (codes13 + codes2) // 16
+    assert wp.alignment == 256 and all(o % 256 == 0 for o in (wp.w13_scales_off, wp.w2_codes_off, wp.w2_scales_off))
+    nv = fm.plan_weights(8, 160, 96, False, "nvfp4")       # K = 160 pads to two 128-K fragments
+    assert nv.w13_scales_off - nv.w13_codes_off == 8 * (96 // 16) * 2 * 1024
+
+
+@pytest.mark.parametrize("E,H,I,fmt,err", [(8, 100, 128, "mxfp4", 2), (8, 256, 48, "nvfp4", 2),
+                                           (0, 256, 128, "mxfp4", 1), (2000, 256, 128, "mxfp4", 2)])
+def test_weight_plan_rejects(E, H, I, fmt, err):
+    import fp8_moe_amd as fm
+    with pytest.raises(fm.B12xError) as e:
+        fm.plan_weights(E, H, I, True, fmt)
+    assert e.value.status == err
+
+
+def test_support_matrix():
+    import fp8_moe_amd as fm
+    mx_g = fm.plan_weights(8, 256, 128, True, "mxfp4")
+    mx_r = fm.plan_weights(8, 256, 128, False, "mxfp4")
+    nv_g = fm.plan_weights(8, 256, 128, True, "nvfp4")
+    assert fm.is_supported(mx_g, 2, 16, "bf16", "silu")
+    assert fm.is_supported(mx_g, 2, 16, "mxfp8", "silu")
+    assert fm.is_supported(mx_r, 2, 16, "mxfp8", "relu2")
+    assert fm.is_supported(nv_g, 2, 16, "bf16", "silu")
+    assert not fm.is_supported(nv_g, 2, 16, "mxfp8", "silu")      # NVFP4 x MXFP8 is not built
+    assert not fm.is_supported(mx_g, 2, 16, "bf16", "relu2")      # gated weights need SiLU
+    assert not fm.is_supported(mx_g, 0, 16, "bf16", "silu")
+
+
+def test_scratch_grows_with_capacity_only():
+    import fp8_moe_amd as fm
+    wp = fm.plan_weights(128, 2048, 768, True, "mxfp4")
+    small = fm.plan(wp, 8, 32).scratch_specs()[0].bytes
+    big = fm.plan(wp, 8, 4096).scratch_specs()[0].bytes
+    assert 0 < small < big
+    p = fm.plan(wp, 8, 32)
+    for name in fm.REGIONS:
+        off, n = p.scratch_region(name)
+        assert off % 256 == 0 and off + n <= p.scratch_specs()[0].bytes
+
+
+class _FakeTensor:
+    """Stand-in device tensor for binding validation (bind never touches memory)."""
+
+    def __init__(self, ptr, shape, stride0, dtype, numel=0):
+        self.ptr, self.shape, self._s0, self.dtype, self._n = ptr, shape, stride0, dtype, numel
+
+    def data_ptr(self):
+        return self.ptr
+
+    def stride(self, i):
+        return self._s0
+
+    def numel(self):
+        return self._n
+
+    def is_contiguous(self):
+        return True
+
+
+def _bind_status(p, ex, T, a_ptr=0x10000, a_stride=256, out_ptr=0x900000, scratch_ptr=0x4000000, scratch_bytes=None,
+                 ids_ptr=0x200000, tw_ptr=0x300000):
+    import fp8_moe_amd as fm
+    if scratch_bytes is None:
+        scratch_bytes = p.scratch_specs()[0].bytes
+    b = fm.Binding()
+    return fm.lib().b12x_moe_bind(p.handle, ctypes.c_void_p(scratch_ptr), scratch_bytes, ctypes.byref(ex),
+                                  ctypes.c_void_p(a_ptr), T, a_stride, ctypes.c_void_p(ids_ptr),
+                                  ctypes.c_void_p(tw_ptr), ctypes.c_void_p(out_ptr), 256, ctypes.byref(b)), b
+
+
+def test_bind_validation_on_host():
+    import fp8_moe_amd as fm
+    wp = fm.plan_weights(8, 256, 128, True, "mxfp4")
+    p = fm.plan(wp, 2, 16)
+    ex = fm.Experts(wp, ctypes.c_void_p(0x7000000), wp.prepared_bytes)
+    st, b = _bind_status(p, ex, 16)
+    assert st == 0
+    assert fm.binding_query(b, "T") == 16 and fm.binding_query(b, "tile_rows") % fm.binding_query(b, "row_pad") == 0
+    assert _bind_status(p, ex, 17)[0] == 3                                   # capacity
+    assert _bind_status(p, ex, 16, a_ptr=0x10008)[0] == 5                    # misaligned a
+    assert _bind_status(p, ex, 16, scratch_ptr=0x4000080)[0] == 5            # misaligned scratch
+    assert _bind_status(p, ex, 16, scratch_bytes=1024)[0] == 4               # scratch too small
+    assert _bind_status(p, ex, 16, out_ptr=0x10000 + 512)[0] == 1            # out aliases a
+    assert _bind_status(p, ex, 16, a_stride=100)[0] == 1                     # stride < H
+    assert _bind_status(p, ex, 0, a_ptr=0, out_ptr=0, ids_ptr=0, tw_ptr=0)[0] == 0   # T = 0 needs no buffers
+    other = fm.plan_weights(8, 256, 128, True, "nvfp4")
+    ex2 = fm.Experts(other, ctypes.c_void_p(0x7000000), other.prepared_bytes)
+    assert _bind_status(p, ex2, 16)[0] == 6                                  # layout mismatch
+    assert fm.lib().b12x_moe_run(None, None) == 1
+
+
+def test_status_strings():
+    import fp8_moe_amd as fm
+    for s in range(8):
+        assert fm.lib().b12x_status_string(s)
+    assert fm.lib().b12x_status_string(99) == b"unknown status"

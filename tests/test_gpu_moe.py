@@ -1,0 +1,165 @@
+"""End-to-end parity of the fused MoE on the GPU against the fp64 oracle:
+every workload at its full size (sampled tokens where the oracle would take
+too long), small shapes with ragged tiles and ragged K, edge cases, run-to-run
+determinism, token-permutation invariance and graph replay."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from moe_cases import Problem, compare, small_workload
+
+pytestmark = pytest.mark.gpu
+
+_PROBLEMS = {}
+
+
+def problem(name, max_tokens):
+    key = (name, max_tokens)
+    if key not in _PROBLEMS:
+        _PROBLEMS.clear()
+        torch.cuda.empty_cache()
+        _PROBLEMS[key] = Problem(synth.WORKLOADS[name], max_tokens)
+    return _PROBLEMS[key]
+
+
+def _inputs(wl, T):
+    x = synth.make_x(wl, T, device="cuda")
+    ids, tw = synth.make_routing(wl, T, device="cuda")
+    return x, ids, tw
+
+
+# (workload, T, sampled token rows or None for all)
+FULL = [
+    ("tiny", 16, None),
+    ("decode", 1, None), ("decode", 8, None), ("decode", 32, [0, 13, 31]),
+    ("mixed", 1, None), ("mixed", 64, [0, 40, 63]), ("mixed", 512, [3, 511]), ("mixed", 2048, [0, 2047]),
+    ("prefill", 4096, [0, 4095]),
+    ("skew", 8192, [1, 8191]),
+]
+
+
+@pytest.mark.parametrize("name,T,rows", FULL)
+def test_workload_parity(name, T, rows):
+    print(f"parity {name} T={T} rows={rows}", flush=True)
+    wl = synth.WORKLOADS[name]
+    pr = problem(name, max(wl.tokens))
+    x, ids, tw = _inputs(wl, T)
+    out, _ = pr.run(x, ids, tw)
+    torch.cuda.synchronize()
+    ref = pr.oracle(x, ids, tw, rows)
+    got = out if rows is None else out[rows]
+    rel_fro, rel_max, ok = compare(got, ref)
+    print(f"  rel_fro={rel_fro:.3e} rel_max={rel_max:.3e}", flush=True)
+    assert ok, (rel_fro, rel_max)
+    assert torch.isfinite(out.float()).all()
+
+
+SMALL = [
+    # name, E, H, I, k, gated, wfmt, afmt, T
+    ("multi_tile", 2, 256, 128, 1, True, "mxfp4", "bf16", 300),
+    ("ragged_k_gated", 4, 160, 96, 2, True, "mxfp4", "bf16", 40),
+    ("ragged_k_nv", 4, 160, 96, 2, True, "nvfp4", "bf16", 40),
+    ("ragged_k_a8", 4, 160, 96, 2, False, "mxfp4", "mxfp8", 40),
+    ("a8_multi_tile", 3, 288, 224, 2, False, "mxfp4", "mxfp8", 400),
+    ("nv_relu2", 5, 256, 192, 3, False, "nvfp4", "bf16", 77),
+    ("mx_relu2", 5, 256, 192, 3, False, "mxfp4", "bf16", 77),
+    ("a8_gated", 6, 256, 128, 2, True, "mxfp4", "mxfp8", 50),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
+def test_small_shapes(case):
+    name, E, H, I, k, gated, wfmt, afmt, T = case
+    print(f"small {case}", flush=True)
+    wl = small_workload(name, E, H, I, k, gated, wfmt, afmt, x_lognormal=afmt == "mxfp8")
+    pr = Problem(wl, T, gen_device="cpu")
+    x, ids, tw = _inputs(wl, T)
+    out, _ = pr.run(x, ids, tw)
+    torch.cuda.synchronize()
+    rel_fro, rel_max, ok = compare(out, pr.oracle(x, ids, tw))
+    print(f"  rel_fro={rel_fro:.3e} rel_max={rel_max:.3e}", flush=True)
+    assert ok, (rel_fro, rel_max)
+
+
+def test_bad_and_duplicate_ids_and_strided_io():
+    wl = small_workload("edge", 8, 256, 128, 3)
+    pr = Problem(wl, 64, gen_device="cpu")
+    x, ids, tw = _inputs(wl, 64)
+    ids = ids.clone()
+    ids[0, 1] = -1
+    ids[1, 2] = 8
+    ids[2, 0] = 10 ** 6
+    ids[3, :] = 5
+    ids[4, 1] = ids[4, 0]
+    xs = torch.zeros(64, 256 + 40, dtype=torch.bfloat16, device="cuda")
+    xs[:, :256] = x
+    outs = torch.full((64, 256 + 24), 7.0, dtype=torch.bfloat16, device="cuda")
+    pr.run(xs[:, :256], ids, tw, outs[:, :256])
+    torch.cuda.synchronize()
+    rel_fro, rel_max, ok = compare(outs[:, :256], pr.oracle(x, ids, tw))
+    assert ok, (rel_fro, rel_max)
+    assert torch.all(outs[:, 256:] == 7.0)           # nothing written past H
+
+
+def test_zero_tokens_is_a_noop():
+    import fp8_moe_amd as fm
+    wl = small_workload("empty", 4, 256, 128, 2)
+    pr = Problem(wl, 8, gen_device="cpu")
+    x = torch.empty(0, 256, dtype=torch.bfloat16, device="cuda")
+    ids = torch.empty(0, 2, dtype=torch.int32, device="cuda")
+    tw = torch.empty(0, 2, dtype=torch.float32, device="cuda")
+    b, out = pr.model.bind(x, ids, tw)
+    fm.run(b)
+    torch.cuda.synchronize()
+    assert out.shape == (0, 256)
+
+
+def test_capacity_error():
+    import fp8_moe_amd as fm
+    wl = small_workload("cap", 4, 256, 128, 2)
+    pr = Problem(wl, 8, gen_device="cpu")
+    x, ids, tw = _inputs(wl, 9)
+    with pytest.raises(fm.B12xError) as e:
+        pr.model.bind(x, ids, tw)
+    assert e.value.status == 3
+
+
+@pytest.mark.parametrize("name", ["tiny", "mixed"])
+def test_deterministic_and_permutation_invariant(name):
+    wl = synth.WORKLOADS[name] if name == "tiny" else small_workload("perm", 16, 288, 224, 4, False, "mxfp4",
+                                                                      "mxfp8", x_lognormal=True)
+    T = 96
+    pr = Problem(wl, T, gen_device="cpu")
+    x, ids, tw = _inputs(wl, T)
+    a, _ = pr.run(x, ids, tw)
+    a = a.clone()
+    b, _ = pr.run(x, ids, tw)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    perm = torch.randperm(T, generator=torch.Generator().manual_seed(5)).cuda()
+    c, _ = pr.run(x[perm].contiguous(), ids[perm].contiguous(), tw[perm].contiguous())
+    assert torch.equal(a[perm].view(torch.int16), c.view(torch.int16))
+
+
+def test_graph_replay_matches_eager():
+    import fp8_moe_amd as fm
+    wl = synth.WORKLOADS["decode"]
+    pr = problem("decode", 32)
+    x, ids, tw = _inputs(wl, 8)
+    out = torch.empty(8, wl.H, dtype=torch.bfloat16, device="cuda")
+    b, _ = pr.model.bind(x, ids, tw, out)
+    fm.run(b)
+    torch.cuda.synchronize()
+    eager = out.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        fm.run(b, stream=s)
+    for i in range(3):
+        out.fill_(0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), i
+        _ = (x.float() * 2).sum()      # unrelated eager work between replays
