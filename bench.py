@@ -1,0 +1,320 @@
+"""Benchmark of the fused block-scaled-FP4 MoE on one MI355X.
+
+Headline workload: decode, MXFP4 weights x BF16 activations (W4A16),
+E=128, H=2048, I=768, top_k=8, SiLU-gated, one batch each of T = 1, 8 and 32
+tokens per step.  Metric: weight GB/s = touched-expert weight bytes (packed
+FP4 codes + block scales of every expert the batch routes to) / time.
+
+Method: C prepared copies of the weights (more than the 256 MB Infinity
+Cache holds) and S input sets rotate, so each call streams cold weights;
+S steps are captured in one graph and replayed (no host launch overhead in
+the timed region); timing with events around K steps after W warmup steps.
+The dominant kernel (GEMM1, gate/up + SiLU) is also timed launch by launch
+with event pairs on its stream for the roofline object.  Extra lines report
+prefill (NVFP4, T=4096) TFLOP/s and the W4A8 (MXFP8 x MXFP4, ReLU^2) T=1
+decode, and the CPU oracle's rate on a bounded sample.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extra] [--no-cpu]
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2516.6      # 256 CU x 2.4 GHz x 4096 FLOP/clk (dense)
+N_WEIGHT_COPIES = 5            # 5 x 323 MB > 256 MB Infinity Cache
+N_SETS = 10                    # input sets per graph (also the steps per replay)
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def _events():
+    import torch
+    return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+
+def touched_experts(ids, E):
+    ids = ids.reshape(-1).tolist()
+    return len({e for e in ids if 0 <= e < E})
+
+
+def build_decode(fm, synth, torch):
+    wl = synth.WORKLOADS["decode"]
+    Ts = wl.tokens
+    w = synth.make_weights(wl, device="cuda")
+    wp = fm.plan_weights(wl.E, wl.H, wl.I, wl.gated, wl.weight_format)
+    copies = [fm.prepare_weights(wp, w["w13_codes"], w["w13_scales"], w["w2_codes"], w["w2_scales"])
+              for _ in range(N_WEIGHT_COPIES)]
+    plan = fm.plan(wp, wl.k, max(Ts), wl.act_format, "silu")
+    scratch = fm.alloc_scratch(plan)
+    per_expert = wl.weight_bytes_per_expert()
+    w13_per_expert = wl.n13 * wl.H // 2 + wl.n13 * wl.H // wl.group
+    sets = {}
+    for T in Ts:
+        rows = []
+        for s in range(N_SETS):
+            x = synth.make_x(wl, T, device="cuda", salt=s)
+            ids, tw = synth.make_routing(wl, T, device="cuda", salt=s)
+            out = torch.empty(T, wl.H, dtype=torch.bfloat16, device="cuda")
+            copy = copies[(s * len(Ts) + Ts.index(T)) % N_WEIGHT_COPIES]   # reuse distance: 5 calls
+            b = fm.bind(plan, scratch, copy, x, ids, tw, out)
+            n_e = touched_experts(ids.cpu(), wl.E)
+            rows.append(dict(x=x, ids=ids, tw=tw, out=out, binding=b, experts=n_e, bytes=n_e * per_expert,
+                             w13_bytes=n_e * w13_per_expert))
+        sets[T] = rows
+    return wl, w, plan, scratch, copies, sets
+
+
+def capture(torch, fm, bindings, stream):
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for b in bindings:
+            fm.run(b, stream=stream)
+    return g
+
+
+def time_graph(torch, g, stream, reps):
+    e0, e1 = _events()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        e0.record(stream)
+        for _ in range(reps):
+            g.replay()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / 1e3  # seconds
+
+
+def time_stage_launches(torch, fm, bindings, stage, stream, repeats=3):
+    """Mean duration (s) of one stage's kernel, event pair around each launch.
+    The stages before it ran for every binding beforehand (valid routing)."""
+    for b in bindings:
+        fm.run(b, stream=stream)
+    pairs = []
+    with torch.cuda.stream(stream):
+        for _ in range(repeats):
+            for b in bindings:
+                e0, e1 = _events()
+                e0.record(stream)
+                fm.run_stage(b, stage, stream=stream)
+                e1.record(stream)
+                pairs.append((e0, e1))
+    torch.cuda.synchronize()
+    return sum(a.elapsed_time(b) for a, b in pairs) / len(pairs) / 1e3
+
+
+def cpu_baseline(wl, w_host, sets_host, budget_s=12.0):
+    """The fp64 oracle on the host: decode T=1 calls until ~budget_s seconds."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    from oracle import Weights, fused_moe
+    cores = len(os.sched_getaffinity(0))
+    weights = Weights(wl.weight_format, wl.gated, **w_host)
+    done_bytes, calls = 0, 0
+    t0 = time.perf_counter()
+    with threadpool_limits(limits=cores):
+        while True:
+            xb, ids, tw, nbytes = sets_host[calls % len(sets_host)]
+            fused_moe(xb, ids, tw, weights, act_format=wl.act_format)
+            done_bytes += nbytes
+            calls += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
+    dt = time.perf_counter() - t0
+    return {"value": done_bytes / dt / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": f"{calls} decode T=1 calls (E=128, H=2048, I=768, top_k=8, MXFP4 W4A16), "
+                      f"{dt:.1f} s; weight bytes of touched experts / wall time; BLAS limited to {cores} threads, "
+                      f"elementwise NumPy single-threaded",
+            "seconds_per_call": dt / calls}
+
+
+def bench_prefill(fm, synth, torch, stream, reps=10):
+    wl = synth.WORKLOADS["prefill"]
+    T = wl.tokens[0]
+    w = synth.make_weights(wl, device="cuda")
+    wp = fm.plan_weights(wl.E, wl.H, wl.I, wl.gated, wl.weight_format)
+    ex = fm.prepare_weights(wp, w["w13_codes"], w["w13_scales"], w["w2_codes"], w["w2_scales"],
+                            w["w13_global"], w["w2_global"])
+    del w
+    plan = fm.plan(wp, wl.k, T, wl.act_format, "silu")
+    scratch = fm.alloc_scratch(plan)
+    x = synth.make_x(wl, T, device="cuda")
+    ids, tw = synth.make_routing(wl, T, device="cuda")
+    out = torch.empty(T, wl.H, dtype=torch.bfloat16, device="cuda")
+    b = fm.bind(plan, scratch, ex, x, ids, tw, out)
+    for _ in range(2):
+        fm.run(b, stream=stream)
+    g = capture(torch, fm, [b], stream)
+    g.replay()
+    sec = time_graph(torch, g, stream, reps) / reps
+    flops = 6.0 * wl.H * wl.I * T * wl.k
+    stages = {st: time_stage_launches(torch, fm, [b], st, stream, repeats=3) * 1e6
+              for st in ("route", "gemm1", "gemm2", "combine")}
+    return {"T": T, "us": sec * 1e6, "tflops": flops / sec / 1e12,
+            "frac_bf16_peak": flops / sec / 1e12 / BF16_PEAK_TFLOPS, "stage_us": stages,
+            "gemm1_tflops": 4.0 * wl.H * wl.I * T * wl.k / (stages["gemm1"] * 1e-6) / 1e12,
+            "gemm2_tflops": 2.0 * wl.H * wl.I * T * wl.k / (stages["gemm2"] * 1e-6) / 1e12}
+
+
+def bench_mixed_t1(fm, synth, torch, stream, reps=50):
+    wl = synth.WORKLOADS["mixed"]
+    w = synth.make_weights(wl, device="cuda")
+    wp = fm.plan_weights(wl.E, wl.H, wl.I, wl.gated, wl.weight_format)
+    copies = [fm.prepare_weights(wp, w["w13_codes"], w["w13_scales"], w["w2_codes"], w["w2_scales"])
+              for _ in range(2)]   # 2 x 1.13 GB
+    del w
+    plan = fm.plan(wp, wl.k, 1, wl.act_format, "relu2")
+    scratch = fm.alloc_scratch(plan)
+    bs, nbytes = [], 0
+    for s in range(N_SETS):
+        x = synth.make_x(wl, 1, device="cuda", salt=s)
+        ids, tw = synth.make_routing(wl, 1, device="cuda", salt=s)
+        out = torch.empty(1, wl.H, dtype=torch.bfloat16, device="cuda")
+        bs.append((fm.bind(plan, scratch, copies[s % 2], x, ids, tw, out), x, ids, tw, out))
+        nbytes += touched_experts(ids.cpu(), wl.E) * wl.weight_bytes_per_expert()
+    g = capture(torch, fm, [t[0] for t in bs], stream)
+    g.replay()
+    sec = time_graph(torch, g, stream, reps) / (reps * N_SETS)
+    gbs = nbytes / N_SETS / sec / 1e9
+    return {"T": 1, "us": sec * 1e6, "weight_GBs": gbs, "frac_hbm": gbs / HBM_PEAK_GBS}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-extra", action="store_true", help="skip the prefill and W4A8 lines")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the fused MoE here is a "
+              f"single-GPU build and a multi-GPU figure is not produced.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import fp8_moe_amd as fm
+    import synth
+    torch.cuda.set_device(0)
+    stream = torch.cuda.Stream()
+
+    log("building decode workload")
+    wl, w, plan, scratch, copies, sets = build_decode(fm, synth, torch)
+    Ts = wl.tokens
+    # cpu baseline inputs (host copies) before the source weights go
+    w_host = synth.oracle_weights_kwargs(w) if not args.no_cpu else None
+    sets_host = [(row["x"].cpu().view(torch.int16).numpy().view("uint16"), row["ids"].cpu().numpy(),
+                  row["tw"].cpu().numpy(), row["bytes"]) for row in sets[1]]
+    del w
+
+    # warm everything once eagerly (first launches, lazy module loads)
+    for T in Ts:
+        for row in sets[T]:
+            fm.run(row["binding"], stream=stream)
+    torch.cuda.synchronize()
+
+    # one graph = N_SETS steps (a step = one call at each T); a second graph holds
+    # the remainder so that exactly --steps steps are timed
+    step_bindings = [sets[T][s]["binding"] for s in range(N_SETS) for T in Ts]
+    g_all = capture(torch, fm, step_bindings, stream)
+
+    def run_steps(n):
+        full, rem = divmod(n, N_SETS)
+        g_rem = capture(torch, fm, step_bindings[:rem * len(Ts)], stream) if rem else None
+        e0, e1 = _events()
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            e0.record(stream)
+            for _ in range(full):
+                g_all.replay()
+            if g_rem is not None:
+                g_rem.replay()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / 1e3
+
+    log("timing decode steps")
+    run_steps(max(args.warmup, 1))
+    steps = args.steps
+    elapsed = run_steps(steps)
+    ms_per_step = elapsed / steps * 1e3
+    bytes_per_step = sum(row["bytes"] for T in Ts for row in sets[T]) / N_SETS
+    value = bytes_per_step / (ms_per_step / 1e3) / 1e9
+
+    # per-T breakdown (graph of the N_SETS calls at one T)
+    per_t = {}
+    for T in Ts:
+        g = capture(torch, fm, [row["binding"] for row in sets[T]], stream)
+        g.replay()
+        reps = max(1, steps // N_SETS)
+        sec = time_graph(torch, g, stream, reps) / (reps * N_SETS)
+        nb = sum(row["bytes"] for row in sets[T]) / N_SETS
+        ne = sum(row["experts"] for row in sets[T]) / N_SETS
+        per_t[f"T{T}"] = {"us": sec * 1e6, "touched_experts": ne, "weight_MB": nb / 1e6,
+                          "weight_GBs": nb / sec / 1e9, "frac_hbm": nb / sec / 1e9 / HBM_PEAK_GBS,
+                          "tflops": 6.0 * wl.H * wl.I * T * wl.k / sec / 1e12}
+
+    # dominant kernel: the gate/up kernel (2/3 of the weight bytes), launch-by-launch events;
+    # small T runs the decode path (gate/up kernel "decode1"), larger T the grouped GEMM1
+    durs, w13b, durs2 = [], [], []
+    for T in Ts:
+        bl = [row["binding"] for row in sets[T]]
+        path = fm.binding_query(bl[0], "path")
+        st1, st2 = ("decode1", "decode2") if path == 2 else ("gemm1", "gemm2")
+        durs.append(time_stage_launches(torch, fm, bl, st1, stream, repeats=3))
+        durs2.append(time_stage_launches(torch, fm, bl, st2, stream, repeats=3))
+        w13b.append(sum(row["w13_bytes"] for row in sets[T]) / N_SETS)
+        per_t[f"T{T}"]["path"] = "decode" if path == 2 else "grouped"
+        per_t[f"T{T}"]["gate_up_kernel_us"] = durs[-1] * 1e6
+        per_t[f"T{T}"]["down_kernel_us"] = durs2[-1] * 1e6
+    avg_dur = sum(durs) / len(durs)
+    avg_bytes = sum(w13b) / len(w13b)
+    achieved = avg_bytes / avg_dur / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "kernel": "decode_kernel<MXFP4, BF16, SILU> (gate/up, decode path)",
+                "avg_launch_us": round(avg_dur * 1e6, 3),
+                "algorithmic_bytes_per_launch": round(avg_bytes),
+                "per_T_launch_us": {f"T{T}": round(d * 1e6, 3) for T, d in zip(Ts, durs)}}
+
+    result = {
+        "metric": "fused-MoE weight GB/s (decode T=1,8,32; MXFP4 W4A16)",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": max(args.warmup, 1),
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "decode: MXFP4 W4A16, E=128, H=2048, I=768, top_k=8, SiLU-gated, "
+                               "one batch each of T=1, 8, 32 per step, cold weights (5 rotating copies)",
+                   "global_batch": sum(Ts), "seq_len": 1, "parallelism": "none (1 GPU)"},
+        "roofline": roofline,
+        "per_T": per_t,
+    }
+    if not args.no_extra:
+        log("prefill line")
+        result["prefill"] = bench_prefill(fm, synth, torch, stream)
+        log("w4a8 line")
+        result["w4a8_mixed_T1"] = bench_mixed_t1(fm, synth, torch, stream)
+    if not args.no_cpu:
+        log("cpu oracle baseline")
+        result["cpu_baseline"] = cpu_baseline(wl, w_host, sets_host)
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

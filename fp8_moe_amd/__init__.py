@@ -26,7 +26,7 @@ LIB_PATH = os.path.join(_HERE, "libb12x_moe.so")
 WEIGHT_FORMATS = {"mxfp4": 1, "nvfp4": 2}
 ACT_FORMATS = {"bf16": 1, "mxfp8": 2}
 ACTIVATIONS = {"silu": 1, "relu2": 2}
-STAGES = {"route": 1, "quant_x": 2, "gemm1": 3, "gemm2": 4, "combine": 5}
+STAGES = {"route": 1, "quant_x": 2, "gemm1": 3, "gemm2": 4, "combine": 5, "decode1": 6, "decode2": 7}
 QUERIES = {"path": 1, "tile_rows": 2, "row_pad": 3, "T": 4, "num_stages": 5}
 REGIONS = {"counts": 1, "offsets": 2, "padded_offsets": 3, "sorted": 4, "pos": 5, "tiles": 6, "ntiles": 7}
 
@@ -68,7 +68,8 @@ class Experts(ctypes.Structure):
 
 class Caps(ctypes.Structure):
     _fields_ = [("struct_size", ctypes.c_uint32), ("top_k", ctypes.c_int32), ("weights", WeightPlan),
-                ("act_format", ctypes.c_int32), ("activation", ctypes.c_int32), ("max_tokens", ctypes.c_int64)]
+                ("act_format", ctypes.c_int32), ("activation", ctypes.c_int32), ("decode_max_pairs", ctypes.c_int32),
+                ("max_tokens", ctypes.c_int64)]
 
 
 class ScratchSpec(ctypes.Structure):
@@ -178,8 +179,11 @@ def prepare_weights(wplan, w13_codes, w13_scales, w2_codes, w2_scales, w13_globa
 
 # ---------------------------------------------------------------- op plan
 
-def make_caps(wplan, top_k, max_tokens, act_format="bf16", activation="silu"):
-    return Caps(ctypes.sizeof(Caps), top_k, wplan, ACT_FORMATS[act_format], ACTIVATIONS[activation], max_tokens)
+def make_caps(wplan, top_k, max_tokens, act_format="bf16", activation="silu", decode_max_pairs=0):
+    """decode_max_pairs: largest T*k routed to the decode path (0: library
+    default, negative: always use the grouped path)."""
+    return Caps(ctypes.sizeof(Caps), top_k, wplan, ACT_FORMATS[act_format], ACTIVATIONS[activation],
+                decode_max_pairs, max_tokens)
 
 
 def is_supported(wplan, top_k, max_tokens, act_format="bf16", activation="silu"):
@@ -214,8 +218,8 @@ class Plan:
             self._h = None
 
 
-def plan(wplan, top_k, max_tokens, act_format="bf16", activation="silu"):
-    caps = make_caps(wplan, top_k, max_tokens, act_format, activation)
+def plan(wplan, top_k, max_tokens, act_format="bf16", activation="silu", decode_max_pairs=0):
+    caps = make_caps(wplan, top_k, max_tokens, act_format, activation, decode_max_pairs)
     h = ctypes.c_void_p()
     _check(_lib.b12x_moe_plan(ctypes.byref(caps), ctypes.byref(h)))
     return Plan(h, caps)
@@ -277,13 +281,14 @@ class FusedMoE:
     """Convenience holder for one prepared model layer: weights plan,
     prepared experts and an op plan at a given capacity."""
 
-    def __init__(self, E, H, I, top_k, weight_format, act_format, activation, max_tokens, weights, stream=None):
+    def __init__(self, E, H, I, top_k, weight_format, act_format, activation, max_tokens, weights, stream=None,
+                 decode_max_pairs=0):
         gated = activation == "silu"
         self.wplan = plan_weights(E, H, I, gated, weight_format)
         self.experts = prepare_weights(self.wplan, weights["w13_codes"], weights["w13_scales"],
                                        weights["w2_codes"], weights["w2_scales"], weights.get("w13_global"),
                                        weights.get("w2_global"), stream=stream)
-        self.plan = plan(self.wplan, top_k, max_tokens, act_format, activation)
+        self.plan = plan(self.wplan, top_k, max_tokens, act_format, activation, decode_max_pairs)
         self.scratch = alloc_scratch(self.plan, weights["w13_codes"].device)
         self.H = H
 

@@ -14,7 +14,7 @@ OUT = os.path.join(HERE, "libb12x_moe.so")
 BUILD = os.path.join(HERE, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["api.cpp", "pack.hip", "route.hip", "quant.hip", "gemm.hip", "combine.hip"]
+SOURCES = ["api.cpp", "pack.hip", "route.hip", "quant.hip", "gemm.hip", "combine.hip", "decode.hip"]
 
 # -packed-fp32-ops: keep hipcc from emitting packed fp32 VALU ops.
 FLAGS = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-function",

@@ -199,6 +199,11 @@ b12x_status b12x_moe_plan(const b12x_moe_caps* caps, b12x_moe_plan_t* out) {
   p->max_rows = (int64_t)align_up(p->max_rows, kRowPad);
   p->max_tiles = (p->max_rows + kTileRows - 1) / kTileRows + p->E;
   p->max_chunks = (p->max_pairs + kRouteChunk - 1) / kRouteChunk;
+  // decode path: every wave keeps its K fragments in registers (<= 8 of them)
+  const bool decode_ok = (p->l13.kf + 3) / 4 <= kDecodeMaxKPerWave && (p->l2.kf + 3) / 4 <= kDecodeMaxKPerWave;
+  int dmax = caps->decode_max_pairs == 0 ? kDecodePairs : caps->decode_max_pairs;
+  if (dmax > kDecodePairs) dmax = kDecodePairs;
+  p->decode_max_pairs = (decode_ok && dmax > 0) ? dmax : 0;
   const bool a8 = p->afmt == B12X_ACT_MXFP8;
   uint64_t len[R_COUNT_] = {0};
   len[R_COUNTS] = 4ull * p->E;
@@ -277,7 +282,7 @@ b12x_status b12x_moe_bind(b12x_moe_plan_t p, void* scratch, uint64_t scratch_byt
   BindingImpl b;
   memset(&b, 0, sizeof(b));
   b.magic = kBindingMagic;
-  b.path = 1;
+  b.path = (T > 0 && T * p->k <= p->decode_max_pairs) ? 2 : 1;
   b.E = p->E; b.H = p->H; b.I = p->I; b.k = p->k;
   b.gated = p->gated; b.wfmt = p->wfmt; b.afmt = p->afmt; b.act = p->act;
   b.T = T; b.a_stride = a_stride; b.out_stride = out_stride;
@@ -320,18 +325,27 @@ static b12x_status get_binding(const b12x_moe_binding* binding, BindingImpl* b) 
   return B12X_OK;
 }
 
+static bool stage_in_path(const BindingImpl& b, int stage) {
+  if (stage == B12X_STAGE_QUANT_X) return b.afmt == B12X_ACT_MXFP8;
+  if (b.path == 2) return stage == B12X_STAGE_DECODE1 || stage == B12X_STAGE_DECODE2;
+  return stage >= B12X_STAGE_ROUTE && stage <= B12X_STAGE_COMBINE;
+}
+
 static b12x_status run_stage(const BindingImpl& b, int stage, hipStream_t s) {
+  if (stage < B12X_STAGE_ROUTE || stage > B12X_STAGE_DECODE2)
+    return fail(B12X_ERR_INVALID_ARGUMENT, "unknown stage %d", stage);
+  if (!stage_in_path(b, stage))
+    return fail(B12X_ERR_UNSUPPORTED, "stage %d is not part of this binding's path (%s)", stage,
+                b.path == 2 ? "decode" : "grouped");
   int err = 0;
   switch (stage) {
     case B12X_STAGE_ROUTE: err = launch_route(b, s); break;
-    case B12X_STAGE_QUANT_X:
-      if (b.afmt != B12X_ACT_MXFP8) return fail(B12X_ERR_UNSUPPORTED, "QUANT_X runs only with MXFP8 activations");
-      err = launch_quant_rows(b.a, b.T, b.H, b.a_stride, b.xq, b.Hp, b.xs, b.Hp / 32, s);
-      break;
+    case B12X_STAGE_QUANT_X: err = launch_quant_rows(b.a, b.T, b.H, b.a_stride, b.xq, b.Hp, b.xs, b.Hp / 32, s); break;
     case B12X_STAGE_GEMM1: err = launch_gemm1(b, s); break;
     case B12X_STAGE_GEMM2: err = launch_gemm2(b, s); break;
     case B12X_STAGE_COMBINE: err = launch_combine(b, s); break;
-    default: return fail(B12X_ERR_INVALID_ARGUMENT, "unknown stage %d", stage);
+    case B12X_STAGE_DECODE1: err = launch_decode1(b, s); break;
+    case B12X_STAGE_DECODE2: err = launch_decode2(b, s); break;
   }
   if (err) return hip_fail(err, "kernel launch");
   return B12X_OK;
@@ -351,10 +365,13 @@ b12x_status b12x_moe_run(const b12x_moe_binding* binding, void* stream) {
   if (st) return st;
   if (b.T == 0) return B12X_OK;
   hipStream_t s = (hipStream_t)stream;
-  const int stages[5] = {B12X_STAGE_ROUTE, B12X_STAGE_QUANT_X, B12X_STAGE_GEMM1, B12X_STAGE_GEMM2,
-                         B12X_STAGE_COMBINE};
-  for (int i = 0; i < 5; ++i) {
-    if (stages[i] == B12X_STAGE_QUANT_X && b.afmt != B12X_ACT_MXFP8) continue;
+  static const int grouped[5] = {B12X_STAGE_ROUTE, B12X_STAGE_QUANT_X, B12X_STAGE_GEMM1, B12X_STAGE_GEMM2,
+                                 B12X_STAGE_COMBINE};
+  static const int decode[3] = {B12X_STAGE_QUANT_X, B12X_STAGE_DECODE1, B12X_STAGE_DECODE2};
+  const int* stages = b.path == 2 ? decode : grouped;
+  const int n = b.path == 2 ? 3 : 5;
+  for (int i = 0; i < n; ++i) {
+    if (!stage_in_path(b, stages[i])) continue;
     st = run_stage(b, stages[i], s);
     if (st) return st;
   }
@@ -371,7 +388,7 @@ b12x_status b12x_moe_binding_query(const b12x_moe_binding* binding, int32_t what
     case B12X_QUERY_TILE_ROWS: *value = kTileRows; break;
     case B12X_QUERY_ROW_PAD: *value = kRowPad; break;
     case B12X_QUERY_T: *value = b.T; break;
-    case B12X_QUERY_NUM_STAGES: *value = b.afmt == B12X_ACT_MXFP8 ? 5 : 4; break;
+    case B12X_QUERY_NUM_STAGES: *value = (b.path == 2 ? 2 : 4) + (b.afmt == B12X_ACT_MXFP8 ? 1 : 0); break;
     default: return fail(B12X_ERR_INVALID_ARGUMENT, "unknown query %d", what);
   }
   return B12X_OK;

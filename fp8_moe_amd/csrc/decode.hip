@@ -1,0 +1,605 @@
+// Small-batch decode path of the fused MoE (b12x README "What's in here": the
+// micro-kernel decode path of fused_moe).  For T*k <= kDecodePairs it replaces
+// the routing buffers and the grouped GEMMs with two launches in which every
+// touched expert's weights are read exactly once:
+//   D1 (gate/up): workgroup = (touched-expert slot, group of FR weight
+//      fragments).  Each workgroup finds its expert and that expert's pairs
+//      (stable by pair id) from topk_ids in LDS, its 4 waves split K, issue
+//      every fragment load and activation load up front, run MFMAs and add
+//      their partial sums in LDS in a fixed wave order; the activation
+//      (SiLU-gated or ReLU^2) then writes h by pair id (bf16, or MXFP8 codes
+//      and scales for W4A8).
+//   D2 (down + combine): workgroup = one 16-column fragment of the output,
+//      over all touched experts.  Its 8 waves take the experts round robin and
+//      stream (expert, row chunk, K fragment) steps through a register ring of
+//      DEPTH outstanding loads; each finished row chunk leaves y rows (by pair)
+//      in LDS; the workgroup then combines out[t] = sum_j w[t,j] * y[t*k+j]
+//      in ascending slot order and rounds once to bf16.  No atomics, no
+//      cross-workgroup traffic: the result does not depend on scheduling.
+#include "device_common.h"
+
+namespace b12x {
+
+constexpr int kDecThreads = 256;
+
+struct DecodeParams {
+  const int32_t* ids;
+  const float* tw;
+  int T, k, E, P;
+  // A operand: bf16 rows or MXFP8 codes + scales, indexed by token (D1) or pair (D2)
+  const uint16_t* a16;
+  const uint8_t* a8;
+  const uint8_t* as;
+  int64_t a_stride;   // elements (bf16) or bytes (codes)
+  int64_t as_stride;  // bytes
+  int a_by_token;
+  int64_t K;
+  int KF;
+  // B operand (prepared weights)
+  const uint8_t* bcodes;
+  const uint8_t* bscales;
+  const float* bglobal;
+  int64_t b_codes_expert, b_scales_expert;
+  int NF, KFS;
+  int n_groups;  // fragment groups per expert
+  // D1 outputs
+  uint16_t* h16;
+  uint8_t* h8;
+  uint8_t* hs;
+  int64_t h_stride, hs_stride;
+  // D2 output
+  uint16_t* out;
+  int64_t out_stride;
+};
+
+enum { DMODE_SILU = 1, DMODE_RELU2 = 2 };
+
+struct DecodeRoute {
+  int e;          // expert of this workgroup's slot, or -1
+  int m;          // pairs routed to e
+  int n_touched;  // distinct valid experts
+};
+
+// Expert of slot `slot` (slot-th smallest distinct valid id) and its pairs in
+// ascending pair order, from topk_ids held in LDS.  All threads call it.
+__device__ DecodeRoute decode_route(const DecodeParams& p, int slot, int* s_ids, uint32_t* s_bits, int* s_rows,
+                                    int* s_info) {
+  const int tid = threadIdx.x;
+  const int words = (p.E + 31) >> 5;
+  for (int i = tid; i < words; i += kDecThreads) s_bits[i] = 0;
+  __syncthreads();
+  for (int q = tid; q < p.P; q += kDecThreads) {
+    const int e = p.ids[q];
+    const bool v = e >= 0 && e < p.E;
+    s_ids[q] = v ? e : -1;
+    if (v) atomicOr(&s_bits[e >> 5], 1u << (e & 31));
+  }
+  __syncthreads();
+  if (tid < 64) {  // wave 0: prefix popcount over the bitmap
+    int before = 0, found = -1;
+    for (int base = 0; base < words; base += 64) {
+      const int w = base + tid;
+      const uint32_t bits = w < words ? s_bits[w] : 0u;
+      const int c = __builtin_popcount(bits);
+      int incl = c;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int t = __shfl_up(incl, off);
+        if (tid >= off) incl += t;
+      }
+      const int excl = before + incl - c;
+      if (slot >= excl && slot < excl + c) {
+        uint32_t b = bits;
+        for (int r = slot - excl; r > 0; --r) b &= b - 1;  // drop the lower set bits
+        found = w * 32 + __builtin_ctz(b);
+      }
+      before += __shfl(incl, 63);
+    }
+    const uint64_t has = __ballot(found >= 0);
+    const int e = has ? __shfl(found, __builtin_ctzll(has)) : -1;
+    if (tid == 0) {
+      s_info[0] = e;
+      s_info[1] = before;
+    }
+  }
+  __syncthreads();
+  const int e = s_info[0];
+  DecodeRoute r;
+  r.e = e;
+  r.n_touched = s_info[1];
+  r.m = 0;
+  if (e < 0) return r;
+  // stable list of e's pairs: ballots per wave, waves ordered by a prefix
+  const int wave = tid >> 6, lane = tid & 63;
+  const uint64_t below = lane ? (~0ull >> (64 - lane)) : 0ull;
+  int total = 0;
+  for (int base = 0; base < p.P; base += kDecThreads) {
+    const int q = base + tid;
+    const bool hit = q < p.P && s_ids[q] == e;
+    const uint64_t bal = __ballot(hit);
+    if (lane == 0) s_info[4 + wave] = __builtin_popcountll(bal);
+    __syncthreads();
+    int off = total;
+    for (int w = 0; w < wave; ++w) off += s_info[4 + w];
+    if (hit) s_rows[off + __builtin_popcountll(bal & below)] = q;
+    total += s_info[4] + s_info[5] + s_info[6] + s_info[7];
+    __syncthreads();
+  }
+  r.m = total;
+  return r;
+}
+
+template <int WF, int AF, int MODE, int FR, int KW>
+__global__ __launch_bounds__(kDecThreads) void decode_kernel(const DecodeParams p) {
+  constexpr bool A8 = AF == B12X_ACT_MXFP8;
+  __shared__ int s_ids[kDecodePairs];
+  __shared__ int s_rows[kDecodePairs];
+  __shared__ uint32_t s_bits[kMaxExperts / 32];
+  __shared__ int s_info[8];
+  __shared__ f32x4 s_red[4][FR][64];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int g = lane >> 4, r16 = lane & 15;
+  const int slot = blockIdx.x / p.n_groups, grp = blockIdx.x % p.n_groups;
+
+  const DecodeRoute rt = decode_route(p, slot, s_ids, s_bits, s_rows, s_info);
+  if (rt.e < 0) return;
+  const int e = rt.e;
+
+  // ---- this wave's K fragments and the workgroup's weight fragments
+  const int kper = (p.KF + 3) / 4;
+  const int kb = wave * kper, ke = min(p.KF, kb + kper);
+  const int f0 = grp * FR;
+  const uint8_t* bcodes = p.bcodes + (int64_t)e * p.b_codes_expert;
+  const uint8_t* bscales = p.bscales + (int64_t)e * p.b_scales_expert;
+  uint4 bq[FR][KW];
+  uint32_t bs[FR][KW];
+#pragma unroll
+  for (int j = 0; j < FR; ++j) {
+#pragma unroll
+    for (int i = 0; i < KW; ++i) {
+      const int kf = kb + i, f = f0 + j;
+      if (kf < ke && f < p.NF) {
+        bq[j][i] = *(const uint4*)(bcodes + ((int64_t)f * p.KF + kf) * kFragBytes + lane * 16);
+        const int sg = WF == B12X_WEIGHT_MXFP4 ? kf >> 2 : kf >> 1;
+        bs[j][i] = *(const uint32_t*)(bscales + ((int64_t)f * p.KFS + sg) * kScaleGroupBytes + lane * 4);
+      } else {
+        bq[j][i] = make_uint4(0, 0, 0, 0);
+        bs[j][i] = 0;
+      }
+    }
+  }
+  const float gsc = p.bglobal ? p.bglobal[e] : 1.0f;
+
+  for (int r0 = 0; r0 < rt.m; r0 += 16) {
+    // ---- A rows: lane (r16, g) owns row r0 + r16
+    const int rr = r0 + r16;
+    int64_t src = -1;
+    if (rr < rt.m) src = p.a_by_token ? s_rows[rr] / p.k : s_rows[rr];
+    f32x4 acc[FR];
+#pragma unroll
+    for (int j = 0; j < FR; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (!A8) {
+      uint4 av[KW][4];
+#pragma unroll
+      for (int i = 0; i < KW; ++i) {
+        const int kf = kb + i;
+        const int64_t k0 = (int64_t)kf * kFragK + 32 * g;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) av[i][s] = make_uint4(0, 0, 0, 0);
+        if (kf < ke && src >= 0 && k0 < p.K) {
+          const uint4* ap = (const uint4*)(p.a16 + src * p.a_stride + k0);
+#pragma unroll
+          for (int s = 0; s < 4; ++s) av[i][s] = ap[s];
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < KW; ++i) {
+        const int kf = kb + i;
+        if (kf < ke) {
+#pragma unroll
+          for (int s = 0; s < 4; ++s) {
+            const bf16x8 afr = __builtin_bit_cast(bf16x8, av[i][s]);
+#pragma unroll
+            for (int j = 0; j < FR; ++j) {
+              const uint4 q = bq[j][i];
+              const uint32_t dw = s == 0 ? q.x : s == 1 ? q.y : s == 2 ? q.z : q.w;
+              float sc;
+              if constexpr (WF == B12X_WEIGHT_MXFP4) sc = e8m0_as_scale((bs[j][i] >> (8 * (kf & 3))) & 0xFFu);
+              else sc = e4m3_value((bs[j][i] >> (8 * (2 * (kf & 1) + (s >> 1)))) & 0xFFu);
+              acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr, dequant8_bf16<WF>(dw, sc), acc[j], 0, 0, 0);
+            }
+          }
+        }
+      }
+    } else {
+      uint4 a0[KW], a1[KW];
+      int sa[KW];
+      const int kblocks = (int)(p.K / 32);
+#pragma unroll
+      for (int i = 0; i < KW; ++i) {
+        const int kf = kb + i;
+        const int64_t k0 = (int64_t)kf * kFragK;
+        a0[i] = make_uint4(0, 0, 0, 0);
+        a1[i] = make_uint4(0, 0, 0, 0);
+        sa[i] = 127;
+        if (kf < ke && src >= 0) {
+          const uint8_t* ap = p.a8 + src * p.a_stride + k0;
+          if (k0 + 16 * g < p.K) a0[i] = *(const uint4*)(ap + 16 * g);
+          if (k0 + 64 + 16 * g < p.K) a1[i] = *(const uint4*)(ap + 64 + 16 * g);
+          if (4 * kf + g < kblocks) sa[i] = p.as[src * p.as_stride + 4 * kf + g];
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < KW; ++i) {
+        const int kf = kb + i;
+        if (kf < ke) {
+          const i32x8 afr = {(int)a0[i].x, (int)a0[i].y, (int)a0[i].z, (int)a0[i].w,
+                             (int)a1[i].x, (int)a1[i].y, (int)a1[i].z, (int)a1[i].w};
+#pragma unroll
+          for (int j = 0; j < FR; ++j) {
+            const uint4 q = bq[j][i];
+            const i32x8 bfr = {(int)q.x, (int)q.y, (int)q.z, (int)q.w, 0, 0, 0, 0};
+            const int sb = (int)((bs[j][i] >> (8 * (kf & 3))) & 0xFFu);
+            acc[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(afr, bfr, acc[j], 0, 4, 0, sa[i], 0, sb);
+          }
+        }
+      }
+    }
+    // ---- split-K partial sums, added in wave order
+#pragma unroll
+    for (int j = 0; j < FR; ++j) s_red[wave][j][lane] = acc[j];
+    __syncthreads();
+    if (wave == 0) {
+      f32x4 v[FR];
+#pragma unroll
+      for (int j = 0; j < FR; ++j) {
+        v[j] = s_red[0][j][lane];
+#pragma unroll
+        for (int w = 1; w < 4; ++w) v[j] += s_red[w][j][lane];
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = r0 + 4 * g + i;
+        const bool live = row < rt.m;
+        const int64_t pr = live ? s_rows[row] : 0;
+        {
+          constexpr int NH = MODE == DMODE_SILU ? FR / 2 : FR;  // h column blocks of 16
+          float hv[NH];
+#pragma unroll
+          for (int q = 0; q < NH; ++q) {
+            if constexpr (MODE == DMODE_SILU) {
+              const float gt = v[2 * q][i] * gsc, up = v[2 * q + 1][i] * gsc;
+              hv[q] = gt / (1.0f + __expf(-gt)) * up;
+            } else {
+              const float z = v[q][i] * gsc;
+              hv[q] = z > 0.f ? z * z : 0.f;
+            }
+          }
+          const int hcol0 = MODE == DMODE_SILU ? 16 * (f0 / 2) : 16 * f0;
+          const int nh = MODE == DMODE_SILU ? max(0, min(NH, (p.NF - f0) / 2)) : max(0, min(NH, p.NF - f0));
+          if constexpr (!A8) {
+#pragma unroll
+            for (int q = 0; q < NH; ++q)
+              if (live && q < nh) p.h16[pr * p.h_stride + hcol0 + 16 * q + r16] = (uint16_t)bf16_rne(hv[q]);
+          } else {
+#pragma unroll
+            for (int blk = 0; blk < NH / 2; ++blk) {
+              if (2 * blk < nh) {
+                float mx = fmaxf(fabsf(hv[2 * blk]), fabsf(hv[2 * blk + 1]));
+                mx = fmaxf(mx, __shfl_xor(mx, 1));
+                mx = fmaxf(mx, __shfl_xor(mx, 2));
+                mx = fmaxf(mx, __shfl_xor(mx, 4));
+                mx = fmaxf(mx, __shfl_xor(mx, 8));
+                const int sx = mx_scale_exp(f32_bits(mx));
+                const int64_t col = hcol0 + 32 * blk + r16;
+                if (live) {
+                  p.h8[pr * p.h_stride + col] = (uint8_t)e4m3_encode_scaled(f32_bits(hv[2 * blk]), sx);
+                  p.h8[pr * p.h_stride + col + 16] = (uint8_t)e4m3_encode_scaled(f32_bits(hv[2 * blk + 1]), sx);
+                  if (r16 == 0) p.hs[pr * p.hs_stride + (hcol0 + 32 * blk) / 32] = (uint8_t)(sx + 127);
+                }
+              }
+            }
+          }
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+}
+
+// ---- D2: down projection + combine, one output fragment per workgroup ----------
+constexpr int kDownThreads = 512;
+constexpr int kDownWaves = kDownThreads / 64;
+
+template <int WF, int AF, int DEPTH>
+__global__ __launch_bounds__(kDownThreads) void decode_down_kernel(const DecodeParams p) {
+  constexpr bool A8 = AF == B12X_ACT_MXFP8;
+  __shared__ int s_ids[kDecodePairs];
+  __shared__ uint32_t s_bits[kMaxExperts / 32];
+  __shared__ int s_exp[kDecodePairs];  // touched experts, ascending
+  __shared__ int s_ntouched;
+  __shared__ float s_y[kDecodePairs][kFragN];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int g = lane >> 4, r16 = lane & 15;
+  const int f = blockIdx.x;  // output columns [16 f, 16 f + 16)
+
+  const int words = (p.E + 31) >> 5;
+  for (int i = tid; i < words; i += kDownThreads) s_bits[i] = 0;
+  __syncthreads();
+  for (int q = tid; q < p.P; q += kDownThreads) {
+    const int e = p.ids[q];
+    const bool v = e >= 0 && e < p.E;
+    s_ids[q] = v ? e : -1;
+    if (v) atomicOr(&s_bits[e >> 5], 1u << (e & 31));
+  }
+  __syncthreads();
+  if (wave == 0) {  // the touched experts in ascending order
+    int before = 0;
+    for (int base = 0; base < words; base += 64) {
+      const int w = base + lane;
+      uint32_t bits = w < words ? s_bits[w] : 0u;
+      const int c = __builtin_popcount(bits);
+      int incl = c;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int t = __shfl_up(incl, off);
+        if (lane >= off) incl += t;
+      }
+      int idx = before + incl - c;
+      while (bits) {
+        s_exp[idx++] = w * 32 + __builtin_ctz(bits);
+        bits &= bits - 1;
+      }
+      before += __shfl(incl, 63);
+    }
+    if (lane == 0) s_ntouched = before;
+  }
+  __syncthreads();
+  const int n_touched = s_ntouched;
+
+  // ---- issue iterator over this wave's (expert slot, row chunk, K fragment) steps
+  int i_slot = wave, i_r0 = 0, i_kf = 0, i_m = 0, i_e = 0, i_pair = -1;
+  auto enter = [&]() {  // rows of expert s_exp[i_slot]: count, and this lane's pair of row i_r0 + r16
+    i_e = s_exp[i_slot];
+    const int want = i_r0 + r16;
+    int base = 0, pair = -1;
+    for (int c = 0; c < p.P; c += 64) {
+      const bool hit = c + lane < p.P && s_ids[c + lane] == i_e;
+      const uint64_t bal = __ballot(hit);
+      const int cnt = __builtin_popcountll(bal);
+      if (pair < 0 && want >= base && want < base + cnt) {
+        uint64_t b = bal;
+        for (int r = want - base; r > 0; --r) b &= b - 1;
+        pair = c + __builtin_ctzll(b);
+      }
+      base += cnt;
+    }
+    i_m = base;
+    i_pair = pair;
+  };
+  if (i_slot < n_touched) enter();
+
+  uint4 rb[DEPTH];
+  uint32_t rs[DEPTH];
+  uint4 ra[DEPTH][A8 ? 2 : 4];
+  int rsa[DEPTH];
+  int rpair[DEPTH];
+  int rmeta[DEPTH];  // bit 9: valid, bit 8: last K fragment of the row chunk, bits 0-7: K fragment
+  float rgs[DEPTH];
+  const int kblocks = (int)(p.K / 32);
+
+  auto issue = [&](int u) {
+    if (i_slot >= n_touched) {
+      rmeta[u] = 0;
+      return;
+    }
+    const int kf = i_kf, e = i_e;
+    rb[u] = *(const uint4*)(p.bcodes + (int64_t)e * p.b_codes_expert + ((int64_t)f * p.KF + kf) * kFragBytes +
+                            lane * 16);
+    const int sg = WF == B12X_WEIGHT_MXFP4 ? kf >> 2 : kf >> 1;
+    rs[u] = *(const uint32_t*)(p.bscales + (int64_t)e * p.b_scales_expert + ((int64_t)f * p.KFS + sg) *
+                               kScaleGroupBytes + lane * 4);
+    const int64_t k0 = (int64_t)kf * kFragK;
+#pragma unroll
+    for (int s = 0; s < (A8 ? 2 : 4); ++s) ra[u][s] = make_uint4(0, 0, 0, 0);
+    rsa[u] = 127;
+    if (i_pair >= 0) {
+      if constexpr (!A8) {
+        if (k0 + 32 * g < p.K) {
+          const uint4* ap = (const uint4*)(p.a16 + (int64_t)i_pair * p.a_stride + k0 + 32 * g);
+#pragma unroll
+          for (int s = 0; s < 4; ++s) ra[u][s] = ap[s];
+        }
+      } else {
+        const uint8_t* ap = p.a8 + (int64_t)i_pair * p.a_stride + k0;
+        if (k0 + 16 * g < p.K) ra[u][0] = *(const uint4*)(ap + 16 * g);
+        if (k0 + 64 + 16 * g < p.K) ra[u][1] = *(const uint4*)(ap + 64 + 16 * g);
+        if (4 * kf + g < kblocks) rsa[u] = p.as[(int64_t)i_pair * p.as_stride + 4 * kf + g];
+      }
+    }
+    rpair[u] = i_pair;
+    rgs[u] = p.bglobal ? p.bglobal[e] : 1.0f;
+    rmeta[u] = kf | ((kf == p.KF - 1) ? 0x100 : 0) | 0x200;
+    if (++i_kf == p.KF) {  // advance
+      i_kf = 0;
+      i_r0 += 16;
+      if (i_r0 >= i_m) {
+        i_r0 = 0;
+        i_slot += kDownWaves;
+      }
+      if (i_slot < n_touched) enter();
+    }
+  };
+
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  auto consume = [&](int u) {
+    const int meta = rmeta[u];
+    const int kf = meta & 0xFF;
+    if constexpr (!A8) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const uint32_t dw = s == 0 ? rb[u].x : s == 1 ? rb[u].y : s == 2 ? rb[u].z : rb[u].w;
+        float sc;
+        if constexpr (WF == B12X_WEIGHT_MXFP4) sc = e8m0_as_scale((rs[u] >> (8 * (kf & 3))) & 0xFFu);
+        else sc = e4m3_value((rs[u] >> (8 * (2 * (kf & 1) + (s >> 1)))) & 0xFFu);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ra[u][s]),
+                                                      dequant8_bf16<WF>(dw, sc), acc, 0, 0, 0);
+      }
+    } else {
+      const i32x8 afr = {(int)ra[u][0].x, (int)ra[u][0].y, (int)ra[u][0].z, (int)ra[u][0].w,
+                         (int)ra[u][1].x, (int)ra[u][1].y, (int)ra[u][1].z, (int)ra[u][1].w};
+      const i32x8 bfr = {(int)rb[u].x, (int)rb[u].y, (int)rb[u].z, (int)rb[u].w, 0, 0, 0, 0};
+      const int sb = (int)((rs[u] >> (8 * (kf & 3))) & 0xFFu);
+      acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(afr, bfr, acc, 0, 4, 0, rsa[u], 0, sb);
+    }
+    if (meta & 0x100) {  // row chunk done: y rows by pair into LDS
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int pr = __shfl(rpair[u], 4 * g + i);
+        if (pr >= 0) s_y[pr][r16] = acc[i] * rgs[u];
+      }
+      acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  };
+
+#pragma unroll
+  for (int u = 0; u < DEPTH; ++u) issue(u);
+  bool more = true;
+  while (more) {
+    more = false;
+#pragma unroll
+    for (int u = 0; u < DEPTH; ++u) {
+      if (rmeta[u]) {
+        consume(u);
+        more = true;
+      }
+      issue(u);
+    }
+  }
+  __syncthreads();
+
+  // ---- combine this fragment's columns: ascending slot order, one bf16 rounding
+  const int c0 = f * kFragN;
+  for (int i = tid; i < p.T * kFragN; i += kDownThreads) {
+    const int t = i / kFragN, c = i % kFragN;
+    float a = 0.f;
+    for (int j = 0; j < p.k; ++j) {
+      const int q = t * p.k + j;
+      if (s_ids[q] >= 0) a = fmaf(p.tw[q], s_y[q][c], a);
+    }
+    p.out[(int64_t)t * p.out_stride + c0 + c] = (uint16_t)bf16_rne(a);
+  }
+}
+
+template <int MODE, int FR, int KW>
+static int launch_decode_kw(const BindingImpl& b, const DecodeParams& p, int n_slots, hipStream_t s) {
+  const dim3 grid((unsigned)(n_slots * p.n_groups));
+  const bool nv = b.wfmt == B12X_WEIGHT_NVFP4, a8 = b.afmt == B12X_ACT_MXFP8;
+  if (a8)
+    hipLaunchKernelGGL((decode_kernel<B12X_WEIGHT_MXFP4, B12X_ACT_MXFP8, MODE, FR, KW>), grid, dim3(kDecThreads), 0,
+                       s, p);
+  else if (nv)
+    hipLaunchKernelGGL((decode_kernel<B12X_WEIGHT_NVFP4, B12X_ACT_BF16, MODE, FR, KW>), grid, dim3(kDecThreads), 0,
+                       s, p);
+  else
+    hipLaunchKernelGGL((decode_kernel<B12X_WEIGHT_MXFP4, B12X_ACT_BF16, MODE, FR, KW>), grid, dim3(kDecThreads), 0,
+                       s, p);
+  return (int)hipGetLastError();
+}
+
+// K fragments per wave: the smallest of 2, 4, 8 that covers ceil(KF / 4).
+template <int MODE, int FR>
+static int launch_decode_t(const BindingImpl& b, const DecodeParams& p, int n_slots, hipStream_t s) {
+  const int kper = (p.KF + 3) / 4;
+  if (kper <= 2) return launch_decode_kw<MODE, FR, 2>(b, p, n_slots, s);
+  if (kper <= 4) return launch_decode_kw<MODE, FR, 4>(b, p, n_slots, s);
+  return launch_decode_kw<MODE, FR, 8>(b, p, n_slots, s);
+}
+
+static DecodeParams common_params(const BindingImpl& b) {
+  DecodeParams p = {};
+  p.ids = b.ids;
+  p.tw = b.tw;
+  p.T = (int)b.T;
+  p.k = b.k;
+  p.E = b.E;
+  p.P = (int)(b.T * b.k);
+  return p;
+}
+
+static int decode_slots(const BindingImpl& b) { return (int)(b.T * b.k < b.E ? b.T * b.k : b.E); }
+
+int launch_decode1(const BindingImpl& b, hipStream_t s) {
+  DecodeParams p = common_params(b);
+  const bool a8 = b.afmt == B12X_ACT_MXFP8;
+  p.a16 = b.a;
+  p.a8 = b.xq;
+  p.as = b.xs;
+  p.a_stride = a8 ? b.Hp : b.a_stride;
+  p.as_stride = b.Hp / 32;
+  p.a_by_token = 1;
+  p.K = b.H;
+  p.KF = (int)b.kf13;
+  p.bcodes = b.w13_codes;
+  p.bscales = b.w13_scales;
+  p.bglobal = b.w13_global;
+  p.b_codes_expert = b.nf13 * b.kf13 * kFragBytes;
+  p.b_scales_expert = b.nf13 * b.kfs13 * kScaleGroupBytes;
+  p.NF = (int)b.nf13;
+  p.KFS = (int)b.kfs13;
+  p.h16 = (uint16_t*)b.h;
+  p.h8 = (uint8_t*)b.h;
+  p.hs = b.hs;
+  p.h_stride = b.Ip;
+  p.hs_stride = b.Ip / 32;
+  const int n_slots = decode_slots(b);
+  if (b.gated) {
+    if (a8) {  // an MXFP8 block of h (32 columns) needs two gate/up pairs
+      p.n_groups = (p.NF + 3) / 4;
+      return launch_decode_t<DMODE_SILU, 4>(b, p, n_slots, s);
+    }
+    p.n_groups = (p.NF + 1) / 2;
+    return launch_decode_t<DMODE_SILU, 2>(b, p, n_slots, s);
+  }
+  p.n_groups = (p.NF + 1) / 2;
+  return launch_decode_t<DMODE_RELU2, 2>(b, p, n_slots, s);
+}
+
+int launch_decode2(const BindingImpl& b, hipStream_t s) {
+  DecodeParams p = common_params(b);
+  const bool a8 = b.afmt == B12X_ACT_MXFP8, nv = b.wfmt == B12X_WEIGHT_NVFP4;
+  p.a16 = (const uint16_t*)b.h;
+  p.a8 = (const uint8_t*)b.h;
+  p.as = b.hs;
+  p.a_stride = b.Ip;
+  p.as_stride = b.Ip / 32;
+  p.a_by_token = 0;
+  p.K = b.I;
+  p.KF = (int)b.kf2;
+  p.bcodes = b.w2_codes;
+  p.bscales = b.w2_scales;
+  p.bglobal = b.w2_global;
+  p.b_codes_expert = b.nf2 * b.kf2 * kFragBytes;
+  p.b_scales_expert = b.nf2 * b.kfs2 * kScaleGroupBytes;
+  p.NF = (int)b.nf2;
+  p.KFS = (int)b.kfs2;
+  p.out = b.out;
+  p.out_stride = b.out_stride;
+  const dim3 grid((unsigned)p.NF), block(kDownThreads);
+  if (a8)
+    hipLaunchKernelGGL((decode_down_kernel<B12X_WEIGHT_MXFP4, B12X_ACT_MXFP8, 8>), grid, block, 0, s, p);
+  else if (nv)
+    hipLaunchKernelGGL((decode_down_kernel<B12X_WEIGHT_NVFP4, B12X_ACT_BF16, 6>), grid, block, 0, s, p);
+  else
+    hipLaunchKernelGGL((decode_down_kernel<B12X_WEIGHT_MXFP4, B12X_ACT_BF16, 6>), grid, block, 0, s, p);
+  return (int)hipGetLastError();
+}
+
+}  // namespace b12x

@@ -90,4 +90,35 @@ __device__ __forceinline__ float e4m3_value(uint32_t c) {
 // scaled FP4 conversions read exactly that field.
 __device__ __forceinline__ float e8m0_as_scale(uint32_t c) { return bits_f32(c << 23); }
 
+__device__ __forceinline__ bf16x8 u32x4_as_bf16x8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  i32x4 v = {(int)a, (int)b, (int)c, (int)d};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// Eight FP4 codes (one dword, low nibble first) -> eight bf16 (as 4 dwords).
+template <int WF>
+__device__ __forceinline__ bf16x8 dequant8_bf16(uint32_t codes, float scale) {
+  if constexpr (WF == B12X_WEIGHT_MXFP4) {
+    const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 0);
+    const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 1);
+    const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 2);
+    const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 3);
+    return u32x4_as_bf16x8(__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1),
+                           __builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, p3));
+  } else {
+    uint32_t out[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      f32x2 v;
+      if (b == 0) v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 0);
+      if (b == 1) v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 1);
+      if (b == 2) v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 2);
+      if (b == 3) v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 3);
+      const uint32_t lo = f32_bits(v.x * scale), hi = f32_bits(v.y * scale);
+      out[b] = __builtin_amdgcn_perm(hi, lo, 0x07060302u);  // exact: <= 6 significant bits
+    }
+    return u32x4_as_bf16x8(out[0], out[1], out[2], out[3]);
+  }
+}
+
 }  // namespace b12x

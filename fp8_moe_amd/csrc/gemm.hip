@@ -62,37 +62,6 @@ struct GemmParams {
 
 enum { MODE_SILU = 1, MODE_RELU2 = 2, MODE_DOWN = 3 };
 
-__device__ __forceinline__ bf16x8 u32x4_as_bf16x8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
-  i32x4 v = {(int)a, (int)b, (int)c, (int)d};
-  return __builtin_bit_cast(bf16x8, v);
-}
-
-// Eight FP4 codes (one dword, low nibble first) -> eight bf16 (as 4 dwords).
-template <int WF>
-__device__ __forceinline__ bf16x8 dequant8(uint32_t codes, float scale) {
-  if constexpr (WF == B12X_WEIGHT_MXFP4) {
-    const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 0);
-    const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 1);
-    const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 2);
-    const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 3);
-    return u32x4_as_bf16x8(__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1),
-                           __builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, p3));
-  } else {
-    uint32_t out[4];
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      f32x2 v;
-      if (b == 0) v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 0);
-      if (b == 1) v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 1);
-      if (b == 2) v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 2);
-      if (b == 3) v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 3);
-      const uint32_t lo = f32_bits(v.x * scale), hi = f32_bits(v.y * scale);
-      out[b] = __builtin_amdgcn_perm(hi, lo, 0x07060302u);  // exact: <= 6 significant bits
-    }
-    return u32x4_as_bf16x8(out[0], out[1], out[2], out[3]);
-  }
-}
-
 template <int WF, int AF, int MODE>
 __global__ __launch_bounds__(kGemmThreads, 2) void moe_gemm_kernel(const GemmParams p) {
   constexpr bool A8 = AF == B12X_ACT_MXFP8;
@@ -230,7 +199,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void moe_gemm_kernel(const GemmPar
               float sc;
               if constexpr (WF == B12X_WEIGHT_MXFP4) sc = e8m0_as_scale((bs[j] >> (8 * (kf & 3))) & 0xFFu);
               else sc = e4m3_value((bs[j] >> (8 * (2 * (kf & 1) + (s >> 1)))) & 0xFFu);
-              bfr[j] = dequant8<WF>(dw, sc);
+              bfr[j] = dequant8_bf16<WF>(dw, sc);
             }
           }
 #pragma unroll

@@ -37,6 +37,9 @@ constexpr int kRowPad = 16;      // per-expert row padding = MFMA row block
 constexpr int kTileFrags = 8;    // 16-row weight fragments per GEMM tile (N = 128)
 constexpr int kRouteChunk = 1024;  // routing pairs per workgroup
 constexpr int kMaxExperts = 1024;
+// ---- decode path -------------------------------------------------------------
+constexpr int kDecodePairs = 256;     // T*k at or below which the decode path runs
+constexpr int kDecodeMaxKPerWave = 8; // K fragments per wave: K <= 4 * 8 * 128
 
 struct MatrixLayout {
   int64_t n = 0, k = 0;     // logical rows / contraction length
@@ -65,6 +68,7 @@ struct PlanImpl {
   MatrixLayout l13, l2;
   int64_t Hp = 0, Ip = 0;  // H, I rounded up to 128
   int64_t max_pairs = 0, max_rows = 0, max_tiles = 0, max_chunks = 0;
+  int decode_max_pairs = 0;  // largest T*k that takes the decode path (0: never)
   uint64_t off[16] = {0};   // scratch region offsets, indexed by Region
   uint64_t len[16] = {0};   // scratch region sizes
   uint64_t scratch_bytes = 0;
@@ -129,6 +133,8 @@ int launch_quant_rows(const uint16_t* x, int64_t rows, int64_t cols, int64_t str
 int launch_gemm1(const BindingImpl& b, hipStream_t s);
 int launch_gemm2(const BindingImpl& b, hipStream_t s);
 int launch_combine(const BindingImpl& b, hipStream_t s);
+int launch_decode1(const BindingImpl& b, hipStream_t s);
+int launch_decode2(const BindingImpl& b, hipStream_t s);
 const char* hip_error_name(int err);
 
 }  // namespace b12x

@@ -81,26 +81,26 @@ WORKLOADS = {
 _STREAMS = {"x": 1, "w13": 2, "w2": 3, "ids": 4, "weights": 5}
 
 
-def _gen(wl, stream, tokens, device):
+def _gen(wl, stream, tokens, device, salt=0):
     idx = list(WORKLOADS).index(wl.name) if wl.name in WORKLOADS else 7
-    seed = (BASE_SEED * 1000003 + idx * 10007 + _STREAMS[stream] * 101 + tokens) % (2 ** 62)
+    seed = (BASE_SEED * 1000003 + idx * 10007 + _STREAMS[stream] * 101 + tokens + salt * 7919) % (2 ** 62)
     g = torch.Generator(device=device)
     g.manual_seed(seed)
     return g
 
 
-def make_x(wl, T, device="cpu"):
-    """bf16 activations [T, H]."""
-    g = _gen(wl, "x", T, device)
+def make_x(wl, T, device="cpu", salt=0):
+    """bf16 activations [T, H]; ``salt`` selects another draw of the same shape."""
+    g = _gen(wl, "x", T, device, salt)
     x = torch.randn(T, wl.H, generator=g, device=device, dtype=torch.float32)
     if wl.x_lognormal:
         x = x * torch.exp(torch.randn(T, 1, generator=g, device=device, dtype=torch.float32))
     return x.to(torch.bfloat16)
 
 
-def make_routing(wl, T, device="cpu"):
+def make_routing(wl, T, device="cpu", salt=0):
     """(topk_ids int32 [T, k], topk_weights float32 [T, k])."""
-    g = _gen(wl, "ids", T, device)
+    g = _gen(wl, "ids", T, device, salt)
     if wl.routing == "uniform":
         scores = torch.rand(T, wl.E, generator=g, device=device)
     elif wl.routing == "zipf":
@@ -113,7 +113,7 @@ def make_routing(wl, T, device="cpu"):
     else:
         raise ValueError(wl.routing)
     ids = torch.topk(scores, wl.k, dim=1).indices.to(torch.int32)
-    gw = _gen(wl, "weights", T, device)
+    gw = _gen(wl, "weights", T, device, salt)
     logits = torch.randn(T, wl.k, generator=gw, device=device, dtype=torch.float32)
     return ids.contiguous(), torch.softmax(logits, dim=1).contiguous()
 

@@ -35,14 +35,15 @@ def compare(gpu_out, ref):
 class Problem:
     """A workload instance on the GPU: source weights, prepared weights, plan."""
 
-    def __init__(self, wl, max_tokens, gen_device="cuda", weights=None):
+    def __init__(self, wl, max_tokens, gen_device="cuda", weights=None, decode_max_pairs=0):
         import fp8_moe_amd as fm
         self.wl = wl
         self.fm = fm
         self.w = weights if weights is not None else synth.make_weights(wl, device=gen_device)
         self.wd = {k: (None if v is None else v.cuda()) for k, v in self.w.items()}
         self.model = fm.FusedMoE(wl.E, wl.H, wl.I, wl.k, wl.weight_format, wl.act_format,
-                                 "silu" if wl.gated else "relu2", max_tokens, self.wd)
+                                 "silu" if wl.gated else "relu2", max_tokens, self.wd,
+                                 decode_max_pairs=decode_max_pairs)
 
     def run(self, x, ids, tw, out=None):
         binding, out = self.model.bind(x, ids, tw, out)

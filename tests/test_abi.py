@@ -93,7 +93,7 @@ class _FakeTensor:
         return True
 
 
-def _bind_status(p, ex, T, a_ptr=0x10000, a_stride=256, out_ptr=0x900000, scratch_ptr=0x4000000, scratch_bytes=None,
+def _bind_status(p, ex, T, a_ptr=0x10000, a_stride=256, out_ptr=0x9000000, scratch_ptr=0x4000000, scratch_bytes=None,
                  ids_ptr=0x200000, tw_ptr=0x300000):
     import fp8_moe_amd as fm
     if scratch_bytes is None:
@@ -101,7 +101,7 @@ def _bind_status(p, ex, T, a_ptr=0x10000, a_stride=256, out_ptr=0x900000, scratc
     b = fm.Binding()
     return fm.lib().b12x_moe_bind(p.handle, ctypes.c_void_p(scratch_ptr), scratch_bytes, ctypes.byref(ex),
                                   ctypes.c_void_p(a_ptr), T, a_stride, ctypes.c_void_p(ids_ptr),
-                                  ctypes.c_void_p(tw_ptr), ctypes.c_void_p(out_ptr), 256, ctypes.byref(b)), b
+                                  ctypes.c_void_p(tw_ptr), ctypes.c_void_p(out_ptr), a_stride, ctypes.byref(b)), b
 
 
 def test_bind_validation_on_host():
@@ -130,3 +130,21 @@ def test_status_strings():
     for s in range(8):
         assert fm.lib().b12x_status_string(s)
     assert fm.lib().b12x_status_string(99) == b"unknown status"
+
+
+def test_path_selection_at_bind():
+    import fp8_moe_amd as fm
+    wp = fm.plan_weights(128, 2048, 768, True, "mxfp4")
+    ex = fm.Experts(wp, ctypes.c_void_p(0x7000000), wp.prepared_bytes)
+    p = fm.plan(wp, 8, 64)
+    assert fm.binding_query(_bind_status(p, ex, 32, a_stride=2048)[1], "path") == 2     # 256 pairs: decode
+    assert fm.binding_query(_bind_status(p, ex, 33, a_stride=2048)[1], "path") == 1     # 264 pairs: grouped
+    never = fm.plan(wp, 8, 64, decode_max_pairs=-1)
+    assert fm.binding_query(_bind_status(never, ex, 1, a_stride=2048)[1], "path") == 1
+    small = fm.plan(wp, 8, 64, decode_max_pairs=64)
+    assert fm.binding_query(_bind_status(small, ex, 8, a_stride=2048)[1], "path") == 2
+    assert fm.binding_query(_bind_status(small, ex, 9, a_stride=2048)[1], "path") == 1
+    wide = fm.plan_weights(8, 7168, 256, True, "nvfp4")                                   # K too long per wave
+    exw = fm.Experts(wide, ctypes.c_void_p(0x7000000), wide.prepared_bytes)
+    pw = fm.plan(wide, 8, 4)
+    assert fm.binding_query(_bind_status(pw, exw, 1, a_stride=7168)[1], "path") == 1

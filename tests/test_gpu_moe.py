@@ -163,3 +163,77 @@ def test_graph_replay_matches_eager():
         torch.cuda.synchronize()
         assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), i
         _ = (x.float() * 2).sum()      # unrelated eager work between replays
+
+
+# decode path (T*k <= 256) against the grouped path and the oracle on the same inputs
+DECODE = [
+    ("tiny", 16), ("decode", 1), ("decode", 8), ("decode", 32), ("mixed", 1), ("mixed", 64),
+]
+
+
+@pytest.mark.parametrize("name,T", DECODE)
+def test_decode_and_grouped_paths_agree(name, T):
+    import fp8_moe_amd as fm
+    print(f"paths {name} T={T}", flush=True)
+    wl = synth.WORKLOADS[name]
+    pr = problem(name, max(wl.tokens))
+    grouped = fm.FusedMoE(wl.E, wl.H, wl.I, wl.k, wl.weight_format, wl.act_format,
+                          "silu" if wl.gated else "relu2", T, pr.wd, decode_max_pairs=-1)
+    x, ids, tw = _inputs(wl, T)
+    b_dec, out_dec = pr.model.bind(x, ids, tw)
+    b_grp, out_grp = grouped.bind(x, ids, tw)
+    assert fm.binding_query(b_dec, "path") == 2 and fm.binding_query(b_grp, "path") == 1
+    fm.run(b_dec)
+    fm.run(b_grp)
+    torch.cuda.synchronize()
+    rows = None if T <= 8 else [0, T // 2, T - 1]
+    ref = pr.oracle(x, ids, tw, rows)
+    for out in (out_dec, out_grp):
+        got = out if rows is None else out[rows]
+        rel_fro, rel_max, ok = compare(got, ref)
+        assert ok, (rel_fro, rel_max)
+    d = (out_dec.float() - out_grp.float()).abs().max().item()
+    assert d <= 2e-2 * out_grp.float().abs().max().item()
+
+
+DECODE_EDGE = [
+    # name, E, H, I, k, gated, wfmt, afmt, T, ids kind
+    ("one_expert_many_rows", 8, 256, 128, 8, True, "mxfp4", "bf16", 32, "one_expert"),
+    ("all_dropped", 8, 256, 128, 2, True, "mxfp4", "bf16", 5, "all_bad"),
+    ("some_dropped_dups", 16, 256, 128, 4, True, "nvfp4", "bf16", 20, "bad_dups"),
+    ("a8_one_expert", 8, 288, 224, 4, False, "mxfp4", "mxfp8", 40, "one_expert"),
+    ("a8_gated", 8, 256, 128, 2, True, "mxfp4", "mxfp8", 30, "uniform"),
+    ("nv_relu2_ragged", 8, 160, 96, 3, False, "nvfp4", "bf16", 50, "uniform"),
+    ("k1", 4, 256, 128, 1, True, "mxfp4", "bf16", 1, "uniform"),
+]
+
+
+@pytest.mark.parametrize("case", DECODE_EDGE, ids=[c[0] for c in DECODE_EDGE])
+def test_decode_edge_cases(case):
+    import fp8_moe_amd as fm
+    name, E, H, I, k, gated, wfmt, afmt, T, kind = case
+    print(f"decode edge {case}", flush=True)
+    wl = small_workload(name, E, H, I, k, gated, wfmt, afmt, x_lognormal=afmt == "mxfp8")
+    pr = Problem(wl, T, gen_device="cpu")
+    x, ids, tw = _inputs(wl, T)
+    ids = ids.clone()
+    if kind == "one_expert":
+        ids[:] = E - 1
+    elif kind == "all_bad":
+        ids[:] = -1
+        ids[0, 0] = E
+    elif kind == "bad_dups":
+        ids[0, 1] = -5
+        ids[1, :] = 3
+        ids[2, 2] = E + 7
+    b, out = pr.model.bind(x, ids, tw)
+    assert fm.binding_query(b, "path") == 2
+    out.fill_(1.0)
+    fm.run(b)
+    torch.cuda.synchronize()
+    ref = pr.oracle(x, ids, tw)
+    rel_fro, rel_max, ok = compare(out, ref)
+    print(f"  rel_fro={rel_fro:.3e} rel_max={rel_max:.3e}", flush=True)
+    assert ok, (rel_fro, rel_max)
+    if kind == "all_bad":
+        assert torch.all(out == 0)
