@@ -195,6 +195,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-extra", action="store_true", help="skip the prefill and W4A8 lines")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--prefill-only", action="store_true", help="only the prefill line (kernel tuning)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the fused MoE here is a "
@@ -207,6 +208,9 @@ def main():
     torch.cuda.set_device(0)
     stream = torch.cuda.Stream()
 
+    if args.prefill_only:
+        print(json.dumps({"prefill": bench_prefill(fm, synth, torch, stream)}))
+        return
     log("building decode workload")
     wl, w, plan, scratch, copies, sets = build_decode(fm, synth, torch)
     Ts = wl.tokens

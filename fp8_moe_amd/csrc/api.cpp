@@ -327,7 +327,7 @@ static b12x_status get_binding(const b12x_moe_binding* binding, BindingImpl* b) 
 
 static bool stage_in_path(const BindingImpl& b, int stage) {
   if (stage == B12X_STAGE_QUANT_X) return b.afmt == B12X_ACT_MXFP8;
-  if (b.path == 2) return stage == B12X_STAGE_DECODE1 || stage == B12X_STAGE_DECODE2;
+  if (b.path == 2) return stage == B12X_STAGE_DECODE1 || stage == B12X_STAGE_DECODE2 || stage == B12X_STAGE_COMBINE;
   return stage >= B12X_STAGE_ROUTE && stage <= B12X_STAGE_COMBINE;
 }
 
@@ -343,7 +343,7 @@ static b12x_status run_stage(const BindingImpl& b, int stage, hipStream_t s) {
     case B12X_STAGE_QUANT_X: err = launch_quant_rows(b.a, b.T, b.H, b.a_stride, b.xq, b.Hp, b.xs, b.Hp / 32, s); break;
     case B12X_STAGE_GEMM1: err = launch_gemm1(b, s); break;
     case B12X_STAGE_GEMM2: err = launch_gemm2(b, s); break;
-    case B12X_STAGE_COMBINE: err = launch_combine(b, s); break;
+    case B12X_STAGE_COMBINE: err = b.path == 2 ? launch_decode_combine(b, s) : launch_combine(b, s); break;
     case B12X_STAGE_DECODE1: err = launch_decode1(b, s); break;
     case B12X_STAGE_DECODE2: err = launch_decode2(b, s); break;
   }
@@ -367,9 +367,9 @@ b12x_status b12x_moe_run(const b12x_moe_binding* binding, void* stream) {
   hipStream_t s = (hipStream_t)stream;
   static const int grouped[5] = {B12X_STAGE_ROUTE, B12X_STAGE_QUANT_X, B12X_STAGE_GEMM1, B12X_STAGE_GEMM2,
                                  B12X_STAGE_COMBINE};
-  static const int decode[3] = {B12X_STAGE_QUANT_X, B12X_STAGE_DECODE1, B12X_STAGE_DECODE2};
+  static const int decode[4] = {B12X_STAGE_QUANT_X, B12X_STAGE_DECODE1, B12X_STAGE_DECODE2, B12X_STAGE_COMBINE};
   const int* stages = b.path == 2 ? decode : grouped;
-  const int n = b.path == 2 ? 3 : 5;
+  const int n = b.path == 2 ? 4 : 5;
   for (int i = 0; i < n; ++i) {
     if (!stage_in_path(b, stages[i])) continue;
     st = run_stage(b, stages[i], s);
@@ -388,7 +388,7 @@ b12x_status b12x_moe_binding_query(const b12x_moe_binding* binding, int32_t what
     case B12X_QUERY_TILE_ROWS: *value = kTileRows; break;
     case B12X_QUERY_ROW_PAD: *value = kRowPad; break;
     case B12X_QUERY_T: *value = b.T; break;
-    case B12X_QUERY_NUM_STAGES: *value = (b.path == 2 ? 2 : 4) + (b.afmt == B12X_ACT_MXFP8 ? 1 : 0); break;
+    case B12X_QUERY_NUM_STAGES: *value = (b.path == 2 ? 3 : 4) + (b.afmt == B12X_ACT_MXFP8 ? 1 : 0); break;
     default: return fail(B12X_ERR_INVALID_ARGUMENT, "unknown query %d", what);
   }
   return B12X_OK;

@@ -1,21 +1,21 @@
 // Small-batch decode path of the fused MoE (b12x README "What's in here": the
-// micro-kernel decode path of fused_moe).  For T*k <= kDecodePairs it replaces
-// the routing buffers and the grouped GEMMs with two launches in which every
-// touched expert's weights are read exactly once:
-//   D1 (gate/up): workgroup = (touched-expert slot, group of FR weight
-//      fragments).  Each workgroup finds its expert and that expert's pairs
-//      (stable by pair id) from topk_ids in LDS, its 4 waves split K, issue
-//      every fragment load and activation load up front, run MFMAs and add
-//      their partial sums in LDS in a fixed wave order; the activation
-//      (SiLU-gated or ReLU^2) then writes h by pair id (bf16, or MXFP8 codes
-//      and scales for W4A8).
-//   D2 (down + combine): workgroup = one 16-column fragment of the output,
-//      over all touched experts.  Its 8 waves take the experts round robin and
-//      stream (expert, row chunk, K fragment) steps through a register ring of
-//      DEPTH outstanding loads; each finished row chunk leaves y rows (by pair)
-//      in LDS; the workgroup then combines out[t] = sum_j w[t,j] * y[t*k+j]
-//      in ascending slot order and rounds once to bf16.  No atomics, no
-//      cross-workgroup traffic: the result does not depend on scheduling.
+// micro-kernel decode path of fused_moe).  For T*k <= kDecodePairs three
+// launches replace the routing buffers and the grouped GEMMs; every touched
+// expert's weights are read exactly once:
+//   D1 (gate/up) and D2 (down): workgroup = (touched-expert slot, run of up to
+//      NG groups of FR weight fragments).  Each workgroup finds its expert and
+//      that expert's pairs (stable by pair id) from topk_ids in LDS; its 4
+//      waves split K, keep their share of the activation rows in registers and
+//      stream the fragment groups with the next group's loads in flight while
+//      the current one runs on the MFMAs; partial sums are added in LDS in a
+//      fixed wave order.  D1 applies SiLU-gated or ReLU^2 and writes h by pair
+//      id (bf16, or MXFP8 codes and scales for W4A8); D2 writes y by pair id
+//      in fp32.
+//   D3 (combine): out[t] = sum_j w[t,j] * y[t*k+j] in ascending slot order,
+//      fp32, one bf16 rounding (the grouped path's combine kernel, reading y
+//      by pair id).
+// No atomics on data and no cross-workgroup synchronization: the result does
+// not depend on scheduling.
 #include "device_common.h"
 
 namespace b12x {
@@ -42,17 +42,19 @@ struct DecodeParams {
   int64_t b_codes_expert, b_scales_expert;
   int NF, KFS;
   int n_groups;  // fragment groups per expert
+  int ng;        // fragment groups per workgroup
+  int n_runs;    // workgroups per expert slot = ceil(n_groups / ng)
   // D1 outputs
   uint16_t* h16;
   uint8_t* h8;
   uint8_t* hs;
   int64_t h_stride, hs_stride;
   // D2 output
-  uint16_t* out;
-  int64_t out_stride;
+  float* y;
+  int64_t y_stride;
 };
 
-enum { DMODE_SILU = 1, DMODE_RELU2 = 2 };
+enum { DMODE_SILU = 1, DMODE_RELU2 = 2, DMODE_DOWN = 3 };
 
 struct DecodeRoute {
   int e;          // expert of this workgroup's slot, or -1
@@ -129,398 +131,245 @@ __device__ DecodeRoute decode_route(const DecodeParams& p, int slot, int* s_ids,
   return r;
 }
 
-template <int WF, int AF, int MODE, int FR, int KW>
+template <int WF, int AF, int MODE, int FR, int KW, int NB>
 __global__ __launch_bounds__(kDecThreads) void decode_kernel(const DecodeParams p) {
   constexpr bool A8 = AF == B12X_ACT_MXFP8;
   __shared__ int s_ids[kDecodePairs];
   __shared__ int s_rows[kDecodePairs];
   __shared__ uint32_t s_bits[kMaxExperts / 32];
   __shared__ int s_info[8];
-  __shared__ f32x4 s_red[4][FR][64];
+  __shared__ f32x4 s_red[2][4][FR][64];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int g = lane >> 4, r16 = lane & 15;
-  const int slot = blockIdx.x / p.n_groups, grp = blockIdx.x % p.n_groups;
+  const int slot = blockIdx.x / p.n_runs, run = blockIdx.x % p.n_runs;
+  const int g_begin = run * p.ng, g_end = min(p.n_groups, g_begin + p.ng);
 
   const DecodeRoute rt = decode_route(p, slot, s_ids, s_bits, s_rows, s_info);
-  if (rt.e < 0) return;
+  if (rt.e < 0 || g_begin >= g_end) return;
   const int e = rt.e;
 
-  // ---- this wave's K fragments and the workgroup's weight fragments
+  // ---- this wave's K fragments
   const int kper = (p.KF + 3) / 4;
   const int kb = wave * kper, ke = min(p.KF, kb + kper);
-  const int f0 = grp * FR;
   const uint8_t* bcodes = p.bcodes + (int64_t)e * p.b_codes_expert;
   const uint8_t* bscales = p.bscales + (int64_t)e * p.b_scales_expert;
-  uint4 bq[FR][KW];
-  uint32_t bs[FR][KW];
-#pragma unroll
-  for (int j = 0; j < FR; ++j) {
-#pragma unroll
-    for (int i = 0; i < KW; ++i) {
-      const int kf = kb + i, f = f0 + j;
-      if (kf < ke && f < p.NF) {
-        bq[j][i] = *(const uint4*)(bcodes + ((int64_t)f * p.KF + kf) * kFragBytes + lane * 16);
-        const int sg = WF == B12X_WEIGHT_MXFP4 ? kf >> 2 : kf >> 1;
-        bs[j][i] = *(const uint32_t*)(bscales + ((int64_t)f * p.KFS + sg) * kScaleGroupBytes + lane * 4);
-      } else {
-        bq[j][i] = make_uint4(0, 0, 0, 0);
-        bs[j][i] = 0;
-      }
-    }
-  }
   const float gsc = p.bglobal ? p.bglobal[e] : 1.0f;
 
+  auto load_b = [&](uint4 (&bq)[FR][KW], uint32_t (&bs)[FR][KW], int grp) {
+#pragma unroll
+    for (int j = 0; j < FR; ++j) {
+#pragma unroll
+      for (int i = 0; i < KW; ++i) {
+        const int kf = kb + i, f = grp * FR + j;
+        if (kf < ke && f < p.NF) {
+          bq[j][i] = *(const uint4*)(bcodes + ((int64_t)f * p.KF + kf) * kFragBytes + lane * 16);
+          const int sg = WF == B12X_WEIGHT_MXFP4 ? kf >> 2 : kf >> 1;
+          bs[j][i] = *(const uint32_t*)(bscales + ((int64_t)f * p.KFS + sg) * kScaleGroupBytes + lane * 4);
+        } else {
+          bq[j][i] = make_uint4(0, 0, 0, 0);
+          bs[j][i] = 0;
+        }
+      }
+    }
+  };
+
+  int par = 0;  // s_red buffer of the current group
   for (int r0 = 0; r0 < rt.m; r0 += 16) {
-    // ---- A rows: lane (r16, g) owns row r0 + r16
+    // ---- activation rows: lane (r16, g) owns row r0 + r16, this wave's K range
     const int rr = r0 + r16;
     int64_t src = -1;
     if (rr < rt.m) src = p.a_by_token ? s_rows[rr] / p.k : s_rows[rr];
-    f32x4 acc[FR];
+    uint4 av[KW][A8 ? 2 : 4];
+    int sa[KW];
+    const int kblocks = (int)(p.K / 32);
 #pragma unroll
-    for (int j = 0; j < FR; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if constexpr (!A8) {
-      uint4 av[KW][4];
+    for (int i = 0; i < KW; ++i) {
+      const int kf = kb + i;
+      const int64_t k0 = (int64_t)kf * kFragK;
 #pragma unroll
-      for (int i = 0; i < KW; ++i) {
-        const int kf = kb + i;
-        const int64_t k0 = (int64_t)kf * kFragK + 32 * g;
+      for (int s = 0; s < (A8 ? 2 : 4); ++s) av[i][s] = make_uint4(0, 0, 0, 0);
+      sa[i] = 127;
+      if (kf < ke && src >= 0) {
+        if constexpr (!A8) {
+          if (k0 + 32 * g < p.K) {
+            const uint4* ap = (const uint4*)(p.a16 + src * p.a_stride + k0 + 32 * g);
 #pragma unroll
-        for (int s = 0; s < 4; ++s) av[i][s] = make_uint4(0, 0, 0, 0);
-        if (kf < ke && src >= 0 && k0 < p.K) {
-          const uint4* ap = (const uint4*)(p.a16 + src * p.a_stride + k0);
-#pragma unroll
-          for (int s = 0; s < 4; ++s) av[i][s] = ap[s];
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < KW; ++i) {
-        const int kf = kb + i;
-        if (kf < ke) {
-#pragma unroll
-          for (int s = 0; s < 4; ++s) {
-            const bf16x8 afr = __builtin_bit_cast(bf16x8, av[i][s]);
-#pragma unroll
-            for (int j = 0; j < FR; ++j) {
-              const uint4 q = bq[j][i];
-              const uint32_t dw = s == 0 ? q.x : s == 1 ? q.y : s == 2 ? q.z : q.w;
-              float sc;
-              if constexpr (WF == B12X_WEIGHT_MXFP4) sc = e8m0_as_scale((bs[j][i] >> (8 * (kf & 3))) & 0xFFu);
-              else sc = e4m3_value((bs[j][i] >> (8 * (2 * (kf & 1) + (s >> 1)))) & 0xFFu);
-              acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr, dequant8_bf16<WF>(dw, sc), acc[j], 0, 0, 0);
-            }
+            for (int s = 0; s < 4; ++s) av[i][s] = ap[s];
           }
-        }
-      }
-    } else {
-      uint4 a0[KW], a1[KW];
-      int sa[KW];
-      const int kblocks = (int)(p.K / 32);
-#pragma unroll
-      for (int i = 0; i < KW; ++i) {
-        const int kf = kb + i;
-        const int64_t k0 = (int64_t)kf * kFragK;
-        a0[i] = make_uint4(0, 0, 0, 0);
-        a1[i] = make_uint4(0, 0, 0, 0);
-        sa[i] = 127;
-        if (kf < ke && src >= 0) {
+        } else {
           const uint8_t* ap = p.a8 + src * p.a_stride + k0;
-          if (k0 + 16 * g < p.K) a0[i] = *(const uint4*)(ap + 16 * g);
-          if (k0 + 64 + 16 * g < p.K) a1[i] = *(const uint4*)(ap + 64 + 16 * g);
+          if (k0 + 16 * g < p.K) av[i][0] = *(const uint4*)(ap + 16 * g);
+          if (k0 + 64 + 16 * g < p.K) av[i][1] = *(const uint4*)(ap + 64 + 16 * g);
           if (4 * kf + g < kblocks) sa[i] = p.as[src * p.as_stride + 4 * kf + g];
         }
       }
+    }
+
+    // one fragment group: MFMAs over this wave's K range, split-K sum, epilogue
+    auto group = [&](uint4 (&bq)[FR][KW], uint32_t (&bs)[FR][KW], int grp) {
+      f32x4 acc[FR];
+#pragma unroll
+      for (int j = 0; j < FR; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int i = 0; i < KW; ++i) {
         const int kf = kb + i;
         if (kf < ke) {
-          const i32x8 afr = {(int)a0[i].x, (int)a0[i].y, (int)a0[i].z, (int)a0[i].w,
-                             (int)a1[i].x, (int)a1[i].y, (int)a1[i].z, (int)a1[i].w};
+          if constexpr (!A8) {
 #pragma unroll
-          for (int j = 0; j < FR; ++j) {
-            const uint4 q = bq[j][i];
-            const i32x8 bfr = {(int)q.x, (int)q.y, (int)q.z, (int)q.w, 0, 0, 0, 0};
-            const int sb = (int)((bs[j][i] >> (8 * (kf & 3))) & 0xFFu);
-            acc[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(afr, bfr, acc[j], 0, 4, 0, sa[i], 0, sb);
+            for (int s = 0; s < 4; ++s) {
+              const bf16x8 afr = __builtin_bit_cast(bf16x8, av[i][s]);
+#pragma unroll
+              for (int j = 0; j < FR; ++j) {
+                const uint4 q = bq[j][i];
+                const uint32_t dw = s == 0 ? q.x : s == 1 ? q.y : s == 2 ? q.z : q.w;
+                float sc;
+                if constexpr (WF == B12X_WEIGHT_MXFP4) sc = e8m0_as_scale((bs[j][i] >> (8 * (kf & 3))) & 0xFFu);
+                else sc = e4m3_value((bs[j][i] >> (8 * (2 * (kf & 1) + (s >> 1)))) & 0xFFu);
+                acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr, dequant8_bf16<WF>(dw, sc), acc[j], 0, 0, 0);
+              }
+            }
+          } else {
+            const i32x8 afr = {(int)av[i][0].x, (int)av[i][0].y, (int)av[i][0].z, (int)av[i][0].w,
+                               (int)av[i][1].x, (int)av[i][1].y, (int)av[i][1].z, (int)av[i][1].w};
+#pragma unroll
+            for (int j = 0; j < FR; ++j) {
+              const uint4 q = bq[j][i];
+              const i32x8 bfr = {(int)q.x, (int)q.y, (int)q.z, (int)q.w, 0, 0, 0, 0};
+              const int sb = (int)((bs[j][i] >> (8 * (kf & 3))) & 0xFFu);
+              acc[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(afr, bfr, acc[j], 0, 4, 0, sa[i], 0, sb);
+            }
           }
         }
       }
-    }
-    // ---- split-K partial sums, added in wave order
 #pragma unroll
-    for (int j = 0; j < FR; ++j) s_red[wave][j][lane] = acc[j];
-    __syncthreads();
-    if (wave == 0) {
-      f32x4 v[FR];
+      for (int j = 0; j < FR; ++j) s_red[par][wave][j][lane] = acc[j];
+      __syncthreads();
+      if (wave == 0) {
+        f32x4 v[FR];
 #pragma unroll
-      for (int j = 0; j < FR; ++j) {
-        v[j] = s_red[0][j][lane];
+        for (int j = 0; j < FR; ++j) {
+          v[j] = s_red[par][0][j][lane];
 #pragma unroll
-        for (int w = 1; w < 4; ++w) v[j] += s_red[w][j][lane];
-      }
+          for (int w = 1; w < 4; ++w) v[j] += s_red[par][w][j][lane];
+        }
+        const int f0 = grp * FR;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = r0 + 4 * g + i;
-        const bool live = row < rt.m;
-        const int64_t pr = live ? s_rows[row] : 0;
-        {
-          constexpr int NH = MODE == DMODE_SILU ? FR / 2 : FR;  // h column blocks of 16
-          float hv[NH];
+        for (int i = 0; i < 4; ++i) {
+          const int row = r0 + 4 * g + i;
+          const bool live = row < rt.m;
+          const int64_t pr = live ? s_rows[row] : 0;
+          if constexpr (MODE == DMODE_DOWN) {
 #pragma unroll
-          for (int q = 0; q < NH; ++q) {
-            if constexpr (MODE == DMODE_SILU) {
-              const float gt = v[2 * q][i] * gsc, up = v[2 * q + 1][i] * gsc;
-              hv[q] = gt / (1.0f + __expf(-gt)) * up;
-            } else {
-              const float z = v[q][i] * gsc;
-              hv[q] = z > 0.f ? z * z : 0.f;
-            }
-          }
-          const int hcol0 = MODE == DMODE_SILU ? 16 * (f0 / 2) : 16 * f0;
-          const int nh = MODE == DMODE_SILU ? max(0, min(NH, (p.NF - f0) / 2)) : max(0, min(NH, p.NF - f0));
-          if constexpr (!A8) {
-#pragma unroll
-            for (int q = 0; q < NH; ++q)
-              if (live && q < nh) p.h16[pr * p.h_stride + hcol0 + 16 * q + r16] = (uint16_t)bf16_rne(hv[q]);
+            for (int j = 0; j < FR; ++j)
+              if (live && f0 + j < p.NF) p.y[pr * p.y_stride + 16 * (f0 + j) + r16] = v[j][i] * gsc;
           } else {
+            constexpr int NH = MODE == DMODE_SILU ? FR / 2 : FR;  // h column blocks of 16
+            float hv[NH];
 #pragma unroll
-            for (int blk = 0; blk < NH / 2; ++blk) {
-              if (2 * blk < nh) {
-                float mx = fmaxf(fabsf(hv[2 * blk]), fabsf(hv[2 * blk + 1]));
-                mx = fmaxf(mx, __shfl_xor(mx, 1));
-                mx = fmaxf(mx, __shfl_xor(mx, 2));
-                mx = fmaxf(mx, __shfl_xor(mx, 4));
-                mx = fmaxf(mx, __shfl_xor(mx, 8));
-                const int sx = mx_scale_exp(f32_bits(mx));
-                const int64_t col = hcol0 + 32 * blk + r16;
-                if (live) {
-                  p.h8[pr * p.h_stride + col] = (uint8_t)e4m3_encode_scaled(f32_bits(hv[2 * blk]), sx);
-                  p.h8[pr * p.h_stride + col + 16] = (uint8_t)e4m3_encode_scaled(f32_bits(hv[2 * blk + 1]), sx);
-                  if (r16 == 0) p.hs[pr * p.hs_stride + (hcol0 + 32 * blk) / 32] = (uint8_t)(sx + 127);
+            for (int q = 0; q < NH; ++q) {
+              if constexpr (MODE == DMODE_SILU) {
+                const float gt = v[2 * q][i] * gsc, up = v[2 * q + 1][i] * gsc;
+                hv[q] = gt / (1.0f + __expf(-gt)) * up;
+              } else {
+                const float z = v[q][i] * gsc;
+                hv[q] = z > 0.f ? z * z : 0.f;
+              }
+            }
+            const int hcol0 = MODE == DMODE_SILU ? 16 * (f0 / 2) : 16 * f0;
+            const int nh = MODE == DMODE_SILU ? max(0, min(NH, (p.NF - f0) / 2)) : max(0, min(NH, p.NF - f0));
+            if constexpr (!A8) {
+#pragma unroll
+              for (int q = 0; q < NH; ++q)
+                if (live && q < nh) p.h16[pr * p.h_stride + hcol0 + 16 * q + r16] = (uint16_t)bf16_rne(hv[q]);
+            } else {
+#pragma unroll
+              for (int blk = 0; blk < NH / 2; ++blk) {
+                if (2 * blk < nh) {
+                  float mx = fmaxf(fabsf(hv[2 * blk]), fabsf(hv[2 * blk + 1]));
+                  mx = fmaxf(mx, __shfl_xor(mx, 1));
+                  mx = fmaxf(mx, __shfl_xor(mx, 2));
+                  mx = fmaxf(mx, __shfl_xor(mx, 4));
+                  mx = fmaxf(mx, __shfl_xor(mx, 8));
+                  const int sx = mx_scale_exp(f32_bits(mx));
+                  const int64_t col = hcol0 + 32 * blk + r16;
+                  if (live) {
+                    p.h8[pr * p.h_stride + col] = (uint8_t)e4m3_encode_scaled(f32_bits(hv[2 * blk]), sx);
+                    p.h8[pr * p.h_stride + col + 16] = (uint8_t)e4m3_encode_scaled(f32_bits(hv[2 * blk + 1]), sx);
+                    if (r16 == 0) p.hs[pr * p.hs_stride + (hcol0 + 32 * blk) / 32] = (uint8_t)(sx + 127);
+                  }
                 }
               }
             }
           }
         }
       }
-    }
-    __syncthreads();
-  }
+      par ^= 1;  // the next group writes the other buffer; one barrier per group suffices
+    };
 
-}
-
-// ---- D2: down projection + combine, one output fragment per workgroup ----------
-constexpr int kDownThreads = 512;
-constexpr int kDownWaves = kDownThreads / 64;
-
-template <int WF, int AF, int DEPTH>
-__global__ __launch_bounds__(kDownThreads) void decode_down_kernel(const DecodeParams p) {
-  constexpr bool A8 = AF == B12X_ACT_MXFP8;
-  __shared__ int s_ids[kDecodePairs];
-  __shared__ uint32_t s_bits[kMaxExperts / 32];
-  __shared__ int s_exp[kDecodePairs];  // touched experts, ascending
-  __shared__ int s_ntouched;
-  __shared__ float s_y[kDecodePairs][kFragN];
-
-  const int tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int lane = tid & 63;
-  const int g = lane >> 4, r16 = lane & 15;
-  const int f = blockIdx.x;  // output columns [16 f, 16 f + 16)
-
-  const int words = (p.E + 31) >> 5;
-  for (int i = tid; i < words; i += kDownThreads) s_bits[i] = 0;
-  __syncthreads();
-  for (int q = tid; q < p.P; q += kDownThreads) {
-    const int e = p.ids[q];
-    const bool v = e >= 0 && e < p.E;
-    s_ids[q] = v ? e : -1;
-    if (v) atomicOr(&s_bits[e >> 5], 1u << (e & 31));
-  }
-  __syncthreads();
-  if (wave == 0) {  // the touched experts in ascending order
-    int before = 0;
-    for (int base = 0; base < words; base += 64) {
-      const int w = base + lane;
-      uint32_t bits = w < words ? s_bits[w] : 0u;
-      const int c = __builtin_popcount(bits);
-      int incl = c;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const int t = __shfl_up(incl, off);
-        if (lane >= off) incl += t;
-      }
-      int idx = before + incl - c;
-      while (bits) {
-        s_exp[idx++] = w * 32 + __builtin_ctz(bits);
-        bits &= bits - 1;
-      }
-      before += __shfl(incl, 63);
-    }
-    if (lane == 0) s_ntouched = before;
-  }
-  __syncthreads();
-  const int n_touched = s_ntouched;
-
-  // ---- issue iterator over this wave's (expert slot, row chunk, K fragment) steps
-  int i_slot = wave, i_r0 = 0, i_kf = 0, i_m = 0, i_e = 0, i_pair = -1;
-  auto enter = [&]() {  // rows of expert s_exp[i_slot]: count, and this lane's pair of row i_r0 + r16
-    i_e = s_exp[i_slot];
-    const int want = i_r0 + r16;
-    int base = 0, pair = -1;
-    for (int c = 0; c < p.P; c += 64) {
-      const bool hit = c + lane < p.P && s_ids[c + lane] == i_e;
-      const uint64_t bal = __ballot(hit);
-      const int cnt = __builtin_popcountll(bal);
-      if (pair < 0 && want >= base && want < base + cnt) {
-        uint64_t b = bal;
-        for (int r = want - base; r > 0; --r) b &= b - 1;
-        pair = c + __builtin_ctzll(b);
-      }
-      base += cnt;
-    }
-    i_m = base;
-    i_pair = pair;
-  };
-  if (i_slot < n_touched) enter();
-
-  uint4 rb[DEPTH];
-  uint32_t rs[DEPTH];
-  uint4 ra[DEPTH][A8 ? 2 : 4];
-  int rsa[DEPTH];
-  int rpair[DEPTH];
-  int rmeta[DEPTH];  // bit 9: valid, bit 8: last K fragment of the row chunk, bits 0-7: K fragment
-  float rgs[DEPTH];
-  const int kblocks = (int)(p.K / 32);
-
-  auto issue = [&](int u) {
-    if (i_slot >= n_touched) {
-      rmeta[u] = 0;
-      return;
-    }
-    const int kf = i_kf, e = i_e;
-    rb[u] = *(const uint4*)(p.bcodes + (int64_t)e * p.b_codes_expert + ((int64_t)f * p.KF + kf) * kFragBytes +
-                            lane * 16);
-    const int sg = WF == B12X_WEIGHT_MXFP4 ? kf >> 2 : kf >> 1;
-    rs[u] = *(const uint32_t*)(p.bscales + (int64_t)e * p.b_scales_expert + ((int64_t)f * p.KFS + sg) *
-                               kScaleGroupBytes + lane * 4);
-    const int64_t k0 = (int64_t)kf * kFragK;
-#pragma unroll
-    for (int s = 0; s < (A8 ? 2 : 4); ++s) ra[u][s] = make_uint4(0, 0, 0, 0);
-    rsa[u] = 127;
-    if (i_pair >= 0) {
-      if constexpr (!A8) {
-        if (k0 + 32 * g < p.K) {
-          const uint4* ap = (const uint4*)(p.a16 + (int64_t)i_pair * p.a_stride + k0 + 32 * g);
-#pragma unroll
-          for (int s = 0; s < 4; ++s) ra[u][s] = ap[s];
-        }
-      } else {
-        const uint8_t* ap = p.a8 + (int64_t)i_pair * p.a_stride + k0;
-        if (k0 + 16 * g < p.K) ra[u][0] = *(const uint4*)(ap + 16 * g);
-        if (k0 + 64 + 16 * g < p.K) ra[u][1] = *(const uint4*)(ap + 64 + 16 * g);
-        if (4 * kf + g < kblocks) rsa[u] = p.as[(int64_t)i_pair * p.as_stride + 4 * kf + g];
-      }
-    }
-    rpair[u] = i_pair;
-    rgs[u] = p.bglobal ? p.bglobal[e] : 1.0f;
-    rmeta[u] = kf | ((kf == p.KF - 1) ? 0x100 : 0) | 0x200;
-    if (++i_kf == p.KF) {  // advance
-      i_kf = 0;
-      i_r0 += 16;
-      if (i_r0 >= i_m) {
-        i_r0 = 0;
-        i_slot += kDownWaves;
-      }
-      if (i_slot < n_touched) enter();
-    }
-  };
-
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  auto consume = [&](int u) {
-    const int meta = rmeta[u];
-    const int kf = meta & 0xFF;
-    if constexpr (!A8) {
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const uint32_t dw = s == 0 ? rb[u].x : s == 1 ? rb[u].y : s == 2 ? rb[u].z : rb[u].w;
-        float sc;
-        if constexpr (WF == B12X_WEIGHT_MXFP4) sc = e8m0_as_scale((rs[u] >> (8 * (kf & 3))) & 0xFFu);
-        else sc = e4m3_value((rs[u] >> (8 * (2 * (kf & 1) + (s >> 1)))) & 0xFFu);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ra[u][s]),
-                                                      dequant8_bf16<WF>(dw, sc), acc, 0, 0, 0);
+    // ---- stream the run of fragment groups; with NB = 2 the next group's
+    // loads are in flight while the current group runs on the MFMAs
+    if constexpr (NB == 2) {
+      uint4 bq0[FR][KW], bq1[FR][KW];
+      uint32_t bs0[FR][KW], bs1[FR][KW];
+      load_b(bq0, bs0, g_begin);
+      for (int gi = g_begin; gi < g_end; gi += 2) {
+        if (gi + 1 < g_end) load_b(bq1, bs1, gi + 1);
+        group(bq0, bs0, gi);
+        if (gi + 1 >= g_end) break;
+        if (gi + 2 < g_end) load_b(bq0, bs0, gi + 2);
+        group(bq1, bs1, gi + 1);
       }
     } else {
-      const i32x8 afr = {(int)ra[u][0].x, (int)ra[u][0].y, (int)ra[u][0].z, (int)ra[u][0].w,
-                         (int)ra[u][1].x, (int)ra[u][1].y, (int)ra[u][1].z, (int)ra[u][1].w};
-      const i32x8 bfr = {(int)rb[u].x, (int)rb[u].y, (int)rb[u].z, (int)rb[u].w, 0, 0, 0, 0};
-      const int sb = (int)((rs[u] >> (8 * (kf & 3))) & 0xFFu);
-      acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(afr, bfr, acc, 0, 4, 0, rsa[u], 0, sb);
-    }
-    if (meta & 0x100) {  // row chunk done: y rows by pair into LDS
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int pr = __shfl(rpair[u], 4 * g + i);
-        if (pr >= 0) s_y[pr][r16] = acc[i] * rgs[u];
+      uint4 bq0[FR][KW];
+      uint32_t bs0[FR][KW];
+      for (int gi = g_begin; gi < g_end; ++gi) {
+        load_b(bq0, bs0, gi);
+        group(bq0, bs0, gi);
       }
-      acc = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-  };
-
-#pragma unroll
-  for (int u = 0; u < DEPTH; ++u) issue(u);
-  bool more = true;
-  while (more) {
-    more = false;
-#pragma unroll
-    for (int u = 0; u < DEPTH; ++u) {
-      if (rmeta[u]) {
-        consume(u);
-        more = true;
-      }
-      issue(u);
-    }
-  }
-  __syncthreads();
-
-  // ---- combine this fragment's columns: ascending slot order, one bf16 rounding
-  const int c0 = f * kFragN;
-  for (int i = tid; i < p.T * kFragN; i += kDownThreads) {
-    const int t = i / kFragN, c = i % kFragN;
-    float a = 0.f;
-    for (int j = 0; j < p.k; ++j) {
-      const int q = t * p.k + j;
-      if (s_ids[q] >= 0) a = fmaf(p.tw[q], s_y[q][c], a);
-    }
-    p.out[(int64_t)t * p.out_stride + c0 + c] = (uint16_t)bf16_rne(a);
   }
 }
 
-template <int MODE, int FR, int KW>
-static int launch_decode_kw(const BindingImpl& b, const DecodeParams& p, int n_slots, hipStream_t s) {
-  const dim3 grid((unsigned)(n_slots * p.n_groups));
-  const bool nv = b.wfmt == B12X_WEIGHT_NVFP4, a8 = b.afmt == B12X_ACT_MXFP8;
-  if (a8)
-    hipLaunchKernelGGL((decode_kernel<B12X_WEIGHT_MXFP4, B12X_ACT_MXFP8, MODE, FR, KW>), grid, dim3(kDecThreads), 0,
-                       s, p);
-  else if (nv)
-    hipLaunchKernelGGL((decode_kernel<B12X_WEIGHT_NVFP4, B12X_ACT_BF16, MODE, FR, KW>), grid, dim3(kDecThreads), 0,
-                       s, p);
-  else
-    hipLaunchKernelGGL((decode_kernel<B12X_WEIGHT_MXFP4, B12X_ACT_BF16, MODE, FR, KW>), grid, dim3(kDecThreads), 0,
-                       s, p);
+template <int WF, int AF, int MODE, int FR, int KW>
+static int launch_decode_kw(const DecodeParams& p, int n_slots, hipStream_t s) {
+  constexpr int NB = FR * KW <= 8 ? 2 : 1;  // double-buffer the weights while registers allow
+  const dim3 grid((unsigned)(n_slots * p.n_runs));
+  hipLaunchKernelGGL((decode_kernel<WF, AF, MODE, FR, KW, NB>), grid, dim3(kDecThreads), 0, s, p);
   return (int)hipGetLastError();
 }
 
+static int decode_slots(const BindingImpl& b) { return (int)(b.T * b.k < b.E ? b.T * b.k : b.E); }
+
+// Fragment groups per workgroup: enough workgroups to cover the chip twice,
+// at most 8 groups in one run.
+static void set_runs(DecodeParams& p, int n_slots) {
+  const int64_t items = (int64_t)n_slots * p.n_groups;
+  int ng = (int)((items + 511) / 512);
+  ng = ng < 1 ? 1 : (ng > 8 ? 8 : ng);
+  p.ng = ng;
+  p.n_runs = (p.n_groups + ng - 1) / ng;
+}
+
 // K fragments per wave: the smallest of 2, 4, 8 that covers ceil(KF / 4).
-template <int MODE, int FR>
-static int launch_decode_t(const BindingImpl& b, const DecodeParams& p, int n_slots, hipStream_t s) {
+template <int WF, int AF, int MODE, int FR>
+static int launch_decode_t(const BindingImpl& b, DecodeParams& p, hipStream_t s) {
+  const int n_slots = decode_slots(b);
+  p.n_groups = (p.NF + FR - 1) / FR;
+  set_runs(p, n_slots);
   const int kper = (p.KF + 3) / 4;
-  if (kper <= 2) return launch_decode_kw<MODE, FR, 2>(b, p, n_slots, s);
-  if (kper <= 4) return launch_decode_kw<MODE, FR, 4>(b, p, n_slots, s);
-  return launch_decode_kw<MODE, FR, 8>(b, p, n_slots, s);
+  if (kper <= 2) return launch_decode_kw<WF, AF, MODE, FR, 2>(p, n_slots, s);
+  if (kper <= 4) return launch_decode_kw<WF, AF, MODE, FR, 4>(p, n_slots, s);
+  return launch_decode_kw<WF, AF, MODE, FR, 8>(p, n_slots, s);
+}
+
+template <int MODE, int FR>
+static int launch_decode_fmt(const BindingImpl& b, DecodeParams& p, hipStream_t s) {
+  if (b.afmt == B12X_ACT_MXFP8) return launch_decode_t<B12X_WEIGHT_MXFP4, B12X_ACT_MXFP8, MODE, FR>(b, p, s);
+  if (b.wfmt == B12X_WEIGHT_NVFP4) return launch_decode_t<B12X_WEIGHT_NVFP4, B12X_ACT_BF16, MODE, FR>(b, p, s);
+  return launch_decode_t<B12X_WEIGHT_MXFP4, B12X_ACT_BF16, MODE, FR>(b, p, s);
 }
 
 static DecodeParams common_params(const BindingImpl& b) {
@@ -533,8 +382,6 @@ static DecodeParams common_params(const BindingImpl& b) {
   p.P = (int)(b.T * b.k);
   return p;
 }
-
-static int decode_slots(const BindingImpl& b) { return (int)(b.T * b.k < b.E ? b.T * b.k : b.E); }
 
 int launch_decode1(const BindingImpl& b, hipStream_t s) {
   DecodeParams p = common_params(b);
@@ -559,22 +406,14 @@ int launch_decode1(const BindingImpl& b, hipStream_t s) {
   p.hs = b.hs;
   p.h_stride = b.Ip;
   p.hs_stride = b.Ip / 32;
-  const int n_slots = decode_slots(b);
-  if (b.gated) {
-    if (a8) {  // an MXFP8 block of h (32 columns) needs two gate/up pairs
-      p.n_groups = (p.NF + 3) / 4;
-      return launch_decode_t<DMODE_SILU, 4>(b, p, n_slots, s);
-    }
-    p.n_groups = (p.NF + 1) / 2;
-    return launch_decode_t<DMODE_SILU, 2>(b, p, n_slots, s);
-  }
-  p.n_groups = (p.NF + 1) / 2;
-  return launch_decode_t<DMODE_RELU2, 2>(b, p, n_slots, s);
+  if (b.gated && a8)  // an MXFP8 block of h (32 columns) = two gate/up pairs
+    return launch_decode_t<B12X_WEIGHT_MXFP4, B12X_ACT_MXFP8, DMODE_SILU, 4>(b, p, s);
+  if (b.gated) return launch_decode_fmt<DMODE_SILU, 2>(b, p, s);
+  return launch_decode_fmt<DMODE_RELU2, 2>(b, p, s);
 }
 
 int launch_decode2(const BindingImpl& b, hipStream_t s) {
   DecodeParams p = common_params(b);
-  const bool a8 = b.afmt == B12X_ACT_MXFP8, nv = b.wfmt == B12X_WEIGHT_NVFP4;
   p.a16 = (const uint16_t*)b.h;
   p.a8 = (const uint8_t*)b.h;
   p.as = b.hs;
@@ -590,16 +429,11 @@ int launch_decode2(const BindingImpl& b, hipStream_t s) {
   p.b_scales_expert = b.nf2 * b.kfs2 * kScaleGroupBytes;
   p.NF = (int)b.nf2;
   p.KFS = (int)b.kfs2;
-  p.out = b.out;
-  p.out_stride = b.out_stride;
-  const dim3 grid((unsigned)p.NF), block(kDownThreads);
-  if (a8)
-    hipLaunchKernelGGL((decode_down_kernel<B12X_WEIGHT_MXFP4, B12X_ACT_MXFP8, 8>), grid, block, 0, s, p);
-  else if (nv)
-    hipLaunchKernelGGL((decode_down_kernel<B12X_WEIGHT_NVFP4, B12X_ACT_BF16, 6>), grid, block, 0, s, p);
-  else
-    hipLaunchKernelGGL((decode_down_kernel<B12X_WEIGHT_MXFP4, B12X_ACT_BF16, 6>), grid, block, 0, s, p);
-  return (int)hipGetLastError();
+  p.y = b.y;
+  p.y_stride = b.H;
+  // 4 fragments (64 output columns) per group unless 8 K fragments per wave need the registers
+  if ((p.KF + 3) / 4 > 4) return launch_decode_fmt<DMODE_DOWN, 2>(b, p, s);
+  return launch_decode_fmt<DMODE_DOWN, 4>(b, p, s);
 }
 
 }  // namespace b12x

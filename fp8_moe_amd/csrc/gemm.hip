@@ -6,10 +6,10 @@
 //   GEMM1: h[row] = act(x[token(row)] . W13_e^T)   (SiLU-gated or ReLU^2)
 //   GEMM2: y[row] = h[row] . W2_e^T
 // over the routing tiles (expert, first row, rows).  A workgroup of 4 waves
-// owns 128 rows x 8 weight fragments (128 output columns); wave (wm, wn)
-// computes rows [64 wm, 64 wm + 64) x fragments [4 wn, 4 wn + 4).  The A rows
-// (bf16 or MXFP8 codes) go through double-buffered LDS; the packed FP4
-// fragments stream from global memory straight into registers.
+// owns 128 rows x 4*NFW weight fragments (16 columns each).  The A rows (bf16
+// or MXFP8 codes) go through double-buffered LDS with a two-step register
+// prefetch; the packed FP4 fragments stream from global memory straight into
+// registers, two K steps ahead.
 //   W4A16: each 1 KB fragment is four 16x16x32 bf16 MFMA operands; FP4 is
 //          turned into bf16 in registers (v_cvt_scalef32_pk_bf16_fp4 with the
 //          E8M0 scale, or fp32 conversion times the E4M3 scale for NVFP4; both
@@ -17,6 +17,8 @@
 //   W4A8:  each fragment is one 16x16x128 scaled MFMA operand (fp8 A x fp4 B,
 //          one E8M0 scale per lane on each side).
 // The NVFP4 per-expert fp32 scale multiplies the fp32 accumulators.
+#include <type_traits>
+
 #include "device_common.h"
 
 namespace b12x {
@@ -62,42 +64,56 @@ struct GemmParams {
 
 enum { MODE_SILU = 1, MODE_RELU2 = 2, MODE_DOWN = 3 };
 
-template <int WF, int AF, int MODE>
-__global__ __launch_bounds__(kGemmThreads, 2) void moe_gemm_kernel(const GemmParams p) {
+// Work items are (tile, N tile); the items are split into 8 contiguous ranges,
+// one per XCD (workgroup i runs on XCD i % 8), so that the workgroups sharing
+// an L2 work on the same row tiles (A reuse) and the same experts (B reuse).
+//
+// Wave w owns all 128 rows of the tile and weight fragments [NFW w, NFW w +
+// NFW): every fragment is dequantized by exactly one wave.  A full tile (128
+// rows) runs a branch-free MFMA loop; a partial tile skips whole 16-row
+// blocks.  Missing fragments (a partial N tile) load a clamped fragment and
+// are dropped in the epilogue.
+template <int WF, int AF, int MODE, int NFW>
+__global__ __launch_bounds__(kGemmThreads, 1) void moe_gemm_kernel(const GemmParams p) {
   constexpr bool A8 = AF == B12X_ACT_MXFP8;
   constexpr int ROWB = A8 ? 144 : 272;  // LDS bytes per A row: 128 K elements + 16 bytes of skew
+  constexpr int NT = 4 * NFW;           // weight fragments per workgroup tile
+  constexpr int LOADS = (kTileRows * (A8 ? 8 : 16) + kGemmThreads - 1) / kGemmThreads;  // A row chunks per thread
+  constexpr int CHUNKS = A8 ? 8 : 16;   // 16-byte chunks per 128-element row
+  constexpr int MF = kTileRows / 16;    // 16-row blocks per tile
+  static_assert(kTileRows % 16 == 0 && kTileRows <= kGemmThreads, "tile rows");
   __shared__ __attribute__((aligned(16))) uint8_t lds_a[2][kTileRows * ROWB];
   __shared__ uint32_t lds_s[2][A8 ? kTileRows : 1];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
-  const int wm = wave >> 1, wn = wave & 1;
   const int g = lane >> 4, r16 = lane & 15;
-  const int total = min(max(p.ntiles[0], 0), p.max_tiles) * p.n_ntiles;
+  const int c = tid % CHUNKS;
 
-  for (int w = blockIdx.x; w < total; w += gridDim.x) {
+  const int n_items = min(max(p.ntiles[0], 0), p.max_tiles) * p.n_ntiles;
+  const int xcd = blockIdx.x & 7, n_local = gridDim.x >> 3;
+  const int lo = (int)((int64_t)n_items * xcd / 8), hi = (int)((int64_t)n_items * (xcd + 1) / 8);
+
+  for (int w = lo + (int)(blockIdx.x >> 3); w < hi; w += n_local) {
     const int tile = w / p.n_ntiles;
     const int nt = w - tile * p.n_ntiles;
     const int e = p.tiles[4 * tile], row0 = p.tiles[4 * tile + 1], nrows = p.tiles[4 * tile + 2];
     if (e < 0 || e >= p.E || row0 < 0 || nrows <= 0 || nrows > kTileRows || row0 + nrows > p.max_rows) continue;
-    const int nmf = max(0, min(4, (nrows - 64 * wm + 15) / 16));
-    const int f0 = nt * kTileFrags + wn * 4;
-    const int nnf = max(0, min(4, p.NF - f0));
+    const int nmf = (nrows + 15) / 16;
+    const int f0 = nt * NT + wave * NFW;
+    const int nnf = max(0, min(NFW, p.NF - f0));
     const uint8_t* bcodes = p.bcodes + (int64_t)e * p.b_codes_expert;
     const uint8_t* bscales = p.bscales + (int64_t)e * p.b_scales_expert;
     const float gsc = p.bglobal ? p.bglobal[e] : 1.0f;
 
-    // ---- A-row sources for this thread's loads
-    constexpr int LOADS = A8 ? 4 : 8;           // rows loaded per thread per K fragment
-    constexpr int CHUNKS = A8 ? 8 : 16;         // 16-byte chunks per 128-element row
-    const int c = tid % CHUNKS;
-    int64_t src_row[LOADS];
+    // ---- A-row sources for this thread's loads (token or row index, -1 = zero row)
+    int src_row[LOADS];
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
       const int rr = tid / CHUNKS + (kGemmThreads / CHUNKS) * i;
-      int64_t sr = -1;
-      if (rr < nrows) {
+      int sr = -1;
+      if (rr < nrows && rr < kTileRows) {
         if (p.sorted) {
           const int pair = p.sorted[row0 + rr];
           sr = (pair >= 0 && pair < p.n_pairs) ? pair / p.k_top : -1;
@@ -107,7 +123,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void moe_gemm_kernel(const GemmPar
       }
       src_row[i] = sr;
     }
-    int64_t s_row = -1;  // A8: scale row loaded by threads 0..127
+    int s_row = -1;  // A8: scale row loaded by threads 0..127
     if (A8 && tid < kTileRows && tid < nrows) {
       if (p.sorted) {
         const int pair = p.sorted[row0 + tid];
@@ -118,16 +134,14 @@ __global__ __launch_bounds__(kGemmThreads, 2) void moe_gemm_kernel(const GemmPar
     }
     const int kblocks = (int)(p.K / 32);
 
-    uint4 ra[LOADS];
-    uint32_t rs = 0;
-    auto load_a = [&](int kf) {
+    auto load_a = [&](uint4 (&ra)[LOADS], uint32_t& rs, int kf) {
       const int64_t k0 = (int64_t)kf * kFragK + (A8 ? 16 : 8) * c;
 #pragma unroll
       for (int i = 0; i < LOADS; ++i) {
         ra[i] = make_uint4(0, 0, 0, 0);
         if (src_row[i] >= 0 && k0 < p.K) {
-          if constexpr (A8) ra[i] = *(const uint4*)(p.a8 + src_row[i] * p.a_stride + k0);
-          else ra[i] = *(const uint4*)(p.a16 + src_row[i] * p.a_stride + k0);
+          if constexpr (A8) ra[i] = *(const uint4*)(p.a8 + (int64_t)src_row[i] * p.a_stride + k0);
+          else ra[i] = *(const uint4*)(p.a16 + (int64_t)src_row[i] * p.a_stride + k0);
         }
       }
       if constexpr (A8) {
@@ -137,130 +151,174 @@ __global__ __launch_bounds__(kGemmThreads, 2) void moe_gemm_kernel(const GemmPar
 #pragma unroll
           for (int b = 0; b < 4; ++b) {
             const int blk = kf * 4 + b;
-            const uint32_t v = blk < kblocks ? p.as[s_row * p.as_stride + blk] : 127u;
+            const uint32_t v = blk < kblocks ? p.as[(int64_t)s_row * p.as_stride + blk] : 127u;
             word |= v << (8 * b);
           }
           rs = word;
         }
       }
     };
-    auto store_a = [&](int buf) {
+    auto store_a = [&](const uint4 (&ra)[LOADS], uint32_t rs, int buf) {
 #pragma unroll
       for (int i = 0; i < LOADS; ++i) {
         const int rr = tid / CHUNKS + (kGemmThreads / CHUNKS) * i;
-        *(uint4*)(&lds_a[buf][rr * ROWB + 16 * c]) = ra[i];
+        if ((kTileRows * CHUNKS) % kGemmThreads == 0 || rr < kTileRows)
+          *(uint4*)(&lds_a[buf][rr * ROWB + 16 * c]) = ra[i];
       }
       if constexpr (A8) {
         if (tid < kTileRows) lds_s[buf][tid] = rs;
       }
     };
-    uint4 bq[4], bq_next[4];
-    uint32_t bs[4], bs_next[4];
-    auto load_b = [&](int kf, uint4* q, uint32_t* sc) {
+    const int flast = p.NF - 1;
+    auto load_b = [&](uint4 (&q)[NFW], uint32_t (&sc)[NFW], int kf) {
       const int sgrp = WF == B12X_WEIGHT_MXFP4 ? kf >> 2 : kf >> 1;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        if (j < nnf) {
-          const int f = f0 + j;
-          q[j] = *(const uint4*)(bcodes + ((int64_t)f * p.KF + kf) * kFragBytes + lane * 16);
-          sc[j] = *(const uint32_t*)(bscales + ((int64_t)f * p.KFS + sgrp) * kScaleGroupBytes + lane * 4);
-        }
+      for (int j = 0; j < NFW; ++j) {
+        const int f = min(f0 + j, flast);
+        q[j] = *(const uint4*)(bcodes + ((int64_t)f * p.KF + kf) * kFragBytes + lane * 16);
+        sc[j] = *(const uint32_t*)(bscales + ((int64_t)f * p.KFS + sgrp) * kScaleGroupBytes + lane * 4);
       }
     };
 
-    f32x4 acc[4][4];
+    f32x4 acc[MF][NFW];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < MF; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < NFW; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    __syncthreads();  // the previous work item is done with LDS
-    load_a(0);
-    store_a(0);
-    load_b(0, bq, bs);
-
-    for (int kf = 0; kf < p.KF; ++kf) {
-      __syncthreads();
-      const int buf = kf & 1;
-      const bool more = kf + 1 < p.KF;
-      if (more) {
-        load_a(kf + 1);
-        load_b(kf + 1, bq_next, bs_next);
-      }
+    // MFMAs of one K fragment over the first NMF 16-row blocks.  W4A16: the
+    // bf16 operands of sub-step s+1 (dequantized weights, LDS activation
+    // reads) are produced while sub-step s runs on the MFMAs; the schedule
+    // interleaves them so the VALU works under the matrix core.
+    auto compute = [&](auto nmf_tag, int buf, const uint4 (&bq)[NFW], const uint32_t (&bs)[NFW], int kf) {
+      constexpr int NMF = decltype(nmf_tag)::value;
       const uint8_t* la = lds_a[buf];
       if constexpr (!A8) {
+        float scl[NFW][2];  // per fragment: scale of the lane's first / second 16 K (NVFP4), or the E8M0 scale
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          bf16x8 bfr[4];
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            if (j < nnf) {
-              const uint32_t dw = s == 0 ? bq[j].x : s == 1 ? bq[j].y : s == 2 ? bq[j].z : bq[j].w;
-              float sc;
-              if constexpr (WF == B12X_WEIGHT_MXFP4) sc = e8m0_as_scale((bs[j] >> (8 * (kf & 3))) & 0xFFu);
-              else sc = e4m3_value((bs[j] >> (8 * (2 * (kf & 1) + (s >> 1)))) & 0xFFu);
-              bfr[j] = dequant8_bf16<WF>(dw, sc);
-            }
-          }
-#pragma unroll
-          for (int mf = 0; mf < 4; ++mf) {
-            if (mf < nmf) {
-              const int row = 64 * wm + 16 * mf + r16;
-              const uint4 av = *(const uint4*)(la + row * ROWB + 64 * g + 16 * s);
-              const bf16x8 afr = u32x4_as_bf16x8(av.x, av.y, av.z, av.w);
-#pragma unroll
-              for (int j = 0; j < 4; ++j)
-                if (j < nnf) acc[mf][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr, bfr[j], acc[mf][j], 0, 0, 0);
-            }
+        for (int j = 0; j < NFW; ++j) {
+          if constexpr (WF == B12X_WEIGHT_MXFP4) {
+            scl[j][0] = scl[j][1] = e8m0_as_scale((bs[j] >> (8 * (kf & 3))) & 0xFFu);
+          } else {
+            scl[j][0] = e4m3_value((bs[j] >> (16 * (kf & 1))) & 0xFFu);
+            scl[j][1] = e4m3_value((bs[j] >> (16 * (kf & 1) + 8)) & 0xFFu);
           }
         }
-      } else {
-        i32x8 bfr[4];
-        int sb[4];
+        auto dq = [&](bf16x8 (&out)[NFW], int s) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+          for (int j = 0; j < NFW; ++j) {
+            const uint32_t dw = s == 0 ? bq[j].x : s == 1 ? bq[j].y : s == 2 ? bq[j].z : bq[j].w;
+            out[j] = dequant8_bf16<WF>(dw, scl[j][s >> 1]);
+          }
+        };
+        auto ld = [&](uint4 (&out)[NMF], int s) {
+#pragma unroll
+          for (int mf = 0; mf < NMF; ++mf) out[mf] = *(const uint4*)(la + (16 * mf + r16) * ROWB + 64 * g + 16 * s);
+        };
+        bf16x8 b0[NFW], b1[NFW];
+        uint4 a0[NMF], a1[NMF];
+        dq(b0, 0);
+        ld(a0, 0);
+        auto step = [&](const bf16x8 (&bc)[NFW], const uint4 (&ac)[NMF], bf16x8 (&bn)[NFW], uint4 (&an)[NMF],
+                        int s) {
+          if (s < 3) {
+            ld(an, s + 1);
+            dq(bn, s + 1);
+          }
+#pragma unroll
+          for (int mf = 0; mf < NMF; ++mf) {
+            const bf16x8 afr = __builtin_bit_cast(bf16x8, ac[mf]);
+#pragma unroll
+            for (int j = 0; j < NFW; ++j)
+              acc[mf][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr, bc[j], acc[mf][j], 0, 0, 0);
+          }
+          if (s < 3) {
+            // NMF*NFW MFMAs, each followed by a share of the next sub-step's VALU and LDS work
+#pragma unroll
+            for (int i = 0; i < NMF * NFW; ++i) {
+              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+              __builtin_amdgcn_sched_group_barrier(0x002, WF == B12X_WEIGHT_NVFP4 ? 4 : 2, 0);  // VALU
+              __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+            }
+          }
+        };
+        step(b0, a0, b1, a1, 0);
+        step(b1, a1, b0, a0, 1);
+        step(b0, a0, b1, a1, 2);
+        step(b1, a1, b0, a0, 3);
+      } else {
+        i32x8 bfr[NFW];
+        int sb[NFW];
+#pragma unroll
+        for (int j = 0; j < NFW; ++j) {
           bfr[j] = i32x8{(int)bq[j].x, (int)bq[j].y, (int)bq[j].z, (int)bq[j].w, 0, 0, 0, 0};
           sb[j] = (int)((bs[j] >> (8 * (kf & 3))) & 0xFFu);
         }
 #pragma unroll
-        for (int mf = 0; mf < 4; ++mf) {
-          if (mf < nmf) {
-            const int row = 64 * wm + 16 * mf + r16;
-            const uint4 a0 = *(const uint4*)(la + row * ROWB + 16 * g);
-            const uint4 a1 = *(const uint4*)(la + row * ROWB + 64 + 16 * g);
-            const i32x8 afr = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w,
-                               (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
-            const int sa = (int)((lds_s[buf][row] >> (8 * g)) & 0xFFu);
+        for (int mf = 0; mf < NMF; ++mf) {
+          const int row = 16 * mf + r16;
+          const uint4 x0 = *(const uint4*)(la + row * ROWB + 16 * g);
+          const uint4 x1 = *(const uint4*)(la + row * ROWB + 64 + 16 * g);
+          const i32x8 afr = {(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+          const int sa = (int)((lds_s[buf][row] >> (8 * g)) & 0xFFu);
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-              if (j < nnf)
-                acc[mf][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(afr, bfr[j], acc[mf][j], 0, 4, 0, sa,
-                                                                               0, sb[j]);
-          }
+          for (int j = 0; j < NFW; ++j)
+            acc[mf][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(afr, bfr[j], acc[mf][j], 0, 4, 0, sa, 0,
+                                                                           sb[j]);
         }
       }
-      if (more) {
-        store_a(buf ^ 1);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          bq[j] = bq_next[j];
-          bs[j] = bs_next[j];
-        }
+    };
+
+    // ---- main loop.  A: global loads of step kf+2 are issued at step kf into
+    // the register stage of that parity and written to LDS at the end of step
+    // kf+1; B: loads of step kf+2 are issued after step kf's MFMAs.  The whole
+    // loop is instantiated per count of 16-row blocks (9, or rounded up to even).
+    const bool idle = nnf == 0;  // this wave has no fragments in a partial N tile
+    auto kloop = [&](auto nmf_tag) {
+      uint4 ra0[LOADS], ra1[LOADS];
+      uint32_t rs0 = 0, rs1 = 0;
+      uint4 bq0[NFW], bq1[NFW];
+      uint32_t bs0[NFW], bs1[NFW];
+      __syncthreads();  // the previous work item is done with LDS
+      load_a(ra0, rs0, 0);
+      store_a(ra0, rs0, 0);
+      if (p.KF > 1) load_a(ra1, rs1, 1);
+      load_b(bq0, bs0, 0);
+      if (p.KF > 1) load_b(bq1, bs1, 1);
+      for (int kf = 0; kf < p.KF; kf += 2) {
+        // even step: LDS buffer 0, ra1 holds step kf+1
+        __syncthreads();
+        if (kf + 2 < p.KF) load_a(ra0, rs0, kf + 2);
+        if (!idle) compute(nmf_tag, 0, bq0, bs0, kf);
+        if (kf + 1 < p.KF) store_a(ra1, rs1, 1);
+        if (kf + 2 < p.KF) load_b(bq0, bs0, kf + 2);
+        if (kf + 1 >= p.KF) break;
+        // odd step: LDS buffer 1, ra0 holds step kf+2
+        __syncthreads();
+        if (kf + 3 < p.KF) load_a(ra1, rs1, kf + 3);
+        if (!idle) compute(nmf_tag, 1, bq1, bs1, kf + 1);
+        if (kf + 2 < p.KF) store_a(ra0, rs0, 0);
+        if (kf + 3 < p.KF) load_b(bq1, bs1, kf + 3);
       }
-    }
+    };
+    if (nmf > 8) kloop(std::integral_constant<int, 9>{});
+    else if (nmf > 6) kloop(std::integral_constant<int, 8>{});
+    else if (nmf > 4) kloop(std::integral_constant<int, 6>{});
+    else if (nmf > 2) kloop(std::integral_constant<int, 4>{});
+    else kloop(std::integral_constant<int, 2>{});
 
     // ---- epilogue: lane holds column r16 of each fragment, rows 4 g + i of each 16-row block
     if constexpr (MODE == MODE_DOWN) {
 #pragma unroll
-      for (int mf = 0; mf < 4; ++mf) {
+      for (int mf = 0; mf < MF; ++mf) {
         if (mf < nmf) {
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
+          for (int j = 0; j < NFW; ++j) {
             if (j < nnf) {
               const int col = 16 * (f0 + j) + r16;
 #pragma unroll
               for (int i = 0; i < 4; ++i) {
-                const int64_t row = row0 + 64 * wm + 16 * mf + 4 * g + i;
+                const int64_t row = row0 + 16 * mf + 4 * g + i;
                 p.y[row * p.y_stride + col] = acc[mf][j][i] * gsc;
               }
             }
@@ -268,22 +326,22 @@ __global__ __launch_bounds__(kGemmThreads, 2) void moe_gemm_kernel(const GemmPar
         }
       }
     } else {
-      // activation values: gated -> 2 columns (pairs 0, 1); relu2 -> 4 columns
-      constexpr int NH = MODE == MODE_SILU ? 2 : 4;
+      // activation values: gated -> NFW/2 column blocks (gate/up pairs); relu2 -> NFW blocks
+      constexpr int NH = MODE == MODE_SILU ? NFW / 2 : NFW;
       const int nh = MODE == MODE_SILU ? nnf / 2 : nnf;
       const int hcol0 = MODE == MODE_SILU ? 16 * (f0 / 2) : 16 * f0;
 #pragma unroll
-      for (int mf = 0; mf < 4; ++mf) {
+      for (int mf = 0; mf < MF; ++mf) {
         if (mf < nmf) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const int64_t row = row0 + 64 * wm + 16 * mf + 4 * g + i;
+            const int64_t row = row0 + 16 * mf + 4 * g + i;
             float hv[NH];
 #pragma unroll
             for (int q = 0; q < NH; ++q) {
               if constexpr (MODE == MODE_SILU) {
                 const float gt = acc[mf][2 * q][i] * gsc, up = acc[mf][2 * q + 1][i] * gsc;
-                hv[q] = gt / (1.0f + __expf(-gt)) * up;
+                hv[q] = gt * __builtin_amdgcn_rcpf(1.0f + __expf(-gt)) * up;
               } else {
                 const float z = acc[mf][q][i] * gsc;
                 hv[q] = z > 0.f ? z * z : 0.f;
@@ -294,7 +352,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void moe_gemm_kernel(const GemmPar
               for (int q = 0; q < NH; ++q)
                 if (q < nh) p.h16[row * p.h_stride + hcol0 + 16 * q + r16] = (uint16_t)bf16_rne(hv[q]);
             } else {
-              // MXFP8 blocks of 32 columns = column groups (0, 1) and (2, 3)
+              // MXFP8 blocks of 32 columns = column blocks (2b, 2b+1)
 #pragma unroll
               for (int blk = 0; blk < NH / 2; ++blk) {
                 if (2 * blk < nh) {
@@ -303,11 +361,11 @@ __global__ __launch_bounds__(kGemmThreads, 2) void moe_gemm_kernel(const GemmPar
                   m = fmaxf(m, __shfl_xor(m, 2));
                   m = fmaxf(m, __shfl_xor(m, 4));
                   m = fmaxf(m, __shfl_xor(m, 8));
-                  const int s = mx_scale_exp(f32_bits(m));
+                  const int sx = mx_scale_exp(f32_bits(m));
                   const int64_t col = hcol0 + 32 * blk + r16;
-                  p.h8[row * p.h_stride + col] = (uint8_t)e4m3_encode_scaled(f32_bits(hv[2 * blk]), s);
-                  p.h8[row * p.h_stride + col + 16] = (uint8_t)e4m3_encode_scaled(f32_bits(hv[2 * blk + 1]), s);
-                  if (r16 == 0) p.hs[row * p.hs_stride + (hcol0 + 32 * blk) / 32] = (uint8_t)(s + 127);
+                  p.h8[row * p.h_stride + col] = (uint8_t)e4m3_encode_scaled(f32_bits(hv[2 * blk]), sx);
+                  p.h8[row * p.h_stride + col + 16] = (uint8_t)e4m3_encode_scaled(f32_bits(hv[2 * blk + 1]), sx);
+                  if (r16 == 0) p.hs[row * p.hs_stride + (hcol0 + 32 * blk) / 32] = (uint8_t)(sx + 127);
                 }
               }
             }
@@ -331,12 +389,16 @@ static int cu_count() {
   return g_cu_count[dev];
 }
 
+constexpr int kGemmNFW = 4;  // weight fragments per wave: workgroup tile 128 rows x 256 columns
+
 template <int WF, int AF, int MODE>
 static int launch_gemm_t(const GemmParams& p, int64_t max_work, hipStream_t s) {
-  const int64_t cap = (int64_t)cu_count() * 2;
-  const int64_t grid = max_work < cap ? max_work : cap;
-  if (grid <= 0) return 0;
-  hipLaunchKernelGGL((moe_gemm_kernel<WF, AF, MODE>), dim3((unsigned)grid), dim3(kGemmThreads), 0, s, p);
+  // persistent grid: one workgroup per CU, a multiple of 8 (one share per XCD)
+  int64_t grid = cu_count();
+  if (max_work < grid) grid = (max_work + 7) / 8 * 8;
+  grid = grid / 8 * 8;
+  if (grid <= 0) grid = 8;
+  hipLaunchKernelGGL((moe_gemm_kernel<WF, AF, MODE, kGemmNFW>), dim3((unsigned)grid), dim3(kGemmThreads), 0, s, p);
   return (int)hipGetLastError();
 }
 
@@ -356,7 +418,7 @@ int launch_gemm1(const BindingImpl& b, hipStream_t s) {
   p.max_tiles = (int)b.max_tiles;
   p.max_rows = (int)b.max_rows;
   p.E = b.E;
-  p.n_ntiles = (int)((b.nf13 + kTileFrags - 1) / kTileFrags);
+  p.n_ntiles = (int)((b.nf13 + 4 * kGemmNFW - 1) / (4 * kGemmNFW));
   p.a16 = b.a;
   p.a8 = b.xq;
   p.as = b.xs;
@@ -391,7 +453,7 @@ int launch_gemm2(const BindingImpl& b, hipStream_t s) {
   p.max_tiles = (int)b.max_tiles;
   p.max_rows = (int)b.max_rows;
   p.E = b.E;
-  p.n_ntiles = (int)((b.nf2 + kTileFrags - 1) / kTileFrags);
+  p.n_ntiles = (int)((b.nf2 + 4 * kGemmNFW - 1) / (4 * kGemmNFW));
   p.a16 = (const uint16_t*)b.h;
   p.a8 = (const uint8_t*)b.h;
   p.as = b.hs;

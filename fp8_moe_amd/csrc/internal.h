@@ -32,9 +32,8 @@ constexpr int kScaleGroupBytes = 256;
 constexpr uint32_t kLayoutId = 0x4d4f4501u;  // "MOE", version 1
 
 // ---- grouped path ------------------------------------------------------------
-constexpr int kTileRows = 128;   // rows per GEMM tile (multiple of kRowPad)
+constexpr int kTileRows = 144;   // most rows per GEMM tile (multiple of kRowPad)
 constexpr int kRowPad = 16;      // per-expert row padding = MFMA row block
-constexpr int kTileFrags = 8;    // 16-row weight fragments per GEMM tile (N = 128)
 constexpr int kRouteChunk = 1024;  // routing pairs per workgroup
 constexpr int kMaxExperts = 1024;
 // ---- decode path -------------------------------------------------------------
@@ -135,6 +134,7 @@ int launch_gemm2(const BindingImpl& b, hipStream_t s);
 int launch_combine(const BindingImpl& b, hipStream_t s);
 int launch_decode1(const BindingImpl& b, hipStream_t s);
 int launch_decode2(const BindingImpl& b, hipStream_t s);
+int launch_decode_combine(const BindingImpl& b, hipStream_t s);
 const char* hip_error_name(int err);
 
 }  // namespace b12x

@@ -3,7 +3,8 @@
 // experts run on a persistent grid).  Produces, for pair p = t*k + j:
 // per-expert counts, exclusive offsets, offsets of rows padded per expert to
 // kRowPad, the stable expert-major permutation of the pairs (padding rows -1),
-// each pair's row and the list of (expert, first row, rows) GEMM tiles.
+// each pair's row and the list of (expert, first row, rows) GEMM tiles (each
+// expert's rows split evenly into the fewest tiles of at most kTileRows).
 // Three launches: per-chunk histograms, one scan workgroup, per-chunk scatter.
 // Integer atomics only touch LDS counters whose final values are
 // order-independent; every written position is deterministic.
@@ -67,7 +68,11 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(int E, int n_chunks, i
     }
   }
   const int padded = (cnt + kRowPad - 1) / kRowPad * kRowPad;
-  const int n_t = (padded + kTileRows - 1) / kTileRows;
+  // balanced tiles: the expert's 16-row blocks split as evenly as possible into
+  // the fewest tiles of at most kTileRows rows (larger tiles first)
+  constexpr int kTileBlocks = kTileRows / kRowPad;
+  const int nb = padded / kRowPad;
+  const int n_t = (nb + kTileBlocks - 1) / kTileBlocks;
   int tot_cnt, tot_pad, tot_tiles;
   const int off = block_exclusive_scan(cnt, lds, &tot_cnt);
   const int poffe = block_exclusive_scan(padded, lds, &tot_pad);
@@ -77,9 +82,10 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(int E, int n_chunks, i
     offsets[e] = off;
     poff[e] = poffe;
     for (int r = poffe + cnt; r < poffe + padded; ++r) sorted[r] = -1;
+    const int q = n_t ? nb / n_t : 0, rem = n_t ? nb % n_t : 0;
     for (int i = 0; i < n_t; ++i) {
-      const int r0 = poffe + i * kTileRows;
-      const int rows = min(kTileRows, padded - i * kTileRows);
+      const int r0 = poffe + (i * q + min(i, rem)) * kRowPad;
+      const int rows = (q + (i < rem ? 1 : 0)) * kRowPad;
       *(int4*)(tiles + 4 * (toff + i)) = make_int4(e, r0, rows, 0);
     }
   }

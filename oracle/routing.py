@@ -19,8 +19,10 @@ the GPU stage can be compared with it bit for bit:
   in ascending ``p`` (a stable sort by expert); padding rows hold -1;
 * ``pos[p]`` = the row of pair ``p`` in ``sorted_ids``, or -1 if dropped;
 * ``tiles``: for each expert in ascending order, the rows
-  ``[padded_offsets[e], padded_offsets[e+1])`` cut into tiles of at most
-  ``tile_rows`` rows, as ``(expert, first_row, n_rows)``.
+  ``[padded_offsets[e], padded_offsets[e+1])`` as blocks of ``row_pad`` rows,
+  split into the fewest tiles of at most ``tile_rows`` rows with the block
+  counts as equal as possible (the first ``nb mod n`` tiles take one block
+  more), as ``(expert, first_row, n_rows)``.
 """
 from dataclasses import dataclass
 
@@ -63,13 +65,15 @@ def route(topk_ids, num_experts, row_pad, tile_rows):
             pos[p] = row
             filled[e] += 1
     tiles = []
+    max_blocks = tile_rows // row_pad
     for e in range(E):
-        start, end = padded_offsets[e], padded_offsets[e + 1]
-        r = start
-        while r < end:
-            n = min(tile_rows, end - r)
-            tiles.append((e, r, n))
-            r += n
+        n_blocks = (padded_offsets[e + 1] - padded_offsets[e]) // row_pad
+        n_tiles = -(-n_blocks // max_blocks)
+        r = padded_offsets[e]
+        for i in range(n_tiles):
+            blocks = n_blocks // n_tiles + (1 if i < n_blocks % n_tiles else 0)
+            tiles.append((e, r, blocks * row_pad))
+            r += blocks * row_pad
     i32 = np.int32
     return Routing(
         counts=np.array(counts, dtype=i32),

@@ -18,8 +18,16 @@ def brute_force(ids, E, row_pad, tile_rows):
             rows.append(p)
         while len(rows) % row_pad:
             rows.append(-1)
-        for r in range(start, len(rows), tile_rows):
-            tiles.append((e, r, min(tile_rows, len(rows) - r)))
+        # fewest tiles of <= tile_rows rows, block counts differing by at most one, larger first
+        blocks = (len(rows) - start) // row_pad
+        if blocks:
+            n = -(-blocks // (tile_rows // row_pad))   # whole blocks per tile
+            sizes = sorted([blocks // n + (1 if i < blocks % n else 0) for i in range(n)], reverse=True)
+            assert max(sizes) * row_pad <= tile_rows and max(sizes) - min(sizes) <= 1
+            r = start
+            for b in sizes:
+                tiles.append((e, r, b * row_pad))
+                r += b * row_pad
     counts = [len(p) for p in per_expert]
     return counts, rows, pos, tiles
 
@@ -49,7 +57,7 @@ def _ids(kind, T, k, E, rng):
 
 
 @pytest.mark.parametrize("kind,T,k,E", CASES)
-@pytest.mark.parametrize("row_pad,tile_rows", [(1, 4), (16, 32), (16, 16), (4, 128)])
+@pytest.mark.parametrize("row_pad,tile_rows", [(1, 4), (16, 32), (16, 16), (4, 128), (16, 144), (2, 7)])
 def test_route_matches_brute_force(kind, T, k, E, row_pad, tile_rows):
     rng = np.random.default_rng([sum(map(ord, kind)), row_pad, T, k])
     ids = _ids(kind, T, k, E, rng)
@@ -83,3 +91,4 @@ def test_route_invariants(seed):
         seg = seg[seg >= 0]
         assert np.all(np.diff(seg) > 0)
     assert r.tiles[:, 2].sum() == r.padded_offsets[-1] and np.all(r.tiles[:, 2] <= 24)
+    assert np.all(r.tiles[:, 2] % 8 == 0)
