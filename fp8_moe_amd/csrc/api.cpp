@@ -50,6 +50,11 @@ b12x_status check_desc(const b12x_moe_weight_desc* d) {
     return fail(B12X_ERR_UNSUPPORTED, "H (%d) and I (%d) must be multiples of 32", d->hidden, d->inter);
   if ((int64_t)d->hidden * d->inter * d->num_experts > (int64_t)1 << 40)
     return fail(B12X_ERR_UNSUPPORTED, "weights larger than 2^40 elements");
+  // one expert's packed matrix (K padded to 128) must stay below 1 GiB
+  const int64_t n13 = (int64_t)(d->gated ? 2 : 1) * d->inter;
+  if (n13 * (int64_t)align_up(d->hidden, kFragK) / 2 >= kMaxBufferBytes ||
+      (int64_t)d->hidden * (int64_t)align_up(d->inter, kFragK) / 2 >= kMaxBufferBytes)
+    return fail(B12X_ERR_UNSUPPORTED, "one expert's packed weights exceed 1 GiB");
   return B12X_OK;
 }
 
@@ -226,6 +231,10 @@ b12x_status b12x_moe_plan(const b12x_moe_caps* caps, b12x_moe_plan_t* out) {
     off = align_up(off + len[r], 256);
   }
   p->scratch_bytes = off;
+  if (len[R_XQ] >= (uint64_t)kMaxBufferBytes || len[R_H] >= (uint64_t)kMaxBufferBytes) {
+    delete p;
+    return fail(B12X_ERR_UNSUPPORTED, "max_tokens too large: activation buffers would exceed 1 GiB");
+  }
   *out = p;
   return B12X_OK;
 }
@@ -278,6 +287,7 @@ b12x_status b12x_moe_bind(b12x_moe_plan_t p, void* scratch, uint64_t scratch_byt
     const char* ob = (const char*)out;
     const int64_t abytes = ((T - 1) * a_stride + p->H) * 2, obytes = ((T - 1) * out_stride + p->H) * 2;
     if (ab < ob + obytes && ob < ab + abytes) return fail(B12X_ERR_INVALID_ARGUMENT, "out aliases a");
+    if (abytes >= kMaxBufferBytes) return fail(B12X_ERR_UNSUPPORTED, "a spans 1 GiB or more");
   }
   BindingImpl b;
   memset(&b, 0, sizeof(b));

@@ -21,6 +21,7 @@
 namespace b12x {
 
 constexpr int kDecThreads = 256;
+constexpr int kDecodeMaxRun = 8;  // fragment groups per workgroup at most
 
 struct DecodeParams {
   const int32_t* ids;
@@ -32,6 +33,7 @@ struct DecodeParams {
   const uint8_t* as;
   int64_t a_stride;   // elements (bf16) or bytes (codes)
   int64_t as_stride;  // bytes
+  int64_t a_bytes, as_bytes;  // extents of a16 / a8 and as (at most 1 GiB)
   int a_by_token;
   int64_t K;
   int KF;
@@ -158,23 +160,55 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(const DecodeParams 
   const uint8_t* bscales = p.bscales + (int64_t)e * p.b_scales_expert;
   const float gsc = p.bglobal ? p.bglobal[e] : 1.0f;
 
-  auto load_b = [&](uint4 (&bq)[FR][KW], uint32_t (&bs)[FR][KW], int grp) {
+  // raw buffer loads: a fragment outside the run, the wave's K range or the
+  // expert's matrix (the resources end with the expert) reads zeros, so no
+  // load is behind a branch and each group waits only for its own loads.
+  // Per-lane offsets of (fragment j, K slot i) inside a group are loop
+  // invariant; a group adds one scalar base.
+  const BufRsrc b_rsrc = make_rsrc(bcodes, p.b_codes_expert);
+  const BufRsrc bs_rsrc = make_rsrc(bscales, p.b_scales_expert);
+  // (single-buffered variants, which run with 8 K fragments per wave, compute
+  // the offsets per load instead, to keep their registers for the operands)
+  auto frag_off = [&](int j, int i) {
+    const int kf = kb + i;
+    return kf < ke ? (uint32_t)((j * p.KF + kf) * kFragBytes + lane * 16) : kBufOOB;
+  };
+  auto scale_off = [&](int j, int i) {
+    const int kf = kb + i;
+    const int sg = WF == B12X_WEIGHT_MXFP4 ? kf >> 2 : kf >> 1;
+    return kf < ke ? (uint32_t)((j * p.KFS + sg) * kScaleGroupBytes + lane * 4) : kBufOOB;
+  };
+  uint32_t boff[FR][KW], soff[FR][KW];
+  if constexpr (NB == 2) {
 #pragma unroll
     for (int j = 0; j < FR; ++j) {
 #pragma unroll
       for (int i = 0; i < KW; ++i) {
-        const int kf = kb + i, f = grp * FR + j;
-        if (kf < ke && f < p.NF) {
-          bq[j][i] = *(const uint4*)(bcodes + ((int64_t)f * p.KF + kf) * kFragBytes + lane * 16);
-          const int sg = WF == B12X_WEIGHT_MXFP4 ? kf >> 2 : kf >> 1;
-          bs[j][i] = *(const uint32_t*)(bscales + ((int64_t)f * p.KFS + sg) * kScaleGroupBytes + lane * 4);
+        boff[j][i] = frag_off(j, i);
+        soff[j][i] = scale_off(j, i);
+      }
+    }
+  }
+  auto load_b = [&](uint4 (&bq)[FR][KW], uint32_t (&bs)[FR][KW], int grp) {
+    const bool gv = grp < g_end;
+    const uint32_t cb = gv ? (uint32_t)(grp * FR * p.KF * kFragBytes) : kBufOOB;
+    const uint32_t sb = gv ? (uint32_t)(grp * FR * p.KFS * kScaleGroupBytes) : kBufOOB;
+#pragma unroll
+    for (int j = 0; j < FR; ++j) {
+#pragma unroll
+      for (int i = 0; i < KW; ++i) {
+        if constexpr (NB == 2) {
+          bq[j][i] = buf_load16(b_rsrc, boff[j][i] + cb);
+          bs[j][i] = buf_load4(bs_rsrc, soff[j][i] + sb);
         } else {
-          bq[j][i] = make_uint4(0, 0, 0, 0);
-          bs[j][i] = 0;
+          bq[j][i] = buf_load16(b_rsrc, frag_off(j, i) + cb);
+          bs[j][i] = buf_load4(bs_rsrc, scale_off(j, i) + sb);
         }
       }
     }
   };
+  const BufRsrc a_rsrc = make_rsrc(A8 ? (const void*)p.a8 : (const void*)p.a16, p.a_bytes);
+  const BufRsrc as_rsrc = make_rsrc(p.as, p.as_bytes);
 
   int par = 0;  // s_red buffer of the current group
   for (int r0 = 0; r0 < rt.m; r0 += 16) {
@@ -189,22 +223,20 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(const DecodeParams 
     for (int i = 0; i < KW; ++i) {
       const int kf = kb + i;
       const int64_t k0 = (int64_t)kf * kFragK;
+      const bool rv = kf < ke && src >= 0;
+      if constexpr (!A8) {
+        const uint32_t o = rv && k0 + 32 * g < p.K ? (uint32_t)((src * p.a_stride + k0 + 32 * g) * 2) : kBufOOB;
 #pragma unroll
-      for (int s = 0; s < (A8 ? 2 : 4); ++s) av[i][s] = make_uint4(0, 0, 0, 0);
-      sa[i] = 127;
-      if (kf < ke && src >= 0) {
-        if constexpr (!A8) {
-          if (k0 + 32 * g < p.K) {
-            const uint4* ap = (const uint4*)(p.a16 + src * p.a_stride + k0 + 32 * g);
-#pragma unroll
-            for (int s = 0; s < 4; ++s) av[i][s] = ap[s];
-          }
-        } else {
-          const uint8_t* ap = p.a8 + src * p.a_stride + k0;
-          if (k0 + 16 * g < p.K) av[i][0] = *(const uint4*)(ap + 16 * g);
-          if (k0 + 64 + 16 * g < p.K) av[i][1] = *(const uint4*)(ap + 64 + 16 * g);
-          if (4 * kf + g < kblocks) sa[i] = p.as[src * p.as_stride + 4 * kf + g];
-        }
+        for (int s = 0; s < 4; ++s) av[i][s] = buf_load16(a_rsrc, o == kBufOOB ? kBufOOB : o + 16 * s);
+        sa[i] = 0;
+      } else {
+        const uint32_t o = rv ? (uint32_t)(src * p.a_stride + k0) : kBufOOB;
+        av[i][0] = buf_load16(a_rsrc, o != kBufOOB && k0 + 16 * g < p.K ? o + 16 * g : kBufOOB);
+        av[i][1] = buf_load16(a_rsrc, o != kBufOOB && k0 + 64 + 16 * g < p.K ? o + 64 + 16 * g : kBufOOB);
+        // one E8M0 byte per lane; a block past K reads code 0 (2^-127), which
+        // multiplies zero codes on both sides
+        const bool sv = rv && 4 * kf + g < kblocks;
+        sa[i] = buf_load1(as_rsrc, sv ? (uint32_t)(src * p.as_stride + 4 * kf + g) : kBufOOB);
       }
     }
 
@@ -215,8 +247,8 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(const DecodeParams 
       for (int j = 0; j < FR; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int i = 0; i < KW; ++i) {
-        const int kf = kb + i;
-        if (kf < ke) {
+        const int kf = kb + i;  // past the wave's K range A and B are zero
+        {
           if constexpr (!A8) {
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
@@ -309,19 +341,24 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(const DecodeParams 
       par ^= 1;  // the next group writes the other buffer; one barrier per group suffices
     };
 
-    // ---- stream the run of fragment groups; with NB = 2 the next group's
-    // loads are in flight while the current group runs on the MFMAs
+    // ---- stream the run of fragment groups.  NB = 2: the next group's loads
+    // are in flight while the current group runs on the MFMAs.  The loop body
+    // has no early exit (the odd group is guarded instead) and the scheduling
+    // barriers keep each prefetch ahead of the MFMAs it overlaps, so every
+    // wait covers exactly the group it consumes.
     if constexpr (NB == 2) {
       uint4 bq0[FR][KW], bq1[FR][KW];
       uint32_t bs0[FR][KW], bs1[FR][KW];
       load_b(bq0, bs0, g_begin);
       for (int gi = g_begin; gi < g_end; gi += 2) {
-        if (gi + 1 < g_end) load_b(bq1, bs1, gi + 1);
+        load_b(bq1, bs1, gi + 1);
+        __builtin_amdgcn_sched_barrier(0);
         group(bq0, bs0, gi);
-        if (gi + 1 >= g_end) break;
-        if (gi + 2 < g_end) load_b(bq0, bs0, gi + 2);
-        group(bq1, bs1, gi + 1);
+        load_b(bq0, bs0, gi + 2);
+        __builtin_amdgcn_sched_barrier(0);
+        if (gi + 1 < g_end) group(bq1, bs1, gi + 1);
       }
+      wait_vmem_all();  // the last prefetch (zeros) is not carried into the next row block
     } else {
       uint4 bq0[FR][KW];
       uint32_t bs0[FR][KW];
@@ -344,11 +381,11 @@ static int launch_decode_kw(const DecodeParams& p, int n_slots, hipStream_t s) {
 static int decode_slots(const BindingImpl& b) { return (int)(b.T * b.k < b.E ? b.T * b.k : b.E); }
 
 // Fragment groups per workgroup: enough workgroups to cover the chip twice,
-// at most 8 groups in one run.
+// at most kDecodeMaxRun groups in one run.
 static void set_runs(DecodeParams& p, int n_slots) {
   const int64_t items = (int64_t)n_slots * p.n_groups;
   int ng = (int)((items + 511) / 512);
-  ng = ng < 1 ? 1 : (ng > 8 ? 8 : ng);
+  ng = ng < 1 ? 1 : (ng > kDecodeMaxRun ? kDecodeMaxRun : ng);
   p.ng = ng;
   p.n_runs = (p.n_groups + ng - 1) / ng;
 }
@@ -391,6 +428,8 @@ int launch_decode1(const BindingImpl& b, hipStream_t s) {
   p.as = b.xs;
   p.a_stride = a8 ? b.Hp : b.a_stride;
   p.as_stride = b.Hp / 32;
+  p.a_bytes = a8 ? b.T * b.Hp : b.T * b.a_stride * 2;
+  p.as_bytes = a8 ? b.T * (b.Hp / 32) : 0;
   p.a_by_token = 1;
   p.K = b.H;
   p.KF = (int)b.kf13;
@@ -419,6 +458,8 @@ int launch_decode2(const BindingImpl& b, hipStream_t s) {
   p.as = b.hs;
   p.a_stride = b.Ip;
   p.as_stride = b.Ip / 32;
+  p.a_bytes = b.T * b.k * b.Ip * (b.afmt == B12X_ACT_MXFP8 ? 1 : 2);
+  p.as_bytes = b.afmt == B12X_ACT_MXFP8 ? b.T * b.k * (b.Ip / 32) : 0;
   p.a_by_token = 0;
   p.K = b.I;
   p.KF = (int)b.kf2;

@@ -17,6 +17,38 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
+// Raw buffer loads (CDNA buffer resource, stride 0).  A byte offset at or
+// past the record count returns zeros without a memory access, so a guarded
+// load needs no branch and every load of a loop is issued unconditionally;
+// the compiler then counts outstanding loads exactly and waits only for the
+// ones a step consumes.  Records are limited to kMaxBufferBytes (1 GiB,
+// checked on the host); kBufOOB = 1.5 GiB is out of range, and so are
+// kBufOOB + any in-range offset and 2 * kBufOOB (no 32-bit wrap).
+constexpr uint32_t kBufOOB = 0x60000000u;
+static_assert(kMaxBufferBytes <= (int64_t)kBufOOB && 2ull * kBufOOB < (1ull << 32) &&
+                  (uint64_t)kBufOOB + kMaxBufferBytes < (1ull << 32), "out-of-range marker");
+typedef __amdgpu_buffer_rsrc_t BufRsrc;
+
+__device__ __forceinline__ BufRsrc make_rsrc(const void* base, int64_t bytes) {
+  const int n = (int)(bytes < kMaxBufferBytes ? bytes : kMaxBufferBytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
+}
+__device__ __forceinline__ uint4 buf_load16(BufRsrc r, uint32_t off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ uint32_t buf_load4(BufRsrc r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+__device__ __forceinline__ int buf_load1(BufRsrc r, uint32_t off) {
+  return (int)__builtin_amdgcn_raw_buffer_load_b8(r, off, 0, 0);
+}
+
+// s_waitcnt vmcnt(0) (gfx9 encoding: expcnt and lgkmcnt left at their
+// maxima).  Placed where a loop exits with prefetches still in flight, so that
+// the compiler does not carry those pending loads into the wait counts of
+// every later iteration.
+__device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 __device__ __forceinline__ uint32_t f32_bits(float f) { return __builtin_bit_cast(uint32_t, f); }
 __device__ __forceinline__ float bits_f32(uint32_t u) { return __builtin_bit_cast(float, u); }
 

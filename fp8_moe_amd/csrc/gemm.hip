@@ -6,10 +6,12 @@
 //   GEMM1: h[row] = act(x[token(row)] . W13_e^T)   (SiLU-gated or ReLU^2)
 //   GEMM2: y[row] = h[row] . W2_e^T
 // over the routing tiles (expert, first row, rows).  A workgroup of 4 waves
-// owns 128 rows x 4*NFW weight fragments (16 columns each).  The A rows (bf16
+// owns one routing tile (up to kTileRows = 144 rows) x 4*NFW weight fragments
+// (16 columns each).  The A rows (bf16
 // or MXFP8 codes) go through double-buffered LDS with a two-step register
 // prefetch; the packed FP4 fragments stream from global memory straight into
-// registers, two K steps ahead.
+// registers, two K steps ahead.  All loads are raw buffer loads whose
+// out-of-range offsets read zeros, so none of them sits behind a branch.
 //   W4A16: each 1 KB fragment is four 16x16x32 bf16 MFMA operands; FP4 is
 //          turned into bf16 in registers (v_cvt_scalef32_pk_bf16_fp4 with the
 //          E8M0 scale, or fp32 conversion times the E4M3 scale for NVFP4; both
@@ -39,6 +41,7 @@ struct GemmParams {
   const uint8_t* as;
   int64_t a_stride;   // elements (bf16) or bytes (codes)
   int64_t as_stride;  // bytes
+  int64_t a_bytes, as_bytes;  // extents of a16 / a8 and as (at most 1 GiB)
   const int32_t* sorted;
   int k_top;
   int64_t n_pairs;
@@ -68,11 +71,11 @@ enum { MODE_SILU = 1, MODE_RELU2 = 2, MODE_DOWN = 3 };
 // one per XCD (workgroup i runs on XCD i % 8), so that the workgroups sharing
 // an L2 work on the same row tiles (A reuse) and the same experts (B reuse).
 //
-// Wave w owns all 128 rows of the tile and weight fragments [NFW w, NFW w +
-// NFW): every fragment is dequantized by exactly one wave.  A full tile (128
+// Wave w owns all rows of the tile and weight fragments [NFW w, NFW w +
+// NFW): every fragment is dequantized by exactly one wave.  A full tile (144
 // rows) runs a branch-free MFMA loop; a partial tile skips whole 16-row
-// blocks.  Missing fragments (a partial N tile) load a clamped fragment and
-// are dropped in the epilogue.
+// blocks.  Missing fragments (a partial N tile) load zeros and are dropped
+// in the epilogue.
 template <int WF, int AF, int MODE, int NFW>
 __global__ __launch_bounds__(kGemmThreads, 1) void moe_gemm_kernel(const GemmParams p) {
   constexpr bool A8 = AF == B12X_ACT_MXFP8;
@@ -107,8 +110,16 @@ __global__ __launch_bounds__(kGemmThreads, 1) void moe_gemm_kernel(const GemmPar
     const uint8_t* bscales = p.bscales + (int64_t)e * p.b_scales_expert;
     const float gsc = p.bglobal ? p.bglobal[e] : 1.0f;
 
-    // ---- A-row sources for this thread's loads (token or row index, -1 = zero row)
-    int src_row[LOADS];
+    // ---- buffer resources: every load below is unconditional; a row, K chunk
+    // or fragment outside the problem gets an out-of-range offset (zeros)
+    constexpr int ESZ = A8 ? 1 : 2;  // bytes per A element
+    const BufRsrc a_rsrc = make_rsrc(A8 ? (const void*)p.a8 : (const void*)p.a16, p.a_bytes);
+    const BufRsrc s_rsrc = make_rsrc(p.as, p.as_bytes);
+    const BufRsrc b_rsrc = make_rsrc(bcodes, p.b_codes_expert);
+    const BufRsrc bs_rsrc = make_rsrc(bscales, p.b_scales_expert);
+
+    // byte offset of each of this thread's A rows (token row for GEMM1, h row for GEMM2)
+    uint32_t a_off[LOADS];
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
       const int rr = tid / CHUNKS + (kGemmThreads / CHUNKS) * i;
@@ -121,44 +132,36 @@ __global__ __launch_bounds__(kGemmThreads, 1) void moe_gemm_kernel(const GemmPar
           sr = row0 + rr;
         }
       }
-      src_row[i] = sr;
+      a_off[i] = sr >= 0 ? (uint32_t)(sr * p.a_stride * ESZ) : kBufOOB;
     }
-    int s_row = -1;  // A8: scale row loaded by threads 0..127
+    uint32_t s_off = kBufOOB;  // A8: scale row of threads 0..kTileRows-1
     if (A8 && tid < kTileRows && tid < nrows) {
+      int sr = -1;
       if (p.sorted) {
         const int pair = p.sorted[row0 + tid];
-        s_row = (pair >= 0 && pair < p.n_pairs) ? pair / p.k_top : -1;
+        sr = (pair >= 0 && pair < p.n_pairs) ? pair / p.k_top : -1;
       } else {
-        s_row = row0 + tid;
+        sr = row0 + tid;
       }
+      if (sr >= 0) s_off = (uint32_t)(sr * p.as_stride);
     }
     const int kblocks = (int)(p.K / 32);
 
-    auto load_a = [&](uint4 (&ra)[LOADS], uint32_t& rs, int kf) {
+    // A chunks of K fragment kf (zeros past K or past the last fragment);
+    // A8: the 4 block scales of the row, with the byte mask of real blocks
+    auto load_a = [&](uint4 (&ra)[LOADS], uint32_t& rs, uint32_t& rk, int kf) {
       const int64_t k0 = (int64_t)kf * kFragK + (A8 ? 16 : 8) * c;
+      const bool kin = k0 < p.K;
 #pragma unroll
-      for (int i = 0; i < LOADS; ++i) {
-        ra[i] = make_uint4(0, 0, 0, 0);
-        if (src_row[i] >= 0 && k0 < p.K) {
-          if constexpr (A8) ra[i] = *(const uint4*)(p.a8 + (int64_t)src_row[i] * p.a_stride + k0);
-          else ra[i] = *(const uint4*)(p.a16 + (int64_t)src_row[i] * p.a_stride + k0);
-        }
-      }
+      for (int i = 0; i < LOADS; ++i)
+        ra[i] = buf_load16(a_rsrc, (kin && a_off[i] != kBufOOB) ? a_off[i] + (uint32_t)(k0 * ESZ) : kBufOOB);
       if constexpr (A8) {
-        rs = 0x7F7F7F7Fu;
-        if (s_row >= 0) {
-          uint32_t word = 0;
-#pragma unroll
-          for (int b = 0; b < 4; ++b) {
-            const int blk = kf * 4 + b;
-            const uint32_t v = blk < kblocks ? p.as[(int64_t)s_row * p.as_stride + blk] : 127u;
-            word |= v << (8 * b);
-          }
-          rs = word;
-        }
+        const int nb = min(max(kblocks - 4 * kf, 0), 4);
+        rs = buf_load4(s_rsrc, (nb > 0 && s_off != kBufOOB) ? s_off + 4 * kf : kBufOOB);
+        rk = nb >= 4 ? 0xFFFFFFFFu : (1u << (8 * nb)) - 1u;
       }
     };
-    auto store_a = [&](const uint4 (&ra)[LOADS], uint32_t rs, int buf) {
+    auto store_a = [&](const uint4 (&ra)[LOADS], uint32_t rs, uint32_t rk, int buf) {
 #pragma unroll
       for (int i = 0; i < LOADS; ++i) {
         const int rr = tid / CHUNKS + (kGemmThreads / CHUNKS) * i;
@@ -166,17 +169,19 @@ __global__ __launch_bounds__(kGemmThreads, 1) void moe_gemm_kernel(const GemmPar
           *(uint4*)(&lds_a[buf][rr * ROWB + 16 * c]) = ra[i];
       }
       if constexpr (A8) {
-        if (tid < kTileRows) lds_s[buf][tid] = rs;
+        // blocks past K get the neutral scale 2^0 (their codes are zero)
+        if (tid < kTileRows) lds_s[buf][tid] = (rs & rk) | (0x7F7F7F7Fu & ~rk);
       }
     };
-    const int flast = p.NF - 1;
     auto load_b = [&](uint4 (&q)[NFW], uint32_t (&sc)[NFW], int kf) {
       const int sgrp = WF == B12X_WEIGHT_MXFP4 ? kf >> 2 : kf >> 1;
+      const bool kin = kf < p.KF;
 #pragma unroll
       for (int j = 0; j < NFW; ++j) {
-        const int f = min(f0 + j, flast);
-        q[j] = *(const uint4*)(bcodes + ((int64_t)f * p.KF + kf) * kFragBytes + lane * 16);
-        sc[j] = *(const uint32_t*)(bscales + ((int64_t)f * p.KFS + sgrp) * kScaleGroupBytes + lane * 4);
+        const int f = f0 + j;
+        const bool v = kin && f < p.NF;
+        q[j] = buf_load16(b_rsrc, v ? (uint32_t)((f * p.KF + kf) * kFragBytes + lane * 16) : kBufOOB);
+        sc[j] = buf_load4(bs_rsrc, v ? (uint32_t)((f * p.KFS + sgrp) * kScaleGroupBytes + lane * 4) : kBufOOB);
       }
     };
 
@@ -271,34 +276,36 @@ __global__ __launch_bounds__(kGemmThreads, 1) void moe_gemm_kernel(const GemmPar
 
     // ---- main loop.  A: global loads of step kf+2 are issued at step kf into
     // the register stage of that parity and written to LDS at the end of step
-    // kf+1; B: loads of step kf+2 are issued after step kf's MFMAs.  The whole
-    // loop is instantiated per count of 16-row blocks (9, or rounded up to even).
+    // kf+1; B: loads of step kf+2 are issued after step kf's MFMAs.  No load
+    // is conditional (steps past the end load zeros), so each wait covers only
+    // the loads its step consumes.  The whole loop is instantiated per count
+    // of 16-row blocks (9, or rounded up to even).
     const bool idle = nnf == 0;  // this wave has no fragments in a partial N tile
     auto kloop = [&](auto nmf_tag) {
       uint4 ra0[LOADS], ra1[LOADS];
-      uint32_t rs0 = 0, rs1 = 0;
+      uint32_t rs0 = 0, rs1 = 0, rk0 = 0, rk1 = 0;
       uint4 bq0[NFW], bq1[NFW];
       uint32_t bs0[NFW], bs1[NFW];
       __syncthreads();  // the previous work item is done with LDS
-      load_a(ra0, rs0, 0);
-      store_a(ra0, rs0, 0);
-      if (p.KF > 1) load_a(ra1, rs1, 1);
+      load_a(ra0, rs0, rk0, 0);
+      store_a(ra0, rs0, rk0, 0);
+      load_a(ra1, rs1, rk1, 1);
       load_b(bq0, bs0, 0);
-      if (p.KF > 1) load_b(bq1, bs1, 1);
+      load_b(bq1, bs1, 1);
       for (int kf = 0; kf < p.KF; kf += 2) {
         // even step: LDS buffer 0, ra1 holds step kf+1
         __syncthreads();
-        if (kf + 2 < p.KF) load_a(ra0, rs0, kf + 2);
+        load_a(ra0, rs0, rk0, kf + 2);
         if (!idle) compute(nmf_tag, 0, bq0, bs0, kf);
-        if (kf + 1 < p.KF) store_a(ra1, rs1, 1);
-        if (kf + 2 < p.KF) load_b(bq0, bs0, kf + 2);
+        store_a(ra1, rs1, rk1, 1);
+        load_b(bq0, bs0, kf + 2);
         if (kf + 1 >= p.KF) break;
         // odd step: LDS buffer 1, ra0 holds step kf+2
         __syncthreads();
-        if (kf + 3 < p.KF) load_a(ra1, rs1, kf + 3);
+        load_a(ra1, rs1, rk1, kf + 3);
         if (!idle) compute(nmf_tag, 1, bq1, bs1, kf + 1);
-        if (kf + 2 < p.KF) store_a(ra0, rs0, 0);
-        if (kf + 3 < p.KF) load_b(bq1, bs1, kf + 3);
+        store_a(ra0, rs0, rk0, 0);
+        load_b(bq1, bs1, kf + 3);
       }
     };
     if (nmf > 8) kloop(std::integral_constant<int, 9>{});
@@ -389,7 +396,7 @@ static int cu_count() {
   return g_cu_count[dev];
 }
 
-constexpr int kGemmNFW = 4;  // weight fragments per wave: workgroup tile 128 rows x 256 columns
+constexpr int kGemmNFW = 4;  // weight fragments per wave: workgroup tile 144 rows x 256 columns
 
 template <int WF, int AF, int MODE>
 static int launch_gemm_t(const GemmParams& p, int64_t max_work, hipStream_t s) {
@@ -424,6 +431,8 @@ int launch_gemm1(const BindingImpl& b, hipStream_t s) {
   p.as = b.xs;
   p.a_stride = a8 ? b.Hp : b.a_stride;
   p.as_stride = b.Hp / 32;
+  p.a_bytes = a8 ? b.T * b.Hp : b.T * b.a_stride * 2;
+  p.as_bytes = a8 ? b.T * (b.Hp / 32) : 0;
   p.sorted = b.sorted;
   p.k_top = b.k;
   p.n_pairs = b.T * b.k;
@@ -459,6 +468,8 @@ int launch_gemm2(const BindingImpl& b, hipStream_t s) {
   p.as = b.hs;
   p.a_stride = b.Ip;
   p.as_stride = b.Ip / 32;
+  p.a_bytes = b.max_rows * b.Ip * (a8 ? 1 : 2);
+  p.as_bytes = a8 ? b.max_rows * (b.Ip / 32) : 0;
   p.sorted = nullptr;
   p.k_top = b.k;
   p.K = b.I;
@@ -472,7 +483,6 @@ int launch_gemm2(const BindingImpl& b, hipStream_t s) {
   p.KFS = (int)b.kfs2;
   p.y = b.y;
   p.y_stride = b.H;
-  (void)a8;
   const int64_t max_work = b.max_tiles * p.n_ntiles;
   return dispatch<MODE_DOWN>(b, p, max_work, s);
 }

@@ -38,6 +38,10 @@ constexpr int kRouteChunk = 1024;  // routing pairs per workgroup
 constexpr int kMaxExperts = 1024;
 // ---- decode path -------------------------------------------------------------
 constexpr int kDecodePairs = 256;     // T*k at or below which the decode path runs
+// Kernels address each activation buffer and each expert's weights with
+// 32-bit buffer offsets; buffers are limited to 1 GiB (so that the sum of
+// two out-of-range markers is still out of range).
+constexpr int64_t kMaxBufferBytes = (int64_t)1 << 30;
 constexpr int kDecodeMaxKPerWave = 8; // K fragments per wave: K <= 4 * 8 * 128
 
 struct MatrixLayout {
