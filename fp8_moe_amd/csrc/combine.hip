@@ -8,33 +8,56 @@
 
 namespace b12x {
 
+// One thread per 8 output columns of one token.  The slots are taken 8 at a
+// time: their rows and weights, then all their y loads (a dropped pair loads
+// row 0 and is masked), then the sums in slot order, so the loads of a chunk
+// are in flight together.
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y, int64_t y_stride,
                                                        const int32_t* __restrict__ pos,
                                                        const int32_t* __restrict__ ids, int E,
                                                        const float* __restrict__ tw, int64_t T, int k, int H,
                                                        int64_t max_rows, uint16_t* __restrict__ out,
                                                        int64_t out_stride) {
+  constexpr int kChunk = 8;
   const int64_t groups = H / 8;
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= T * groups) return;
   const int64_t t = idx / groups, c = (idx % groups) * 8;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int j = 0; j < k; ++j) {
-    int row;
-    if (pos) {
-      row = pos[t * k + j];
-    } else {  // rows indexed by pair id; a dropped pair has no row
-      const int e = ids[t * k + j];
-      row = (e >= 0 && e < E) ? (int)(t * k + j) : -1;
+  // grouped path: pos gives the y row; decode path: the row is the pair id
+  const int32_t* key = pos ? pos : ids;
+  for (int j0 = 0; j0 < k; j0 += kChunk) {
+    int raw[kChunk], row[kChunk];
+    float w[kChunk];
+#pragma unroll
+    for (int u = 0; u < kChunk; ++u) {  // clamped slot: every load is in bounds and unconditional
+      const int j = min(j0 + u, k - 1);
+      raw[u] = key[t * k + j];
+      w[u] = tw[t * k + j];
     }
-    if (row < 0 || row >= max_rows) continue;
-    const float w = tw[t * k + j];
-    const float4* src = (const float4*)(y + (int64_t)row * y_stride + c);
-    const float4 a = src[0], b = src[1];
-    acc[0] = fmaf(w, a.x, acc[0]); acc[1] = fmaf(w, a.y, acc[1]);
-    acc[2] = fmaf(w, a.z, acc[2]); acc[3] = fmaf(w, a.w, acc[3]);
-    acc[4] = fmaf(w, b.x, acc[4]); acc[5] = fmaf(w, b.y, acc[5]);
-    acc[6] = fmaf(w, b.z, acc[6]); acc[7] = fmaf(w, b.w, acc[7]);
+#pragma unroll
+    for (int u = 0; u < kChunk; ++u) {
+      const int j = j0 + u;
+      int r;
+      if (pos) r = raw[u];
+      else r = (raw[u] >= 0 && raw[u] < E) ? (int)(t * k + j) : -1;  // a dropped pair has no row
+      row[u] = (j < k && r >= 0 && r < max_rows) ? r : -1;
+    }
+    float4 a[kChunk], b[kChunk];
+#pragma unroll
+    for (int u = 0; u < kChunk; ++u) {
+      const float4* src = (const float4*)(y + (int64_t)(row[u] < 0 ? 0 : row[u]) * y_stride + c);
+      a[u] = src[0];
+      b[u] = src[1];
+    }
+#pragma unroll
+    for (int u = 0; u < kChunk; ++u) {
+      if (row[u] < 0) continue;
+      acc[0] = fmaf(w[u], a[u].x, acc[0]); acc[1] = fmaf(w[u], a[u].y, acc[1]);
+      acc[2] = fmaf(w[u], a[u].z, acc[2]); acc[3] = fmaf(w[u], a[u].w, acc[3]);
+      acc[4] = fmaf(w[u], b[u].x, acc[4]); acc[5] = fmaf(w[u], b[u].y, acc[5]);
+      acc[6] = fmaf(w[u], b[u].z, acc[6]); acc[7] = fmaf(w[u], b[u].w, acc[7]);
+    }
   }
   uint32_t o[4];
 #pragma unroll

@@ -2,26 +2,29 @@
 // micro-kernel decode path of fused_moe).  For T*k <= kDecodePairs three
 // launches replace the routing buffers and the grouped GEMMs; every touched
 // expert's weights are read exactly once:
-//   D1 (gate/up) and D2 (down): workgroup = (touched-expert slot, run of up to
-//      NG groups of FR weight fragments).  Each workgroup finds its expert and
-//      that expert's pairs (stable by pair id) from topk_ids in LDS; its 4
-//      waves split K, keep their share of the activation rows in registers and
-//      stream the fragment groups with the next group's loads in flight while
-//      the current one runs on the MFMAs; partial sums are added in LDS in a
-//      fixed wave order.  D1 applies SiLU-gated or ReLU^2 and writes h by pair
-//      id (bf16, or MXFP8 codes and scales for W4A8); D2 writes y by pair id
-//      in fp32.
+//   D1 (gate/up) and D2 (down): a grid of as many workgroups as the chip
+//      holds at once.  Every workgroup reads topk_ids into LDS, finds the
+//      touched experts (a bitmap and its prefix popcounts) and takes an even,
+//      contiguous share of the items (touched expert in ascending id, group of
+//      FR weight fragments); for each expert of its share it builds that
+//      expert's pair list (stable by pair id).  Its 4 waves split K, keep
+//      their share of the activation rows in registers and take the groups
+//      one at a time (the other resident waves cover the load latency);
+//      partial sums are added in LDS in a fixed wave order.  D1
+//      applies SiLU-gated or ReLU^2 and writes h by pair id (bf16, or MXFP8
+//      codes and scales for W4A8); D2 writes y by pair id in fp32.
 //   D3 (combine): out[t] = sum_j w[t,j] * y[t*k+j] in ascending slot order,
 //      fp32, one bf16 rounding (the grouped path's combine kernel, reading y
 //      by pair id).
 // No atomics on data and no cross-workgroup synchronization: the result does
-// not depend on scheduling.
+// not depend on scheduling or on the grid size.
 #include "device_common.h"
 
 namespace b12x {
 
 constexpr int kDecThreads = 256;
-constexpr int kDecodeMaxRun = 8;  // fragment groups per workgroup at most
+constexpr int kBitWords = kMaxExperts / 32;
+static_assert(kBitWords <= 64, "one wave scans the expert bitmap");
 
 struct DecodeParams {
   const int32_t* ids;
@@ -44,8 +47,6 @@ struct DecodeParams {
   int64_t b_codes_expert, b_scales_expert;
   int NF, KFS;
   int n_groups;  // fragment groups per expert
-  int ng;        // fragment groups per workgroup
-  int n_runs;    // workgroups per expert slot = ceil(n_groups / ng)
   // D1 outputs
   uint16_t* h16;
   uint8_t* h8;
@@ -58,16 +59,10 @@ struct DecodeParams {
 
 enum { DMODE_SILU = 1, DMODE_RELU2 = 2, DMODE_DOWN = 3 };
 
-struct DecodeRoute {
-  int e;          // expert of this workgroup's slot, or -1
-  int m;          // pairs routed to e
-  int n_touched;  // distinct valid experts
-};
-
-// Expert of slot `slot` (slot-th smallest distinct valid id) and its pairs in
-// ascending pair order, from topk_ids held in LDS.  All threads call it.
-__device__ DecodeRoute decode_route(const DecodeParams& p, int slot, int* s_ids, uint32_t* s_bits, int* s_rows,
-                                    int* s_info) {
+// topk_ids -> LDS (invalid ids as -1), the bitmap of valid experts and the
+// exclusive prefix popcounts of its words; returns the number of distinct
+// valid experts.  All threads call it.
+__device__ int decode_prep(const DecodeParams& p, int* s_ids, uint32_t* s_bits, int* s_wpre) {
   const int tid = threadIdx.x;
   const int words = (p.E + 31) >> 5;
   for (int i = tid; i < words; i += kDecThreads) s_bits[i] = 0;
@@ -79,40 +74,38 @@ __device__ DecodeRoute decode_route(const DecodeParams& p, int slot, int* s_ids,
     if (v) atomicOr(&s_bits[e >> 5], 1u << (e & 31));
   }
   __syncthreads();
-  if (tid < 64) {  // wave 0: prefix popcount over the bitmap
-    int before = 0, found = -1;
-    for (int base = 0; base < words; base += 64) {
-      const int w = base + tid;
-      const uint32_t bits = w < words ? s_bits[w] : 0u;
-      const int c = __builtin_popcount(bits);
-      int incl = c;
+  if (tid < 64) {  // wave 0: words <= 64
+    const int c = tid < words ? __builtin_popcount(s_bits[tid]) : 0;
+    int incl = c;
 #pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const int t = __shfl_up(incl, off);
-        if (tid >= off) incl += t;
-      }
-      const int excl = before + incl - c;
-      if (slot >= excl && slot < excl + c) {
-        uint32_t b = bits;
-        for (int r = slot - excl; r > 0; --r) b &= b - 1;  // drop the lower set bits
-        found = w * 32 + __builtin_ctz(b);
-      }
-      before += __shfl(incl, 63);
+    for (int off = 1; off < 64; off <<= 1) {
+      const int t = __shfl_up(incl, off);
+      if (tid >= off) incl += t;
     }
-    const uint64_t has = __ballot(found >= 0);
-    const int e = has ? __shfl(found, __builtin_ctzll(has)) : -1;
-    if (tid == 0) {
-      s_info[0] = e;
-      s_info[1] = before;
-    }
+    if (tid < words) s_wpre[tid] = incl - c;
+    if (tid == 63) s_wpre[kBitWords] = incl;
   }
   __syncthreads();
-  const int e = s_info[0];
-  DecodeRoute r;
-  r.e = e;
-  r.n_touched = s_info[1];
-  r.m = 0;
-  if (e < 0) return r;
+  return __builtin_amdgcn_readfirstlane(s_wpre[kBitWords]);
+}
+
+// Expert of touched slot `slot` (the slot-th smallest distinct valid id) and
+// its pairs in ascending pair order into s_rows; returns the pair count.
+// All threads call it; it starts with a barrier, so the caller may reuse
+// s_rows and s_info right after its own last reads.
+__device__ int decode_expert(const DecodeParams& p, int slot, const int* s_ids, const uint32_t* s_bits,
+                             const int* s_wpre, int* s_rows, int* s_info, int& e_out) {
+  const int tid = threadIdx.x;
+  const int words = (p.E + 31) >> 5;
+  __syncthreads();
+  if (tid < words && slot >= s_wpre[tid] && slot < s_wpre[tid] + __builtin_popcount(s_bits[tid])) {
+    uint32_t b = s_bits[tid];
+    for (int r = slot - s_wpre[tid]; r > 0; --r) b &= b - 1;  // drop the lower set bits
+    s_info[0] = tid * 32 + __builtin_ctz(b);
+  }
+  __syncthreads();
+  const int e = __builtin_amdgcn_readfirstlane(s_info[0]);
+  e_out = e;
   // stable list of e's pairs: ballots per wave, waves ordered by a prefix
   const int wave = tid >> 6, lane = tid & 63;
   const uint64_t below = lane ? (~0ull >> (64 - lane)) : 0ull;
@@ -129,16 +122,16 @@ __device__ DecodeRoute decode_route(const DecodeParams& p, int slot, int* s_ids,
     total += s_info[4] + s_info[5] + s_info[6] + s_info[7];
     __syncthreads();
   }
-  r.m = total;
-  return r;
+  return __builtin_amdgcn_readfirstlane(total);
 }
 
-template <int WF, int AF, int MODE, int FR, int KW, int NB>
+template <int WF, int AF, int MODE, int FR, int KW>
 __global__ __launch_bounds__(kDecThreads) void decode_kernel(const DecodeParams p) {
   constexpr bool A8 = AF == B12X_ACT_MXFP8;
   __shared__ int s_ids[kDecodePairs];
   __shared__ int s_rows[kDecodePairs];
-  __shared__ uint32_t s_bits[kMaxExperts / 32];
+  __shared__ uint32_t s_bits[kBitWords];
+  __shared__ int s_wpre[kBitWords + 1];
   __shared__ int s_info[8];
   __shared__ f32x4 s_red[2][4][FR][64];
 
@@ -146,76 +139,57 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(const DecodeParams 
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int g = lane >> 4, r16 = lane & 15;
-  const int slot = blockIdx.x / p.n_runs, run = blockIdx.x % p.n_runs;
-  const int g_begin = run * p.ng, g_end = min(p.n_groups, g_begin + p.ng);
 
-  const DecodeRoute rt = decode_route(p, slot, s_ids, s_bits, s_rows, s_info);
-  if (rt.e < 0 || g_begin >= g_end) return;
-  const int e = rt.e;
+  const int n_touched = decode_prep(p, s_ids, s_bits, s_wpre);
+  // this workgroup's share of the (touched expert, fragment group) items
+  const int64_t items = (int64_t)n_touched * p.n_groups;
+  const int lo = (int)(items * blockIdx.x / gridDim.x), hi = (int)(items * (blockIdx.x + 1) / gridDim.x);
 
   // ---- this wave's K fragments
   const int kper = (p.KF + 3) / 4;
   const int kb = wave * kper, ke = min(p.KF, kb + kper);
+
+  int par = 0;  // s_red buffer of the current group
+  for (int item = lo; item < hi;) {
+  // ---- one expert's part of the share: groups [g_begin, g_end) of `slot`
+  const int slot = item / p.n_groups;
+  const int g_begin = item - slot * p.n_groups;
+  const int g_end = min(p.n_groups, g_begin + (hi - item));
+  item += g_end - g_begin;
+  int e;
+  const int m = decode_expert(p, slot, s_ids, s_bits, s_wpre, s_rows, s_info, e);
   const uint8_t* bcodes = p.bcodes + (int64_t)e * p.b_codes_expert;
   const uint8_t* bscales = p.bscales + (int64_t)e * p.b_scales_expert;
   const float gsc = p.bglobal ? p.bglobal[e] : 1.0f;
 
-  // raw buffer loads: a fragment outside the run, the wave's K range or the
-  // expert's matrix (the resources end with the expert) reads zeros, so no
-  // load is behind a branch and each group waits only for its own loads.
-  // Per-lane offsets of (fragment j, K slot i) inside a group are loop
-  // invariant; a group adds one scalar base.
+  // raw buffer loads: a fragment outside the wave's K range or the expert's
+  // matrix (the resources end with the expert) reads zeros, so no load is
+  // behind a branch
   const BufRsrc b_rsrc = make_rsrc(bcodes, p.b_codes_expert);
   const BufRsrc bs_rsrc = make_rsrc(bscales, p.b_scales_expert);
-  // (single-buffered variants, which run with 8 K fragments per wave, compute
-  // the offsets per load instead, to keep their registers for the operands)
-  auto frag_off = [&](int j, int i) {
-    const int kf = kb + i;
-    return kf < ke ? (uint32_t)((j * p.KF + kf) * kFragBytes + lane * 16) : kBufOOB;
-  };
-  auto scale_off = [&](int j, int i) {
-    const int kf = kb + i;
-    const int sg = WF == B12X_WEIGHT_MXFP4 ? kf >> 2 : kf >> 1;
-    return kf < ke ? (uint32_t)((j * p.KFS + sg) * kScaleGroupBytes + lane * 4) : kBufOOB;
-  };
-  uint32_t boff[FR][KW], soff[FR][KW];
-  if constexpr (NB == 2) {
-#pragma unroll
-    for (int j = 0; j < FR; ++j) {
-#pragma unroll
-      for (int i = 0; i < KW; ++i) {
-        boff[j][i] = frag_off(j, i);
-        soff[j][i] = scale_off(j, i);
-      }
-    }
-  }
   auto load_b = [&](uint4 (&bq)[FR][KW], uint32_t (&bs)[FR][KW], int grp) {
-    const bool gv = grp < g_end;
-    const uint32_t cb = gv ? (uint32_t)(grp * FR * p.KF * kFragBytes) : kBufOOB;
-    const uint32_t sb = gv ? (uint32_t)(grp * FR * p.KFS * kScaleGroupBytes) : kBufOOB;
+    const uint32_t cb = (uint32_t)(grp * FR * p.KF * kFragBytes);
+    const uint32_t sb = (uint32_t)(grp * FR * p.KFS * kScaleGroupBytes);
 #pragma unroll
     for (int j = 0; j < FR; ++j) {
 #pragma unroll
       for (int i = 0; i < KW; ++i) {
-        if constexpr (NB == 2) {
-          bq[j][i] = buf_load16(b_rsrc, boff[j][i] + cb);
-          bs[j][i] = buf_load4(bs_rsrc, soff[j][i] + sb);
-        } else {
-          bq[j][i] = buf_load16(b_rsrc, frag_off(j, i) + cb);
-          bs[j][i] = buf_load4(bs_rsrc, scale_off(j, i) + sb);
-        }
+        const int kf = kb + i;
+        const int sg = WF == B12X_WEIGHT_MXFP4 ? kf >> 2 : kf >> 1;
+        const bool v = kf < ke;
+        bq[j][i] = buf_load16(b_rsrc, v ? cb + (uint32_t)((j * p.KF + kf) * kFragBytes + lane * 16) : kBufOOB);
+        bs[j][i] = buf_load4(bs_rsrc, v ? sb + (uint32_t)((j * p.KFS + sg) * kScaleGroupBytes + lane * 4) : kBufOOB);
       }
     }
   };
   const BufRsrc a_rsrc = make_rsrc(A8 ? (const void*)p.a8 : (const void*)p.a16, p.a_bytes);
   const BufRsrc as_rsrc = make_rsrc(p.as, p.as_bytes);
 
-  int par = 0;  // s_red buffer of the current group
-  for (int r0 = 0; r0 < rt.m; r0 += 16) {
+  for (int r0 = 0; r0 < m; r0 += 16) {
     // ---- activation rows: lane (r16, g) owns row r0 + r16, this wave's K range
     const int rr = r0 + r16;
     int64_t src = -1;
-    if (rr < rt.m) src = p.a_by_token ? s_rows[rr] / p.k : s_rows[rr];
+    if (rr < m) src = p.a_by_token ? s_rows[rr] / p.k : s_rows[rr];
     uint4 av[KW][A8 ? 2 : 4];
     int sa[KW];
     const int kblocks = (int)(p.K / 32);
@@ -291,7 +265,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(const DecodeParams 
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int row = r0 + 4 * g + i;
-          const bool live = row < rt.m;
+          const bool live = row < m;
           const int64_t pr = live ? s_rows[row] : 0;
           if constexpr (MODE == DMODE_DOWN) {
 #pragma unroll
@@ -341,65 +315,54 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(const DecodeParams 
       par ^= 1;  // the next group writes the other buffer; one barrier per group suffices
     };
 
-    // ---- stream the run of fragment groups.  NB = 2: the next group's loads
-    // are in flight while the current group runs on the MFMAs.  The loop body
-    // has no early exit (the odd group is guarded instead) and the scheduling
-    // barriers keep each prefetch ahead of the MFMAs it overlaps, so every
-    // wait covers exactly the group it consumes.
-    if constexpr (NB == 2) {
-      uint4 bq0[FR][KW], bq1[FR][KW];
-      uint32_t bs0[FR][KW], bs1[FR][KW];
-      load_b(bq0, bs0, g_begin);
-      for (int gi = g_begin; gi < g_end; gi += 2) {
-        load_b(bq1, bs1, gi + 1);
-        __builtin_amdgcn_sched_barrier(0);
-        group(bq0, bs0, gi);
-        load_b(bq0, bs0, gi + 2);
-        __builtin_amdgcn_sched_barrier(0);
-        if (gi + 1 < g_end) group(bq1, bs1, gi + 1);
-      }
-      wait_vmem_all();  // the last prefetch (zeros) is not carried into the next row block
-    } else {
-      uint4 bq0[FR][KW];
-      uint32_t bs0[FR][KW];
-      for (int gi = g_begin; gi < g_end; ++gi) {
-        load_b(bq0, bs0, gi);
-        group(bq0, bs0, gi);
-      }
+    // ---- the groups of this part, one at a time: the other waves and
+    // workgroups on the compute unit keep the memory system busy meanwhile
+    uint4 bq[FR][KW];
+    uint32_t bs[FR][KW];
+    for (int gi = g_begin; gi < g_end; ++gi) {
+      load_b(bq, bs, gi);
+      group(bq, bs, gi);
     }
+  }
   }
 }
 
-template <int WF, int AF, int MODE, int FR, int KW>
-static int launch_decode_kw(const DecodeParams& p, int n_slots, hipStream_t s) {
-  constexpr int NB = FR * KW <= 8 ? 2 : 1;  // double-buffer the weights while registers allow
-  const dim3 grid((unsigned)(n_slots * p.n_runs));
-  hipLaunchKernelGGL((decode_kernel<WF, AF, MODE, FR, KW, NB>), grid, dim3(kDecThreads), 0, s, p);
-  return (int)hipGetLastError();
+// Workgroups the device holds at once for one kernel (cached per device).
+template <typename Kernel>
+static int resident_workgroups(Kernel kernel) {
+  static int cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (!cached[dev]) {
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kDecThreads, 0) != hipSuccess || per_cu < 1)
+      per_cu = 1;
+    cached[dev] = per_cu * device_cu_count();
+  }
+  return cached[dev];
 }
 
-static int decode_slots(const BindingImpl& b) { return (int)(b.T * b.k < b.E ? b.T * b.k : b.E); }
-
-// Fragment groups per workgroup: enough workgroups to cover the chip twice,
-// at most kDecodeMaxRun groups in one run.
-static void set_runs(DecodeParams& p, int n_slots) {
-  const int64_t items = (int64_t)n_slots * p.n_groups;
-  int ng = (int)((items + 511) / 512);
-  ng = ng < 1 ? 1 : (ng > kDecodeMaxRun ? kDecodeMaxRun : ng);
-  p.ng = ng;
-  p.n_runs = (p.n_groups + ng - 1) / ng;
+// One workgroup per resident slot, never more than the items of the largest
+// possible touched set (min(T*k, E) experts).
+template <int WF, int AF, int MODE, int FR, int KW>
+static int launch_decode_kw(const BindingImpl& b, const DecodeParams& p, hipStream_t s) {
+  auto kernel = decode_kernel<WF, AF, MODE, FR, KW>;
+  const int64_t max_slots = b.T * b.k < b.E ? b.T * b.k : b.E;
+  int64_t grid = resident_workgroups(kernel);
+  if (grid > max_slots * p.n_groups) grid = max_slots * p.n_groups;
+  if (grid < 1) grid = 1;
+  hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kDecThreads), 0, s, p);
+  return (int)hipGetLastError();
 }
 
 // K fragments per wave: the smallest of 2, 4, 8 that covers ceil(KF / 4).
 template <int WF, int AF, int MODE, int FR>
 static int launch_decode_t(const BindingImpl& b, DecodeParams& p, hipStream_t s) {
-  const int n_slots = decode_slots(b);
   p.n_groups = (p.NF + FR - 1) / FR;
-  set_runs(p, n_slots);
   const int kper = (p.KF + 3) / 4;
-  if (kper <= 2) return launch_decode_kw<WF, AF, MODE, FR, 2>(p, n_slots, s);
-  if (kper <= 4) return launch_decode_kw<WF, AF, MODE, FR, 4>(p, n_slots, s);
-  return launch_decode_kw<WF, AF, MODE, FR, 8>(p, n_slots, s);
+  if (kper <= 2) return launch_decode_kw<WF, AF, MODE, FR, 2>(b, p, s);
+  if (kper <= 4) return launch_decode_kw<WF, AF, MODE, FR, 4>(b, p, s);
+  return launch_decode_kw<WF, AF, MODE, FR, 8>(b, p, s);
 }
 
 template <int MODE, int FR>

@@ -43,12 +43,6 @@ __device__ __forceinline__ int buf_load1(BufRsrc r, uint32_t off) {
   return (int)__builtin_amdgcn_raw_buffer_load_b8(r, off, 0, 0);
 }
 
-// s_waitcnt vmcnt(0) (gfx9 encoding: expcnt and lgkmcnt left at their
-// maxima).  Placed where a loop exits with prefetches still in flight, so that
-// the compiler does not carry those pending loads into the wait counts of
-// every later iteration.
-__device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
-
 __device__ __forceinline__ uint32_t f32_bits(float f) { return __builtin_bit_cast(uint32_t, f); }
 __device__ __forceinline__ float bits_f32(uint32_t u) { return __builtin_bit_cast(float, u); }
 

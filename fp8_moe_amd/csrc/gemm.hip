@@ -385,7 +385,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void moe_gemm_kernel(const GemmPar
 
 static int g_cu_count[64];
 
-static int cu_count() {
+int device_cu_count() {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
   if (!g_cu_count[dev]) {
@@ -401,7 +401,7 @@ constexpr int kGemmNFW = 4;  // weight fragments per wave: workgroup tile 144 ro
 template <int WF, int AF, int MODE>
 static int launch_gemm_t(const GemmParams& p, int64_t max_work, hipStream_t s) {
   // persistent grid: one workgroup per CU, a multiple of 8 (one share per XCD)
-  int64_t grid = cu_count();
+  int64_t grid = device_cu_count();
   if (max_work < grid) grid = (max_work + 7) / 8 * 8;
   grid = grid / 8 * 8;
   if (grid <= 0) grid = 8;

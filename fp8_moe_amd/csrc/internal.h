@@ -136,6 +136,8 @@ int launch_quant_rows(const uint16_t* x, int64_t rows, int64_t cols, int64_t str
 int launch_gemm1(const BindingImpl& b, hipStream_t s);
 int launch_gemm2(const BindingImpl& b, hipStream_t s);
 int launch_combine(const BindingImpl& b, hipStream_t s);
+// compute units of the current device (cached per device)
+int device_cu_count();
 int launch_decode1(const BindingImpl& b, hipStream_t s);
 int launch_decode2(const BindingImpl& b, hipStream_t s);
 int launch_decode_combine(const BindingImpl& b, hipStream_t s);
