@@ -39,6 +39,15 @@ __device__ __forceinline__ uint4 buf_load16(BufRsrc r, uint32_t off) {
 __device__ __forceinline__ uint32_t buf_load4(BufRsrc r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
 }
+// The same with a scalar (wave-uniform) part of the offset in soff.  Callers
+// keep voff + soff inside the resource for every in-range voff, so the result
+// does not depend on whether the hardware range-checks soff.
+__device__ __forceinline__ uint4 buf_load16s(BufRsrc r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+__device__ __forceinline__ uint32_t buf_load4s(BufRsrc r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+}
 __device__ __forceinline__ int buf_load1(BufRsrc r, uint32_t off) {
   return (int)__builtin_amdgcn_raw_buffer_load_b8(r, off, 0, 0);
 }

@@ -118,8 +118,13 @@ __global__ __launch_bounds__(kGemmThreads, 1) void moe_gemm_kernel(const GemmPar
     const BufRsrc b_rsrc = make_rsrc(bcodes, p.b_codes_expert);
     const BufRsrc bs_rsrc = make_rsrc(bscales, p.b_scales_expert);
 
-    // byte offset of each of this thread's A rows (token row for GEMM1, h row for GEMM2)
-    uint32_t a_off[LOADS];
+    // Per-lane offsets are fixed for the work item; the K step adds a scalar
+    // offset.  Steps past the last K fragment (the prefetch at the end of the
+    // loop) reload the last fragment, whose data is never used, so every
+    // address stays inside its row.
+    // byte offset of this thread's 16-byte chunk c of each of its A rows
+    // (token row for GEMM1, h row for GEMM2); rows outside the tile read zeros
+    uint32_t a_voff[LOADS];
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
       const int rr = tid / CHUNKS + (kGemmThreads / CHUNKS) * i;
@@ -132,9 +137,9 @@ __global__ __launch_bounds__(kGemmThreads, 1) void moe_gemm_kernel(const GemmPar
           sr = row0 + rr;
         }
       }
-      a_off[i] = sr >= 0 ? (uint32_t)(sr * p.a_stride * ESZ) : kBufOOB;
+      a_voff[i] = sr >= 0 ? (uint32_t)(sr * p.a_stride * ESZ + 16 * c) : kBufOOB;
     }
-    uint32_t s_off = kBufOOB;  // A8: scale row of threads 0..kTileRows-1
+    uint32_t s_voff = kBufOOB;  // A8: scale row of threads 0..kTileRows-1
     if (A8 && tid < kTileRows && tid < nrows) {
       int sr = -1;
       if (p.sorted) {
@@ -143,21 +148,29 @@ __global__ __launch_bounds__(kGemmThreads, 1) void moe_gemm_kernel(const GemmPar
       } else {
         sr = row0 + tid;
       }
-      if (sr >= 0) s_off = (uint32_t)(sr * p.as_stride);
+      if (sr >= 0) s_voff = (uint32_t)(sr * p.as_stride);
     }
     const int kblocks = (int)(p.K / 32);
+    // K not a multiple of 128: in the last fragment a chunk past K reads zeros
+    const int k_last = (int)(p.K - (int64_t)(p.KF - 1) * kFragK);  // elements in the last fragment
+    const bool ragged = k_last < kFragK;
+    const bool chunk_in_last = (A8 ? 16 : 8) * c < k_last;
 
-    // A chunks of K fragment kf (zeros past K or past the last fragment);
-    // A8: the 4 block scales of the row, with the byte mask of real blocks
+    // A chunks of K fragment kf; A8: the 4 block scales of the row, with the
+    // byte mask of real blocks
     auto load_a = [&](uint4 (&ra)[LOADS], uint32_t& rs, uint32_t& rk, int kf) {
-      const int64_t k0 = (int64_t)kf * kFragK + (A8 ? 16 : 8) * c;
-      const bool kin = k0 < p.K;
+      const int kfc = min(kf, p.KF - 1);
+      const uint32_t soff = (uint32_t)(kfc * kFragK * ESZ);
+      if (ragged && kfc == p.KF - 1) {
 #pragma unroll
-      for (int i = 0; i < LOADS; ++i)
-        ra[i] = buf_load16(a_rsrc, (kin && a_off[i] != kBufOOB) ? a_off[i] + (uint32_t)(k0 * ESZ) : kBufOOB);
+        for (int i = 0; i < LOADS; ++i) ra[i] = buf_load16s(a_rsrc, chunk_in_last ? a_voff[i] : kBufOOB, soff);
+      } else {
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i) ra[i] = buf_load16s(a_rsrc, a_voff[i], soff);
+      }
       if constexpr (A8) {
-        const int nb = min(max(kblocks - 4 * kf, 0), 4);
-        rs = buf_load4(s_rsrc, (nb > 0 && s_off != kBufOOB) ? s_off + 4 * kf : kBufOOB);
+        const int nb = min(max(kblocks - 4 * kfc, 0), 4);
+        rs = buf_load4s(s_rsrc, s_voff, (uint32_t)(4 * kfc));
         rk = nb >= 4 ? 0xFFFFFFFFu : (1u << (8 * nb)) - 1u;
       }
     };
@@ -173,15 +186,22 @@ __global__ __launch_bounds__(kGemmThreads, 1) void moe_gemm_kernel(const GemmPar
         if (tid < kTileRows) lds_s[buf][tid] = (rs & rk) | (0x7F7F7F7Fu & ~rk);
       }
     };
+    // weight fragments f0 + j: per-lane offsets (zeros past the matrix) and
+    // the K step as a scalar offset
+    uint32_t b_voff[NFW], bs_voff[NFW];
+#pragma unroll
+    for (int j = 0; j < NFW; ++j) {
+      const int f = f0 + j;
+      b_voff[j] = f < p.NF ? (uint32_t)(f * p.KF * kFragBytes + lane * 16) : kBufOOB;
+      bs_voff[j] = f < p.NF ? (uint32_t)(f * p.KFS * kScaleGroupBytes + lane * 4) : kBufOOB;
+    }
     auto load_b = [&](uint4 (&q)[NFW], uint32_t (&sc)[NFW], int kf) {
-      const int sgrp = WF == B12X_WEIGHT_MXFP4 ? kf >> 2 : kf >> 1;
-      const bool kin = kf < p.KF;
+      const int kfc = min(kf, p.KF - 1);
+      const int sgrp = WF == B12X_WEIGHT_MXFP4 ? kfc >> 2 : kfc >> 1;
 #pragma unroll
       for (int j = 0; j < NFW; ++j) {
-        const int f = f0 + j;
-        const bool v = kin && f < p.NF;
-        q[j] = buf_load16(b_rsrc, v ? (uint32_t)((f * p.KF + kf) * kFragBytes + lane * 16) : kBufOOB);
-        sc[j] = buf_load4(bs_rsrc, v ? (uint32_t)((f * p.KFS + sgrp) * kScaleGroupBytes + lane * 4) : kBufOOB);
+        q[j] = buf_load16s(b_rsrc, b_voff[j], (uint32_t)(kfc * kFragBytes));
+        sc[j] = buf_load4s(bs_rsrc, bs_voff[j], (uint32_t)(sgrp * kScaleGroupBytes));
       }
     };
 
@@ -195,8 +215,9 @@ __global__ __launch_bounds__(kGemmThreads, 1) void moe_gemm_kernel(const GemmPar
     // bf16 operands of sub-step s+1 (dequantized weights, LDS activation
     // reads) are produced while sub-step s runs on the MFMAs; the schedule
     // interleaves them so the VALU works under the matrix core.
-    auto compute = [&](auto nmf_tag, int buf, const uint4 (&bq)[NFW], const uint32_t (&bs)[NFW], int kf) {
+    auto compute = [&](auto nmf_tag, auto buf_tag, const uint4 (&bq)[NFW], const uint32_t (&bs)[NFW], int kf) {
       constexpr int NMF = decltype(nmf_tag)::value;
+      constexpr int buf = decltype(buf_tag)::value;  // also the parity of kf
       const uint8_t* la = lds_a[buf];
       if constexpr (!A8) {
         float scl[NFW][2];  // per fragment: scale of the lane's first / second 16 K (NVFP4), or the E8M0 scale
@@ -204,9 +225,10 @@ __global__ __launch_bounds__(kGemmThreads, 1) void moe_gemm_kernel(const GemmPar
         for (int j = 0; j < NFW; ++j) {
           if constexpr (WF == B12X_WEIGHT_MXFP4) {
             scl[j][0] = scl[j][1] = e8m0_as_scale((bs[j] >> (8 * (kf & 3))) & 0xFFu);
-          } else {
-            scl[j][0] = e4m3_value((bs[j] >> (16 * (kf & 1))) & 0xFFu);
-            scl[j][1] = e4m3_value((bs[j] >> (16 * (kf & 1) + 8)) & 0xFFu);
+          } else {  // the two E4M3 scales of this K fragment, decoded by the hardware (OCP E4M3)
+            const f32x2 sv = __builtin_amdgcn_cvt_pk_f32_fp8((int)bs[j], buf == 1);
+            scl[j][0] = sv.x;
+            scl[j][1] = sv.y;
           }
         }
         auto dq = [&](bf16x8 (&out)[NFW], int s) {
@@ -296,14 +318,14 @@ __global__ __launch_bounds__(kGemmThreads, 1) void moe_gemm_kernel(const GemmPar
         // even step: LDS buffer 0, ra1 holds step kf+1
         __syncthreads();
         load_a(ra0, rs0, rk0, kf + 2);
-        if (!idle) compute(nmf_tag, 0, bq0, bs0, kf);
+        if (!idle) compute(nmf_tag, std::integral_constant<int, 0>{}, bq0, bs0, kf);
         store_a(ra1, rs1, rk1, 1);
         load_b(bq0, bs0, kf + 2);
         if (kf + 1 >= p.KF) break;
         // odd step: LDS buffer 1, ra0 holds step kf+2
         __syncthreads();
         load_a(ra1, rs1, rk1, kf + 3);
-        if (!idle) compute(nmf_tag, 1, bq1, bs1, kf + 1);
+        if (!idle) compute(nmf_tag, std::integral_constant<int, 1>{}, bq1, bs1, kf + 1);
         store_a(ra0, rs0, rk0, 0);
         load_b(bq1, bs1, kf + 3);
       }
