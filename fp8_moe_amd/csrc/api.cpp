@@ -210,6 +210,9 @@ b12x_status b12x_moe_plan(const b12x_moe_caps* caps, b12x_moe_plan_t* out) {
   if (dmax > kDecodePairs) dmax = kDecodePairs;
   p->decode_max_pairs = (decode_ok && dmax > 0) ? dmax : 0;
   const bool a8 = p->afmt == B12X_ACT_MXFP8;
+  // NVFP4 weights with bf16 activations: the grouped path's GEMM1 reads a
+  // scaled f16 copy of a (2 bytes per element) and one exponent per row
+  const bool x16 = p->wfmt == B12X_WEIGHT_NVFP4 && !a8;
   uint64_t len[R_COUNT_] = {0};
   len[R_COUNTS] = 4ull * p->E;
   len[R_OFFSETS] = 4ull * (p->E + 1);
@@ -219,8 +222,8 @@ b12x_status b12x_moe_plan(const b12x_moe_caps* caps, b12x_moe_plan_t* out) {
   len[R_TILES] = 16ull * p->max_tiles;
   len[R_NTILES] = 16;
   len[R_CHUNK] = 4ull * p->max_chunks * p->E;
-  len[R_XQ] = a8 ? (uint64_t)p->max_tokens * p->Hp : 0;
-  len[R_XS] = a8 ? (uint64_t)p->max_tokens * (p->Hp / 32) : 0;
+  len[R_XQ] = a8 ? (uint64_t)p->max_tokens * p->Hp : (x16 ? 2ull * p->max_tokens * p->Hp : 0);
+  len[R_XS] = a8 ? (uint64_t)p->max_tokens * (p->Hp / 32) : (x16 ? 4ull * p->max_tokens : 0);
   len[R_H] = (uint64_t)p->max_rows * p->Ip * (a8 ? 1 : 2);
   len[R_HS] = a8 ? (uint64_t)p->max_rows * (p->Ip / 32) : 0;
   len[R_Y] = 4ull * p->max_rows * p->H;
@@ -295,6 +298,7 @@ b12x_status b12x_moe_bind(b12x_moe_plan_t p, void* scratch, uint64_t scratch_byt
   b.path = (T > 0 && T * p->k <= p->decode_max_pairs) ? 2 : 1;
   b.E = p->E; b.H = p->H; b.I = p->I; b.k = p->k;
   b.gated = p->gated; b.wfmt = p->wfmt; b.afmt = p->afmt; b.act = p->act;
+  b.a_f16 = b.path == 1 && p->wfmt == B12X_WEIGHT_NVFP4 && p->afmt == B12X_ACT_BF16;
   b.T = T; b.a_stride = a_stride; b.out_stride = out_stride;
   b.Hp = p->Hp; b.Ip = p->Ip; b.max_rows = p->max_rows; b.max_tiles = p->max_tiles;
   b.nf13 = p->l13.nf; b.kf13 = p->l13.kf; b.kfs13 = p->l13.kfs;
@@ -336,7 +340,7 @@ static b12x_status get_binding(const b12x_moe_binding* binding, BindingImpl* b) 
 }
 
 static bool stage_in_path(const BindingImpl& b, int stage) {
-  if (stage == B12X_STAGE_QUANT_X) return b.afmt == B12X_ACT_MXFP8;
+  if (stage == B12X_STAGE_QUANT_X) return b.afmt == B12X_ACT_MXFP8 || b.a_f16;
   if (b.path == 2) return stage == B12X_STAGE_DECODE1 || stage == B12X_STAGE_DECODE2 || stage == B12X_STAGE_COMBINE;
   return stage >= B12X_STAGE_ROUTE && stage <= B12X_STAGE_COMBINE;
 }
@@ -350,7 +354,10 @@ static b12x_status run_stage(const BindingImpl& b, int stage, hipStream_t s) {
   int err = 0;
   switch (stage) {
     case B12X_STAGE_ROUTE: err = launch_route(b, s); break;
-    case B12X_STAGE_QUANT_X: err = launch_quant_rows(b.a, b.T, b.H, b.a_stride, b.xq, b.Hp, b.xs, b.Hp / 32, s); break;
+    case B12X_STAGE_QUANT_X:
+      err = b.a_f16 ? launch_f16_rows(b.a, b.T, b.H, b.a_stride, (uint16_t*)b.xq, b.Hp, (int32_t*)b.xs, s)
+                    : launch_quant_rows(b.a, b.T, b.H, b.a_stride, b.xq, b.Hp, b.xs, b.Hp / 32, s);
+      break;
     case B12X_STAGE_GEMM1: err = launch_gemm1(b, s); break;
     case B12X_STAGE_GEMM2: err = launch_gemm2(b, s); break;
     case B12X_STAGE_COMBINE: err = b.path == 2 ? launch_decode_combine(b, s) : launch_combine(b, s); break;
@@ -398,7 +405,9 @@ b12x_status b12x_moe_binding_query(const b12x_moe_binding* binding, int32_t what
     case B12X_QUERY_TILE_ROWS: *value = kTileRows; break;
     case B12X_QUERY_ROW_PAD: *value = kRowPad; break;
     case B12X_QUERY_T: *value = b.T; break;
-    case B12X_QUERY_NUM_STAGES: *value = (b.path == 2 ? 3 : 4) + (b.afmt == B12X_ACT_MXFP8 ? 1 : 0); break;
+    case B12X_QUERY_NUM_STAGES:
+      *value = (b.path == 2 ? 3 : 4) + (stage_in_path(b, B12X_STAGE_QUANT_X) ? 1 : 0);
+      break;
     default: return fail(B12X_ERR_INVALID_ARGUMENT, "unknown query %d", what);
   }
   return B12X_OK;

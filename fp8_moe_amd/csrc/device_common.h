@@ -16,6 +16,13 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// Activation format of the grouped GEMMs beyond the public ones: a scaled f16
+// copy of bf16 activations (one power-of-two exponent per row), used with
+// NVFP4 weights.
+constexpr int kActF16 = 3;
 
 // Raw buffer loads (CDNA buffer resource, stride 0).  A byte offset at or
 // past the record count returns zeros without a memory access, so a guarded
@@ -154,6 +161,32 @@ __device__ __forceinline__ bf16x8 dequant8_bf16(uint32_t codes, float scale) {
     }
     return u32x4_as_bf16x8(out[0], out[1], out[2], out[3]);
   }
+}
+
+// NVFP4 weights for the f16 MFMA: one E4M3 block scale s = 2^E * F (F in
+// [1, 2) with at most 4 significant bits; sign kept in F).  The scaled FP4
+// conversion applies 2^E (it reads only the exponent field of its scale) and
+// one packed f16 multiply applies F to two values: 8 instructions for 8
+// weights.  Every product has at most 6 significant bits and lies in
+// [2^-10, 2688] (or is zero), so it is exact in f16.
+struct NvScaleF16 {
+  float e;   // 2^E as the scaled conversion's scale operand
+  f16x2 f;   // F, F
+};
+__device__ __forceinline__ NvScaleF16 nv_scale_f16(float s) {
+  const uint32_t b = f32_bits(s);
+  NvScaleF16 r;
+  r.e = bits_f32(b & 0x7F800000u);  // s = 0: exponent field 0, the products are 0
+  const float fm = bits_f32((b & 0x807FFFFFu) | 0x3F800000u);
+  r.f = __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(fm, fm));  // exact: <= 4 significant bits
+  return r;
+}
+__device__ __forceinline__ f16x8 dequant8_f16_nv(uint32_t codes, const NvScaleF16& sc) {
+  const f16x2 p0 = __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, sc.e, 0)) * sc.f;
+  const f16x2 p1 = __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, sc.e, 1)) * sc.f;
+  const f16x2 p2 = __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, sc.e, 2)) * sc.f;
+  const f16x2 p3 = __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, sc.e, 3)) * sc.f;
+  return f16x8{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
 }
 
 }  // namespace b12x

@@ -42,6 +42,7 @@ struct GemmParams {
   int64_t a_stride;   // elements (bf16) or bytes (codes)
   int64_t as_stride;  // bytes
   int64_t a_bytes, as_bytes;  // extents of a16 / a8 and as (at most 1 GiB)
+  const int32_t* a_exp;       // f16 activations: power-of-two exponent of each token row
   const int32_t* sorted;
   int k_top;
   int64_t n_pairs;
@@ -79,6 +80,9 @@ enum { MODE_SILU = 1, MODE_RELU2 = 2, MODE_DOWN = 3 };
 template <int WF, int AF, int MODE, int NFW>
 __global__ __launch_bounds__(kGemmThreads, 1) void moe_gemm_kernel(const GemmParams p) {
   constexpr bool A8 = AF == B12X_ACT_MXFP8;
+  constexpr bool F16 = AF == kActF16;  // f16 activations x NVFP4 weights dequantized to f16
+  static_assert(!F16 || WF == B12X_WEIGHT_NVFP4, "f16 activations run with NVFP4 weights");
+  using OpT = std::conditional_t<F16, f16x8, bf16x8>;  // 16-bit MFMA operand type
   constexpr int ROWB = A8 ? 144 : 272;  // LDS bytes per A row: 128 K elements + 16 bytes of skew
   constexpr int NT = 4 * NFW;           // weight fragments per workgroup tile
   constexpr int LOADS = (kTileRows * (A8 ? 8 : 16) + kGemmThreads - 1) / kGemmThreads;  // A row chunks per thread
@@ -87,6 +91,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void moe_gemm_kernel(const GemmPar
   static_assert(kTileRows % 16 == 0 && kTileRows <= kGemmThreads, "tile rows");
   __shared__ __attribute__((aligned(16))) uint8_t lds_a[2][kTileRows * ROWB];
   __shared__ uint32_t lds_s[2][A8 ? kTileRows : 1];
+  __shared__ float lds_rs[F16 ? kTileRows : 1];  // f16: 2^exponent of each tile row
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -220,52 +225,61 @@ __global__ __launch_bounds__(kGemmThreads, 1) void moe_gemm_kernel(const GemmPar
       constexpr int buf = decltype(buf_tag)::value;  // also the parity of kf
       const uint8_t* la = lds_a[buf];
       if constexpr (!A8) {
-        float scl[NFW][2];  // per fragment: scale of the lane's first / second 16 K (NVFP4), or the E8M0 scale
+        float scl[NFW][2];       // per fragment: scale of the lane's first / second 16 K (NVFP4), or the E8M0 scale
+        NvScaleF16 scf[NFW][2];  // the same split for the f16 dequantization
 #pragma unroll
         for (int j = 0; j < NFW; ++j) {
           if constexpr (WF == B12X_WEIGHT_MXFP4) {
             scl[j][0] = scl[j][1] = e8m0_as_scale((bs[j] >> (8 * (kf & 3))) & 0xFFu);
           } else {  // the two E4M3 scales of this K fragment, decoded by the hardware (OCP E4M3)
             const f32x2 sv = __builtin_amdgcn_cvt_pk_f32_fp8((int)bs[j], buf == 1);
-            scl[j][0] = sv.x;
-            scl[j][1] = sv.y;
+            if constexpr (F16) {
+              scf[j][0] = nv_scale_f16(sv.x);
+              scf[j][1] = nv_scale_f16(sv.y);
+            } else {
+              scl[j][0] = sv.x;
+              scl[j][1] = sv.y;
+            }
           }
         }
-        auto dq = [&](bf16x8 (&out)[NFW], int s) {
+        auto dq = [&](OpT (&out)[NFW], int s) {
 #pragma unroll
           for (int j = 0; j < NFW; ++j) {
             const uint32_t dw = s == 0 ? bq[j].x : s == 1 ? bq[j].y : s == 2 ? bq[j].z : bq[j].w;
-            out[j] = dequant8_bf16<WF>(dw, scl[j][s >> 1]);
+            if constexpr (F16) out[j] = dequant8_f16_nv(dw, scf[j][s >> 1]);
+            else out[j] = dequant8_bf16<WF>(dw, scl[j][s >> 1]);
           }
         };
         auto ld = [&](uint4 (&out)[NMF], int s) {
 #pragma unroll
           for (int mf = 0; mf < NMF; ++mf) out[mf] = *(const uint4*)(la + (16 * mf + r16) * ROWB + 64 * g + 16 * s);
         };
-        bf16x8 b0[NFW], b1[NFW];
+        OpT b0[NFW], b1[NFW];
         uint4 a0[NMF], a1[NMF];
         dq(b0, 0);
         ld(a0, 0);
-        auto step = [&](const bf16x8 (&bc)[NFW], const uint4 (&ac)[NMF], bf16x8 (&bn)[NFW], uint4 (&an)[NMF],
-                        int s) {
+        auto step = [&](const OpT (&bc)[NFW], const uint4 (&ac)[NMF], OpT (&bn)[NFW], uint4 (&an)[NMF], int s) {
           if (s < 3) {
             ld(an, s + 1);
             dq(bn, s + 1);
           }
 #pragma unroll
           for (int mf = 0; mf < NMF; ++mf) {
-            const bf16x8 afr = __builtin_bit_cast(bf16x8, ac[mf]);
+            const OpT afr = __builtin_bit_cast(OpT, ac[mf]);
 #pragma unroll
-            for (int j = 0; j < NFW; ++j)
-              acc[mf][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr, bc[j], acc[mf][j], 0, 0, 0);
+            for (int j = 0; j < NFW; ++j) {
+              if constexpr (F16) acc[mf][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(afr, bc[j], acc[mf][j], 0, 0, 0);
+              else acc[mf][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr, bc[j], acc[mf][j], 0, 0, 0);
+            }
           }
           if (s < 3) {
             // NMF*NFW MFMAs, each followed by a share of the next sub-step's VALU and LDS work
+            constexpr int kValu = (WF == B12X_WEIGHT_NVFP4 && !F16) ? 4 : 2;
 #pragma unroll
             for (int i = 0; i < NMF * NFW; ++i) {
-              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-              __builtin_amdgcn_sched_group_barrier(0x002, WF == B12X_WEIGHT_NVFP4 ? 4 : 2, 0);  // VALU
-              __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);      // MFMA
+              __builtin_amdgcn_sched_group_barrier(0x002, kValu, 0);  // VALU
+              __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);      // DS read
             }
           }
         };
@@ -309,6 +323,16 @@ __global__ __launch_bounds__(kGemmThreads, 1) void moe_gemm_kernel(const GemmPar
       uint4 bq0[NFW], bq1[NFW];
       uint32_t bs0[NFW], bs1[NFW];
       __syncthreads();  // the previous work item is done with LDS
+      if constexpr (F16) {  // 2^exponent of each row's token (read by the epilogue)
+        if (tid < kTileRows) {
+          int ex = 0;
+          if (tid < nrows) {
+            const int pair = p.sorted[row0 + tid];
+            if (pair >= 0 && pair < p.n_pairs) ex = p.a_exp[pair / p.k_top];
+          }
+          lds_rs[tid] = bits_f32((uint32_t)(127 + ex) << 23);
+        }
+      }
       load_a(ra0, rs0, rk0, 0);
       store_a(ra0, rs0, rk0, 0);
       load_a(ra1, rs1, rk1, 1);
@@ -365,14 +389,15 @@ __global__ __launch_bounds__(kGemmThreads, 1) void moe_gemm_kernel(const GemmPar
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int64_t row = row0 + 16 * mf + 4 * g + i;
+            const float rsc = F16 ? gsc * lds_rs[F16 ? 16 * mf + 4 * g + i : 0] : gsc;  // f16: undo the row's 2^-e
             float hv[NH];
 #pragma unroll
             for (int q = 0; q < NH; ++q) {
               if constexpr (MODE == MODE_SILU) {
-                const float gt = acc[mf][2 * q][i] * gsc, up = acc[mf][2 * q + 1][i] * gsc;
+                const float gt = acc[mf][2 * q][i] * rsc, up = acc[mf][2 * q + 1][i] * rsc;
                 hv[q] = gt * __builtin_amdgcn_rcpf(1.0f + __expf(-gt)) * up;
               } else {
-                const float z = acc[mf][q][i] * gsc;
+                const float z = acc[mf][q][i] * rsc;
                 hv[q] = z > 0.f ? z * z : 0.f;
               }
             }
@@ -435,6 +460,9 @@ template <int MODE>
 static int dispatch(const BindingImpl& b, const GemmParams& p, int64_t max_work, hipStream_t s) {
   const bool nv = b.wfmt == B12X_WEIGHT_NVFP4, a8 = b.afmt == B12X_ACT_MXFP8;
   if (a8) return launch_gemm_t<B12X_WEIGHT_MXFP4, B12X_ACT_MXFP8, MODE>(p, max_work, s);
+  if constexpr (MODE != MODE_DOWN) {
+    if (p.a_exp) return launch_gemm_t<B12X_WEIGHT_NVFP4, kActF16, MODE>(p, max_work, s);
+  }
   if (nv) return launch_gemm_t<B12X_WEIGHT_NVFP4, B12X_ACT_BF16, MODE>(p, max_work, s);
   return launch_gemm_t<B12X_WEIGHT_MXFP4, B12X_ACT_BF16, MODE>(p, max_work, s);
 }
@@ -455,6 +483,12 @@ int launch_gemm1(const BindingImpl& b, hipStream_t s) {
   p.as_stride = b.Hp / 32;
   p.a_bytes = a8 ? b.T * b.Hp : b.T * b.a_stride * 2;
   p.as_bytes = a8 ? b.T * (b.Hp / 32) : 0;
+  if (b.a_f16) {  // NVFP4 x bf16: the scaled f16 copy of a and its row exponents
+    p.a16 = (const uint16_t*)b.xq;
+    p.a_stride = b.Hp;
+    p.a_bytes = b.T * b.Hp * 2;
+    p.a_exp = (const int32_t*)b.xs;
+  }
   p.sorted = b.sorted;
   p.k_top = b.k;
   p.n_pairs = b.T * b.k;

@@ -87,6 +87,7 @@ struct BindingImpl {
   uint32_t magic;
   int32_t path;
   int32_t E, H, I, k, gated, wfmt, afmt, act;
+  int32_t a_f16;  // grouped path, NVFP4 x bf16: GEMM1 reads the scaled f16 copy of a (xq) and row exponents (xs)
   int64_t T, a_stride, out_stride;
   int64_t Hp, Ip, max_rows, max_tiles;
   int64_t nf13, kf13, kfs13, nf2, kf2, kfs2;
@@ -133,6 +134,8 @@ int launch_copy_f32(const float* src, float* dst, int n, hipStream_t s);
 int launch_route(const BindingImpl& b, hipStream_t s);
 int launch_quant_rows(const uint16_t* x, int64_t rows, int64_t cols, int64_t stride, uint8_t* codes,
                       int64_t code_stride, uint8_t* scales, int64_t scale_stride, hipStream_t s);
+int launch_f16_rows(const uint16_t* x, int64_t rows, int64_t cols, int64_t stride, uint16_t* out,
+                    int64_t out_stride, int32_t* exps, hipStream_t s);
 int launch_gemm1(const BindingImpl& b, hipStream_t s);
 int launch_gemm2(const BindingImpl& b, hipStream_t s);
 int launch_combine(const BindingImpl& b, hipStream_t s);

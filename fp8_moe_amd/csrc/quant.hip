@@ -55,4 +55,54 @@ int launch_quant_rows(const uint16_t* x, int64_t rows, int64_t cols, int64_t str
   return (int)hipGetLastError();
 }
 
+// Scaled f16 copy of bf16 rows for the NVFP4 weight GEMMs, which dequantize
+// the weights to f16 (half the conversion work of bf16 on gfx950, see the
+// grouped GEMM).  Row r is multiplied by 2^-e[r] with e[r] = floor(log2
+// max|x_r|) - 14 (clamped to [-110, 110]; 0 for an all-zero row), which puts
+// the row maximum in [2^14, 2^15): every bf16 value above 2^-31 of the row
+// maximum is then exact in f16, and the GEMM multiplies its fp32 results by
+// 2^e[r].  One workgroup per row.
+__global__ __launch_bounds__(256) void f16_rows_kernel(const uint16_t* __restrict__ x, int64_t cols, int64_t stride,
+                                                        uint16_t* __restrict__ out, int64_t out_stride,
+                                                        int32_t* __restrict__ exps) {
+  __shared__ uint32_t s_max[4];
+  const int64_t r = blockIdx.x;
+  const uint16_t* src = x + r * stride;
+  uint32_t m = 0;  // bf16 magnitude bits compare like the values
+  for (int64_t c = threadIdx.x * 8; c < cols; c += 256 * 8) {
+    const uint4 v = *(const uint4*)(src + c);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) m = max(m, max(w[i] & 0x7FFFu, (w[i] >> 16) & 0x7FFFu));
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
+  if ((threadIdx.x & 63) == 0) s_max[threadIdx.x >> 6] = m;
+  __syncthreads();
+  m = max(max(s_max[0], s_max[1]), max(s_max[2], s_max[3]));
+  int e = m ? ilog2_mag(m << 16) - 14 : 0;
+  e = e < -110 ? -110 : (e > 110 ? 110 : e);
+  const float mul = bits_f32((uint32_t)(127 - e) << 23);  // 2^-e, exact
+  for (int64_t c = threadIdx.x * 8; c < cols; c += 256 * 8) {
+    const uint4 v = *(const uint4*)(src + c);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const _Float16 lo = (_Float16)(bf16_to_f32(w[i] & 0xFFFFu) * mul);
+      const _Float16 hi = (_Float16)(bf16_to_f32(w[i] >> 16) * mul);
+      o[i] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+    }
+    *(uint4*)(out + r * out_stride + c) = make_uint4(o[0], o[1], o[2], o[3]);
+  }
+  if (threadIdx.x == 0) exps[r] = e;
+}
+
+int launch_f16_rows(const uint16_t* x, int64_t rows, int64_t cols, int64_t stride, uint16_t* out,
+                    int64_t out_stride, int32_t* exps, hipStream_t s) {
+  if (rows == 0) return 0;
+  hipLaunchKernelGGL(f16_rows_kernel, dim3((unsigned)rows), dim3(256), 0, s, x, cols, stride, out, out_stride, exps);
+  return (int)hipGetLastError();
+}
+
 }  // namespace b12x

@@ -237,3 +237,37 @@ def test_decode_edge_cases(case):
     assert ok, (rel_fro, rel_max)
     if kind == "all_bad":
         assert torch.all(out == 0)
+
+
+def test_nvfp4_rows_of_extreme_magnitude():
+    """NVFP4 x bf16 on the grouped path: rows scaled far up and down, a zero
+    row and a row mixing large and tiny values, compared row by row (each row
+    on its own scale) with the fp64 oracle.  (The per-tensor NVFP4 scale
+    multiplies the fp32 accumulators, so intermediates must stay finite
+    before it: row scales up to 2^40 here.)"""
+    import fp8_moe_amd as fm
+    wl = small_workload("nv_range", 4, 256, 128, 2, True, "nvfp4", "bf16")
+    T = 40
+    pr = Problem(wl, T, gen_device="cpu", decode_max_pairs=-1)
+    x, ids, tw = _inputs(wl, T)
+    scale = torch.ones(T, 1, dtype=torch.float32)
+    scale[0], scale[1], scale[2], scale[3] = 2.0 ** 40, 2.0 ** -50, 2.0 ** 25, 2.0 ** -30
+    xs = (x.float().cpu() * scale)
+    xs[4] = 0.0
+    xs[5, ::2] *= 2.0 ** -40                     # half the row 2^40 smaller than the rest
+    x = xs.to(torch.bfloat16).cuda()
+    b, out = pr.model.bind(x, ids, tw)
+    assert fm.binding_query(b, "path") == 1
+    fm.run(b)
+    torch.cuda.synchronize()
+    ref = pr.oracle(x, ids, tw)
+    got = out.detach().cpu().to(torch.float64).numpy()
+    assert np.all(np.isfinite(got))
+    assert np.all(got[4] == 0.0)
+    for t in range(T):
+        if t == 4:
+            continue
+        n = np.linalg.norm(ref[t])
+        assert n > 0, t
+        rel = np.linalg.norm(got[t] - ref[t]) / n
+        assert rel <= 5e-3, (t, rel)
