@@ -9,12 +9,15 @@ Method: C prepared copies of the weights (more than the 256 MB Infinity
 Cache holds) and S input sets rotate, so each call streams cold weights;
 S steps are captured in one graph and replayed (no host launch overhead in
 the timed region); timing with events around K steps after W warmup steps.
-The dominant kernel (GEMM1, gate/up + SiLU) is also timed launch by launch
-with event pairs on its stream for the roofline object.  Extra lines report
+The dominant kernel (the gate/up kernel of the decode path) is also timed on
+its own, as a graph of its launches between events on its stream, for the
+roofline object; its HBM traffic comes from the committed counter record in
+profiles/ when that record matches the kernel sources.  Extra lines report
 prefill (NVFP4, T=4096) TFLOP/s and the W4A8 (MXFP8 x MXFP4, ReLU^2) T=1
 decode, and the CPU oracle's rate on a bounded sample.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extra] [--no-cpu]
+       python bench.py --decode-t T [--steps K]   (one T only, for counter and trace runs)
 """
 import argparse
 import json
@@ -46,9 +49,11 @@ def touched_experts(ids, E):
     return len({e for e in ids if 0 <= e < E})
 
 
-def build_decode(fm, synth, torch):
+def build_decode(fm, synth, torch, only_t=None):
     wl = synth.WORKLOADS["decode"]
     Ts = wl.tokens
+    if only_t is not None and only_t not in Ts:
+        raise SystemExit(f"--decode-t must be one of {Ts}")
     w = synth.make_weights(wl, device="cuda")
     wp = fm.plan_weights(wl.E, wl.H, wl.I, wl.gated, wl.weight_format)
     copies = [fm.prepare_weights(wp, w["w13_codes"], w["w13_scales"], w["w2_codes"], w["w2_scales"])
@@ -59,6 +64,8 @@ def build_decode(fm, synth, torch):
     w13_per_expert = wl.n13 * wl.H // 2 + wl.n13 * wl.H // wl.group
     sets = {}
     for T in Ts:
+        if only_t is not None and T != only_t:
+            continue
         rows = []
         for s in range(N_SETS):
             x = synth.make_x(wl, T, device="cuda", salt=s)
@@ -71,6 +78,21 @@ def build_decode(fm, synth, torch):
                              w13_bytes=n_e * w13_per_expert))
         sets[T] = rows
     return wl, w, plan, scratch, copies, sets
+
+
+def bench_decode_t(fm, synth, torch, stream, T, reps):
+    """The decode workload at one T: the 10 input sets of the headline step (rotating
+    weight copies) captured in one graph and replayed `reps` times."""
+    wl, _, _, _, _, sets = build_decode(fm, synth, torch, only_t=T)
+    bl = [row["binding"] for row in sets[T]]
+    for b in bl:
+        fm.run(b, stream=stream)
+    g = capture(torch, fm, bl, stream)
+    g.replay()
+    sec = time_graph(torch, g, stream, reps) / (reps * len(bl))
+    nb = sum(row["bytes"] for row in sets[T]) / len(bl)
+    return {"decode_T": T, "calls": reps * len(bl), "us_per_call": sec * 1e6, "weight_GBs": nb / sec / 1e9,
+            "w13_bytes_per_call": sum(row["w13_bytes"] for row in sets[T]) / len(bl)}
 
 
 def capture(torch, fm, bindings, stream):
@@ -93,6 +115,20 @@ def time_graph(torch, g, stream, reps):
     return e0.elapsed_time(e1) / 1e3  # seconds
 
 
+def time_stage_graph(torch, fm, bindings, stage, stream, reps=10):
+    """Mean duration (s) of one stage's kernel: a graph of that stage for every
+    binding, replayed `reps` times between two events on `stream`.  The stages
+    before it ran for every binding beforehand (their outputs are in place)."""
+    for b in bindings:
+        fm.run(b, stream=stream)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for b in bindings:
+            fm.run_stage(b, stage, stream=stream)
+    g.replay()
+    return time_graph(torch, g, stream, reps) / (reps * len(bindings))
+
+
 def time_stage_launches(torch, fm, bindings, stage, stream, repeats=3):
     """Mean duration (s) of one stage's kernel, event pair around each launch.
     The stages before it ran for every binding beforehand (valid routing)."""
@@ -109,6 +145,34 @@ def time_stage_launches(torch, fm, bindings, stage, stream, repeats=3):
                 pairs.append((e0, e1))
     torch.cuda.synchronize()
     return sum(a.elapsed_time(b) for a, b in pairs) / len(pairs) / 1e3
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_gate_up_traffic.json")
+TRAFFIC_SOURCES = ["fp8_moe_amd/csrc/decode.hip", "fp8_moe_amd/csrc/device_common.h",
+                   "fp8_moe_amd/csrc/internal.h"]
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for rel in TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per gate/up launch from the committed counter record (FETCH_SIZE and
+    WRITE_SIZE, calibrated on a plain copy kernel), or None when the record is missing
+    or was taken on different kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256") != kernel_source_hash():
+        return None
+    return rec.get("bytes_per_launch")
 
 
 def cpu_baseline(wl, w_host, sets_host, budget_s=12.0):
@@ -196,6 +260,11 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="skip the prefill and W4A8 lines")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--prefill-only", action="store_true", help="only the prefill line (kernel tuning)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="five plain 1 GiB device copies (the reference for the HBM byte counters)")
+    ap.add_argument("--decode-t", type=int, default=0,
+                    help="only the decode workload at this T (one of 1, 8, 32), --steps graph replays of its "
+                         "10 input sets (for counter and trace runs)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the fused MoE here is a "
@@ -210,6 +279,18 @@ def main():
 
     if args.prefill_only:
         print(json.dumps({"prefill": bench_prefill(fm, synth, torch, stream)}))
+        return
+    if args.copy_calibration:
+        # a plain device copy of exactly 1 GiB per dispatch (counter calibration)
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": src.numel() * 4, "dispatches": 5}))
+        return
+    if args.decode_t:
+        print(json.dumps(bench_decode_t(fm, synth, torch, stream, args.decode_t, max(args.steps, 1))))
         return
     log("building decode workload")
     wl, w, plan, scratch, copies, sets = build_decode(fm, synth, torch)
@@ -267,15 +348,15 @@ def main():
                           "weight_GBs": nb / sec / 1e9, "frac_hbm": nb / sec / 1e9 / HBM_PEAK_GBS,
                           "tflops": 6.0 * wl.H * wl.I * T * wl.k / sec / 1e12}
 
-    # dominant kernel: the gate/up kernel (2/3 of the weight bytes), launch-by-launch events;
-    # small T runs the decode path (gate/up kernel "decode1"), larger T the grouped GEMM1
+    # dominant kernel: the gate/up kernel (2/3 of the weight bytes), timed as a graph of
+    # its own launches; small T runs the decode path (gate/up kernel "decode1")
     durs, w13b, durs2 = [], [], []
     for T in Ts:
         bl = [row["binding"] for row in sets[T]]
         path = fm.binding_query(bl[0], "path")
         st1, st2 = ("decode1", "decode2") if path == 2 else ("gemm1", "gemm2")
-        durs.append(time_stage_launches(torch, fm, bl, st1, stream, repeats=3))
-        durs2.append(time_stage_launches(torch, fm, bl, st2, stream, repeats=3))
+        durs.append(time_stage_graph(torch, fm, bl, st1, stream))
+        durs2.append(time_stage_graph(torch, fm, bl, st2, stream))
         w13b.append(sum(row["w13_bytes"] for row in sets[T]) / N_SETS)
         per_t[f"T{T}"]["path"] = "decode" if path == 2 else "grouped"
         per_t[f"T{T}"]["gate_up_kernel_us"] = durs[-1] * 1e6
@@ -284,7 +365,7 @@ def main():
     avg_bytes = sum(w13b) / len(w13b)
     achieved = avg_bytes / avg_dur / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
                 "kernel": "decode_kernel<MXFP4, BF16, SILU> (gate/up, decode path)",
                 "avg_launch_us": round(avg_dur * 1e6, 3),
                 "algorithmic_bytes_per_launch": round(avg_bytes),
