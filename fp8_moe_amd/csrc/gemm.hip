@@ -7,15 +7,17 @@
 //   GEMM2: y[row] = h[row] . W2_e^T
 // over the routing tiles (expert, first row, rows).  A workgroup of 4 waves
 // owns one routing tile (up to kTileRows = 144 rows) x 4*NFW weight fragments
-// (16 columns each).  The A rows (bf16
-// or MXFP8 codes) go through double-buffered LDS with a two-step register
-// prefetch; the packed FP4 fragments stream from global memory straight into
-// registers, two K steps ahead.  All loads are raw buffer loads whose
-// out-of-range offsets read zeros, so none of them sits behind a branch.
-//   W4A16: each 1 KB fragment is four 16x16x32 bf16 MFMA operands; FP4 is
-//          turned into bf16 in registers (v_cvt_scalef32_pk_bf16_fp4 with the
-//          E8M0 scale, or fp32 conversion times the E4M3 scale for NVFP4; both
-//          products are exact in bf16).
+// (16 columns each).  The packed FP4 fragments stream from global memory
+// straight into registers.  The activation rows reach LDS by DMA
+// (buffer_load ... lds) for 16-bit activations, in a ring of four stages
+// loaded three K steps ahead, or through registers into two LDS buffers for
+// MXFP8 activations.  All loads are raw buffer loads whose out-of-range
+// offsets read zeros, so none of them sits behind a branch.
+//   W4A16: each 1 KB fragment is four 16x16x32 MFMA operands; FP4 is turned
+//          into bf16 in registers (v_cvt_scalef32_pk_bf16_fp4 with the E8M0
+//          scale, or fp32 conversion times the E4M3 scale for NVFP4; both
+//          products are exact in bf16), or into f16 for NVFP4 weights with
+//          the scaled f16 copy of the activations (see dequant8_f16_nv).
 //   W4A8:  each fragment is one 16x16x128 scaled MFMA operand (fp8 A x fp4 B,
 //          one E8M0 scale per lane on each side).
 // The NVFP4 per-expert fp32 scale multiplies the fp32 accumulators.
@@ -89,8 +91,16 @@ __global__ __launch_bounds__(kGemmThreads, 1) void moe_gemm_kernel(const GemmPar
   constexpr int CHUNKS = A8 ? 8 : 16;   // 16-byte chunks per 128-element row
   constexpr int MF = kTileRows / 16;    // 16-row blocks per tile
   static_assert(kTileRows % 16 == 0 && kTileRows <= kGemmThreads, "tile rows");
-  __shared__ __attribute__((aligned(16))) uint8_t lds_a[2][kTileRows * ROWB];
+  // W4A8: activations through registers into two LDS buffers of ROWB-byte rows
+  __shared__ __attribute__((aligned(16))) uint8_t lds_a[2][A8 ? kTileRows * ROWB : 16];
   __shared__ uint32_t lds_s[2][A8 ? kTileRows : 1];
+  // W4A16 (bf16 or f16 activations): kStages LDS stages of 256-byte rows filled by DMA; each
+  // stage is its own array so that the compiler tracks the DMA of each stage separately
+  constexpr int kStageBytes = A8 ? 16 : kTileRows * 256;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_st0[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_st1[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_st2[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_st3[kStageBytes];
   __shared__ float lds_rs[F16 ? kTileRows : 1];  // f16: 2^exponent of each tile row
 
   const int tid = threadIdx.x;
@@ -200,14 +210,14 @@ __global__ __launch_bounds__(kGemmThreads, 1) void moe_gemm_kernel(const GemmPar
       b_voff[j] = f < p.NF ? (uint32_t)(f * p.KF * kFragBytes + lane * 16) : kBufOOB;
       bs_voff[j] = f < p.NF ? (uint32_t)(f * p.KFS * kScaleGroupBytes + lane * 4) : kBufOOB;
     }
+    // scales first: a step needs them before its codes
     auto load_b = [&](uint4 (&q)[NFW], uint32_t (&sc)[NFW], int kf) {
       const int kfc = min(kf, p.KF - 1);
       const int sgrp = WF == B12X_WEIGHT_MXFP4 ? kfc >> 2 : kfc >> 1;
 #pragma unroll
-      for (int j = 0; j < NFW; ++j) {
-        q[j] = buf_load16s(b_rsrc, b_voff[j], (uint32_t)(kfc * kFragBytes));
-        sc[j] = buf_load4s(bs_rsrc, bs_voff[j], (uint32_t)(sgrp * kScaleGroupBytes));
-      }
+      for (int j = 0; j < NFW; ++j) sc[j] = buf_load4s(bs_rsrc, bs_voff[j], (uint32_t)(sgrp * kScaleGroupBytes));
+#pragma unroll
+      for (int j = 0; j < NFW; ++j) q[j] = buf_load16s(b_rsrc, b_voff[j], (uint32_t)(kfc * kFragBytes));
     };
 
     f32x4 acc[MF][NFW];
@@ -220,10 +230,10 @@ __global__ __launch_bounds__(kGemmThreads, 1) void moe_gemm_kernel(const GemmPar
     // bf16 operands of sub-step s+1 (dequantized weights, LDS activation
     // reads) are produced while sub-step s runs on the MFMAs; the schedule
     // interleaves them so the VALU works under the matrix core.
-    auto compute = [&](auto nmf_tag, auto buf_tag, const uint4 (&bq)[NFW], const uint32_t (&bs)[NFW], int kf) {
+    auto compute = [&](auto nmf_tag, auto par_tag, const uint8_t* la, const uint4 (&bq)[NFW],
+                       const uint32_t (&bs)[NFW], int kf) {
       constexpr int NMF = decltype(nmf_tag)::value;
-      constexpr int buf = decltype(buf_tag)::value;  // also the parity of kf
-      const uint8_t* la = lds_a[buf];
+      constexpr int par = decltype(par_tag)::value;  // parity of kf (selects the NVFP4 scale word)
       if constexpr (!A8) {
         float scl[NFW][2];       // per fragment: scale of the lane's first / second 16 K (NVFP4), or the E8M0 scale
         NvScaleF16 scf[NFW][2];  // the same split for the f16 dequantization
@@ -232,7 +242,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void moe_gemm_kernel(const GemmPar
           if constexpr (WF == B12X_WEIGHT_MXFP4) {
             scl[j][0] = scl[j][1] = e8m0_as_scale((bs[j] >> (8 * (kf & 3))) & 0xFFu);
           } else {  // the two E4M3 scales of this K fragment, decoded by the hardware (OCP E4M3)
-            const f32x2 sv = __builtin_amdgcn_cvt_pk_f32_fp8((int)bs[j], buf == 1);
+            const f32x2 sv = __builtin_amdgcn_cvt_pk_f32_fp8((int)bs[j], par == 1);
             if constexpr (F16) {
               scf[j][0] = nv_scale_f16(sv.x);
               scf[j][1] = nv_scale_f16(sv.y);
@@ -250,9 +260,11 @@ __global__ __launch_bounds__(kGemmThreads, 1) void moe_gemm_kernel(const GemmPar
             else out[j] = dequant8_bf16<WF>(dw, scl[j][s >> 1]);
           }
         };
+        // row 16 mf + r16, 16-byte chunk 4 g + s, stored at chunk position (4 g + s) ^ r16
         auto ld = [&](uint4 (&out)[NMF], int s) {
+          const uint8_t* lp = la + r16 * 256 + 16 * ((4 * g + s) ^ r16);
 #pragma unroll
-          for (int mf = 0; mf < NMF; ++mf) out[mf] = *(const uint4*)(la + (16 * mf + r16) * ROWB + 64 * g + 16 * s);
+          for (int mf = 0; mf < NMF; ++mf) out[mf] = *(const uint4*)(lp + mf * 16 * 256);
         };
         OpT b0[NFW], b1[NFW];
         uint4 a0[NMF], a1[NMF];
@@ -301,7 +313,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void moe_gemm_kernel(const GemmPar
           const uint4 x0 = *(const uint4*)(la + row * ROWB + 16 * g);
           const uint4 x1 = *(const uint4*)(la + row * ROWB + 64 + 16 * g);
           const i32x8 afr = {(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
-          const int sa = (int)((lds_s[buf][row] >> (8 * g)) & 0xFFu);
+          const int sa = (int)((lds_s[par][row] >> (8 * g)) & 0xFFu);
 #pragma unroll
           for (int j = 0; j < NFW; ++j)
             acc[mf][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(afr, bfr[j], acc[mf][j], 0, 4, 0, sa, 0,
@@ -323,16 +335,6 @@ __global__ __launch_bounds__(kGemmThreads, 1) void moe_gemm_kernel(const GemmPar
       uint4 bq0[NFW], bq1[NFW];
       uint32_t bs0[NFW], bs1[NFW];
       __syncthreads();  // the previous work item is done with LDS
-      if constexpr (F16) {  // 2^exponent of each row's token (read by the epilogue)
-        if (tid < kTileRows) {
-          int ex = 0;
-          if (tid < nrows) {
-            const int pair = p.sorted[row0 + tid];
-            if (pair >= 0 && pair < p.n_pairs) ex = p.a_exp[pair / p.k_top];
-          }
-          lds_rs[tid] = bits_f32((uint32_t)(127 + ex) << 23);
-        }
-      }
       load_a(ra0, rs0, rk0, 0);
       store_a(ra0, rs0, rk0, 0);
       load_a(ra1, rs1, rk1, 1);
@@ -342,23 +344,137 @@ __global__ __launch_bounds__(kGemmThreads, 1) void moe_gemm_kernel(const GemmPar
         // even step: LDS buffer 0, ra1 holds step kf+1
         __syncthreads();
         load_a(ra0, rs0, rk0, kf + 2);
-        if (!idle) compute(nmf_tag, std::integral_constant<int, 0>{}, bq0, bs0, kf);
+        if (!idle) compute(nmf_tag, std::integral_constant<int, 0>{}, lds_a[0], bq0, bs0, kf);
         store_a(ra1, rs1, rk1, 1);
         load_b(bq0, bs0, kf + 2);
         if (kf + 1 >= p.KF) break;
         // odd step: LDS buffer 1, ra0 holds step kf+2
         __syncthreads();
         load_a(ra1, rs1, rk1, kf + 3);
-        if (!idle) compute(nmf_tag, std::integral_constant<int, 1>{}, bq1, bs1, kf + 1);
+        if (!idle) compute(nmf_tag, std::integral_constant<int, 1>{}, lds_a[1], bq1, bs1, kf + 1);
         store_a(ra0, rs0, rk0, 0);
         load_b(bq1, bs1, kf + 3);
       }
     };
-    if (nmf > 8) kloop(std::integral_constant<int, 9>{});
-    else if (nmf > 6) kloop(std::integral_constant<int, 8>{});
-    else if (nmf > 4) kloop(std::integral_constant<int, 6>{});
-    else if (nmf > 2) kloop(std::integral_constant<int, 4>{});
-    else kloop(std::integral_constant<int, 2>{});
+
+    // ---- W4A16 main loop: activations global -> LDS by DMA (buffer_load ... lds) into
+    // kStages stages, weights into kStages register stages, both kAhead K steps ahead.
+    // DMA instruction j of wave w fills rows kRowsPerWave w + 4 j + lane/16 of a stage;
+    // position lane%16 of a row holds its 16-byte chunk (lane%16) ^ (row & 15), so the
+    // MFMA operand reads of 16 rows hit 16 different bank groups.  Step kf waits for its
+    // own loads (the later steps' loads stay in flight), then a barrier makes every
+    // wave's DMA of the stage visible and frees the stage read at step kf - 1, which the
+    // loads of step kf + kAhead then refill.  Every step issues the same loads (steps
+    // past the end reload the last fragment and are not computed), so the wait counts
+    // are exact.
+    constexpr int kStages = 4;
+    constexpr int kAhead = kStages - 1;
+    constexpr int kRowsPerWave = kTileRows / 4;
+    constexpr int kDma = kRowsPerWave / 4;        // 1 KB DMA instructions per wave per step
+    constexpr int kLoadsPerStep = kDma + 2 * NFW;  // VMEM instructions a wave issues per step
+    static_assert(kRowsPerWave % 4 == 0 && (kAhead - 1) * kLoadsPerStep < 64, "DMA rows / wait count");
+    auto stage_lds = [&](auto st_tag) -> uint8_t* {
+      constexpr int ST = decltype(st_tag)::value;
+      if constexpr (ST == 0) return lds_st0;
+      else if constexpr (ST == 1) return lds_st1;
+      else if constexpr (ST == 2) return lds_st2;
+      else return lds_st3;
+    };
+    auto fill_row_scales = [&]() {  // f16: 2^exponent of each row's token (read by the epilogue)
+      if constexpr (F16) {
+        if (tid < kTileRows) {
+          int ex = 0;
+          if (tid < nrows) {
+            const int pair = p.sorted[row0 + tid];
+            if (pair >= 0 && pair < p.n_pairs) ex = p.a_exp[pair / p.k_top];
+          }
+          lds_rs[tid] = bits_f32((uint32_t)(127 + ex) << 23);
+        }
+      }
+    };
+    auto kloop_dma = [&](auto nmf_tag) {
+      // per-lane DMA source offsets (row and swizzled chunk); zeros past the tile; in a
+      // ragged last K fragment, zeros past K as well
+      uint32_t dvoff[kDma];
+      uint32_t in_last = 0;  // bit j: the chunk of DMA j lies inside K in the last fragment
+#pragma unroll
+      for (int j = 0; j < kDma; ++j) {
+        const int rr = kRowsPerWave * wave + 4 * j + (lane >> 4);
+        const int chunk = (lane & 15) ^ (rr & 15);
+        int sr = -1;
+        if (rr < nrows) {
+          if (p.sorted) {
+            const int pair = p.sorted[row0 + rr];
+            sr = (pair >= 0 && pair < p.n_pairs) ? pair / p.k_top : -1;
+          } else {
+            sr = row0 + rr;
+          }
+        }
+        dvoff[j] = sr >= 0 ? (uint32_t)(sr * p.a_stride * 2 + 16 * chunk) : kBufOOB;
+        if (8 * chunk < k_last) in_last |= 1u << j;
+      }
+      auto dma_a = [&](auto st_tag, int kf) {
+        const int kfc = min(kf, p.KF - 1);
+        const uint32_t soff = (uint32_t)(kfc * kFragK * 2);
+        uint8_t* base = stage_lds(st_tag) + kRowsPerWave * wave * 256;
+        if (ragged && kfc == p.KF - 1) {
+#pragma unroll
+          for (int j = 0; j < kDma; ++j)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, (__attribute__((address_space(3))) void*)(base + 1024 * j),
+                                                     16, ((in_last >> j) & 1u) ? dvoff[j] : kBufOOB, soff, 0, 0);
+        } else {
+#pragma unroll
+          for (int j = 0; j < kDma; ++j)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, (__attribute__((address_space(3))) void*)(base + 1024 * j),
+                                                     16, dvoff[j], soff, 0, 0);
+        }
+      };
+      uint4 bq[kStages][NFW];
+      uint32_t bs[kStages][NFW];
+      auto issue = [&](auto st_tag, int kf) {
+        constexpr int ST = decltype(st_tag)::value;
+        dma_a(st_tag, kf);
+        load_b(bq[ST], bs[ST], kf);
+      };
+      auto step = [&](auto st_tag, int kf) {
+        constexpr int ST = decltype(st_tag)::value;
+        constexpr int NX = (ST + kAhead) % kStages;
+        constexpr int N = (kAhead - 1) * kLoadsPerStep;
+        __builtin_amdgcn_sched_barrier(0);
+        // s_waitcnt vmcnt(N) (gfx9 encoding: vmcnt bits [3:0] and [15:14], expcnt 7, lgkmcnt 0)
+        __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (0 << 8));
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        issue(std::integral_constant<int, NX>{}, kf + kAhead);
+        __builtin_amdgcn_sched_barrier(0);
+        if (kf < p.KF && !idle) compute(nmf_tag, std::integral_constant<int, ST & 1>{}, stage_lds(st_tag), bq[ST], bs[ST], kf);
+      };
+      __syncthreads();  // the previous work item is done with LDS
+      fill_row_scales();
+      issue(std::integral_constant<int, 0>{}, 0);
+      issue(std::integral_constant<int, 1>{}, 1);
+      issue(std::integral_constant<int, 2>{}, 2);
+      for (int kf = 0; kf < p.KF; kf += kStages) {
+        step(std::integral_constant<int, 0>{}, kf);
+        step(std::integral_constant<int, 1>{}, kf + 1);
+        step(std::integral_constant<int, 2>{}, kf + 2);
+        step(std::integral_constant<int, 3>{}, kf + 3);
+      }
+    };
+    if constexpr (A8) {
+      if (nmf > 8) kloop(std::integral_constant<int, 9>{});
+      else if (nmf > 6) kloop(std::integral_constant<int, 8>{});
+      else if (nmf > 4) kloop(std::integral_constant<int, 6>{});
+      else if (nmf > 2) kloop(std::integral_constant<int, 4>{});
+      else kloop(std::integral_constant<int, 2>{});
+    } else {
+      static_assert(kStages == 4, "the loop body is written for four stages");
+      if (nmf > 8) kloop_dma(std::integral_constant<int, 9>{});
+      else if (nmf > 6) kloop_dma(std::integral_constant<int, 8>{});
+      else if (nmf > 4) kloop_dma(std::integral_constant<int, 6>{});
+      else if (nmf > 2) kloop_dma(std::integral_constant<int, 4>{});
+      else kloop_dma(std::integral_constant<int, 2>{});
+    }
 
     // ---- epilogue: lane holds column r16 of each fragment, rows 4 g + i of each 16-row block
     if constexpr (MODE == MODE_DOWN) {
@@ -428,7 +544,10 @@ __global__ __launch_bounds__(kGemmThreads, 1) void moe_gemm_kernel(const GemmPar
       }
     }
   }
+  // no DMA into LDS may still be in flight when the workgroup's LDS is released
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
 }
+
 
 static int g_cu_count[64];
 
