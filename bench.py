@@ -115,6 +115,68 @@ def time_graph(torch, g, stream, reps):
     return e0.elapsed_time(e1) / 1e3  # seconds
 
 
+def time_graph_samples(torch, g, stream, reps):
+    """Per-replay durations (s) of `reps` back-to-back replays, from one event
+    recorded between consecutive replays."""
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        ev[0].record(stream)
+        for i in range(reps):
+            g.replay()
+            ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    return [ev[i].elapsed_time(ev[i + 1]) / 1e3 for i in range(reps)]
+
+
+def percentile(xs, q):
+    xs = sorted(xs)
+    return xs[min(len(xs) - 1, max(0, int(round(q * (len(xs) - 1)))))]
+
+
+def measure_ceilings(fm, torch, stream):
+    """Achieved ceilings of this device: the best rate of a plain streaming read
+    of 1 GiB (over a few grid sizes) and the sustained rate of an MFMA register
+    loop (bf16 and f16, two workgroups of four waves per CU)."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    nbytes = 1 << 30
+    src = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
+    best = 0.0
+    for per_cu in (4, 8, 16):
+        wg = cus * per_cu
+        sink = torch.empty(wg * 256, dtype=torch.int32, device="cuda")
+        per = (nbytes // 16) // wg
+        read = wg * (per // 1024) * 1024 * 16
+        for _ in range(2):
+            fm.probe_stream_read(src, sink, wg, stream=stream)
+        e0, e1 = _events()
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            e0.record(stream)
+            for _ in range(10):
+                fm.probe_stream_read(src, sink, wg, stream=stream)
+            e1.record(stream)
+        torch.cuda.synchronize()
+        best = max(best, read * 10 / (e0.elapsed_time(e1) / 1e3) / 1e9)
+    del src
+    out = {"stream_read_GBs": round(best, 1)}
+    wg, iters = cus * 2, 4000
+    sink = torch.empty(wg * 256, dtype=torch.float32, device="cuda")
+    for name, f16 in (("mfma_bf16_TFLOPs", False), ("mfma_f16_TFLOPs", True)):
+        fm.probe_mfma(sink, wg, 10, f16=f16, stream=stream)
+        e0, e1 = _events()
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            e0.record(stream)
+            for _ in range(3):
+                fm.probe_mfma(sink, wg, iters, f16=f16, stream=stream)
+            e1.record(stream)
+        torch.cuda.synchronize()
+        flops = 3.0 * wg * 4 * 16 * 16384 * iters
+        out[name] = round(flops / (e0.elapsed_time(e1) / 1e3) / 1e12, 1)
+    return out
+
+
 def time_stage_graph(torch, fm, bindings, stage, stream, reps=10):
     """Mean duration (s) of one stage's kernel: a graph of that stage for every
     binding, replayed `reps` times between two events on `stream`.  The stages
@@ -222,7 +284,7 @@ def bench_prefill(fm, synth, torch, stream, reps=10):
     sec = time_graph(torch, g, stream, reps) / reps
     flops = 6.0 * wl.H * wl.I * T * wl.k
     stages = {st: time_stage_launches(torch, fm, [b], st, stream, repeats=3) * 1e6
-              for st in ("route", "gemm1", "gemm2", "combine")}
+              for st in ("route", "quant_x", "gemm1", "gemm2", "combine")}
     return {"T": T, "us": sec * 1e6, "tflops": flops / sec / 1e12,
             "frac_bf16_peak": flops / sec / 1e12 / BF16_PEAK_TFLOPS, "stage_us": stages,
             "gemm1_tflops": 4.0 * wl.H * wl.I * T * wl.k / (stages["gemm1"] * 1e-6) / 1e12,
@@ -340,13 +402,16 @@ def main():
     for T in Ts:
         g = capture(torch, fm, [row["binding"] for row in sets[T]], stream)
         g.replay()
-        reps = max(1, steps // N_SETS)
-        sec = time_graph(torch, g, stream, reps) / (reps * N_SETS)
+        reps = max(10, steps // N_SETS)
+        samples = [t / N_SETS for t in time_graph_samples(torch, g, stream, reps)]
+        sec = sum(samples) / reps
         nb = sum(row["bytes"] for row in sets[T]) / N_SETS
         ne = sum(row["experts"] for row in sets[T]) / N_SETS
         per_t[f"T{T}"] = {"us": sec * 1e6, "touched_experts": ne, "weight_MB": nb / 1e6,
                           "weight_GBs": nb / sec / 1e9, "frac_hbm": nb / sec / 1e9 / HBM_PEAK_GBS,
-                          "tflops": 6.0 * wl.H * wl.I * T * wl.k / sec / 1e12}
+                          "tflops": 6.0 * wl.H * wl.I * T * wl.k / sec / 1e12,
+                          "us_p10_p50_p90": [round(percentile(samples, q) * 1e6, 2) for q in (0.1, 0.5, 0.9)],
+                          "replays": reps}
 
     # dominant kernel: the gate/up kernel (2/3 of the weight bytes), timed as a graph of
     # its own launches; small T runs the decode path (gate/up kernel "decode1")
@@ -390,9 +455,14 @@ def main():
         "roofline": roofline,
         "per_T": per_t,
     }
+    log("achieved ceilings")
+    ceil = measure_ceilings(fm, torch, stream)
+    ceil["decode_gate_up_frac_of_stream_read"] = round(achieved / ceil["stream_read_GBs"], 4)
+    result["ceilings"] = ceil
     if not args.no_extra:
         log("prefill line")
         result["prefill"] = bench_prefill(fm, synth, torch, stream)
+        ceil["prefill_frac_of_mfma_f16"] = round(result["prefill"]["tflops"] / ceil["mfma_f16_TFLOPs"], 4)
         log("w4a8 line")
         result["w4a8_mixed_T1"] = bench_mixed_t1(fm, synth, torch, stream)
     if not args.no_cpu:

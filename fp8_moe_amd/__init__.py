@@ -12,7 +12,7 @@ mirrors b12x's fused_moe (README "Using it"):
     binding = bind(plan, scratch, experts, x, topk_ids, topk_weights, out)
     run(binding)
 
-The library must be built (``python -m fp8_moe_amd.build``); importing this
+The library must be built (``python fp8_moe_amd/build.py``); importing this
 module fails loudly when it is missing.  There is no fallback path.
 """
 import ctypes
@@ -83,7 +83,7 @@ class Binding(ctypes.Structure):
 
 def _load():
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built; run `python -m fp8_moe_amd.build` (there is no fallback)")
+        raise ImportError(f"{LIB_PATH} is not built; run `python fp8_moe_amd/build.py` (there is no fallback)")
     lib = ctypes.CDLL(LIB_PATH)
     st = ctypes.c_int32
     P = ctypes.POINTER
@@ -102,6 +102,8 @@ def _load():
         "b12x_moe_binding_query": (st, [P(Binding), ctypes.c_int32, P(i64)]),
         "b12x_moe_scratch_region": (st, [vp, ctypes.c_int32, P(ctypes.c_uint64), P(ctypes.c_uint64)]),
         "b12x_mxfp8_quantize_rows": (st, [vp, i64, i64, i64, vp, vp, vp]),
+        "b12x_probe_stream_read": (st, [vp, ctypes.c_uint64, vp, ctypes.c_int32, vp]),
+        "b12x_probe_mfma": (st, [vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, vp]),
         "b12x_status_string": (ctypes.c_char_p, [st]),
         "b12x_last_error": (ctypes.c_char_p, []),
     }
@@ -116,7 +118,8 @@ _lib = _load()
 EXPORTED = ("b12x_moe_plan_weights", "b12x_moe_prepare_weights", "b12x_moe_is_supported", "b12x_moe_plan",
             "b12x_moe_plan_destroy", "b12x_moe_scratch_specs", "b12x_moe_bind", "b12x_moe_run",
             "b12x_moe_run_stage", "b12x_moe_binding_query", "b12x_moe_scratch_region",
-            "b12x_mxfp8_quantize_rows", "b12x_status_string", "b12x_last_error")
+            "b12x_mxfp8_quantize_rows", "b12x_probe_stream_read", "b12x_probe_mfma", "b12x_status_string",
+            "b12x_last_error")
 
 
 def lib():
@@ -275,6 +278,24 @@ def mxfp8_quantize_rows(x, codes=None, scales=None, stream=None):
     _check(_lib.b12x_mxfp8_quantize_rows(_ptr(x), rows, cols, x.stride(0), _ptr(codes), _ptr(scales),
                                          _stream(stream)))
     return codes, scales
+
+
+def probe_stream_read(src, sink, workgroups, stream=None):
+    """Measurement probe: stream `src` (any contiguous device tensor, 16-byte
+    multiple) through `workgroups` workgroups; sink: int32/uint32 tensor of
+    workgroups*256 elements."""
+    if sink.numel() < workgroups * 256:
+        raise ValueError("sink needs workgroups*256 elements")
+    _check(_lib.b12x_probe_stream_read(_ptr(src), src.numel() * src.element_size(), _ptr(sink), workgroups,
+                                       _stream(stream)))
+
+
+def probe_mfma(sink, workgroups, iterations, f16=False, stream=None):
+    """Measurement probe: 16 * iterations 16x16x32 MFMAs per wave, four waves
+    per workgroup; sink: float32 tensor of workgroups*256 elements."""
+    if sink.dtype != torch.float32 or sink.numel() < workgroups * 256:
+        raise ValueError("sink must be float32 with workgroups*256 elements")
+    _check(_lib.b12x_probe_mfma(_ptr(sink), workgroups, iterations, int(bool(f16)), _stream(stream)))
 
 
 class FusedMoE:

@@ -1,6 +1,6 @@
 """Build ``libb12x_moe.so`` (all HIP kernels + the C ABI) for gfx950 in-tree.
 
-Usage: ``python -m fp8_moe_amd.build`` (or ``build()`` from Python).  Always
+Usage: ``python fp8_moe_amd/build.py`` (or ``build()`` from Python).  Always
 recompiles every source; objects go to ``fp8_moe_amd/_build/``.
 """
 import concurrent.futures as cf
@@ -14,7 +14,7 @@ OUT = os.path.join(HERE, "libb12x_moe.so")
 BUILD = os.path.join(HERE, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["api.cpp", "pack.hip", "route.hip", "quant.hip", "gemm.hip", "combine.hip", "decode.hip"]
+SOURCES = ["api.cpp", "pack.hip", "route.hip", "quant.hip", "gemm.hip", "combine.hip", "decode.hip", "probes.hip"]
 
 # -packed-fp32-ops: keep hipcc from emitting packed fp32 VALU ops.
 FLAGS = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-function",

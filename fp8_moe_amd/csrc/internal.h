@@ -139,6 +139,8 @@ int launch_f16_rows(const uint16_t* x, int64_t rows, int64_t cols, int64_t strid
 int launch_gemm1(const BindingImpl& b, hipStream_t s);
 int launch_gemm2(const BindingImpl& b, hipStream_t s);
 int launch_combine(const BindingImpl& b, hipStream_t s);
+int launch_probe_read(const void* src, uint64_t bytes, uint32_t* sink, int workgroups, hipStream_t s);
+int launch_probe_mfma(float* sink, int workgroups, int iterations, bool f16, hipStream_t s);
 // compute units of the current device (cached per device)
 int device_cu_count();
 int launch_decode1(const BindingImpl& b, hipStream_t s);
