@@ -25,15 +25,22 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   const int64_t t = idx / groups, c = (idx % groups) * 8;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   // grouped path: pos gives the y row; decode path: the row is the pair id
+  // itself, so its y loads do not wait for the ids (which only mask them)
   const int32_t* key = pos ? pos : ids;
   for (int j0 = 0; j0 < k; j0 += kChunk) {
     int raw[kChunk], row[kChunk];
     float w[kChunk];
+    float4 a[kChunk], b[kChunk];
 #pragma unroll
     for (int u = 0; u < kChunk; ++u) {  // clamped slot: every load is in bounds and unconditional
       const int j = min(j0 + u, k - 1);
       raw[u] = key[t * k + j];
       w[u] = tw[t * k + j];
+      if (!pos) {  // row t*k + j < T*k <= max_rows
+        const float4* src = (const float4*)(y + (t * k + j) * y_stride + c);
+        a[u] = src[0];
+        b[u] = src[1];
+      }
     }
 #pragma unroll
     for (int u = 0; u < kChunk; ++u) {
@@ -43,12 +50,13 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
       else r = (raw[u] >= 0 && raw[u] < E) ? (int)(t * k + j) : -1;  // a dropped pair has no row
       row[u] = (j < k && r >= 0 && r < max_rows) ? r : -1;
     }
-    float4 a[kChunk], b[kChunk];
+    if (pos) {
 #pragma unroll
-    for (int u = 0; u < kChunk; ++u) {
-      const float4* src = (const float4*)(y + (int64_t)(row[u] < 0 ? 0 : row[u]) * y_stride + c);
-      a[u] = src[0];
-      b[u] = src[1];
+      for (int u = 0; u < kChunk; ++u) {
+        const float4* src = (const float4*)(y + (int64_t)(row[u] < 0 ? 0 : row[u]) * y_stride + c);
+        a[u] = src[0];
+        b[u] = src[1];
+      }
     }
 #pragma unroll
     for (int u = 0; u < kChunk; ++u) {

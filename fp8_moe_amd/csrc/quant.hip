@@ -1,48 +1,34 @@
 // MXFP8 row quantizer (b12x README "What's in here": quantization.mxfp8 row
 // quantizer, the dynamic activation quantization of the W4A8 MoE modes;
-// "PCIe DMA wire modes": one E8M0 scale per 32 values).  One thread per
-// 32-element block: amax, shared exponent, 32 E4M3 codes, integer only.
+// "PCIe DMA wire modes": one E8M0 scale per 32 values): amax, shared
+// exponent and E4M3 codes per 32-element block, integer only.
 #include "device_common.h"
 
 namespace b12x {
 
+// Eight lanes per 32-element block, four values each (an aligned group of 8
+// lanes of a wave, so a group is wholly in or out of range): the block's
+// largest magnitude by lane exchange, then each lane encodes its four values.
 __global__ __launch_bounds__(256) void quant_rows_kernel(const uint16_t* __restrict__ x, int64_t rows,
                                                           int64_t blocks_per_row, int64_t stride,
                                                           uint8_t* __restrict__ codes, int64_t code_stride,
                                                           uint8_t* __restrict__ scales, int64_t scale_stride) {
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= rows * blocks_per_row) return;
-  const int64_t r = idx / blocks_per_row, blk = idx % blocks_per_row;
-  const uint4* src = (const uint4*)(x + r * stride + blk * 32);
-  uint32_t w[16];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint4 v = src[i];
-    w[4 * i + 0] = v.x; w[4 * i + 1] = v.y; w[4 * i + 2] = v.z; w[4 * i + 3] = v.w;
-  }
-  uint32_t amax = 0;  // bf16 magnitude bits compare like the values
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    amax = max(amax, w[i] & 0x7FFFu);
-    amax = max(amax, (w[i] >> 16) & 0x7FFFu);
-  }
+  const int64_t blk_all = idx >> 3;
+  if (blk_all >= rows * blocks_per_row) return;
+  const int part = (int)(idx & 7);  // elements [4 part, 4 part + 4) of the block
+  const int64_t r = blk_all / blocks_per_row, blk = blk_all % blocks_per_row;
+  const uint2 v = *(const uint2*)(x + r * stride + blk * 32 + 4 * part);
+  // bf16 magnitude bits compare like the values
+  uint32_t amax = max(max(v.x & 0x7FFFu, (v.x >> 16) & 0x7FFFu), max(v.y & 0x7FFFu, (v.y >> 16) & 0x7FFFu));
+  amax = max(amax, (uint32_t)__shfl_xor((int)amax, 1));
+  amax = max(amax, (uint32_t)__shfl_xor((int)amax, 2));
+  amax = max(amax, (uint32_t)__shfl_xor((int)amax, 4));
   const int s = mx_scale_exp(amax << 16);
-  uint32_t out[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    uint32_t word = 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int el = 4 * i + j;
-      const uint32_t h = (w[el >> 1] >> (16 * (el & 1))) & 0xFFFFu;
-      word |= e4m3_encode_scaled(h << 16, s) << (8 * j);
-    }
-    out[i] = word;
-  }
-  uint4* dst = (uint4*)(codes + r * code_stride + blk * 32);
-  dst[0] = make_uint4(out[0], out[1], out[2], out[3]);
-  dst[1] = make_uint4(out[4], out[5], out[6], out[7]);
-  scales[r * scale_stride + blk] = (uint8_t)(s + 127);
+  const uint32_t word = e4m3_encode_scaled(v.x << 16, s) | (e4m3_encode_scaled(v.x & 0xFFFF0000u, s) << 8) |
+                        (e4m3_encode_scaled(v.y << 16, s) << 16) | (e4m3_encode_scaled(v.y & 0xFFFF0000u, s) << 24);
+  *(uint32_t*)(codes + r * code_stride + blk * 32 + 4 * part) = word;
+  if (part == 0) scales[r * scale_stride + blk] = (uint8_t)(s + 127);
 }
 
 int launch_quant_rows(const uint16_t* x, int64_t rows, int64_t cols, int64_t stride, uint8_t* codes,
@@ -50,7 +36,7 @@ int launch_quant_rows(const uint16_t* x, int64_t rows, int64_t cols, int64_t str
   const int64_t bpr = cols / 32;
   const int64_t total = rows * bpr;
   if (total == 0) return 0;
-  hipLaunchKernelGGL(quant_rows_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, x, rows, bpr,
+  hipLaunchKernelGGL(quant_rows_kernel, dim3((unsigned)((8 * total + 255) / 256)), dim3(256), 0, s, x, rows, bpr,
                      stride, codes, code_stride, scales, scale_stride);
   return (int)hipGetLastError();
 }
