@@ -256,14 +256,16 @@ def cpu_baseline(wl, w_host, sets_host, budget_s=12.0):
             if time.perf_counter() - t0 >= budget_s:
                 break
     dt = time.perf_counter() - t0
+    flops_per_call = 6.0 * wl.H * wl.I * 1 * wl.k  # T = 1
     return {"value": done_bytes / dt / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "tokens_per_s": calls / dt, "gflops": flops_per_call * calls / dt / 1e9,
             "sample": f"{calls} decode T=1 calls (E=128, H=2048, I=768, top_k=8, MXFP4 W4A16), "
                       f"{dt:.1f} s; weight bytes of touched experts / wall time; BLAS limited to {cores} threads, "
                       f"elementwise NumPy single-threaded",
             "seconds_per_call": dt / calls}
 
 
-def bench_prefill(fm, synth, torch, stream, reps=10):
+def bench_prefill(fm, synth, torch, stream, reps=20):
     wl = synth.WORKLOADS["prefill"]
     T = wl.tokens[0]
     w = synth.make_weights(wl, device="cuda")
@@ -281,11 +283,13 @@ def bench_prefill(fm, synth, torch, stream, reps=10):
         fm.run(b, stream=stream)
     g = capture(torch, fm, [b], stream)
     g.replay()
-    sec = time_graph(torch, g, stream, reps) / reps
+    samples = time_graph_samples(torch, g, stream, reps)
+    sec = sum(samples) / reps
     flops = 6.0 * wl.H * wl.I * T * wl.k
     stages = {st: time_stage_launches(torch, fm, [b], st, stream, repeats=3) * 1e6
               for st in ("route", "quant_x", "gemm1", "gemm2", "combine")}
-    return {"T": T, "us": sec * 1e6, "tflops": flops / sec / 1e12,
+    return {"T": T, "us": sec * 1e6, "us_p10_p50_p90": [round(percentile(samples, q) * 1e6, 1) for q in (0.1, 0.5, 0.9)],
+            "runs": reps, "tflops": flops / sec / 1e12,
             "frac_bf16_peak": flops / sec / 1e12 / BF16_PEAK_TFLOPS, "stage_us": stages,
             "gemm1_tflops": 4.0 * wl.H * wl.I * T * wl.k / (stages["gemm1"] * 1e-6) / 1e12,
             "gemm2_tflops": 2.0 * wl.H * wl.I * T * wl.k / (stages["gemm2"] * 1e-6) / 1e12}
@@ -402,7 +406,7 @@ def main():
     for T in Ts:
         g = capture(torch, fm, [row["binding"] for row in sets[T]], stream)
         g.replay()
-        reps = max(10, steps // N_SETS)
+        reps = max(20, steps // N_SETS)  # >= 200 calls
         samples = [t / N_SETS for t in time_graph_samples(torch, g, stream, reps)]
         sec = sum(samples) / reps
         nb = sum(row["bytes"] for row in sets[T]) / N_SETS
@@ -411,7 +415,7 @@ def main():
                           "weight_GBs": nb / sec / 1e9, "frac_hbm": nb / sec / 1e9 / HBM_PEAK_GBS,
                           "tflops": 6.0 * wl.H * wl.I * T * wl.k / sec / 1e12,
                           "us_p10_p50_p90": [round(percentile(samples, q) * 1e6, 2) for q in (0.1, 0.5, 0.9)],
-                          "replays": reps}
+                          "calls": reps * N_SETS}
 
     # dominant kernel: the gate/up kernel (2/3 of the weight bytes), timed as a graph of
     # its own launches; small T runs the decode path (gate/up kernel "decode1")

@@ -4,6 +4,10 @@
       kernel_trace.csv -> markdown table of kernel durations (per kernel and grid)
   python profile_summary.py counters CSV [NAME_SUBSTRING]
       counter_collection.csv -> mean value per dispatch of each counter, per kernel
+  python profile_summary.py mfma CSV [CSV ...] [--filter NAME]
+      counter_collection.csv passes -> per kernel: MFMA busy share of SIMD cycles
+      (SQ_VALU_MFMA_BUSY_CYCLES over GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs), VALU and LDS
+      instructions per MFMA, wait share, as a markdown table
   python profile_summary.py traffic OUT.json --kernel NAME --calib-fetch CSV --calib-write CSV
                                     --fetch CSV [CSV ...] --write CSV [CSV ...]
       HBM bytes per launch of one kernel: FETCH_SIZE and WRITE_SIZE (KiB per dispatch)
@@ -91,6 +95,28 @@ def traffic(args):
     print(json.dumps(rec, indent=1))
 
 
+XCDS = 8          # GRBM_GUI_ACTIVE is summed over the XCDs
+SIMDS = 256 * 4   # compute units x SIMDs
+
+
+def mfma_table(paths, name_filter=""):
+    merged = collections.defaultdict(dict)
+    for p in paths:
+        for name, d in counter_means(p, name_filter).items():
+            merged[name].update(d)
+    out = ["| kernel | MFMA busy (of SIMD cycles) | MFMA instr | VALU instr / MFMA | LDS instr / MFMA | "
+           "wait cycles / wave cycles | VMEM rd instr / MFMA |", "|---|---:|---:|---:|---:|---:|---:|"]
+    for name, d in sorted(merged.items()):
+        def g(k):
+            return d.get(k, float("nan"))
+        busy = g("SQ_VALU_MFMA_BUSY_CYCLES") / (g("GRBM_GUI_ACTIVE") / XCDS * SIMDS)
+        mf = g("SQ_INSTS_MFMA")
+        out.append(f"| `{name}` | {100 * busy:.1f}% | {mf:.4g} | {g('SQ_INSTS_VALU') / mf:.2f} | "
+                   f"{g('SQ_INSTS_LDS') / mf:.2f} | {g('SQ_WAIT_ANY') / g('SQ_WAVE_CYCLES'):.2f} | "
+                   f"{g('SQ_INSTS_VMEM_RD') / mf:.2f} |")
+    return "\n".join(out) + "\n"
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -102,6 +128,9 @@ def main():
     c = sub.add_parser("counters")
     c.add_argument("csv")
     c.add_argument("name", nargs="?", default="")
+    m = sub.add_parser("mfma")
+    m.add_argument("csv", nargs="+")
+    m.add_argument("--filter", default="")
     r = sub.add_parser("traffic")
     r.add_argument("out")
     r.add_argument("--kernel", required=True, help="substring of the kernel name")
@@ -114,6 +143,8 @@ def main():
     a = ap.parse_args()
     if a.cmd == "trace":
         sys.stdout.write(trace(a.csv, a.title, a.command, a.filter))
+    elif a.cmd == "mfma":
+        sys.stdout.write(mfma_table(a.csv, a.filter))
     elif a.cmd == "counters":
         for name, d in sorted(counter_means(a.csv, a.name).items()):
             print(name)
