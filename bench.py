@@ -9,10 +9,11 @@ Method: C prepared copies of the weights (more than the 256 MB Infinity
 Cache holds) and S input sets rotate, so each call streams cold weights;
 S steps are captured in one graph and replayed (no host launch overhead in
 the timed region); timing with events around K steps after W warmup steps.
-The dominant kernel (the gate/up kernel of the decode path) is also timed on
-its own, as a graph of its launches between events on its stream, for the
-roofline object; its HBM traffic comes from the committed counter record in
-profiles/ when that record matches the kernel sources.  Extra lines report
+The dominant kernel (the decode path's fused gate/up + down kernel) is also
+timed for the roofline object, in the sequence it runs in: graphs of (fused
+kernel, combine) less graphs of the combines alone; its HBM traffic comes from
+the committed counter record in profiles/ when that record matches the kernel
+sources.  Extra lines report
 prefill (NVFP4, T=4096) TFLOP/s and the W4A8 (MXFP8 x MXFP4, ReLU^2) T=1
 decode, and the CPU oracle's rate on a bounded sample.
 
@@ -177,16 +178,18 @@ def measure_ceilings(fm, torch, stream):
     return out
 
 
-def time_stage_graph(torch, fm, bindings, stage, stream, reps=10):
-    """Mean duration (s) of one stage's kernel: a graph of that stage for every
-    binding, replayed `reps` times between two events on `stream`.  The stages
-    before it ran for every binding beforehand (their outputs are in place)."""
+def time_stage_graph(torch, fm, bindings, stages, stream, reps=10):
+    """Mean duration (s) per binding of the given stages' kernels: a graph of
+    those stages for every binding, replayed `reps` times between two events
+    on `stream`.  Every binding ran in full beforehand (inputs of any stage
+    are in place)."""
     for b in bindings:
         fm.run(b, stream=stream)
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=stream):
         for b in bindings:
-            fm.run_stage(b, stage, stream=stream)
+            for stage in stages:
+                fm.run_stage(b, stage, stream=stream)
     g.replay()
     return time_graph(torch, g, stream, reps) / (reps * len(bindings))
 
@@ -209,7 +212,7 @@ def time_stage_launches(torch, fm, bindings, stage, stream, repeats=3):
     return sum(a.elapsed_time(b) for a, b in pairs) / len(pairs) / 1e3
 
 
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_gate_up_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_kernel_traffic.json")
 TRAFFIC_SOURCES = ["fp8_moe_amd/csrc/decode.hip", "fp8_moe_amd/csrc/device_common.h",
                    "fp8_moe_amd/csrc/internal.h"]
 
@@ -223,16 +226,19 @@ def kernel_source_hash():
     return h.hexdigest()
 
 
-def measured_traffic():
-    """HBM bytes per gate/up launch from the committed counter record (FETCH_SIZE and
-    WRITE_SIZE, calibrated on a plain copy kernel), or None when the record is missing
-    or was taken on different kernel sources."""
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` (its name up to the template arguments) from the
+    committed counter record (FETCH_SIZE and WRITE_SIZE, calibrated on a plain copy
+    kernel), or None when the record is missing, is for another kernel or was taken on
+    different kernel sources."""
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
     if rec.get("source_sha256") != kernel_source_hash():
+        return None
+    if rec.get("kernel", "").split("<")[0] != kernel.split("<")[0]:
         return None
     return rec.get("bytes_per_launch")
 
@@ -417,25 +423,41 @@ def main():
                           "us_p10_p50_p90": [round(percentile(samples, q) * 1e6, 2) for q in (0.1, 0.5, 0.9)],
                           "calls": reps * N_SETS}
 
-    # dominant kernel: the gate/up kernel (2/3 of the weight bytes), timed as a graph of
-    # its own launches; small T runs the decode path (gate/up kernel "decode1")
-    durs, w13b, durs2 = [], [], []
+    # dominant kernel: the decode path's fused gate/up + down kernel (all touched weight
+    # bytes), timed in the sequence it runs in: a graph of (fused kernel, combine) per input
+    # set less a graph of the combines alone (the combine advances the call epoch that the
+    # fused kernel's waits compare against, so each launch really waits for its gate/up
+    # groups).  Without the fused kernel (unfused decode or grouped path) the gate/up
+    # kernel alone, with the W13 bytes.
+    durs, kbytes = [], []
+    fused_all = True
     for T in Ts:
         bl = [row["binding"] for row in sets[T]]
         path = fm.binding_query(bl[0], "path")
-        st1, st2 = ("decode1", "decode2") if path == 2 else ("gemm1", "gemm2")
-        durs.append(time_stage_graph(torch, fm, bl, st1, stream))
-        durs2.append(time_stage_graph(torch, fm, bl, st2, stream))
-        w13b.append(sum(row["w13_bytes"] for row in sets[T]) / N_SETS)
-        per_t[f"T{T}"]["path"] = "decode" if path == 2 else "grouped"
-        per_t[f"T{T}"]["gate_up_kernel_us"] = durs[-1] * 1e6
-        per_t[f"T{T}"]["down_kernel_us"] = durs2[-1] * 1e6
+        fused = path == 2 and fm.binding_query(bl[0], "num_stages") == 2
+        fused_all = fused_all and fused
+        if fused:
+            d = (time_stage_graph(torch, fm, bl, ["decode1", "combine"], stream)
+                 - time_stage_graph(torch, fm, bl, ["combine"], stream))
+            nb = sum(row["bytes"] for row in sets[T]) / N_SETS
+            per_t[f"T{T}"]["decode_kernel_us"] = d * 1e6
+        else:
+            st1, st2 = ("decode1", "decode2") if path == 2 else ("gemm1", "gemm2")
+            d = time_stage_graph(torch, fm, bl, [st1], stream)
+            nb = sum(row["w13_bytes"] for row in sets[T]) / N_SETS
+            per_t[f"T{T}"]["gate_up_kernel_us"] = d * 1e6
+            per_t[f"T{T}"]["down_kernel_us"] = time_stage_graph(torch, fm, bl, [st2], stream) * 1e6
+        durs.append(d)
+        kbytes.append(nb)
+        per_t[f"T{T}"]["path"] = ("decode, fused" if fused else "decode") if path == 2 else "grouped"
     avg_dur = sum(durs) / len(durs)
-    avg_bytes = sum(w13b) / len(w13b)
+    avg_bytes = sum(kbytes) / len(kbytes)
     achieved = avg_bytes / avg_dur / 1e9
+    kname = ("decode_fused_kernel<MXFP4, SILU> (gate/up + down, decode path)" if fused_all
+             else "decode_kernel<MXFP4, BF16, SILU> (gate/up, decode path)")
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
-                "kernel": "decode_kernel<MXFP4, BF16, SILU> (gate/up, decode path)",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(kname.split(" ")[0]),
+                "kernel": kname,
                 "avg_launch_us": round(avg_dur * 1e6, 3),
                 "algorithmic_bytes_per_launch": round(avg_bytes),
                 "per_T_launch_us": {f"T{T}": round(d * 1e6, 3) for T, d in zip(Ts, durs)}}
@@ -461,7 +483,7 @@ def main():
     }
     log("achieved ceilings")
     ceil = measure_ceilings(fm, torch, stream)
-    ceil["decode_gate_up_frac_of_stream_read"] = round(achieved / ceil["stream_read_GBs"], 4)
+    ceil["decode_kernel_frac_of_stream_read"] = round(achieved / ceil["stream_read_GBs"], 4)
     result["ceilings"] = ceil
     if not args.no_extra:
         log("prefill line")

@@ -227,6 +227,10 @@ b12x_status b12x_moe_plan(const b12x_moe_caps* caps, b12x_moe_plan_t* out) {
   len[R_H] = (uint64_t)p->max_rows * p->Ip * (a8 ? 1 : 2);
   len[R_HS] = a8 ? (uint64_t)p->max_rows * (p->Ip / 32) : 0;
   len[R_Y] = 4ull * p->max_rows * p->H;
+  {  // decode path: epoch, status and one flag per (touched expert slot, gate/up group of 2 fragments)
+    const int64_t slots = p->decode_max_pairs < p->E ? p->decode_max_pairs : p->E;
+    len[R_DSYNC] = p->decode_max_pairs > 0 ? kDecodeFlagsOffset + 8ull * slots * ((p->l13.nf + 1) / 2) : 0;
+  }
   uint64_t off = 0;
   for (int r = 1; r < R_COUNT_; ++r) {
     p->off[r] = off;
@@ -327,6 +331,7 @@ b12x_status b12x_moe_bind(b12x_moe_plan_t p, void* scratch, uint64_t scratch_byt
   b.h = sb + p->off[R_H];
   b.hs = p->len[R_HS] ? sb + p->off[R_HS] : nullptr;
   b.y = (float*)(sb + p->off[R_Y]);
+  b.dsync = p->len[R_DSYNC] ? sb + p->off[R_DSYNC] : nullptr;
   memset(binding, 0, sizeof(*binding));
   memcpy(binding, &b, sizeof(b));
   return B12X_OK;
@@ -341,7 +346,9 @@ static b12x_status get_binding(const b12x_moe_binding* binding, BindingImpl* b) 
 
 static bool stage_in_path(const BindingImpl& b, int stage) {
   if (stage == B12X_STAGE_QUANT_X) return b.afmt == B12X_ACT_MXFP8 || b.a_f16;
-  if (b.path == 2) return stage == B12X_STAGE_DECODE1 || stage == B12X_STAGE_DECODE2 || stage == B12X_STAGE_COMBINE;
+  if (b.path == 2)
+    return stage == B12X_STAGE_DECODE1 || stage == B12X_STAGE_COMBINE ||
+           (stage == B12X_STAGE_DECODE2 && !decode_fused(b));
   return stage >= B12X_STAGE_ROUTE && stage <= B12X_STAGE_COMBINE;
 }
 
@@ -406,7 +413,7 @@ b12x_status b12x_moe_binding_query(const b12x_moe_binding* binding, int32_t what
     case B12X_QUERY_ROW_PAD: *value = kRowPad; break;
     case B12X_QUERY_T: *value = b.T; break;
     case B12X_QUERY_NUM_STAGES:
-      *value = (b.path == 2 ? 3 : 4) + (stage_in_path(b, B12X_STAGE_QUANT_X) ? 1 : 0);
+      *value = (b.path == 2 ? (decode_fused(b) ? 2 : 3) : 4) + (stage_in_path(b, B12X_STAGE_QUANT_X) ? 1 : 0);
       break;
     default: return fail(B12X_ERR_INVALID_ARGUMENT, "unknown query %d", what);
   }

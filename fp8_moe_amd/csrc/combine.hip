@@ -17,11 +17,17 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
                                                        const int32_t* __restrict__ ids, int E,
                                                        const float* __restrict__ tw, int64_t T, int k, int H,
                                                        int64_t max_rows, uint16_t* __restrict__ out,
-                                                       int64_t out_stride) {
+                                                       int64_t out_stride, int32_t* epoch,
+                                                       const int32_t* status) {
   constexpr int kChunk = 8;
+  // decode path: the call is over once the combine runs; advance the epoch
+  // that tags the next call's completion flags
+  if (epoch && blockIdx.x == 0 && threadIdx.x == 0) atomicAdd(epoch, 1);
   const int64_t groups = H / 8;
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= T * groups) return;
+  // a wait of the fused decode kernel gave up: the output is NaN, not stale
+  const bool failed = status && __hip_atomic_load(status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0;
   const int64_t t = idx / groups, c = (idx % groups) * 8;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   // grouped path: pos gives the y row; decode path: the row is the pair id
@@ -69,22 +75,29 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   }
   uint32_t o[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) o[i] = bf16_rne(acc[2 * i]) | (bf16_rne(acc[2 * i + 1]) << 16);
+  for (int i = 0; i < 4; ++i) o[i] = failed ? 0x7FC07FC0u : bf16_rne(acc[2 * i]) | (bf16_rne(acc[2 * i + 1]) << 16);
   *(uint4*)(out + t * out_stride + c) = make_uint4(o[0], o[1], o[2], o[3]);
 }
 
-static int launch_combine_rows(const BindingImpl& b, const int32_t* pos, hipStream_t s) {
+static int launch_combine_rows(const BindingImpl& b, const int32_t* pos, int32_t* epoch, const int32_t* status,
+                               hipStream_t s) {
   const int64_t total = b.T * (b.H / 8);
   if (total == 0) return 0;
   hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, b.y, (int64_t)b.H, pos,
-                     b.ids, b.E, b.tw, b.T, b.k, b.H, b.max_rows, b.out, b.out_stride);
+                     b.ids, b.E, b.tw, b.T, b.k, b.H, b.max_rows, b.out, b.out_stride, epoch, status);
   return (int)hipGetLastError();
 }
 
 // grouped path: y rows in routing order, located through pos
-int launch_combine(const BindingImpl& b, hipStream_t s) { return launch_combine_rows(b, b.pos, s); }
+int launch_combine(const BindingImpl& b, hipStream_t s) {
+  return launch_combine_rows(b, b.pos, nullptr, nullptr, s);
+}
 
 // decode path: y rows indexed by pair id
-int launch_decode_combine(const BindingImpl& b, hipStream_t s) { return launch_combine_rows(b, nullptr, s); }
+int launch_decode_combine(const BindingImpl& b, hipStream_t s) {
+  int32_t* epoch = b.dsync ? (int32_t*)(b.dsync + kDecodeEpochOffset) : nullptr;
+  const int32_t* status = decode_fused(b) ? (const int32_t*)(b.dsync + kDecodeStatusOffset) : nullptr;
+  return launch_combine_rows(b, nullptr, epoch, status, s);
+}
 
 }  // namespace b12x

@@ -18,6 +18,8 @@
 //      by pair id).
 // No atomics on data and no cross-workgroup synchronization: the result does
 // not depend on scheduling or on the grid size.
+#include <stdlib.h>
+
 #include "device_common.h"
 
 namespace b12x {
@@ -55,6 +57,16 @@ struct DecodeParams {
   // D2 output
   float* y;
   int64_t y_stride;
+  // fused gate/up + down (one launch): completion flag of every (touched
+  // expert slot, gate/up group), flags_per_slot of them per slot; a flag
+  // holds the call's tag once that group's h rows are stored.  epoch is
+  // advanced by the combine after every call; status is set when a wait
+  // gives up (the combine then writes NaN).
+  uint64_t* flags;
+  int flags_per_slot;
+  const int32_t* epoch;
+  int32_t* status;
+  int64_t h_bytes;  // extent of h16 (device-coherent stores and loads)
 };
 
 enum { DMODE_SILU = 1, DMODE_RELU2 = 2, DMODE_DOWN = 3 };
@@ -125,22 +137,49 @@ __device__ int decode_expert(const DecodeParams& p, int slot, const int* s_ids, 
   return __builtin_amdgcn_readfirstlane(total);
 }
 
-template <int WF, int AF, int MODE, int FR, int KW>
-__global__ __launch_bounds__(kDecThreads) void decode_kernel(const DecodeParams p) {
+struct DecodeLds {
+  int ids[kDecodePairs];
+  int rows[kDecodePairs];
+  uint32_t bits[kBitWords];
+  int wpre[kBitWords + 1];
+  int info[8];
+};
+
+// Tag of this call's completion flags: never 0 and never a previous call's.
+__device__ __forceinline__ uint64_t flag_tag(const int32_t* epoch) {
+  const uint32_t e = (uint32_t)__hip_atomic_load(epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return ((uint64_t)e << 32) | 0xB12DF1A9u;
+}
+
+// Upper bound on the polls of one wait (each at least one round trip to
+// memory plus a sleep: far beyond any wait that can end).
+constexpr int kWaitPolls = 1 << 18;
+
+// This workgroup's share of the (touched expert slot, group of FR weight
+// fragments) items of one GEMV.  FUSE = 0: a launch of its own.  FUSE = 1:
+// the gate/up phase of the fused kernel: h is stored device-coherent and
+// each finished group raises its flag.  FUSE = 2: the down phase: before an
+// expert's part, wave 0 waits until every gate/up group of that expert has
+// raised its flag, and h is loaded device-coherent.
+template <int WF, int AF, int MODE, int FR, int KW, int FUSE>
+__device__ __forceinline__ void decode_items(const DecodeParams& p, DecodeLds& L, f32x4* red, int n_touched,
+                                             uint64_t tag) {
   constexpr bool A8 = AF == B12X_ACT_MXFP8;
-  __shared__ int s_ids[kDecodePairs];
-  __shared__ int s_rows[kDecodePairs];
-  __shared__ uint32_t s_bits[kBitWords];
-  __shared__ int s_wpre[kBitWords + 1];
-  __shared__ int s_info[8];
-  __shared__ f32x4 s_red[2][4][FR][64];
+  static_assert(FUSE == 0 || !A8, "the fused kernel runs 16-bit activations");
+  static_assert(FUSE != 1 || MODE != DMODE_DOWN, "phase 1 is gate/up");
+  static_assert(FUSE != 2 || MODE == DMODE_DOWN, "phase 2 is down");
+  int* const s_ids = L.ids;
+  int* const s_rows = L.rows;
+  uint32_t* const s_bits = L.bits;
+  int* const s_wpre = L.wpre;
+  int* const s_info = L.info;
+  auto s_red = [&](int par, int w, int j) -> f32x4& { return red[((par * 4 + w) * FR + j) * 64 + (threadIdx.x & 63)]; };
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int g = lane >> 4, r16 = lane & 15;
 
-  const int n_touched = decode_prep(p, s_ids, s_bits, s_wpre);
   // this workgroup's share of the (touched expert, fragment group) items
   const int64_t items = (int64_t)n_touched * p.n_groups;
   const int lo = (int)(items * blockIdx.x / gridDim.x), hi = (int)(items * (blockIdx.x + 1) / gridDim.x);
@@ -156,6 +195,23 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(const DecodeParams 
   const int g_begin = item - slot * p.n_groups;
   const int g_end = min(p.n_groups, g_begin + (hi - item));
   item += g_end - g_begin;
+  if constexpr (FUSE == 2) {
+    // wave 0 waits until every gate/up group of this expert has raised its
+    // flag (the barrier that opens decode_expert holds the other waves)
+    if (wave == 0) {
+      const uint64_t* f = p.flags + (int64_t)slot * p.flags_per_slot;
+      for (int poll = 0;; ++poll) {
+        const bool ok =
+            lane >= p.flags_per_slot || __hip_atomic_load(f + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == tag;
+        if (__ballot(!ok) == 0) break;
+        if (poll >= kWaitPolls) {
+          if (lane == 0) __hip_atomic_store(p.status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(8);
+      }
+    }
+  }
   int e;
   const int m = decode_expert(p, slot, s_ids, s_bits, s_wpre, s_rows, s_info, e);
   const uint8_t* bcodes = p.bcodes + (int64_t)e * p.b_codes_expert;
@@ -183,6 +239,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(const DecodeParams 
     }
   };
   const BufRsrc a_rsrc = make_rsrc(A8 ? (const void*)p.a8 : (const void*)p.a16, p.a_bytes);
+  [[maybe_unused]] const BufRsrc h_rsrc = make_rsrc(p.h16, FUSE == 1 ? p.h_bytes : 0);
   const BufRsrc as_rsrc = make_rsrc(p.as, p.as_bytes);
 
   for (int r0 = 0; r0 < m; r0 += 16) {
@@ -201,7 +258,10 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(const DecodeParams 
       if constexpr (!A8) {
         const uint32_t o = rv && k0 + 32 * g < p.K ? (uint32_t)((src * p.a_stride + k0 + 32 * g) * 2) : kBufOOB;
 #pragma unroll
-        for (int s = 0; s < 4; ++s) av[i][s] = buf_load16(a_rsrc, o == kBufOOB ? kBufOOB : o + 16 * s);
+        for (int s = 0; s < 4; ++s) {
+          if constexpr (FUSE == 2) av[i][s] = buf_load16_dev(a_rsrc, o == kBufOOB ? kBufOOB : o + 16 * s);
+          else av[i][s] = buf_load16(a_rsrc, o == kBufOOB ? kBufOOB : o + 16 * s);
+        }
         sa[i] = 0;
       } else {
         const uint32_t o = rv ? (uint32_t)(src * p.a_stride + k0) : kBufOOB;
@@ -251,15 +311,15 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(const DecodeParams 
         }
       }
 #pragma unroll
-      for (int j = 0; j < FR; ++j) s_red[par][wave][j][lane] = acc[j];
+      for (int j = 0; j < FR; ++j) s_red(par, wave, j) = acc[j];
       __syncthreads();
       if (wave == 0) {
         f32x4 v[FR];
 #pragma unroll
         for (int j = 0; j < FR; ++j) {
-          v[j] = s_red[par][0][j][lane];
+          v[j] = s_red(par, 0, j);
 #pragma unroll
-          for (int w = 1; w < 4; ++w) v[j] += s_red[par][w][j][lane];
+          for (int w = 1; w < 4; ++w) v[j] += s_red(par, w, j);
         }
         const int f0 = grp * FR;
 #pragma unroll
@@ -288,8 +348,15 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(const DecodeParams 
             const int nh = MODE == DMODE_SILU ? max(0, min(NH, (p.NF - f0) / 2)) : max(0, min(NH, p.NF - f0));
             if constexpr (!A8) {
 #pragma unroll
-              for (int q = 0; q < NH; ++q)
-                if (live && q < nh) p.h16[pr * p.h_stride + hcol0 + 16 * q + r16] = (uint16_t)bf16_rne(hv[q]);
+              for (int q = 0; q < NH; ++q) {
+                if (live && q < nh) {
+                  if constexpr (FUSE == 1)
+                    buf_store2_dev(h_rsrc, (uint32_t)((pr * p.h_stride + hcol0 + 16 * q + r16) * 2),
+                                   (uint16_t)bf16_rne(hv[q]));
+                  else
+                    p.h16[pr * p.h_stride + hcol0 + 16 * q + r16] = (uint16_t)bf16_rne(hv[q]);
+                }
+              }
             } else {
 #pragma unroll
               for (int blk = 0; blk < NH / 2; ++blk) {
@@ -324,31 +391,70 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(const DecodeParams 
       group(bq, bs, gi);
     }
   }
+  if constexpr (FUSE == 1) {
+    // wave 0 stored this part's h rows; once they are visible device-wide,
+    // raise the groups' flags
+    if (wave == 0) {
+      wait_vmem();
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      uint64_t* f = p.flags + (int64_t)slot * p.flags_per_slot;
+      for (int gi = g_begin + lane; gi < g_end; gi += 64)
+        __hip_atomic_store(f + gi, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
   }
 }
 
-// Workgroups the device holds at once for one kernel (cached per device).
+template <int WF, int AF, int MODE, int FR, int KW>
+__global__ __launch_bounds__(kDecThreads) void decode_kernel(const DecodeParams p) {
+  __shared__ DecodeLds L;
+  __shared__ f32x4 s_red[2 * 4 * FR * 64];
+  const int n_touched = decode_prep(p, L.ids, L.bits, L.wpre);
+  decode_items<WF, AF, MODE, FR, KW, 0>(p, L, s_red, n_touched, 0);
+}
+
+// Gate/up and down in one launch (16-bit activations): every workgroup takes
+// its share of the gate/up items, then its share of the down items; a down
+// part waits only for the gate/up groups of its own expert.  The grid is at
+// most the resident capacity, and no workgroup waits before its gate/up
+// share is done, so every awaited group is being computed by a running
+// workgroup.
+template <int WF, int MODE1, int FR1, int KW1, int FR2, int KW2>
+__global__ __launch_bounds__(kDecThreads) void decode_fused_kernel(const DecodeParams p1, const DecodeParams p2) {
+  constexpr int FRM = FR1 > FR2 ? FR1 : FR2;
+  __shared__ DecodeLds L;
+  __shared__ f32x4 s_red[2 * 4 * FRM * 64];
+  if (blockIdx.x == 0 && threadIdx.x == 0)
+    __hip_atomic_store(p1.status, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const uint64_t tag = flag_tag(p1.epoch);
+  const int n_touched = decode_prep(p1, L.ids, L.bits, L.wpre);
+  decode_items<WF, B12X_ACT_BF16, MODE1, FR1, KW1, 1>(p1, L, s_red, n_touched, tag);
+  decode_items<WF, B12X_ACT_BF16, DMODE_DOWN, FR2, KW2, 2>(p2, L, s_red, n_touched, tag);
+}
+
+// Workgroups the device holds at once for one kernel (per device, cached by
+// the caller: one cache per kernel).
 template <typename Kernel>
-static int resident_workgroups(Kernel kernel) {
-  static int cached[64];
+static int resident_workgroups(Kernel kernel, int (&cache)[64]) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-  if (!cached[dev]) {
+  if (!cache[dev]) {
     int per_cu = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kDecThreads, 0) != hipSuccess || per_cu < 1)
       per_cu = 1;
-    cached[dev] = per_cu * device_cu_count();
+    cache[dev] = per_cu * device_cu_count();
   }
-  return cached[dev];
+  return cache[dev];
 }
 
 // One workgroup per resident slot, never more than the items of the largest
 // possible touched set (min(T*k, E) experts).
 template <int WF, int AF, int MODE, int FR, int KW>
 static int launch_decode_kw(const BindingImpl& b, const DecodeParams& p, hipStream_t s) {
+  static int cache[64];
   auto kernel = decode_kernel<WF, AF, MODE, FR, KW>;
   const int64_t max_slots = b.T * b.k < b.E ? b.T * b.k : b.E;
-  int64_t grid = resident_workgroups(kernel);
+  int64_t grid = resident_workgroups(kernel, cache);
   if (grid > max_slots * p.n_groups) grid = max_slots * p.n_groups;
   if (grid < 1) grid = 1;
   hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kDecThreads), 0, s, p);
@@ -383,7 +489,7 @@ static DecodeParams common_params(const BindingImpl& b) {
   return p;
 }
 
-int launch_decode1(const BindingImpl& b, hipStream_t s) {
+static DecodeParams gate_up_params(const BindingImpl& b) {
   DecodeParams p = common_params(b);
   const bool a8 = b.afmt == B12X_ACT_MXFP8;
   p.a16 = b.a;
@@ -408,13 +514,11 @@ int launch_decode1(const BindingImpl& b, hipStream_t s) {
   p.hs = b.hs;
   p.h_stride = b.Ip;
   p.hs_stride = b.Ip / 32;
-  if (b.gated && a8)  // an MXFP8 block of h (32 columns) = two gate/up pairs
-    return launch_decode_t<B12X_WEIGHT_MXFP4, B12X_ACT_MXFP8, DMODE_SILU, 4>(b, p, s);
-  if (b.gated) return launch_decode_fmt<DMODE_SILU, 2>(b, p, s);
-  return launch_decode_fmt<DMODE_RELU2, 2>(b, p, s);
+  p.h_bytes = b.T * b.k * b.Ip * 2;
+  return p;
 }
 
-int launch_decode2(const BindingImpl& b, hipStream_t s) {
+static DecodeParams down_params(const BindingImpl& b) {
   DecodeParams p = common_params(b);
   p.a16 = (const uint16_t*)b.h;
   p.a8 = (const uint8_t*)b.h;
@@ -435,6 +539,72 @@ int launch_decode2(const BindingImpl& b, hipStream_t s) {
   p.KFS = (int)b.kfs2;
   p.y = b.y;
   p.y_stride = b.H;
+  return p;
+}
+
+bool decode_fused(const BindingImpl& b) {
+  const char* ev = getenv("B12X_DFUSE");
+  if (ev && atoi(ev) == 0) return false;
+  // one wave polls the flags of an expert: at most 64 gate/up groups
+  return b.path == 2 && b.afmt == B12X_ACT_BF16 && b.dsync && (b.kf13 + 3) / 4 <= 4 && (b.kf2 + 3) / 4 <= 4 &&
+         (b.nf13 + 1) / 2 <= 64;
+}
+
+// Gate/up groups of FR1 = 2 fragments, down groups of FR2 = 4 (as the
+// separate launches use them at these K), grid as for one launch of the
+// larger item count.
+template <int WF, int MODE1, int KW1, int KW2>
+static int launch_fused_kw(const BindingImpl& b, DecodeParams& p1, DecodeParams& p2, hipStream_t s) {
+  static int cache[64];
+  auto kernel = decode_fused_kernel<WF, MODE1, 2, KW1, 4, KW2>;
+  p1.n_groups = (p1.NF + 1) / 2;
+  p2.n_groups = (p2.NF + 3) / 4;
+  const int64_t max_slots = b.T * b.k < b.E ? b.T * b.k : b.E;
+  const int64_t items = max_slots * (p1.n_groups > p2.n_groups ? p1.n_groups : p2.n_groups);
+  int64_t grid = resident_workgroups(kernel, cache);
+  if (grid > items) grid = items;
+  if (grid < 1) grid = 1;
+  hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kDecThreads), 0, s, p1, p2);
+  return (int)hipGetLastError();
+}
+
+template <int WF, int MODE1>
+static int launch_fused_t(const BindingImpl& b, DecodeParams& p1, DecodeParams& p2, hipStream_t s) {
+  const bool k1 = (p1.KF + 3) / 4 <= 2, k2 = (p2.KF + 3) / 4 <= 2;
+  if (k1 && k2) return launch_fused_kw<WF, MODE1, 2, 2>(b, p1, p2, s);
+  if (k1) return launch_fused_kw<WF, MODE1, 2, 4>(b, p1, p2, s);
+  if (k2) return launch_fused_kw<WF, MODE1, 4, 2>(b, p1, p2, s);
+  return launch_fused_kw<WF, MODE1, 4, 4>(b, p1, p2, s);
+}
+
+static int launch_fused(const BindingImpl& b, hipStream_t s) {
+  DecodeParams p1 = gate_up_params(b), p2 = down_params(b);
+  uint8_t* sync = b.dsync;
+  for (DecodeParams* p : {&p1, &p2}) {
+    p->epoch = (const int32_t*)(sync + kDecodeEpochOffset);
+    p->status = (int32_t*)(sync + kDecodeStatusOffset);
+    p->flags = (uint64_t*)(sync + kDecodeFlagsOffset);
+    p->flags_per_slot = (int)((b.nf13 + 1) / 2);
+  }
+  const bool nv = b.wfmt == B12X_WEIGHT_NVFP4;
+  if (b.gated)
+    return nv ? launch_fused_t<B12X_WEIGHT_NVFP4, DMODE_SILU>(b, p1, p2, s)
+              : launch_fused_t<B12X_WEIGHT_MXFP4, DMODE_SILU>(b, p1, p2, s);
+  return nv ? launch_fused_t<B12X_WEIGHT_NVFP4, DMODE_RELU2>(b, p1, p2, s)
+            : launch_fused_t<B12X_WEIGHT_MXFP4, DMODE_RELU2>(b, p1, p2, s);
+}
+
+int launch_decode1(const BindingImpl& b, hipStream_t s) {
+  if (decode_fused(b)) return launch_fused(b, s);
+  DecodeParams p = gate_up_params(b);
+  if (b.gated && b.afmt == B12X_ACT_MXFP8)  // an MXFP8 block of h (32 columns) = two gate/up pairs
+    return launch_decode_t<B12X_WEIGHT_MXFP4, B12X_ACT_MXFP8, DMODE_SILU, 4>(b, p, s);
+  if (b.gated) return launch_decode_fmt<DMODE_SILU, 2>(b, p, s);
+  return launch_decode_fmt<DMODE_RELU2, 2>(b, p, s);
+}
+
+int launch_decode2(const BindingImpl& b, hipStream_t s) {
+  DecodeParams p = down_params(b);
   // 4 fragments (64 output columns) per group unless 8 K fragments per wave need the registers
   if ((p.KF + 3) / 4 > 4) return launch_decode_fmt<DMODE_DOWN, 2>(b, p, s);
   return launch_decode_fmt<DMODE_DOWN, 4>(b, p, s);

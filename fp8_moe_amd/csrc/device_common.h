@@ -59,6 +59,28 @@ __device__ __forceinline__ int buf_load1(BufRsrc r, uint32_t off) {
   return (int)__builtin_amdgcn_raw_buffer_load_b8(r, off, 0, 0);
 }
 
+// Device-coherent accesses: cache policy SC1 (device scope), the accesses the
+// compiler emits for relaxed device-scope atomic loads and stores.  The L2
+// caches of the XCDs are not coherent with each other for ordinary accesses;
+// an SC1 store writes through to the device's coherence point and counts as
+// complete (vmcnt) once it is visible there, and an SC1 load reads from that
+// point.  Data handed between workgroups of one kernel this way needs no
+// cache writeback or invalidation: the writer waits for its stores
+// (vmcnt(0)) before it raises a flag with a device-scope store, and the
+// reader loads with SC1 after it has seen the flag.
+constexpr int kCpolDevice = 16;  // SC1
+__device__ __forceinline__ uint4 buf_load16_dev(BufRsrc r, uint32_t off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCpolDevice));
+}
+__device__ __forceinline__ uint64_t buf_load8_dev(BufRsrc r, uint32_t off) {
+  return __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kCpolDevice));
+}
+__device__ __forceinline__ void buf_store2_dev(BufRsrc r, uint32_t off, uint16_t v) {
+  __builtin_amdgcn_raw_buffer_store_b16(v, r, off, 0, kCpolDevice);
+}
+// s_waitcnt vmcnt(0) alone (expcnt and lgkmcnt at their maxima; gfx9 encoding)
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 __device__ __forceinline__ uint32_t f32_bits(float f) { return __builtin_bit_cast(uint32_t, f); }
 __device__ __forceinline__ float bits_f32(uint32_t u) { return __builtin_bit_cast(float, u); }
 

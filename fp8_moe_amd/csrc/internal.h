@@ -38,6 +38,11 @@ constexpr int kRouteChunk = 1024;  // routing pairs per workgroup
 constexpr int kMaxExperts = 1024;
 // ---- decode path -------------------------------------------------------------
 constexpr int kDecodePairs = 256;     // T*k at or below which the decode path runs
+// decode synchronization region: int32 call epoch, int32 status, then one
+// uint64 completion flag per (touched expert slot, gate/up group of 2 fragments)
+constexpr int kDecodeEpochOffset = 0;
+constexpr int kDecodeStatusOffset = 4;
+constexpr int kDecodeFlagsOffset = 64;
 // Kernels address each activation buffer and each expert's weights with
 // 32-bit buffer offsets; buffers are limited to 1 GiB (so that the sum of
 // two out-of-range markers is still out of range).
@@ -79,7 +84,7 @@ struct PlanImpl {
 
 enum Region {
   R_COUNTS = 1, R_OFFSETS = 2, R_POFF = 3, R_SORTED = 4, R_POS = 5, R_TILES = 6, R_NTILES = 7,
-  R_CHUNK = 8, R_XQ = 9, R_XS = 10, R_H = 11, R_HS = 12, R_Y = 13, R_COUNT_ = 14
+  R_CHUNK = 8, R_XQ = 9, R_XS = 10, R_H = 11, R_HS = 12, R_Y = 13, R_DSYNC = 14, R_COUNT_ = 15
 };
 
 // Everything a run needs, resolved at bind time (trivially copyable).
@@ -114,6 +119,7 @@ struct BindingImpl {
   void* h;
   uint8_t* hs;
   float* y;
+  uint8_t* dsync;  // decode path: call epoch, status and the fused kernel's completion flags
 };
 constexpr uint32_t kBindingMagic = 0xb12b1d01u;
 static_assert(sizeof(BindingImpl) <= sizeof(b12x_moe_binding), "binding does not fit the ABI struct");
@@ -146,6 +152,8 @@ int device_cu_count();
 int launch_decode1(const BindingImpl& b, hipStream_t s);
 int launch_decode2(const BindingImpl& b, hipStream_t s);
 int launch_decode_combine(const BindingImpl& b, hipStream_t s);
+// the decode path runs gate/up and down as one launch (DECODE1) for this binding
+bool decode_fused(const BindingImpl& b);
 const char* hip_error_name(int err);
 
 }  // namespace b12x
