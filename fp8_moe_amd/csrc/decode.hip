@@ -18,8 +18,6 @@
 //      by pair id).
 // No atomics on data and no cross-workgroup synchronization: the result does
 // not depend on scheduling or on the grid size.
-#include <stdlib.h>
-
 #include "device_common.h"
 
 namespace b12x {
@@ -67,6 +65,7 @@ struct DecodeParams {
   const int32_t* epoch;
   int32_t* status;
   int64_t h_bytes;  // extent of h16 (device-coherent stores and loads)
+  int deal;         // 0: one contiguous share per workgroup; else chunks of this many items dealt round-robin
 };
 
 enum { DMODE_SILU = 1, DMODE_RELU2 = 2, DMODE_DOWN = 3 };
@@ -182,13 +181,26 @@ __device__ __forceinline__ void decode_items(const DecodeParams& p, DecodeLds& L
 
   // this workgroup's share of the (touched expert, fragment group) items
   const int64_t items = (int64_t)n_touched * p.n_groups;
-  const int lo = (int)(items * blockIdx.x / gridDim.x), hi = (int)(items * (blockIdx.x + 1) / gridDim.x);
+  int lo, hi;
+  int chunk_id = (int)blockIdx.x;
+  // With at least p.deal items per workgroup: chunks of p.deal consecutive
+  // items dealt round-robin (chunk c to workgroup c % grid).  Otherwise (and
+  // with p.deal = 0) one contiguous share per workgroup.
+  const int deal = p.deal && items >= (int64_t)p.deal * gridDim.x ? p.deal : 0;
+  if (deal) {
+    lo = chunk_id * deal;
+    hi = (int)min(items, (int64_t)lo + deal);
+  } else {  // one contiguous share
+    lo = (int)(items * blockIdx.x / gridDim.x);
+    hi = (int)(items * (blockIdx.x + 1) / gridDim.x);
+  }
 
   // ---- this wave's K fragments
   const int kper = (p.KF + 3) / 4;
   const int kb = wave * kper, ke = min(p.KF, kb + kper);
 
   int par = 0;  // s_red buffer of the current group
+  for (;;) {
   for (int item = lo; item < hi;) {
   // ---- one expert's part of the share: groups [g_begin, g_end) of `slot`
   const int slot = item / p.n_groups;
@@ -403,6 +415,12 @@ __device__ __forceinline__ void decode_items(const DecodeParams& p, DecodeLds& L
     }
   }
   }
+  if (!deal) break;
+  chunk_id += (int)gridDim.x;
+  lo = chunk_id * deal;
+  if (lo >= items) break;
+  hi = (int)min(items, (int64_t)lo + deal);
+  }
 }
 
 template <int WF, int AF, int MODE, int FR, int KW>
@@ -543,8 +561,6 @@ static DecodeParams down_params(const BindingImpl& b) {
 }
 
 bool decode_fused(const BindingImpl& b) {
-  const char* ev = getenv("B12X_DFUSE");
-  if (ev && atoi(ev) == 0) return false;
   // one wave polls the flags of an expert: at most 64 gate/up groups
   return b.path == 2 && b.afmt == B12X_ACT_BF16 && b.dsync && (b.kf13 + 3) / 4 <= 4 && (b.kf2 + 3) / 4 <= 4 &&
          (b.nf13 + 1) / 2 <= 64;
@@ -585,6 +601,7 @@ static int launch_fused(const BindingImpl& b, hipStream_t s) {
     p->status = (int32_t*)(sync + kDecodeStatusOffset);
     p->flags = (uint64_t*)(sync + kDecodeFlagsOffset);
     p->flags_per_slot = (int)((b.nf13 + 1) / 2);
+    p->deal = 2;
   }
   const bool nv = b.wfmt == B12X_WEIGHT_NVFP4;
   if (b.gated)

@@ -165,6 +165,44 @@ def test_graph_replay_matches_eager():
         _ = (x.float() * 2).sum()      # unrelated eager work between replays
 
 
+def test_decode_binding_reused_with_new_inputs():
+    """One decode binding run again and again while its inputs change in place
+    (x, then the routing): every output matches the oracle for the inputs of
+    its own call, in eager runs and in replays of one captured graph.  The
+    fused decode kernel's down phase waits for flags tagged with a per-call
+    epoch, so it never consumes the h rows of an earlier call."""
+    import fp8_moe_amd as fm
+    wl = synth.WORKLOADS["decode"]
+    pr = problem("decode", 32)
+    T = 8
+    x, ids, tw = _inputs(wl, T)
+    b, out = pr.model.bind(x, ids, tw)
+    assert fm.binding_query(b, "path") == 2
+    variants = []
+    for salt in range(1, 4):
+        xs = synth.make_x(wl, T, device="cuda", salt=100 + salt)
+        ids_s, tw_s = synth.make_routing(wl, T, device="cuda", salt=100 + salt)
+        variants.append((xs, ids_s, tw_s))
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        fm.run(b, stream=s)
+    for i, (xs, ids_s, tw_s) in enumerate(variants * 2):
+        x.copy_(xs)
+        ids.copy_(ids_s)
+        tw.copy_(tw_s)
+        out.fill_(0)
+        torch.cuda.synchronize()
+        if i < len(variants):
+            fm.run(b)
+        else:
+            g.replay()
+        torch.cuda.synchronize()
+        rel_fro, rel_max, ok = compare(out, pr.oracle(x, ids, tw))
+        assert ok, (i, rel_fro, rel_max)
+
+
 # decode path (T*k <= 256) against the grouped path and the oracle on the same inputs
 DECODE = [
     ("tiny", 16), ("decode", 1), ("decode", 8), ("decode", 32), ("mixed", 1), ("mixed", 64),
@@ -205,6 +243,10 @@ DECODE_EDGE = [
     ("a8_gated", 8, 256, 128, 2, True, "mxfp4", "mxfp8", 30, "uniform"),
     ("nv_relu2_ragged", 8, 160, 96, 3, False, "nvfp4", "bf16", 50, "uniform"),
     ("k1", 4, 256, 128, 1, True, "mxfp4", "bf16", 1, "uniform"),
+    # bf16 shapes outside the fused gate/up + down kernel: 5 K fragments per wave,
+    # and 68 gate/up groups per expert
+    ("separate_long_k", 8, 2304, 128, 2, True, "mxfp4", "bf16", 6, "uniform"),
+    ("separate_many_groups", 8, 256, 1088, 2, True, "nvfp4", "bf16", 5, "uniform"),
 ]
 
 
@@ -228,6 +270,8 @@ def test_decode_edge_cases(case):
         ids[2, 2] = E + 7
     b, out = pr.model.bind(x, ids, tw)
     assert fm.binding_query(b, "path") == 2
+    fused = afmt == "bf16" and not name.startswith("separate")
+    assert fm.binding_query(b, "num_stages") == (2 if fused else 3 + (afmt == "mxfp8"))
     out.fill_(1.0)
     fm.run(b)
     torch.cuda.synchronize()
