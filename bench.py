@@ -14,8 +14,9 @@ timed for the roofline object, in the sequence it runs in: graphs of (fused
 kernel, combine) less graphs of the combines alone; its HBM traffic comes from
 the committed counter record in profiles/ when that record matches the kernel
 sources.  Extra lines report
-prefill (NVFP4, T=4096) TFLOP/s and the W4A8 (MXFP8 x MXFP4, ReLU^2) T=1
-decode, and the CPU oracle's rate on a bounded sample.
+prefill (NVFP4, T=4096) TFLOP/s, the dense block-scaled GEMM (4096^3), the
+W4A8 (MXFP8 x MXFP4, ReLU^2) T=1 decode, and the CPU oracle's rate on a
+bounded sample.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extra] [--no-cpu]
        python bench.py --decode-t T [--steps K]   (one T only, for counter and trace runs)
@@ -301,6 +302,30 @@ def bench_prefill(fm, synth, torch, stream, reps=20):
             "gemm2_tflops": 2.0 * wl.H * wl.I * T * wl.k / (stages["gemm2"] * 1e-6) / 1e12}
 
 
+def bench_dense_mm(fm, synth, torch, stream, m=4096, n=4096, k=4096, reps=20):
+    """Dense block-scaled GEMM (gemm.blockscaled mm) at m x n x k, NVFP4 and MXFP4
+    weights, bf16 activations: TFLOP/s over a graph of `reps` calls."""
+    res = {"shape": [m, n, k]}
+    x = synth.make_dense_x(m, k, seed=0, device="cuda")
+    out = torch.empty(m, n, dtype=torch.bfloat16, device="cuda")
+    for fmt in ("nvfp4", "mxfp4"):
+        codes, scales, glob = synth.make_dense_weight(n, k, fmt, seed=0, device="cuda")
+        wp = fm.gemm_pack_weight(codes, scales, fmt)
+        for _ in range(2):
+            fm.gemm_mm(x, wp, n, fmt, glob, out=out, stream=stream)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            fm.gemm_mm(x, wp, n, fmt, glob, out=out, stream=stream)
+        g.replay()
+        samples = time_graph_samples(torch, g, stream, reps)
+        sec = sorted(samples)[len(samples) // 2]
+        tf = 2.0 * m * n * k / sec / 1e12
+        res[fmt] = {"us_p50": round(sec * 1e6, 1), "tflops": round(tf, 1),
+                    "frac_bf16_peak": round(tf / BF16_PEAK_TFLOPS, 4)}
+    return res
+
+
 def bench_mixed_t1(fm, synth, torch, stream, reps=50):
     wl = synth.WORKLOADS["mixed"]
     w = synth.make_weights(wl, device="cuda")
@@ -489,6 +514,8 @@ def main():
         log("prefill line")
         result["prefill"] = bench_prefill(fm, synth, torch, stream)
         ceil["prefill_frac_of_mfma_f16"] = round(result["prefill"]["tflops"] / ceil["mfma_f16_TFLOPs"], 4)
+        log("dense mm line")
+        result["dense_mm"] = bench_dense_mm(fm, synth, torch, stream)
         log("w4a8 line")
         result["w4a8_mixed_T1"] = bench_mixed_t1(fm, synth, torch, stream)
     if not args.no_cpu:

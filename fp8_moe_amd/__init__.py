@@ -102,6 +102,9 @@ def _load():
         "b12x_moe_binding_query": (st, [P(Binding), ctypes.c_int32, P(i64)]),
         "b12x_moe_scratch_region": (st, [vp, ctypes.c_int32, P(ctypes.c_uint64), P(ctypes.c_uint64)]),
         "b12x_mxfp8_quantize_rows": (st, [vp, i64, i64, i64, vp, vp, vp]),
+        "b12x_gemm_packed_bytes": (st, [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P(ctypes.c_uint64)]),
+        "b12x_gemm_pack_weight": (st, [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, vp, vp, vp, ctypes.c_uint64, vp]),
+        "b12x_gemm_mm": (st, [vp, i64, i64, vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, vp, vp, i64, vp]),
         "b12x_probe_stream_read": (st, [vp, ctypes.c_uint64, vp, ctypes.c_int32, vp]),
         "b12x_probe_mfma": (st, [vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, vp]),
         "b12x_status_string": (ctypes.c_char_p, [st]),
@@ -118,7 +121,8 @@ _lib = _load()
 EXPORTED = ("b12x_moe_plan_weights", "b12x_moe_prepare_weights", "b12x_moe_is_supported", "b12x_moe_plan",
             "b12x_moe_plan_destroy", "b12x_moe_scratch_specs", "b12x_moe_bind", "b12x_moe_run",
             "b12x_moe_run_stage", "b12x_moe_binding_query", "b12x_moe_scratch_region",
-            "b12x_mxfp8_quantize_rows", "b12x_probe_stream_read", "b12x_probe_mfma", "b12x_status_string",
+            "b12x_mxfp8_quantize_rows", "b12x_gemm_packed_bytes", "b12x_gemm_pack_weight", "b12x_gemm_mm",
+            "b12x_probe_stream_read", "b12x_probe_mfma", "b12x_status_string",
             "b12x_last_error")
 
 
@@ -278,6 +282,35 @@ def mxfp8_quantize_rows(x, codes=None, scales=None, stream=None):
     _check(_lib.b12x_mxfp8_quantize_rows(_ptr(x), rows, cols, x.stride(0), _ptr(codes), _ptr(scales),
                                          _stream(stream)))
     return codes, scales
+
+
+_WFMT = {"mxfp4": 1, "nvfp4": 2}
+
+
+def gemm_pack_weight(codes, scales, weight_format, stream=None):
+    """Dense block-scaled weight W [n, k] (uint8 codes [n, k/2], uint8 scales
+    [n, k/32] or [n, k/16]) -> packed uint8 device tensor for gemm_mm."""
+    n, k = codes.shape[0], codes.shape[1] * 2
+    nb = ctypes.c_uint64()
+    _check(_lib.b12x_gemm_packed_bytes(n, k, _WFMT[weight_format], ctypes.byref(nb)))
+    dst = torch.empty(nb.value, dtype=torch.uint8, device=codes.device)
+    _check(_lib.b12x_gemm_pack_weight(n, k, _WFMT[weight_format], _ptr(codes), _ptr(scales), _ptr(dst), nb.value,
+                                      _stream(stream)))
+    return dst
+
+
+def gemm_mm(x, w_packed, n, weight_format, global_scale=None, out=None, stream=None):
+    """out[m, n] = bf16(x[m, :] . W[n, :]): x bf16 [m, k] with unit column stride,
+    w_packed from gemm_pack_weight, global_scale a 1-element float32 device
+    tensor (NVFP4)."""
+    m, k = x.shape
+    if x.dtype != torch.bfloat16 or x.stride(1) != 1:
+        raise ValueError("x must be bf16 with unit column stride")
+    if out is None:
+        out = torch.empty(m, n, dtype=torch.bfloat16, device=x.device)
+    _check(_lib.b12x_gemm_mm(_ptr(x), m, x.stride(0), _ptr(w_packed), n, k, _WFMT[weight_format], _ptr(global_scale),
+                             _ptr(out), out.stride(0), _stream(stream)))
+    return out
 
 
 def probe_stream_read(src, sink, workgroups, stream=None):

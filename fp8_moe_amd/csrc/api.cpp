@@ -3,6 +3,7 @@
 // and bind logic touch no device; only prepare_weights, run, run_stage and
 // quantize_rows enqueue kernels.
 #include <stdarg.h>
+#include <stdint.h>
 #include <stdio.h>
 #include <string.h>
 
@@ -432,6 +433,75 @@ b12x_status b12x_mxfp8_quantize_rows(const void* x, int64_t rows, int64_t cols, 
   int err = launch_quant_rows((const uint16_t*)x, rows, cols, stride, codes, cols, scales, cols / 32,
                               (hipStream_t)stream);
   if (err) return hip_fail(err, "quantize rows");
+  return B12X_OK;
+}
+
+static b12x_status dense_layout(int32_t n, int32_t k, int32_t weight_format, MatrixLayout* l) {
+  if (weight_format != B12X_WEIGHT_MXFP4 && weight_format != B12X_WEIGHT_NVFP4)
+    return fail(B12X_ERR_INVALID_ARGUMENT, "unknown weight format %d", weight_format);
+  if (n < 16 || k < 32) return fail(B12X_ERR_INVALID_ARGUMENT, "n must be >= 16 and k >= 32");
+  if (n % 16 || k % 32) return fail(B12X_ERR_UNSUPPORTED, "n (%d) must be a multiple of 16 and k (%d) of 32", n, k);
+  *l = make_matrix_layout(n, k, weight_format);
+  if (l->codes_per_expert >= (uint64_t)kMaxBufferBytes || l->scales_per_expert >= (uint64_t)kMaxBufferBytes)
+    return fail(B12X_ERR_UNSUPPORTED, "packed weight reaches 1 GiB");
+  return B12X_OK;
+}
+
+b12x_status b12x_gemm_packed_bytes(int32_t n, int32_t k, int32_t weight_format, uint64_t* bytes) {
+  if (!bytes) return fail(B12X_ERR_INVALID_ARGUMENT, "bytes is NULL");
+  MatrixLayout l;
+  b12x_status st = dense_layout(n, k, weight_format, &l);
+  if (st) return st;
+  *bytes = dense_scales_offset(l) + l.scales_per_expert;
+  return B12X_OK;
+}
+
+b12x_status b12x_gemm_pack_weight(int32_t n, int32_t k, int32_t weight_format, const void* codes, const void* scales,
+                                  void* dst, uint64_t dst_bytes, void* stream) {
+  MatrixLayout l;
+  b12x_status st = dense_layout(n, k, weight_format, &l);
+  if (st) return st;
+  if (!codes || !scales || !dst) return fail(B12X_ERR_INVALID_ARGUMENT, "NULL device pointer");
+  const uint64_t need = dense_scales_offset(l) + l.scales_per_expert;
+  if (dst_bytes < need)
+    return fail(B12X_ERR_SCRATCH_TOO_SMALL, "packed weight buffer %llu < %llu bytes", (unsigned long long)dst_bytes,
+                (unsigned long long)need);
+  if (!aligned(codes, 16) || !aligned(dst, 256))
+    return fail(B12X_ERR_MISALIGNED, "codes must be 16-byte aligned and dst 256-byte aligned");
+  PackArgs a;
+  a.src_codes = (const uint8_t*)codes;
+  a.src_scales = (const uint8_t*)scales;
+  a.dst_codes = (uint8_t*)dst;
+  a.dst_scales = (uint8_t*)dst + dense_scales_offset(l);
+  a.E = 1;
+  a.l = l;
+  a.wfmt = weight_format;
+  a.gated_interleave = 0;
+  const int err = launch_pack(a, (hipStream_t)stream);
+  if (err) return hip_fail(err, "pack weight");
+  return B12X_OK;
+}
+
+b12x_status b12x_gemm_mm(const void* x, int64_t m, int64_t x_stride, const void* w_packed, int32_t n, int32_t k,
+                         int32_t weight_format, const float* global_scale, void* out, int64_t out_stride,
+                         void* stream) {
+  MatrixLayout l;
+  b12x_status st = dense_layout(n, k, weight_format, &l);
+  if (st) return st;
+  if (m < 0) return fail(B12X_ERR_INVALID_ARGUMENT, "m must be >= 0");
+  if (m == 0) return B12X_OK;
+  if (!x || !w_packed || !out) return fail(B12X_ERR_INVALID_ARGUMENT, "NULL device pointer");
+  if (weight_format == B12X_WEIGHT_NVFP4 && !global_scale)
+    return fail(B12X_ERR_INVALID_ARGUMENT, "NVFP4 weights need their fp32 tensor scale");
+  if (x_stride < k || out_stride < n) return fail(B12X_ERR_INVALID_ARGUMENT, "row strides smaller than k or n");
+  if (!aligned(x, 16) || x_stride % 8 || !aligned(w_packed, 256) || !aligned(out, 2))
+    return fail(B12X_ERR_MISALIGNED, "x and its row stride must be 16-byte aligned, the packed weight 256-byte");
+  if (m >= INT32_MAX / 2 || (uint64_t)m * (uint64_t)x_stride * 2 >= (uint64_t)kMaxBufferBytes)
+    return fail(B12X_ERR_UNSUPPORTED, "the rows of x span 1 GiB or more");
+  const int err = launch_dense_mm((const uint16_t*)x, m, x_stride, (const uint8_t*)w_packed, l, weight_format,
+                                  weight_format == B12X_WEIGHT_NVFP4 ? global_scale : nullptr, (uint16_t*)out,
+                                  out_stride, (hipStream_t)stream);
+  if (err) return hip_fail(err, "dense mm");
   return B12X_OK;
 }
 

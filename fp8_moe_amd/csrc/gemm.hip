@@ -66,9 +66,14 @@ struct GemmParams {
   int64_t hs_stride;
   float* y;
   int64_t y_stride;
+  // dense GEMM (MODE_DENSE): dense_m rows of a, tiles of kTileRows rows in
+  // order (no tile list, one weight matrix), bf16 output rows
+  int64_t dense_m;
+  uint16_t* out16;
+  int64_t out_stride;
 };
 
-enum { MODE_SILU = 1, MODE_RELU2 = 2, MODE_DOWN = 3 };
+enum { MODE_SILU = 1, MODE_RELU2 = 2, MODE_DOWN = 3, MODE_DENSE = 4 };
 
 // Work items are (tile, N tile); the items are split into 8 contiguous ranges,
 // one per XCD (workgroup i runs on XCD i % 8), so that the workgroups sharing
@@ -109,14 +114,25 @@ __global__ __launch_bounds__(kGemmThreads, 1) void moe_gemm_kernel(const GemmPar
   const int g = lane >> 4, r16 = lane & 15;
   const int c = tid % CHUNKS;
 
-  const int n_items = min(max(p.ntiles[0], 0), p.max_tiles) * p.n_ntiles;
+  const int n_row_tiles =
+      MODE == MODE_DENSE ? (int)((p.dense_m + kTileRows - 1) / kTileRows) : min(max(p.ntiles[0], 0), p.max_tiles);
+  const int n_items = n_row_tiles * p.n_ntiles;
   const int xcd = blockIdx.x & 7, n_local = gridDim.x >> 3;
   const int lo = (int)((int64_t)n_items * xcd / 8), hi = (int)((int64_t)n_items * (xcd + 1) / 8);
 
   for (int w = lo + (int)(blockIdx.x >> 3); w < hi; w += n_local) {
     const int tile = w / p.n_ntiles;
     const int nt = w - tile * p.n_ntiles;
-    const int e = p.tiles[4 * tile], row0 = p.tiles[4 * tile + 1], nrows = p.tiles[4 * tile + 2];
+    int e, row0, nrows;
+    if constexpr (MODE == MODE_DENSE) {
+      e = 0;
+      row0 = tile * kTileRows;
+      nrows = (int)min((int64_t)kTileRows, p.dense_m - row0);
+    } else {
+      e = p.tiles[4 * tile];
+      row0 = p.tiles[4 * tile + 1];
+      nrows = p.tiles[4 * tile + 2];
+    }
     if (e < 0 || e >= p.E || row0 < 0 || nrows <= 0 || nrows > kTileRows || row0 + nrows > p.max_rows) continue;
     const int nmf = (nrows + 15) / 16;
     const int f0 = nt * NT + wave * NFW;
@@ -477,7 +493,24 @@ __global__ __launch_bounds__(kGemmThreads, 1) void moe_gemm_kernel(const GemmPar
     }
 
     // ---- epilogue: lane holds column r16 of each fragment, rows 4 g + i of each 16-row block
-    if constexpr (MODE == MODE_DOWN) {
+    if constexpr (MODE == MODE_DENSE) {
+#pragma unroll
+      for (int mf = 0; mf < MF; ++mf) {
+        if (mf < nmf) {
+#pragma unroll
+          for (int j = 0; j < NFW; ++j) {
+            if (j < nnf) {
+              const int col = 16 * (f0 + j) + r16;
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const int64_t row = row0 + 16 * mf + 4 * g + i;
+                if (16 * mf + 4 * g + i < nrows) p.out16[row * p.out_stride + col] = (uint16_t)bf16_rne(acc[mf][j][i] * gsc);
+              }
+            }
+          }
+        }
+      }
+    } else if constexpr (MODE == MODE_DOWN) {
 #pragma unroll
       for (int mf = 0; mf < MF; ++mf) {
         if (mf < nmf) {
@@ -660,6 +693,35 @@ int launch_gemm2(const BindingImpl& b, hipStream_t s) {
   p.y_stride = b.H;
   const int64_t max_work = b.max_tiles * p.n_ntiles;
   return dispatch<MODE_DOWN>(b, p, max_work, s);
+}
+
+// Dense GEMM out[m, n] = bf16(x[m, :] . W[n, :] * g): the grouped GEMM's down
+// path with one weight matrix and the rows of x in tiles of kTileRows.
+int launch_dense_mm(const uint16_t* x, int64_t m, int64_t x_stride, const uint8_t* w, const MatrixLayout& l,
+                    int wfmt, const float* global_scale, uint16_t* out, int64_t out_stride, hipStream_t s) {
+  GemmParams p = {};
+  p.dense_m = m;
+  p.max_rows = (int)m;
+  p.max_tiles = (int)((m + kTileRows - 1) / kTileRows);
+  p.E = 1;
+  p.n_ntiles = (int)((l.nf + 4 * kGemmNFW - 1) / (4 * kGemmNFW));
+  p.a16 = x;
+  p.a_stride = x_stride;
+  p.a_bytes = m * x_stride * 2;
+  p.K = l.k;
+  p.KF = (int)l.kf;
+  p.bcodes = w;
+  p.bscales = w + dense_scales_offset(l);
+  p.bglobal = global_scale;
+  p.b_codes_expert = (int64_t)l.codes_per_expert;
+  p.b_scales_expert = (int64_t)l.scales_per_expert;
+  p.NF = (int)l.nf;
+  p.KFS = (int)l.kfs;
+  p.out16 = out;
+  p.out_stride = out_stride;
+  const int64_t max_work = (int64_t)p.max_tiles * p.n_ntiles;
+  if (wfmt == B12X_WEIGHT_NVFP4) return launch_gemm_t<B12X_WEIGHT_NVFP4, B12X_ACT_BF16, MODE_DENSE>(p, max_work, s);
+  return launch_gemm_t<B12X_WEIGHT_MXFP4, B12X_ACT_BF16, MODE_DENSE>(p, max_work, s);
 }
 
 }  // namespace b12x

@@ -14,6 +14,7 @@ What it computes (plain, slow, fp64, NumPy):
   stable token permutation, per-expert padded row tiles, inverse positions.
 * ``ffn``      - the routed-expert FFN: gather, gate/up projection, SiLU-gated
   or ReLU^2 activation, down projection and the top-k-weighted combine.
+* ``gemm``     - the dense block-scaled FP4 GEMM (gemm.blockscaled mm).
 
 Sources are the b12x pages: the README ("What's in here" and "Using it": the
 fused_moe op, its W4A16 / dynamic-W4A8 modes, the SiLU / ReLU2 activations and
@@ -31,3 +32,4 @@ from .formats import (  # noqa: F401
 )
 from .routing import route  # noqa: F401
 from .ffn import fused_moe, Weights  # noqa: F401
+from .gemm import blockscaled_mm  # noqa: F401

@@ -179,6 +179,27 @@ def make_weights(wl, device="cpu", std=0.02):
     return out
 
 
+def make_dense_weight(n, k, weight_format, seed, device="cpu", std=0.02):
+    """One packed weight matrix W [n, k] (N(0, std) quantized like the expert
+    weights): (codes uint8 [n, k/2], scales uint8 [n, k/G], global fp32 [1] or
+    None) on ``device``."""
+    g = torch.Generator(device=device)
+    g.manual_seed((BASE_SEED * 1000003 + 99991 * n + 7919 * k + seed) % (2 ** 62))
+    w = torch.randn(n, k, generator=g, device=device, dtype=torch.float32) * std
+    if weight_format == "mxfp4":
+        codes, scales = _encode_mxfp4(w)
+        return codes, scales, None
+    codes, scales, glob = _encode_nvfp4(w)
+    return codes, scales, torch.tensor([float(glob)], dtype=torch.float32, device=device)
+
+
+def make_dense_x(m, k, seed, device="cpu"):
+    """bf16 activation rows [m, k] for the dense GEMM, N(0, 1)."""
+    g = torch.Generator(device=device)
+    g.manual_seed((BASE_SEED * 1000003 + 104729 * m + 31 * k + seed + 17) % (2 ** 62))
+    return torch.randn(m, k, generator=g, device=device, dtype=torch.float32).to(torch.bfloat16)
+
+
 def oracle_weights_kwargs(wdict, experts=None):
     """The weight dict as host NumPy arrays for building the oracle's
     ``Weights``; with ``experts`` given, each array becomes a mapping
