@@ -94,7 +94,7 @@ def dequant_nvfp4(packed, scales, global_scale):
     """NVFP4 block [N, K]: E2M1(code) * E4M3(scale[n, k//16]) * g, exact in fp64.
 
     ``global_scale`` is the fp32 tensor scale of this matrix (one per expert
-    and matrix in this build: the per-tensor scale broadcast).
+    and matrix here: the per-tensor scale broadcast).
     """
     vals = e2m1_decode(unpack_fp4(packed))
     sc = e4m3_decode(scales)
