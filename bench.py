@@ -272,8 +272,11 @@ def cpu_baseline(wl, w_host, sets_host, budget_s=12.0):
             "seconds_per_call": dt / calls}
 
 
-def bench_prefill(fm, synth, torch, stream, reps=20):
+def bench_prefill(fm, synth, torch, stream, reps=20, act_format=None):
     wl = synth.WORKLOADS["prefill"]
+    if act_format is not None:  # the same experts with another activation format
+        import dataclasses
+        wl = dataclasses.replace(wl, act_format=act_format)
     T = wl.tokens[0]
     w = synth.make_weights(wl, device="cuda")
     wp = fm.plan_weights(wl.E, wl.H, wl.I, wl.gated, wl.weight_format)
@@ -514,6 +517,10 @@ def main():
         log("prefill line")
         result["prefill"] = bench_prefill(fm, synth, torch, stream)
         ceil["prefill_frac_of_mfma_f16"] = round(result["prefill"]["tflops"] / ceil["mfma_f16_TFLOPs"], 4)
+        log("prefill line, NVFP4 x MXFP8")
+        pa8 = bench_prefill(fm, synth, torch, stream, act_format="mxfp8")
+        result["prefill_w4a8_nvfp4"] = {k: pa8[k] for k in ("T", "us", "us_p10_p50_p90", "tflops", "frac_bf16_peak",
+                                                            "stage_us")}
         log("dense mm line")
         result["dense_mm"] = bench_dense_mm(fm, synth, torch, stream)
         log("w4a8 line")

@@ -77,8 +77,6 @@ b12x_status check_caps(const b12x_moe_caps* c) {
     return fail(B12X_ERR_INVALID_ARGUMENT, "unknown activation %d", c->activation);
   if ((c->activation == B12X_ACTIVATION_SILU_GATED) != (c->weights.desc.gated == 1))
     return fail(B12X_ERR_UNSUPPORTED, "SiLU-gated experts need gated weights and ReLU^2 needs non-gated ones");
-  if (c->act_format == B12X_ACT_MXFP8 && c->weights.desc.weight_format != B12X_WEIGHT_MXFP4)
-    return fail(B12X_ERR_UNSUPPORTED, "MXFP8 activations run with MXFP4 weights only");
   return B12X_OK;
 }
 
@@ -210,10 +208,13 @@ b12x_status b12x_moe_plan(const b12x_moe_caps* caps, b12x_moe_plan_t* out) {
   int dmax = caps->decode_max_pairs == 0 ? kDecodePairs : caps->decode_max_pairs;
   if (dmax > kDecodePairs) dmax = kDecodePairs;
   p->decode_max_pairs = (decode_ok && dmax > 0) ? dmax : 0;
-  const bool a8 = p->afmt == B12X_ACT_MXFP8;
+  const bool a8 = a8_native(p->wfmt, p->afmt);
   // NVFP4 weights with bf16 activations: the grouped path's GEMM1 reads a
-  // scaled f16 copy of a (2 bytes per element) and one exponent per row
-  const bool x16 = p->wfmt == B12X_WEIGHT_NVFP4 && !a8;
+  // scaled f16 copy of a (2 bytes per element) and one exponent per row.
+  // NVFP4 weights with MXFP8 activations: both paths read the bf16 copy of
+  // a's MXFP8 round trip.
+  const bool x16 = p->wfmt == B12X_WEIGHT_NVFP4 && p->afmt == B12X_ACT_BF16;
+  const bool xrt = a8_bf16(p->wfmt, p->afmt);
   uint64_t len[R_COUNT_] = {0};
   len[R_COUNTS] = 4ull * p->E;
   len[R_OFFSETS] = 4ull * (p->E + 1);
@@ -223,7 +224,7 @@ b12x_status b12x_moe_plan(const b12x_moe_caps* caps, b12x_moe_plan_t* out) {
   len[R_TILES] = 16ull * p->max_tiles;
   len[R_NTILES] = 16;
   len[R_CHUNK] = 4ull * p->max_chunks * p->E;
-  len[R_XQ] = a8 ? (uint64_t)p->max_tokens * p->Hp : (x16 ? 2ull * p->max_tokens * p->Hp : 0);
+  len[R_XQ] = a8 ? (uint64_t)p->max_tokens * p->Hp : (x16 || xrt ? 2ull * p->max_tokens * p->Hp : 0);
   len[R_XS] = a8 ? (uint64_t)p->max_tokens * (p->Hp / 32) : (x16 ? 4ull * p->max_tokens : 0);
   len[R_H] = (uint64_t)p->max_rows * p->Ip * (a8 ? 1 : 2);
   len[R_HS] = a8 ? (uint64_t)p->max_rows * (p->Ip / 32) : 0;
@@ -363,8 +364,10 @@ static b12x_status run_stage(const BindingImpl& b, int stage, hipStream_t s) {
   switch (stage) {
     case B12X_STAGE_ROUTE: err = launch_route(b, s); break;
     case B12X_STAGE_QUANT_X:
-      err = b.a_f16 ? launch_f16_rows(b.a, b.T, b.H, b.a_stride, (uint16_t*)b.xq, b.Hp, (int32_t*)b.xs, s)
-                    : launch_quant_rows(b.a, b.T, b.H, b.a_stride, b.xq, b.Hp, b.xs, b.Hp / 32, s);
+      if (b.a_f16) err = launch_f16_rows(b.a, b.T, b.H, b.a_stride, (uint16_t*)b.xq, b.Hp, (int32_t*)b.xs, s);
+      else if (a8_bf16(b.wfmt, b.afmt))
+        err = launch_mx_roundtrip_rows(b.a, b.T, b.H, b.a_stride, (uint16_t*)b.xq, b.Hp, s);
+      else err = launch_quant_rows(b.a, b.T, b.H, b.a_stride, b.xq, b.Hp, b.xs, b.Hp / 32, s);
       break;
     case B12X_STAGE_GEMM1: err = launch_gemm1(b, s); break;
     case B12X_STAGE_GEMM2: err = launch_gemm2(b, s); break;

@@ -164,7 +164,9 @@ template <int WF, int AF, int MODE, int FR, int KW, int FUSE>
 __device__ __forceinline__ void decode_items(const DecodeParams& p, DecodeLds& L, f32x4* red, int n_touched,
                                              uint64_t tag) {
   constexpr bool A8 = AF == B12X_ACT_MXFP8;
+  constexpr bool RT = AF == kActRt;  // bf16 MXFP8 round trips: h stored as its own round trip
   static_assert(FUSE == 0 || !A8, "the fused kernel runs 16-bit activations");
+  static_assert(FUSE == 0 || !RT, "the fused kernel stores plain bf16 h");
   static_assert(FUSE != 1 || MODE != DMODE_DOWN, "phase 1 is gate/up");
   static_assert(FUSE != 2 || MODE == DMODE_DOWN, "phase 2 is down");
   int* const s_ids = L.ids;
@@ -358,7 +360,27 @@ __device__ __forceinline__ void decode_items(const DecodeParams& p, DecodeLds& L
             }
             const int hcol0 = MODE == DMODE_SILU ? 16 * (f0 / 2) : 16 * f0;
             const int nh = MODE == DMODE_SILU ? max(0, min(NH, (p.NF - f0) / 2)) : max(0, min(NH, p.NF - f0));
-            if constexpr (!A8) {
+            if constexpr (RT) {
+              // h as the bf16 value of its MXFP8 round trip (blocks of 32
+              // columns = column blocks (2b, 2b+1))
+              static_assert(NH % 2 == 0, "whole MXFP8 blocks per group");
+#pragma unroll
+              for (int blk = 0; blk < NH / 2; ++blk) {
+                if (2 * blk < nh) {
+                  float mx = fmaxf(fabsf(hv[2 * blk]), fabsf(hv[2 * blk + 1]));
+                  mx = fmaxf(mx, __shfl_xor(mx, 1));
+                  mx = fmaxf(mx, __shfl_xor(mx, 2));
+                  mx = fmaxf(mx, __shfl_xor(mx, 4));
+                  mx = fmaxf(mx, __shfl_xor(mx, 8));
+                  const int sx = mx_scale_exp(f32_bits(mx));
+                  const int64_t col = hcol0 + 32 * blk + r16;
+                  if (live) {
+                    p.h16[pr * p.h_stride + col] = (uint16_t)mx_roundtrip_bf16(hv[2 * blk], sx);
+                    p.h16[pr * p.h_stride + col + 16] = (uint16_t)mx_roundtrip_bf16(hv[2 * blk + 1], sx);
+                  }
+                }
+              }
+            } else if constexpr (!A8) {
 #pragma unroll
               for (int q = 0; q < NH; ++q) {
                 if (live && q < nh) {
@@ -491,7 +513,7 @@ static int launch_decode_t(const BindingImpl& b, DecodeParams& p, hipStream_t s)
 
 template <int MODE, int FR>
 static int launch_decode_fmt(const BindingImpl& b, DecodeParams& p, hipStream_t s) {
-  if (b.afmt == B12X_ACT_MXFP8) return launch_decode_t<B12X_WEIGHT_MXFP4, B12X_ACT_MXFP8, MODE, FR>(b, p, s);
+  if (a8_native(b.wfmt, b.afmt)) return launch_decode_t<B12X_WEIGHT_MXFP4, B12X_ACT_MXFP8, MODE, FR>(b, p, s);
   if (b.wfmt == B12X_WEIGHT_NVFP4) return launch_decode_t<B12X_WEIGHT_NVFP4, B12X_ACT_BF16, MODE, FR>(b, p, s);
   return launch_decode_t<B12X_WEIGHT_MXFP4, B12X_ACT_BF16, MODE, FR>(b, p, s);
 }
@@ -509,7 +531,7 @@ static DecodeParams common_params(const BindingImpl& b) {
 
 static DecodeParams gate_up_params(const BindingImpl& b) {
   DecodeParams p = common_params(b);
-  const bool a8 = b.afmt == B12X_ACT_MXFP8;
+  const bool a8 = a8_native(b.wfmt, b.afmt);
   p.a16 = b.a;
   p.a8 = b.xq;
   p.as = b.xs;
@@ -517,6 +539,11 @@ static DecodeParams gate_up_params(const BindingImpl& b) {
   p.as_stride = b.Hp / 32;
   p.a_bytes = a8 ? b.T * b.Hp : b.T * b.a_stride * 2;
   p.as_bytes = a8 ? b.T * (b.Hp / 32) : 0;
+  if (a8_bf16(b.wfmt, b.afmt)) {  // NVFP4 x MXFP8: the bf16 copy of a's MXFP8 round trip
+    p.a16 = (const uint16_t*)b.xq;
+    p.a_stride = b.Hp;
+    p.a_bytes = b.T * b.Hp * 2;
+  }
   p.a_by_token = 1;
   p.K = b.H;
   p.KF = (int)b.kf13;
@@ -543,8 +570,9 @@ static DecodeParams down_params(const BindingImpl& b) {
   p.as = b.hs;
   p.a_stride = b.Ip;
   p.as_stride = b.Ip / 32;
-  p.a_bytes = b.T * b.k * b.Ip * (b.afmt == B12X_ACT_MXFP8 ? 1 : 2);
-  p.as_bytes = b.afmt == B12X_ACT_MXFP8 ? b.T * b.k * (b.Ip / 32) : 0;
+  const bool a8 = a8_native(b.wfmt, b.afmt);  // else h is bf16
+  p.a_bytes = b.T * b.k * b.Ip * (a8 ? 1 : 2);
+  p.as_bytes = a8 ? b.T * b.k * (b.Ip / 32) : 0;
   p.a_by_token = 0;
   p.K = b.I;
   p.KF = (int)b.kf2;
@@ -614,8 +642,11 @@ static int launch_fused(const BindingImpl& b, hipStream_t s) {
 int launch_decode1(const BindingImpl& b, hipStream_t s) {
   if (decode_fused(b)) return launch_fused(b, s);
   DecodeParams p = gate_up_params(b);
-  if (b.gated && b.afmt == B12X_ACT_MXFP8)  // an MXFP8 block of h (32 columns) = two gate/up pairs
+  if (b.gated && a8_native(b.wfmt, b.afmt))  // an MXFP8 block of h (32 columns) = two gate/up pairs
     return launch_decode_t<B12X_WEIGHT_MXFP4, B12X_ACT_MXFP8, DMODE_SILU, 4>(b, p, s);
+  if (a8_bf16(b.wfmt, b.afmt))
+    return b.gated ? launch_decode_t<B12X_WEIGHT_NVFP4, kActRt, DMODE_SILU, 4>(b, p, s)
+                   : launch_decode_t<B12X_WEIGHT_NVFP4, kActRt, DMODE_RELU2, 2>(b, p, s);
   if (b.gated) return launch_decode_fmt<DMODE_SILU, 2>(b, p, s);
   return launch_decode_fmt<DMODE_RELU2, 2>(b, p, s);
 }

@@ -23,6 +23,10 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 // copy of bf16 activations (one power-of-two exponent per row), used with
 // NVFP4 weights.
 constexpr int kActF16 = 3;
+// bf16 activations that are MXFP8 round trips (NVFP4 weights x MXFP8
+// activations): the operand path is bf16, and the gate/up epilogue stores h
+// as the bf16 value of its own MXFP8 round trip.
+constexpr int kActRt = 4;
 
 // Raw buffer loads (CDNA buffer resource, stride 0).  A byte offset at or
 // past the record count returns zeros without a memory access, so a guarded
@@ -148,6 +152,13 @@ __device__ __forceinline__ float e4m3_value(uint32_t c) {
   const uint32_t e = (c >> 3) & 15u, m = c & 7u;
   const float mag = e ? bits_f32(((e + 120u) << 23) | (m << 20)) : (float)m * 0.001953125f;
   return (c & 0x80u) ? -mag : mag;
+}
+
+// bf16 bits of the MXFP8 round trip of v (fp32) in a block with exponent s:
+// E4M3 code of v / 2^s, decoded and multiplied by 2^s (exact in fp32; exact in
+// bf16 above its subnormal range, 2^-133).
+__device__ __forceinline__ uint32_t mx_roundtrip_bf16(float v, int s) {
+  return bf16_rne(ldexpf(e4m3_value(e4m3_encode_scaled(f32_bits(v), s)), s));
 }
 
 // E8M0 scale code as the fp32 whose exponent field is the code; the gfx950

@@ -88,6 +88,7 @@ template <int WF, int AF, int MODE, int NFW>
 __global__ __launch_bounds__(kGemmThreads, 1) void moe_gemm_kernel(const GemmParams p) {
   constexpr bool A8 = AF == B12X_ACT_MXFP8;
   constexpr bool F16 = AF == kActF16;  // f16 activations x NVFP4 weights dequantized to f16
+  constexpr bool RT = AF == kActRt;    // bf16 MXFP8 round trips (NVFP4 x MXFP8): h stored as its round trip
   static_assert(!F16 || WF == B12X_WEIGHT_NVFP4, "f16 activations run with NVFP4 weights");
   using OpT = std::conditional_t<F16, f16x8, bf16x8>;  // 16-bit MFMA operand type
   constexpr int ROWB = A8 ? 144 : 272;  // LDS bytes per A row: 128 K elements + 16 bytes of skew
@@ -550,7 +551,25 @@ __global__ __launch_bounds__(kGemmThreads, 1) void moe_gemm_kernel(const GemmPar
                 hv[q] = z > 0.f ? z * z : 0.f;
               }
             }
-            if constexpr (!A8) {
+            if constexpr (RT) {
+              // MXFP8 blocks of 32 columns = column blocks (2b, 2b+1); h is the
+              // bf16 value of its round trip
+              static_assert(NH % 2 == 0, "whole MXFP8 blocks per wave");
+#pragma unroll
+              for (int blk = 0; blk < NH / 2; ++blk) {
+                if (2 * blk < nh) {
+                  float m = fmaxf(fabsf(hv[2 * blk]), fabsf(hv[2 * blk + 1]));
+                  m = fmaxf(m, __shfl_xor(m, 1));
+                  m = fmaxf(m, __shfl_xor(m, 2));
+                  m = fmaxf(m, __shfl_xor(m, 4));
+                  m = fmaxf(m, __shfl_xor(m, 8));
+                  const int sx = mx_scale_exp(f32_bits(m));
+                  const int64_t col = hcol0 + 32 * blk + r16;
+                  p.h16[row * p.h_stride + col] = (uint16_t)mx_roundtrip_bf16(hv[2 * blk], sx);
+                  p.h16[row * p.h_stride + col + 16] = (uint16_t)mx_roundtrip_bf16(hv[2 * blk + 1], sx);
+                }
+              }
+            } else if constexpr (!A8) {
 #pragma unroll
               for (int q = 0; q < NH; ++q)
                 if (q < nh) p.h16[row * p.h_stride + hcol0 + 16 * q + r16] = (uint16_t)bf16_rne(hv[q]);
@@ -610,8 +629,11 @@ static int launch_gemm_t(const GemmParams& p, int64_t max_work, hipStream_t s) {
 
 template <int MODE>
 static int dispatch(const BindingImpl& b, const GemmParams& p, int64_t max_work, hipStream_t s) {
-  const bool nv = b.wfmt == B12X_WEIGHT_NVFP4, a8 = b.afmt == B12X_ACT_MXFP8;
+  const bool nv = b.wfmt == B12X_WEIGHT_NVFP4, a8 = a8_native(b.wfmt, b.afmt);
   if (a8) return launch_gemm_t<B12X_WEIGHT_MXFP4, B12X_ACT_MXFP8, MODE>(p, max_work, s);
+  if constexpr (MODE != MODE_DOWN) {
+    if (a8_bf16(b.wfmt, b.afmt)) return launch_gemm_t<B12X_WEIGHT_NVFP4, kActRt, MODE>(p, max_work, s);
+  }
   if constexpr (MODE != MODE_DOWN) {
     if (p.a_exp) return launch_gemm_t<B12X_WEIGHT_NVFP4, kActF16, MODE>(p, max_work, s);
   }
@@ -621,7 +643,7 @@ static int dispatch(const BindingImpl& b, const GemmParams& p, int64_t max_work,
 
 int launch_gemm1(const BindingImpl& b, hipStream_t s) {
   GemmParams p = {};
-  const bool a8 = b.afmt == B12X_ACT_MXFP8;
+  const bool a8 = a8_native(b.wfmt, b.afmt);
   p.tiles = b.tiles;
   p.ntiles = b.ntiles;
   p.max_tiles = (int)b.max_tiles;
@@ -640,6 +662,11 @@ int launch_gemm1(const BindingImpl& b, hipStream_t s) {
     p.a_stride = b.Hp;
     p.a_bytes = b.T * b.Hp * 2;
     p.a_exp = (const int32_t*)b.xs;
+  }
+  if (a8_bf16(b.wfmt, b.afmt)) {  // NVFP4 x MXFP8: the bf16 copy of a's MXFP8 round trip
+    p.a16 = (const uint16_t*)b.xq;
+    p.a_stride = b.Hp;
+    p.a_bytes = b.T * b.Hp * 2;
   }
   p.sorted = b.sorted;
   p.k_top = b.k;
@@ -664,7 +691,7 @@ int launch_gemm1(const BindingImpl& b, hipStream_t s) {
 
 int launch_gemm2(const BindingImpl& b, hipStream_t s) {
   GemmParams p = {};
-  const bool a8 = b.afmt == B12X_ACT_MXFP8;
+  const bool a8 = a8_native(b.wfmt, b.afmt);  // else h is bf16
   p.tiles = b.tiles;
   p.ntiles = b.ntiles;
   p.max_tiles = (int)b.max_tiles;

@@ -38,6 +38,12 @@ constexpr int kRouteChunk = 1024;  // routing pairs per workgroup
 constexpr int kMaxExperts = 1024;
 // ---- decode path -------------------------------------------------------------
 constexpr int kDecodePairs = 256;     // T*k at or below which the decode path runs
+// MXFP8 activations: with MXFP4 weights the scaled fp8 x fp4 MFMA multiplies
+// the codes (native); with NVFP4 weights (whose E4M3 block scales per 16 have
+// no place in that MFMA) x and h are round-tripped through MXFP8 and the
+// exact bf16 values multiply the NVFP4 weights on the bf16 MFMA.
+inline bool a8_native(int wfmt, int afmt) { return afmt == B12X_ACT_MXFP8 && wfmt == B12X_WEIGHT_MXFP4; }
+inline bool a8_bf16(int wfmt, int afmt) { return afmt == B12X_ACT_MXFP8 && wfmt == B12X_WEIGHT_NVFP4; }
 // decode synchronization region: int32 call epoch, int32 status, then one
 // uint64 completion flag per (touched expert slot, gate/up group of 2 fragments)
 constexpr int kDecodeEpochOffset = 0;
@@ -140,6 +146,8 @@ int launch_copy_f32(const float* src, float* dst, int n, hipStream_t s);
 int launch_route(const BindingImpl& b, hipStream_t s);
 int launch_quant_rows(const uint16_t* x, int64_t rows, int64_t cols, int64_t stride, uint8_t* codes,
                       int64_t code_stride, uint8_t* scales, int64_t scale_stride, hipStream_t s);
+int launch_mx_roundtrip_rows(const uint16_t* x, int64_t rows, int64_t cols, int64_t stride, uint16_t* out,
+                             int64_t out_stride, hipStream_t s);
 int launch_f16_rows(const uint16_t* x, int64_t rows, int64_t cols, int64_t stride, uint16_t* out,
                     int64_t out_stride, int32_t* exps, hipStream_t s);
 int launch_gemm1(const BindingImpl& b, hipStream_t s);

@@ -31,6 +31,37 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const uint16_t* __restr
   if (part == 0) scales[r * scale_stride + blk] = (uint8_t)(s + 127);
 }
 
+// The same blocks, writing bf16 of each value's MXFP8 round trip instead of
+// codes and scales (NVFP4 weights x MXFP8 activations).
+__global__ __launch_bounds__(256) void mx_roundtrip_rows_kernel(const uint16_t* __restrict__ x, int64_t rows,
+                                                                 int64_t blocks_per_row, int64_t stride,
+                                                                 uint16_t* __restrict__ out, int64_t out_stride) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t blk_all = idx >> 3;
+  if (blk_all >= rows * blocks_per_row) return;
+  const int part = (int)(idx & 7);
+  const int64_t r = blk_all / blocks_per_row, blk = blk_all % blocks_per_row;
+  const uint2 v = *(const uint2*)(x + r * stride + blk * 32 + 4 * part);
+  uint32_t amax = max(max(v.x & 0x7FFFu, (v.x >> 16) & 0x7FFFu), max(v.y & 0x7FFFu, (v.y >> 16) & 0x7FFFu));
+  amax = max(amax, (uint32_t)__shfl_xor((int)amax, 1));
+  amax = max(amax, (uint32_t)__shfl_xor((int)amax, 2));
+  amax = max(amax, (uint32_t)__shfl_xor((int)amax, 4));
+  const int s = mx_scale_exp(amax << 16);
+  const uint32_t lo = mx_roundtrip_bf16(bits_f32(v.x << 16), s) | (mx_roundtrip_bf16(bits_f32(v.x & 0xFFFF0000u), s) << 16);
+  const uint32_t hi = mx_roundtrip_bf16(bits_f32(v.y << 16), s) | (mx_roundtrip_bf16(bits_f32(v.y & 0xFFFF0000u), s) << 16);
+  *(uint2*)(out + r * out_stride + blk * 32 + 4 * part) = make_uint2(lo, hi);
+}
+
+int launch_mx_roundtrip_rows(const uint16_t* x, int64_t rows, int64_t cols, int64_t stride, uint16_t* out,
+                             int64_t out_stride, hipStream_t s) {
+  const int64_t bpr = cols / 32;
+  const int64_t total = rows * bpr;
+  if (total == 0) return 0;
+  hipLaunchKernelGGL(mx_roundtrip_rows_kernel, dim3((unsigned)((8 * total + 255) / 256)), dim3(256), 0, s, x, rows,
+                     bpr, stride, out, out_stride);
+  return (int)hipGetLastError();
+}
+
 int launch_quant_rows(const uint16_t* x, int64_t rows, int64_t cols, int64_t stride, uint8_t* codes,
                       int64_t code_stride, uint8_t* scales, int64_t scale_stride, hipStream_t s) {
   const int64_t bpr = cols / 32;

@@ -57,7 +57,7 @@ def test_support_matrix():
     assert fm.is_supported(mx_g, 2, 16, "mxfp8", "silu")
     assert fm.is_supported(mx_r, 2, 16, "mxfp8", "relu2")
     assert fm.is_supported(nv_g, 2, 16, "bf16", "silu")
-    assert not fm.is_supported(nv_g, 2, 16, "mxfp8", "silu")      # NVFP4 x MXFP8 is not built
+    assert fm.is_supported(nv_g, 2, 16, "mxfp8", "silu")          # NVFP4 x MXFP8 through bf16 round trips
     assert not fm.is_supported(mx_g, 2, 16, "bf16", "relu2")      # gated weights need SiLU
     assert not fm.is_supported(mx_g, 0, 16, "bf16", "silu")
 

@@ -65,6 +65,10 @@ SMALL = [
     ("nv_relu2", 5, 256, 192, 3, False, "nvfp4", "bf16", 77),
     ("mx_relu2", 5, 256, 192, 3, False, "mxfp4", "bf16", 77),
     ("a8_gated", 6, 256, 128, 2, True, "mxfp4", "mxfp8", 50),
+    # NVFP4 weights x MXFP8 activations (bf16 round trips), grouped path
+    ("nv_a8_gated", 4, 256, 128, 2, True, "nvfp4", "mxfp8", 200),
+    ("nv_a8_relu2_ragged", 5, 160, 96, 3, False, "nvfp4", "mxfp8", 120),
+    ("nv_a8_mid", 16, 1024, 512, 4, True, "nvfp4", "mxfp8", 256),
 ]
 
 
@@ -245,6 +249,8 @@ DECODE_EDGE = [
     ("k1", 4, 256, 128, 1, True, "mxfp4", "bf16", 1, "uniform"),
     # bf16 shapes outside the fused gate/up + down kernel: 5 K fragments per wave,
     # and 68 gate/up groups per expert
+    ("nv_a8_gated_decode", 8, 256, 128, 2, True, "nvfp4", "mxfp8", 10, "uniform"),
+    ("nv_a8_relu2_decode", 8, 288, 224, 4, False, "nvfp4", "mxfp8", 30, "one_expert"),
     ("separate_long_k", 8, 2304, 128, 2, True, "mxfp4", "bf16", 6, "uniform"),
     ("separate_many_groups", 8, 256, 1088, 2, True, "nvfp4", "bf16", 5, "uniform"),
 ]
