@@ -225,7 +225,7 @@ b12x_status b12x_moe_plan(const b12x_moe_caps* caps, b12x_moe_plan_t* out) {
   len[R_NTILES] = 16;
   len[R_CHUNK] = 4ull * p->max_chunks * p->E;
   len[R_XQ] = a8 ? (uint64_t)p->max_tokens * p->Hp : (x16 || xrt ? 2ull * p->max_tokens * p->Hp : 0);
-  len[R_XS] = a8 ? (uint64_t)p->max_tokens * (p->Hp / 32) : (x16 ? 4ull * p->max_tokens : 0);
+  len[R_XS] = a8 ? (uint64_t)p->max_tokens * (p->Hp / 32) : (x16 || xrt ? 4ull * p->max_tokens : 0);
   len[R_H] = (uint64_t)p->max_rows * p->Ip * (a8 ? 1 : 2);
   len[R_HS] = a8 ? (uint64_t)p->max_rows * (p->Ip / 32) : 0;
   len[R_Y] = 4ull * p->max_rows * p->H;
@@ -304,7 +304,9 @@ b12x_status b12x_moe_bind(b12x_moe_plan_t p, void* scratch, uint64_t scratch_byt
   b.path = (T > 0 && T * p->k <= p->decode_max_pairs) ? 2 : 1;
   b.E = p->E; b.H = p->H; b.I = p->I; b.k = p->k;
   b.gated = p->gated; b.wfmt = p->wfmt; b.afmt = p->afmt; b.act = p->act;
-  b.a_f16 = b.path == 1 && p->wfmt == B12X_WEIGHT_NVFP4 && p->afmt == B12X_ACT_BF16;
+  // grouped path, NVFP4 weights: GEMM1 reads a scaled f16 copy of a (of its MXFP8 round trips with MXFP8
+  // activations)
+  b.a_f16 = b.path == 1 && p->wfmt == B12X_WEIGHT_NVFP4;
   b.T = T; b.a_stride = a_stride; b.out_stride = out_stride;
   b.Hp = p->Hp; b.Ip = p->Ip; b.max_rows = p->max_rows; b.max_tiles = p->max_tiles;
   b.nf13 = p->l13.nf; b.kf13 = p->l13.kf; b.kfs13 = p->l13.kfs;
@@ -364,7 +366,9 @@ static b12x_status run_stage(const BindingImpl& b, int stage, hipStream_t s) {
   switch (stage) {
     case B12X_STAGE_ROUTE: err = launch_route(b, s); break;
     case B12X_STAGE_QUANT_X:
-      if (b.a_f16) err = launch_f16_rows(b.a, b.T, b.H, b.a_stride, (uint16_t*)b.xq, b.Hp, (int32_t*)b.xs, s);
+      if (b.a_f16)
+        err = launch_f16_rows(b.a, b.T, b.H, b.a_stride, (uint16_t*)b.xq, b.Hp, (int32_t*)b.xs,
+                              a8_bf16(b.wfmt, b.afmt), s);
       else if (a8_bf16(b.wfmt, b.afmt))
         err = launch_mx_roundtrip_rows(b.a, b.T, b.H, b.a_stride, (uint16_t*)b.xq, b.Hp, s);
       else err = launch_quant_rows(b.a, b.T, b.H, b.a_stride, b.xq, b.Hp, b.xs, b.Hp / 32, s);

@@ -27,6 +27,10 @@ constexpr int kActF16 = 3;
 // activations): the operand path is bf16, and the gate/up epilogue stores h
 // as the bf16 value of its own MXFP8 round trip.
 constexpr int kActRt = 4;
+// The same round trips as a scaled f16 copy (NVFP4 weights x MXFP8
+// activations on the grouped path): the f16 operand path of kActF16 with the
+// round-trip epilogue of kActRt.
+constexpr int kActF16Rt = 5;
 
 // Raw buffer loads (CDNA buffer resource, stride 0).  A byte offset at or
 // past the record count returns zeros without a memory access, so a guarded

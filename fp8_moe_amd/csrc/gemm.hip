@@ -87,8 +87,10 @@ enum { MODE_SILU = 1, MODE_RELU2 = 2, MODE_DOWN = 3, MODE_DENSE = 4 };
 template <int WF, int AF, int MODE, int NFW>
 __global__ __launch_bounds__(kGemmThreads, 1) void moe_gemm_kernel(const GemmParams p) {
   constexpr bool A8 = AF == B12X_ACT_MXFP8;
-  constexpr bool F16 = AF == kActF16;  // f16 activations x NVFP4 weights dequantized to f16
-  constexpr bool RT = AF == kActRt;    // bf16 MXFP8 round trips (NVFP4 x MXFP8): h stored as its round trip
+  // f16 activations x NVFP4 weights dequantized to f16
+  constexpr bool F16 = AF == kActF16 || AF == kActF16Rt;
+  // MXFP8 round trips as activations (NVFP4 x MXFP8): h stored as its own round trip
+  constexpr bool RT = AF == kActRt || AF == kActF16Rt;
   static_assert(!F16 || WF == B12X_WEIGHT_NVFP4, "f16 activations run with NVFP4 weights");
   using OpT = std::conditional_t<F16, f16x8, bf16x8>;  // 16-bit MFMA operand type
   constexpr int ROWB = A8 ? 144 : 272;  // LDS bytes per A row: 128 K elements + 16 bytes of skew
@@ -632,10 +634,11 @@ static int dispatch(const BindingImpl& b, const GemmParams& p, int64_t max_work,
   const bool nv = b.wfmt == B12X_WEIGHT_NVFP4, a8 = a8_native(b.wfmt, b.afmt);
   if (a8) return launch_gemm_t<B12X_WEIGHT_MXFP4, B12X_ACT_MXFP8, MODE>(p, max_work, s);
   if constexpr (MODE != MODE_DOWN) {
-    if (a8_bf16(b.wfmt, b.afmt)) return launch_gemm_t<B12X_WEIGHT_NVFP4, kActRt, MODE>(p, max_work, s);
-  }
-  if constexpr (MODE != MODE_DOWN) {
+    // the scaled f16 copy of a (of its MXFP8 round trips with MXFP8 activations), else the
+    // bf16 copy of the round trips
+    if (p.a_exp && a8_bf16(b.wfmt, b.afmt)) return launch_gemm_t<B12X_WEIGHT_NVFP4, kActF16Rt, MODE>(p, max_work, s);
     if (p.a_exp) return launch_gemm_t<B12X_WEIGHT_NVFP4, kActF16, MODE>(p, max_work, s);
+    if (a8_bf16(b.wfmt, b.afmt)) return launch_gemm_t<B12X_WEIGHT_NVFP4, kActRt, MODE>(p, max_work, s);
   }
   if (nv) return launch_gemm_t<B12X_WEIGHT_NVFP4, B12X_ACT_BF16, MODE>(p, max_work, s);
   return launch_gemm_t<B12X_WEIGHT_MXFP4, B12X_ACT_BF16, MODE>(p, max_work, s);
@@ -663,11 +666,7 @@ int launch_gemm1(const BindingImpl& b, hipStream_t s) {
     p.a_bytes = b.T * b.Hp * 2;
     p.a_exp = (const int32_t*)b.xs;
   }
-  if (a8_bf16(b.wfmt, b.afmt)) {  // NVFP4 x MXFP8: the bf16 copy of a's MXFP8 round trip
-    p.a16 = (const uint16_t*)b.xq;
-    p.a_stride = b.Hp;
-    p.a_bytes = b.T * b.Hp * 2;
-  }
+  // (NVFP4 x MXFP8 takes the same route: the copy then holds a's MXFP8 round trips)
   p.sorted = b.sorted;
   p.k_top = b.k;
   p.n_pairs = b.T * b.k;

@@ -98,7 +98,8 @@ struct BindingImpl {
   uint32_t magic;
   int32_t path;
   int32_t E, H, I, k, gated, wfmt, afmt, act;
-  int32_t a_f16;  // grouped path, NVFP4 x bf16: GEMM1 reads the scaled f16 copy of a (xq) and row exponents (xs)
+  int32_t a_f16;  // grouped path, NVFP4 weights: GEMM1 reads a scaled f16 copy of a (xq; of its MXFP8 round trips
+                  // with MXFP8 activations) and row exponents (xs)
   int64_t T, a_stride, out_stride;
   int64_t Hp, Ip, max_rows, max_tiles;
   int64_t nf13, kf13, kfs13, nf2, kf2, kfs2;
@@ -149,7 +150,7 @@ int launch_quant_rows(const uint16_t* x, int64_t rows, int64_t cols, int64_t str
 int launch_mx_roundtrip_rows(const uint16_t* x, int64_t rows, int64_t cols, int64_t stride, uint16_t* out,
                              int64_t out_stride, hipStream_t s);
 int launch_f16_rows(const uint16_t* x, int64_t rows, int64_t cols, int64_t stride, uint16_t* out,
-                    int64_t out_stride, int32_t* exps, hipStream_t s);
+                    int64_t out_stride, int32_t* exps, bool rt, hipStream_t s);
 int launch_gemm1(const BindingImpl& b, hipStream_t s);
 int launch_gemm2(const BindingImpl& b, hipStream_t s);
 int launch_combine(const BindingImpl& b, hipStream_t s);

@@ -79,6 +79,11 @@ int launch_quant_rows(const uint16_t* x, int64_t rows, int64_t cols, int64_t str
 // the row maximum in [2^14, 2^15): every bf16 value above 2^-31 of the row
 // maximum is then exact in f16, and the GEMM multiplies its fp32 results by
 // 2^e[r].  One workgroup per row.
+// RT: the values copied are the MXFP8 round trips of the row (blocks of 32 =
+// 4 consecutive threads, 8 values each); their magnitudes stay within
+// 1 + 2^-4 of the bf16 row maximum the exponent is taken from (a saturated
+// block maximum rounds down), so the f16 copy stays below 2^16.
+template <bool RT>
 __global__ __launch_bounds__(256) void f16_rows_kernel(const uint16_t* __restrict__ x, int64_t cols, int64_t stride,
                                                         uint16_t* __restrict__ out, int64_t out_stride,
                                                         int32_t* __restrict__ exps) {
@@ -100,9 +105,24 @@ __global__ __launch_bounds__(256) void f16_rows_kernel(const uint16_t* __restric
   int e = m ? ilog2_mag(m << 16) - 14 : 0;
   e = e < -110 ? -110 : (e > 110 ? 110 : e);
   const float mul = bits_f32((uint32_t)(127 - e) << 23);  // 2^-e, exact
-  for (int64_t c = threadIdx.x * 8; c < cols; c += 256 * 8) {
-    const uint4 v = *(const uint4*)(src + c);
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  // cols is a multiple of 32: a whole 32-block is 4 threads of one pass, all active or all idle
+  for (int64_t c0 = 0; c0 < cols; c0 += 256 * 8) {
+    const int64_t c = c0 + threadIdx.x * 8;
+    const bool act = c < cols;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (act) v = *(const uint4*)(src + c);
+    uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    if constexpr (RT) {
+      uint32_t bm = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) bm = max(bm, max(w[i] & 0x7FFFu, (w[i] >> 16) & 0x7FFFu));
+      bm = max(bm, (uint32_t)__shfl_xor((int)bm, 1));
+      bm = max(bm, (uint32_t)__shfl_xor((int)bm, 2));
+      const int sb = mx_scale_exp(bm << 16);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        w[i] = mx_roundtrip_bf16(bf16_to_f32(w[i] & 0xFFFFu), sb) | (mx_roundtrip_bf16(bf16_to_f32(w[i] >> 16), sb) << 16);
+    }
     uint32_t o[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -110,15 +130,20 @@ __global__ __launch_bounds__(256) void f16_rows_kernel(const uint16_t* __restric
       const _Float16 hi = (_Float16)(bf16_to_f32(w[i] >> 16) * mul);
       o[i] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
     }
-    *(uint4*)(out + r * out_stride + c) = make_uint4(o[0], o[1], o[2], o[3]);
+    if (act) *(uint4*)(out + r * out_stride + c) = make_uint4(o[0], o[1], o[2], o[3]);
   }
   if (threadIdx.x == 0) exps[r] = e;
 }
 
 int launch_f16_rows(const uint16_t* x, int64_t rows, int64_t cols, int64_t stride, uint16_t* out,
-                    int64_t out_stride, int32_t* exps, hipStream_t s) {
+                    int64_t out_stride, int32_t* exps, bool rt, hipStream_t s) {
   if (rows == 0) return 0;
-  hipLaunchKernelGGL(f16_rows_kernel, dim3((unsigned)rows), dim3(256), 0, s, x, cols, stride, out, out_stride, exps);
+  if (rt)
+    hipLaunchKernelGGL(f16_rows_kernel<true>, dim3((unsigned)rows), dim3(256), 0, s, x, cols, stride, out, out_stride,
+                       exps);
+  else
+    hipLaunchKernelGGL(f16_rows_kernel<false>, dim3((unsigned)rows), dim3(256), 0, s, x, cols, stride, out, out_stride,
+                       exps);
   return (int)hipGetLastError();
 }
 
