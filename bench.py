@@ -179,6 +179,45 @@ def measure_ceilings(fm, torch, stream):
     return out
 
 
+def measure_sized_reads(fm, torch, stream, sizes):
+    """What a plain streaming read achieves at the decode kernel's own sizes:
+    for each name -> bytes, a graph of 10 probe launches that each read a
+    different slice of a 1 GiB buffer (so consecutive launches find nothing in
+    the caches, like the decode bench's rotating weight copies), timed like the
+    kernel (graph replays between two events, divided per launch).  The probe's
+    workgroups read whole 16 KB chunks, so each launch reads the largest such
+    multiple not above the size; the best of a few grid sizes is kept."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    total = 1 << 30
+    src = torch.ones(total // 4, dtype=torch.int32, device="cuda")
+    out = {}
+    for name, size in sizes.items():
+        best = None
+        for per_cu in (1, 2, 3, 4):
+            wg = cus * per_cu
+            chunks = int(size) // (wg * 16384)
+            if chunks == 0:
+                continue
+            read = wg * chunks * 16384
+            n_slices = max(1, total // read)
+            sink = torch.empty(wg * 256, dtype=torch.int32, device="cuda")
+            views = [src[(i % n_slices) * read // 4:(i % n_slices + 1) * read // 4] for i in range(10)]
+            for v in views[:2]:
+                fm.probe_stream_read(v, sink, wg, stream=stream)
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                for v in views:
+                    fm.probe_stream_read(v, sink, wg, stream=stream)
+            g.replay()
+            sec = time_graph(torch, g, stream, 20) / (20 * len(views))
+            rate = read / sec / 1e9
+            if best is None or rate > best["GBs"]:
+                best = {"bytes": read, "us": round(sec * 1e6, 3), "GBs": round(rate, 1), "workgroups": wg}
+        out[name] = best
+    del src
+    return out
+
+
 def time_stage_graph(torch, fm, bindings, stages, stream, reps=10):
     """Mean duration (s) per binding of the given stages' kernels: a graph of
     those stages for every binding, replayed `reps` times between two events
@@ -512,6 +551,14 @@ def main():
     log("achieved ceilings")
     ceil = measure_ceilings(fm, torch, stream)
     ceil["decode_kernel_frac_of_stream_read"] = round(achieved / ceil["stream_read_GBs"], 4)
+    # the same bytes per launch as the decode kernel at each T, streamed by the probe
+    sized = measure_sized_reads(fm, torch, stream, {f"T{T}": b for T, b in zip(Ts, kbytes)})
+    for T, d, b in zip(Ts, durs, kbytes):
+        r = sized[f"T{T}"]
+        if r is not None:
+            r["decode_kernel_GBs"] = round(b / d / 1e9, 1)
+            r["decode_kernel_frac"] = round(b / d / 1e9 / r["GBs"], 4)
+    ceil["stream_read_at_decode_sizes"] = sized
     result["ceilings"] = ceil
     if not args.no_extra:
         log("prefill line")

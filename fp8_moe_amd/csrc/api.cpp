@@ -228,7 +228,10 @@ b12x_status b12x_moe_plan(const b12x_moe_caps* caps, b12x_moe_plan_t* out) {
   len[R_XS] = a8 ? (uint64_t)p->max_tokens * (p->Hp / 32) : (x16 || xrt ? 4ull * p->max_tokens : 0);
   len[R_H] = (uint64_t)p->max_rows * p->Ip * (a8 ? 1 : 2);
   len[R_HS] = a8 ? (uint64_t)p->max_rows * (p->Ip / 32) : 0;
-  len[R_Y] = 4ull * p->max_rows * p->H;
+  {  // y: bf16 rows in routing order (grouped path) or fp32 rows by pair id (decode path)
+    const uint64_t grouped = 2ull * p->max_rows * p->H, decode = 4ull * p->decode_max_pairs * p->H;
+    len[R_Y] = grouped > decode ? grouped : decode;
+  }
   {  // decode path: epoch, status and one flag per (touched expert slot, gate/up group of 2 fragments)
     const int64_t slots = p->decode_max_pairs < p->E ? p->decode_max_pairs : p->E;
     len[R_DSYNC] = p->decode_max_pairs > 0 ? kDecodeFlagsOffset + 8ull * slots * ((p->l13.nf + 1) / 2) : 0;
@@ -335,6 +338,7 @@ b12x_status b12x_moe_bind(b12x_moe_plan_t p, void* scratch, uint64_t scratch_byt
   b.h = sb + p->off[R_H];
   b.hs = p->len[R_HS] ? sb + p->off[R_HS] : nullptr;
   b.y = (float*)(sb + p->off[R_Y]);
+  b.y16 = (uint16_t*)(sb + p->off[R_Y]);
   b.dsync = p->len[R_DSYNC] ? sb + p->off[R_DSYNC] : nullptr;
   memset(binding, 0, sizeof(*binding));
   memcpy(binding, &b, sizeof(b));

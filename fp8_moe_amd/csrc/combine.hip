@@ -2,7 +2,8 @@
 // fused routed-expert FFN; the combine weights are the caller's
 // topk_weights).  out[t] = sum over slots j = 0..k-1 in ascending order of
 // w[t, j] * y[pos[t*k + j]], accumulated in fp32 and rounded once to bf16
-// (nearest even).  A gather, not a scatter: no atomics, so the result does
+// (nearest even).  The grouped path stages y as bf16 rows, the decode path as
+// fp32 rows.  A gather, not a scatter: no atomics, so the result does
 // not depend on scheduling.  A dropped pair (pos = -1) contributes nothing.
 #include "device_common.h"
 
@@ -12,7 +13,21 @@ namespace b12x {
 // time: their rows and weights, then all their y loads (a dropped pair loads
 // row 0 and is masked), then the sums in slot order, so the loads of a chunk
 // are in flight together.
-__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y, int64_t y_stride,
+// Eight consecutive y values of one row, widened to fp32.
+__device__ __forceinline__ void load_y8(const float* y, float4& a, float4& b) {
+  a = ((const float4*)y)[0];
+  b = ((const float4*)y)[1];
+}
+__device__ __forceinline__ void load_y8(const uint16_t* y, float4& a, float4& b) {
+  const uint4 v = *(const uint4*)y;
+  a = make_float4(__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xFFFF0000u), __uint_as_float(v.y << 16),
+                  __uint_as_float(v.y & 0xFFFF0000u));
+  b = make_float4(__uint_as_float(v.z << 16), __uint_as_float(v.z & 0xFFFF0000u), __uint_as_float(v.w << 16),
+                  __uint_as_float(v.w & 0xFFFF0000u));
+}
+
+template <typename YT>
+__global__ __launch_bounds__(256) void combine_kernel(const YT* __restrict__ y, int64_t y_stride,
                                                        const int32_t* __restrict__ pos,
                                                        const int32_t* __restrict__ ids, int E,
                                                        const float* __restrict__ tw, int64_t T, int k, int H,
@@ -42,11 +57,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
       const int j = min(j0 + u, k - 1);
       raw[u] = key[t * k + j];
       w[u] = tw[t * k + j];
-      if (!pos) {  // row t*k + j < T*k <= max_rows
-        const float4* src = (const float4*)(y + (t * k + j) * y_stride + c);
-        a[u] = src[0];
-        b[u] = src[1];
-      }
+      if (!pos) load_y8(y + (t * k + j) * y_stride + c, a[u], b[u]);  // row t*k + j < T*k <= max_rows
     }
 #pragma unroll
     for (int u = 0; u < kChunk; ++u) {
@@ -58,11 +69,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     }
     if (pos) {
 #pragma unroll
-      for (int u = 0; u < kChunk; ++u) {
-        const float4* src = (const float4*)(y + (int64_t)(row[u] < 0 ? 0 : row[u]) * y_stride + c);
-        a[u] = src[0];
-        b[u] = src[1];
-      }
+      for (int u = 0; u < kChunk; ++u) load_y8(y + (int64_t)(row[u] < 0 ? 0 : row[u]) * y_stride + c, a[u], b[u]);
     }
 #pragma unroll
     for (int u = 0; u < kChunk; ++u) {
@@ -79,25 +86,26 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   *(uint4*)(out + t * out_stride + c) = make_uint4(o[0], o[1], o[2], o[3]);
 }
 
-static int launch_combine_rows(const BindingImpl& b, const int32_t* pos, int32_t* epoch, const int32_t* status,
-                               hipStream_t s) {
+template <typename YT>
+static int launch_combine_rows(const BindingImpl& b, const YT* y, const int32_t* pos, int32_t* epoch,
+                               const int32_t* status, hipStream_t s) {
   const int64_t total = b.T * (b.H / 8);
   if (total == 0) return 0;
-  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, b.y, (int64_t)b.H, pos,
-                     b.ids, b.E, b.tw, b.T, b.k, b.H, b.max_rows, b.out, b.out_stride, epoch, status);
+  hipLaunchKernelGGL(combine_kernel<YT>, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, y, (int64_t)b.H,
+                     pos, b.ids, b.E, b.tw, b.T, b.k, b.H, b.max_rows, b.out, b.out_stride, epoch, status);
   return (int)hipGetLastError();
 }
 
-// grouped path: y rows in routing order, located through pos
+// grouped path: bf16 y rows in routing order, located through pos
 int launch_combine(const BindingImpl& b, hipStream_t s) {
-  return launch_combine_rows(b, b.pos, nullptr, nullptr, s);
+  return launch_combine_rows(b, (const uint16_t*)b.y16, b.pos, nullptr, nullptr, s);
 }
 
-// decode path: y rows indexed by pair id
+// decode path: fp32 y rows indexed by pair id
 int launch_decode_combine(const BindingImpl& b, hipStream_t s) {
   int32_t* epoch = b.dsync ? (int32_t*)(b.dsync + kDecodeEpochOffset) : nullptr;
   const int32_t* status = decode_fused(b) ? (const int32_t*)(b.dsync + kDecodeStatusOffset) : nullptr;
-  return launch_combine_rows(b, nullptr, epoch, status, s);
+  return launch_combine_rows(b, (const float*)b.y, nullptr, epoch, status, s);
 }
 
 }  // namespace b12x

@@ -4,7 +4,7 @@
 // w4a8_mx multiplies FP4 weights with dynamically quantized MXFP8
 // activations).  One kernel template serves
 //   GEMM1: h[row] = act(x[token(row)] . W13_e^T)   (SiLU-gated or ReLU^2)
-//   GEMM2: y[row] = h[row] . W2_e^T
+//   GEMM2: y[row] = h[row] . W2_e^T                (stored as bf16)
 // over the routing tiles (expert, first row, rows).  A workgroup of 4 waves
 // owns one routing tile (up to kTileRows = 144 rows) x 4*NFW weight fragments
 // (16 columns each).  The packed FP4 fragments stream from global memory
@@ -64,13 +64,12 @@ struct GemmParams {
   uint8_t* hs;
   int64_t h_stride;
   int64_t hs_stride;
-  float* y;
-  int64_t y_stride;
-  // dense GEMM (MODE_DENSE): dense_m rows of a, tiles of kTileRows rows in
-  // order (no tile list, one weight matrix), bf16 output rows
-  int64_t dense_m;
+  // bf16 output rows: y (MODE_DOWN, one row per routed row, pads included)
+  // or the dense GEMM's out (MODE_DENSE: dense_m rows of a, tiles of
+  // kTileRows rows in order, no tile list, one weight matrix)
   uint16_t* out16;
   int64_t out_stride;
+  int64_t dense_m;
 };
 
 enum { MODE_SILU = 1, MODE_RELU2 = 2, MODE_DOWN = 3, MODE_DENSE = 4 };
@@ -496,7 +495,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void moe_gemm_kernel(const GemmPar
     }
 
     // ---- epilogue: lane holds column r16 of each fragment, rows 4 g + i of each 16-row block
-    if constexpr (MODE == MODE_DENSE) {
+    if constexpr (MODE == MODE_DENSE || MODE == MODE_DOWN) {
 #pragma unroll
       for (int mf = 0; mf < MF; ++mf) {
         if (mf < nmf) {
@@ -507,24 +506,9 @@ __global__ __launch_bounds__(kGemmThreads, 1) void moe_gemm_kernel(const GemmPar
 #pragma unroll
               for (int i = 0; i < 4; ++i) {
                 const int64_t row = row0 + 16 * mf + 4 * g + i;
-                if (16 * mf + 4 * g + i < nrows) p.out16[row * p.out_stride + col] = (uint16_t)bf16_rne(acc[mf][j][i] * gsc);
-              }
-            }
-          }
-        }
-      }
-    } else if constexpr (MODE == MODE_DOWN) {
-#pragma unroll
-      for (int mf = 0; mf < MF; ++mf) {
-        if (mf < nmf) {
-#pragma unroll
-          for (int j = 0; j < NFW; ++j) {
-            if (j < nnf) {
-              const int col = 16 * (f0 + j) + r16;
-#pragma unroll
-              for (int i = 0; i < 4; ++i) {
-                const int64_t row = row0 + 16 * mf + 4 * g + i;
-                p.y[row * p.y_stride + col] = acc[mf][j][i] * gsc;
+                // a routed tile writes all its rows (pads land in their own rows, never read)
+                if (MODE == MODE_DOWN || 16 * mf + 4 * g + i < nrows)
+                  p.out16[row * p.out_stride + col] = (uint16_t)bf16_rne(acc[mf][j][i] * gsc);
               }
             }
           }
@@ -715,8 +699,8 @@ int launch_gemm2(const BindingImpl& b, hipStream_t s) {
   p.b_scales_expert = b.nf2 * b.kfs2 * kScaleGroupBytes;
   p.NF = (int)b.nf2;
   p.KFS = (int)b.kfs2;
-  p.y = b.y;
-  p.y_stride = b.H;
+  p.out16 = b.y16;
+  p.out_stride = b.H;
   const int64_t max_work = b.max_tiles * p.n_ntiles;
   return dispatch<MODE_DOWN>(b, p, max_work, s);
 }

@@ -125,7 +125,8 @@ struct BindingImpl {
   uint8_t* xs;
   void* h;
   uint8_t* hs;
-  float* y;
+  float* y;        // decode path: fp32 rows, one per pair id
+  uint16_t* y16;   // grouped path: bf16 rows in routing order (same memory as y)
   uint8_t* dsync;  // decode path: call epoch, status and the fused kernel's completion flags
 };
 constexpr uint32_t kBindingMagic = 0xb12b1d01u;
