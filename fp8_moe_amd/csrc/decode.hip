@@ -66,6 +66,7 @@ struct DecodeParams {
   int32_t* status;
   int64_t h_bytes;  // extent of h16 (device-coherent stores and loads)
   int deal;         // 0: one contiguous share per workgroup; else chunks of this many items dealt round-robin
+  int prev_groups;  // down phase of the fused kernel: the gate/up phase's groups per expert (same deal)
 };
 
 enum { DMODE_SILU = 1, DMODE_RELU2 = 2, DMODE_DOWN = 3 };
@@ -184,11 +185,26 @@ __device__ __forceinline__ void decode_items(const DecodeParams& p, DecodeLds& L
   // this workgroup's share of the (touched expert, fragment group) items
   const int64_t items = (int64_t)n_touched * p.n_groups;
   int lo, hi;
-  int chunk_id = (int)blockIdx.x;
   // With at least p.deal items per workgroup: chunks of p.deal consecutive
   // items dealt round-robin (chunk c to workgroup c % grid).  Otherwise (and
   // with p.deal = 0) one contiguous share per workgroup.
   const int deal = p.deal && items >= (int64_t)p.deal * gridDim.x ? p.deal : 0;
+  // When the gate/up phase dealt between one and two rounds of chunks, its
+  // first C1 % grid workgroups took two chunks and the others one.  The down
+  // phase then continues that deal (its chunk c goes to workgroup
+  // (C1 + c) % grid), so the workgroups with one gate/up chunk take the first
+  // down chunks instead of leaving a few workgroups with two of each at the
+  // end.  With more gate/up rounds the imbalance is a small share and the
+  // down phase deals from workgroup 0.
+  int chunk_id = (int)blockIdx.x;
+  if (FUSE == 2 && deal) {
+    const int64_t prev = (int64_t)n_touched * p.prev_groups;
+    const int64_t c1 = (prev + deal - 1) / deal;
+    if (c1 >= (int64_t)gridDim.x && c1 < 2 * (int64_t)gridDim.x) {
+      const int start = (int)(c1 - gridDim.x);
+      chunk_id = ((int)blockIdx.x - start + (int)gridDim.x) % (int)gridDim.x;
+    }
+  }
   if (deal) {
     lo = chunk_id * deal;
     hi = (int)min(items, (int64_t)lo + deal);
@@ -603,6 +619,7 @@ static int launch_fused_kw(const BindingImpl& b, DecodeParams& p1, DecodeParams&
   auto kernel = decode_fused_kernel<WF, MODE1, 2, KW1, 4, KW2>;
   p1.n_groups = (p1.NF + 1) / 2;
   p2.n_groups = (p2.NF + 3) / 4;
+  p2.prev_groups = p1.n_groups;
   const int64_t max_slots = b.T * b.k < b.E ? b.T * b.k : b.E;
   const int64_t items = max_slots * (p1.n_groups > p2.n_groups ? p1.n_groups : p2.n_groups);
   int64_t grid = resident_workgroups(kernel, cache);
