@@ -32,7 +32,10 @@ def _inputs(wl, T):
 # (workload, T, sampled token rows or None for all)
 FULL = [
     ("tiny", 16, None),
-    ("decode", 1, None), ("decode", 8, None), ("decode", 32, [0, 13, 31]),
+    # decode T=4: contiguous shares in both phases of the fused kernel; T=8: the down phase
+    # continues the gate/up deal; T=16 and 32: both phases deal from workgroup 0
+    ("decode", 1, None), ("decode", 4, None), ("decode", 8, None), ("decode", 16, [0, 7, 15]),
+    ("decode", 32, [0, 13, 31]),
     ("mixed", 1, None), ("mixed", 64, [0, 40, 63]), ("mixed", 512, [3, 511]), ("mixed", 2048, [0, 2047]),
     ("prefill", 4096, [0, 4095]),
     ("skew", 8192, [1, 8191]),
