@@ -8,8 +8,10 @@ nothing from the product path.
 What it computes (plain, slow, fp64, NumPy):
 
 * ``formats``  - E2M1 / E4M3 / E8M0 decoding, FP4 byte unpacking, MXFP4 and
-  NVFP4 weight dequantization, bf16 decode and round-to-nearest-even, and the
-  MXFP8 row quantizer (E4M3 elements, one E8M0 scale per 32).
+  NVFP4 weight dequantization, bf16 decode and round-to-nearest-even, the
+  MXFP8 row quantizer (E4M3 elements, one E8M0 scale per 32) and the NVFP4
+  activation quantizer (E2M1 elements, one E4M3 scale per 16, fp32 tensor
+  scale).
 * ``routing``  - the integer routing stage: expert histogram, prefix scan,
   stable token permutation, per-expert padded row tiles, inverse positions.
 * ``ffn``      - the routed-expert FFN: gather, gate/up projection, SiLU-gated
@@ -29,6 +31,7 @@ OFP8 definitions.
 from .formats import (  # noqa: F401
     e2m1_decode, e4m3_decode, e8m0_decode, unpack_fp4, dequant_mxfp4, dequant_nvfp4,
     bf16_decode, round_to_bf16, bf16_encode, quantize_mxfp8, dequant_mxfp8,
+    quantize_nvfp4, nvfp4_values, nvfp4_roundtrip,
 )
 from .routing import route  # noqa: F401
 from .ffn import fused_moe, Weights  # noqa: F401

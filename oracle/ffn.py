@@ -8,7 +8,9 @@ What the pages fix (b12x README "What's in here" / "Using it"; vLLM b12x page
 * the op is a routed-expert FFN over caller-supplied ``topk_ids`` /
   ``topk_weights``, with expert weights kept packed in MXFP4 or NVFP4;
 * activations are BF16 (W4A16: inline weight dequant, no activation-scale
-  math) or dynamically quantized MXFP8 (W4A8);
+  math), dynamically quantized MXFP8 (W4A8), or NVFP4 with NVFP4 weights
+  (W4A4; vLLM b12x page "Supported Configurations": NVFP4 MoE takes the
+  checkpoint's activation format);
 * experts are bias-free, SiLU-gated or non-gated ReLU^2;
 * the output is the top-k-weighted combine of the experts' outputs.
 
@@ -21,7 +23,11 @@ Readings where the pages are silent:
 * the expert's intermediate ``h`` is rounded to the precision of the down
   projection's operand before it: bf16 (round to nearest even) for BF16
   activations, MXFP8 (per 32 along I, the same rule as the activations) for
-  MXFP8 activations.
+  MXFP8 activations, NVFP4 (per 16 along I against the expert's activation
+  scale, the same rule as x) for NVFP4 activations.
+* NVFP4 activation scales: one fp32 scale for x (x is quantized once, before
+  it reaches any expert) and one per expert for h, given with the weights as
+  a checkpoint gives its input scales.
 * combine: ``out[t] = sum_j w[t, j] * y[t, j]`` in ascending slot order, with
   the weights used as given (no renormalization); a pair whose id lies outside
   ``[0, E)`` contributes nothing; a repeated id counts once per slot.
@@ -33,7 +39,7 @@ from typing import Optional
 import numpy as np
 
 from .formats import (bf16_decode, dequant_mxfp4, dequant_nvfp4, dequant_mxfp8,
-                      quantize_mxfp8, round_to_bf16)
+                      nvfp4_roundtrip, quantize_mxfp8, round_to_bf16)
 
 
 @dataclass
@@ -43,7 +49,9 @@ class Weights:
     ``w13_codes`` uint8 [E, N1, H/2] with N1 = 2I (gated) or I (ReLU^2);
     ``w13_scales`` uint8 [E, N1, H/G]; ``w2_codes`` uint8 [E, H, I/2];
     ``w2_scales`` uint8 [E, H, I/G]; G = 32 (MXFP4, E8M0) or 16 (NVFP4,
-    E4M3); ``w13_global`` / ``w2_global`` float32 [E] for NVFP4, else None.
+    E4M3); ``w13_global`` / ``w2_global`` float32 [E] for NVFP4, else None;
+    ``a13_global`` (float32 scalar, the scale of x) and ``a2_global``
+    (float32 [E], the scale of each expert's h) for NVFP4 activations.
     Each array may also be a mapping expert -> per-expert array (then
     ``num_experts`` is required); only the experts a call touches are read.
     """
@@ -55,6 +63,8 @@ class Weights:
     w2_scales: np.ndarray
     w13_global: Optional[np.ndarray] = None
     w2_global: Optional[np.ndarray] = None
+    a13_global: Optional[float] = None
+    a2_global: Optional[np.ndarray] = None
     num_experts: Optional[int] = None   # required when the arrays are per-expert mappings
 
     @property
@@ -82,8 +92,9 @@ def _silu(z):
         return z / (1.0 + np.exp(-z))
 
 
-def expert_ffn(xa, w13, w2, gated, intermediate):
-    """One expert on the rows ``xa`` [m, H]: returns y [m, H] (fp64)."""
+def expert_ffn(xa, w13, w2, gated, intermediate, h_global=None):
+    """One expert on the rows ``xa`` [m, H]: returns y [m, H] (fp64).
+    ``h_global``: the expert's NVFP4 activation scale (intermediate "nvfp4")."""
     z = xa @ w13.T
     if gated:
         inter = w13.shape[0] // 2
@@ -94,6 +105,8 @@ def expert_ffn(xa, w13, w2, gated, intermediate):
         h = round_to_bf16(h)
     elif intermediate == "mxfp8":
         h = dequant_mxfp8(*quantize_mxfp8(h))
+    elif intermediate == "nvfp4":
+        h = nvfp4_roundtrip(h, h_global)
     elif intermediate != "none":
         raise ValueError(f"unknown intermediate rounding {intermediate!r}")
     return h @ w2.T
@@ -106,10 +119,12 @@ def fused_moe(x_bits, topk_ids, topk_weights, weights, act_format="bf16",
 
     x_bits: uint16 bf16 patterns [T, H]; topk_ids int32 [T, k];
     topk_weights float32 [T, k]; weights: ``Weights``.
-    act_format: "bf16" (W4A16) or "mxfp8" (W4A8: each row of x is MXFP8
-    quantized per 32 along H and the GEMMs see the dequantized values).
-    intermediate: rounding of h before the down projection; defaults to "bf16"
-    for W4A16 and "mxfp8" for W4A8 ("none" keeps fp64).
+    act_format: "bf16" (W4A16), "mxfp8" (W4A8: each row of x is MXFP8
+    quantized per 32 along H and the GEMMs see the dequantized values) or
+    "nvfp4" (W4A4, NVFP4 weights: x quantized per 16 against
+    ``weights.a13_global``, h against ``weights.a2_global[e]``).
+    intermediate: rounding of h before the down projection; defaults to the
+    activation format ("bf16", "mxfp8" or "nvfp4"; "none" keeps fp64).
     """
     x = bf16_decode(x_bits)
     ids = np.asarray(topk_ids).astype(np.int64)
@@ -120,17 +135,22 @@ def fused_moe(x_bits, topk_ids, topk_weights, weights, act_format="bf16",
         xa = x
     elif act_format == "mxfp8":
         xa = dequant_mxfp8(*quantize_mxfp8(x))
+    elif act_format == "nvfp4":
+        if weights.weight_format != "nvfp4" or weights.a13_global is None or weights.a2_global is None:
+            raise ValueError("NVFP4 activations need NVFP4 weights and their activation scales")
+        xa = nvfp4_roundtrip(x, weights.a13_global)
     else:
         raise ValueError(f"unknown activation format {act_format!r}")
     if intermediate is None:
-        intermediate = "bf16" if act_format == "bf16" else "mxfp8"
+        intermediate = act_format
 
     # y[t, j] for every valid pair, expert by expert (each expert dequantized once)
     y = np.zeros((T, k, x.shape[1]), dtype=np.float64)
     valid = (ids >= 0) & (ids < E)
     for e in np.unique(ids[valid]):
         tt, jj = np.nonzero(ids == e)
-        y[tt, jj] = expert_ffn(xa[tt], weights.w13(e), weights.w2(e), weights.gated, intermediate)
+        hg = None if weights.a2_global is None else weights.a2_global[e]
+        y[tt, jj] = expert_ffn(xa[tt], weights.w13(e), weights.w2(e), weights.gated, intermediate, hg)
 
     out = np.zeros((T, x.shape[1]), dtype=np.float64)
     for j in range(k):

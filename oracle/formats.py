@@ -188,3 +188,77 @@ def dequant_mxfp8(codes, scales):
     vals = e4m3_decode(codes)
     sc = e8m0_decode(scales)
     return vals * np.repeat(sc, 32, axis=-1)
+
+
+def _e2m1_encode_sat(q):
+    """fp64 -> E2M1 codes: round half to even onto {0, 0.5, 1, 1.5, 2, 3, 4, 6}
+    (1 mantissa bit, smallest normal 1, the subnormal 0.5), saturating at 6,
+    sign kept (-0 encodes as 0x8)."""
+    q = np.asarray(q, dtype=_F64)
+    neg = np.signbit(q)
+    r = np.minimum(_round_to_grid(np.minimum(np.abs(q), 6.0), 1, 0), 6.0)
+    # magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6 are codes 0..7
+    _, ex = np.frexp(r)
+    e = ex.astype(np.int64) - 1
+    normal = r >= 1.0
+    m = np.where(normal, np.ldexp(r, -np.where(normal, e, 0)) * 2.0 - 2.0, 0.0).astype(np.int64)
+    mag_code = np.where(normal, ((e + 1) << 1) + m, (r * 2.0).astype(np.int64))
+    return (mag_code | np.where(neg, 0x8, 0)).astype(np.uint8)
+
+
+def _f32(v):
+    return np.asarray(v, dtype=_F64).astype(np.float32)
+
+
+def quantize_nvfp4(v, global_scale):
+    """NVFP4 quantization of activations along the last axis (length a multiple of 16).
+
+    The vLLM b12x page ("Supported Configurations") lists NVFP4 activations
+    for NVFP4 MoE, and the README names an NVFP4 row quantizer
+    (quantization.nvfp4); neither gives the rule.  Reading, the NVFP4 recipe:
+    with g the fp32 per-tensor scale of the activations (the checkpoint's
+    input scale), each block of 16 takes the E4M3 scale
+    s = E4M3_RNE_sat(amax / (6 g)) and each element the E2M1 code
+    E2M1_RNE_sat(v / (s g)); a block whose scale rounds to 0 takes codes 0.
+    The quotients decide integer codes, so they are taken in fp32 as the
+    kernels take them: d = fl32(6 * g), t = fl32(amax / d), u = fl32(s * g),
+    q = fl32(v / u), each one IEEE binary32 rounding of the exact result
+    (the inputs are binary32 values).
+    Returns (codes uint8 [..., K] unpacked, scales uint8 [..., K/16]).
+    """
+    v32 = _f32(v)
+    if not np.isfinite(v32).all():
+        raise ValueError("NVFP4 quantization of a non-finite value")
+    g = np.float32(global_scale)
+    if not (np.isfinite(g) and g > 0):
+        raise ValueError("NVFP4 activation scale must be finite and positive")
+    k = v32.shape[-1]
+    if k % 16:
+        raise ValueError("NVFP4 rows must be a multiple of 16 long")
+    blocks = v32.reshape(v32.shape[:-1] + (k // 16, 16))
+    amax = np.abs(blocks).max(axis=-1)
+    d = np.float32(np.float32(6.0) * g)
+    t = (amax / d).astype(np.float32)
+    scodes = _e4m3_encode_sat(t.astype(_F64))
+    s = e4m3_decode(scodes).astype(np.float32)
+    u = (s * g).astype(np.float32)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        q = (blocks / u[..., None]).astype(np.float32)
+    q = np.where(u[..., None] > 0, q, np.float32(0.0))
+    codes = _e2m1_encode_sat(q.astype(_F64)).reshape(v32.shape)
+    return codes, scodes
+
+
+def nvfp4_values(codes, scales):
+    """E2M1(code) * E4M3(scale) with one scale per 16 codes along the last axis
+    (the round trip without the per-tensor scale, exact in fp64)."""
+    sc = e4m3_decode(scales)
+    if np.isnan(sc).any():
+        raise ValueError("E4M3 NaN block scale")
+    return e2m1_decode(codes) * np.repeat(sc, 16, axis=-1)
+
+
+def nvfp4_roundtrip(v, global_scale):
+    """g * E2M1 * E4M3 of quantize_nvfp4(v, g): the values the GEMMs see."""
+    codes, scales = quantize_nvfp4(v, global_scale)
+    return nvfp4_values(codes, scales) * _F64(np.float32(global_scale))
