@@ -320,7 +320,8 @@ def bench_prefill(fm, synth, torch, stream, reps=20, act_format=None):
     w = synth.make_weights(wl, device="cuda")
     wp = fm.plan_weights(wl.E, wl.H, wl.I, wl.gated, wl.weight_format)
     ex = fm.prepare_weights(wp, w["w13_codes"], w["w13_scales"], w["w2_codes"], w["w2_scales"],
-                            w["w13_global"], w["w2_global"])
+                            w["w13_global"], w["w2_global"], a13_global=w.get("a13_global"),
+                            a2_global=w.get("a2_global"))
     del w
     plan = fm.plan(wp, wl.k, T, wl.act_format, "silu")
     scratch = fm.alloc_scratch(plan)
@@ -567,6 +568,10 @@ def main():
         log("prefill line, NVFP4 x MXFP8")
         pa8 = bench_prefill(fm, synth, torch, stream, act_format="mxfp8")
         result["prefill_w4a8_nvfp4"] = {k: pa8[k] for k in ("T", "us", "us_p10_p50_p90", "tflops", "frac_bf16_peak",
+                                                            "stage_us")}
+        log("prefill line, NVFP4 x NVFP4")
+        pa4 = bench_prefill(fm, synth, torch, stream, act_format="nvfp4")
+        result["prefill_w4a4_nvfp4"] = {k: pa4[k] for k in ("T", "us", "us_p10_p50_p90", "tflops", "frac_bf16_peak",
                                                             "stage_us")}
         log("dense mm line")
         result["dense_mm"] = bench_dense_mm(fm, synth, torch, stream)

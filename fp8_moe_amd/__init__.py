@@ -24,7 +24,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libb12x_moe.so")
 
 WEIGHT_FORMATS = {"mxfp4": 1, "nvfp4": 2}
-ACT_FORMATS = {"bf16": 1, "mxfp8": 2}
+ACT_FORMATS = {"bf16": 1, "mxfp8": 2, "nvfp4": 3}
 ACTIVATIONS = {"silu": 1, "relu2": 2}
 STAGES = {"route": 1, "quant_x": 2, "gemm1": 3, "gemm2": 4, "combine": 5, "decode1": 6, "decode2": 7}
 QUERIES = {"path": 1, "tile_rows": 2, "row_pad": 3, "T": 4, "num_stages": 5}
@@ -54,16 +54,19 @@ class WeightPlan(ctypes.Structure):
                 ("prepared_bytes", ctypes.c_uint64), ("alignment", ctypes.c_uint64),
                 ("w13_codes_off", ctypes.c_uint64), ("w13_scales_off", ctypes.c_uint64),
                 ("w13_global_off", ctypes.c_uint64), ("w2_codes_off", ctypes.c_uint64),
-                ("w2_scales_off", ctypes.c_uint64), ("w2_global_off", ctypes.c_uint64)]
+                ("w2_scales_off", ctypes.c_uint64), ("w2_global_off", ctypes.c_uint64),
+                ("a13_global_off", ctypes.c_uint64), ("a2_global_off", ctypes.c_uint64)]
 
 
 class WeightSrc(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in
-                ("w13_codes", "w13_scales", "w13_global", "w2_codes", "w2_scales", "w2_global")]
+                ("w13_codes", "w13_scales", "w13_global", "w2_codes", "w2_scales", "w2_global", "a13_global",
+                 "a2_global")]
 
 
 class Experts(ctypes.Structure):
-    _fields_ = [("plan", WeightPlan), ("base", ctypes.c_void_p), ("bytes", ctypes.c_uint64)]
+    _fields_ = [("plan", WeightPlan), ("base", ctypes.c_void_p), ("bytes", ctypes.c_uint64),
+                ("act_scales", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 class Caps(ctypes.Structure):
@@ -166,18 +169,23 @@ class PreparedExperts:
 
 
 def prepare_weights(wplan, w13_codes, w13_scales, w2_codes, w2_scales, w13_global=None, w2_global=None,
-                    out=None, stream=None):
-    """Pack source FP4 weights (device tensors, layouts as in the header)."""
+                    out=None, stream=None, a13_global=None, a2_global=None):
+    """Pack source FP4 weights (device tensors, layouts as in the header).
+    a13_global (f32 [1]) / a2_global (f32 [E]): NVFP4 activation scales of x
+    and of each expert's h, needed for NVFP4 activations."""
     dev = w13_codes.device
-    tensors = [w13_codes, w13_scales, w2_codes, w2_scales] + [t for t in (w13_global, w2_global) if t is not None]
+    opt = (w13_global, w2_global, a13_global, a2_global)
+    tensors = [w13_codes, w13_scales, w2_codes, w2_scales] + [t for t in opt if t is not None]
     for t in tensors:
         if not t.is_cuda or not t.is_contiguous():
             raise ValueError("source weights must be contiguous device tensors")
     if out is None:
         out = torch.empty(wplan.prepared_bytes, dtype=torch.uint8, device=dev)
-    src = WeightSrc(w13_codes.data_ptr(), w13_scales.data_ptr(),
-                    None if w13_global is None else w13_global.data_ptr(), w2_codes.data_ptr(),
-                    w2_scales.data_ptr(), None if w2_global is None else w2_global.data_ptr())
+    def p(t):
+        return None if t is None else t.data_ptr()
+
+    src = WeightSrc(w13_codes.data_ptr(), w13_scales.data_ptr(), p(w13_global), w2_codes.data_ptr(),
+                    w2_scales.data_ptr(), p(w2_global), p(a13_global), p(a2_global))
     ex = Experts()
     _check(_lib.b12x_moe_prepare_weights(ctypes.byref(wplan), ctypes.byref(src), _ptr(out), out.numel(),
                                          _stream(stream), ctypes.byref(ex)))
@@ -341,7 +349,8 @@ class FusedMoE:
         self.wplan = plan_weights(E, H, I, gated, weight_format)
         self.experts = prepare_weights(self.wplan, weights["w13_codes"], weights["w13_scales"],
                                        weights["w2_codes"], weights["w2_scales"], weights.get("w13_global"),
-                                       weights.get("w2_global"), stream=stream)
+                                       weights.get("w2_global"), stream=stream,
+                                       a13_global=weights.get("a13_global"), a2_global=weights.get("a2_global"))
         self.plan = plan(self.wplan, top_k, max_tokens, act_format, activation, decode_max_pairs)
         self.scratch = alloc_scratch(self.plan, weights["w13_codes"].device)
         self.H = H

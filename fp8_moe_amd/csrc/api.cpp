@@ -71,8 +71,10 @@ b12x_status check_caps(const b12x_moe_caps* c) {
   if (c->max_tokens < 1) return fail(B12X_ERR_INVALID_ARGUMENT, "max_tokens must be >= 1");
   if (c->max_tokens * c->top_k > ((int64_t)1 << 30))
     return fail(B12X_ERR_UNSUPPORTED, "max_tokens * top_k exceeds 2^30 pairs");
-  if (c->act_format != B12X_ACT_BF16 && c->act_format != B12X_ACT_MXFP8)
+  if (c->act_format != B12X_ACT_BF16 && c->act_format != B12X_ACT_MXFP8 && c->act_format != B12X_ACT_NVFP4)
     return fail(B12X_ERR_INVALID_ARGUMENT, "unknown activation format %d", c->act_format);
+  if (c->act_format == B12X_ACT_NVFP4 && c->weights.desc.weight_format != B12X_WEIGHT_NVFP4)
+    return fail(B12X_ERR_UNSUPPORTED, "NVFP4 activations run with NVFP4 weights only");
   if (c->activation != B12X_ACTIVATION_SILU_GATED && c->activation != B12X_ACTIVATION_RELU2)
     return fail(B12X_ERR_INVALID_ARGUMENT, "unknown activation %d", c->activation);
   if ((c->activation == B12X_ACTIVATION_SILU_GATED) != (c->weights.desc.gated == 1))
@@ -119,6 +121,8 @@ b12x_status b12x_moe_plan_weights(const b12x_moe_weight_desc* d, b12x_moe_weight
   out->w2_scales_off = off;  off = align_up(off + E * l2.scales_per_expert, 256);
   out->w13_global_off = off; off = align_up(off + E * 4, 256);
   out->w2_global_off = off;  off = align_up(off + E * 4, 256);
+  out->a13_global_off = off; off = align_up(off + 4, 256);
+  out->a2_global_off = off;  off = align_up(off + E * 4, 256);
   out->prepared_bytes = off;
   return B12X_OK;
 }
@@ -141,6 +145,8 @@ b12x_status b12x_moe_prepare_weights(const b12x_moe_weight_plan* wp, const b12x_
     return fail(B12X_ERR_INVALID_ARGUMENT, "NULL source weight pointer");
   if (nv && (!src->w13_global || !src->w2_global))
     return fail(B12X_ERR_INVALID_ARGUMENT, "NVFP4 weights need both per-expert fp32 scales");
+  if ((src->a13_global || src->a2_global) && (!nv || !src->a13_global || !src->a2_global))
+    return fail(B12X_ERR_INVALID_ARGUMENT, "activation scales: both a13_global and a2_global, NVFP4 weights only");
   if (!aligned(src->w13_codes, 16) || !aligned(src->w2_codes, 16))
     return fail(B12X_ERR_MISALIGNED, "source codes must be 16-byte aligned");
   hipStream_t s = (hipStream_t)stream;
@@ -169,9 +175,17 @@ b12x_status b12x_moe_prepare_weights(const b12x_moe_weight_plan* wp, const b12x_
     if (!err) err = launch_copy_f32(src->w2_global, (float*)(base + wp->w2_global_off), d.num_experts, s);
     if (err) return hip_fail(err, "copy global scales");
   }
+  const bool act_scales = nv && src->a13_global && src->a2_global;
+  if (act_scales) {
+    err = launch_copy_f32(src->a13_global, (float*)(base + wp->a13_global_off), 1, s);
+    if (!err) err = launch_copy_f32(src->a2_global, (float*)(base + wp->a2_global_off), d.num_experts, s);
+    if (err) return hip_fail(err, "copy activation scales");
+  }
   out->plan = *wp;
   out->base = dst;
   out->bytes = dst_bytes;
+  out->act_scales = act_scales ? 1 : 0;
+  out->reserved = 0;
   return B12X_OK;
 }
 
@@ -211,10 +225,10 @@ b12x_status b12x_moe_plan(const b12x_moe_caps* caps, b12x_moe_plan_t* out) {
   const bool a8 = a8_native(p->wfmt, p->afmt);
   // NVFP4 weights with bf16 activations: the grouped path's GEMM1 reads a
   // scaled f16 copy of a (2 bytes per element) and one exponent per row.
-  // NVFP4 weights with MXFP8 activations: both paths read the bf16 copy of
-  // a's MXFP8 round trip.
+  // NVFP4 weights with MXFP8 (NVFP4) activations: both paths read a copy of
+  // a's MXFP8 (NVFP4) round trips, f16 with row exponents on the grouped path.
   const bool x16 = p->wfmt == B12X_WEIGHT_NVFP4 && p->afmt == B12X_ACT_BF16;
-  const bool xrt = a8_bf16(p->wfmt, p->afmt);
+  const bool xrt = a8_bf16(p->wfmt, p->afmt) || a4_nv(p->afmt);
   uint64_t len[R_COUNT_] = {0};
   len[R_COUNTS] = 4ull * p->E;
   len[R_OFFSETS] = 4ull * (p->E + 1);
@@ -285,6 +299,8 @@ b12x_status b12x_moe_bind(b12x_moe_plan_t p, void* scratch, uint64_t scratch_byt
     return fail(B12X_ERR_LAYOUT_MISMATCH, "prepared weights follow a different weight plan");
   if (!ex->base || ex->bytes < ex->plan.prepared_bytes)
     return fail(B12X_ERR_LAYOUT_MISMATCH, "prepared weight buffer missing or too small");
+  if (a4_nv(p->afmt) && !ex->act_scales)
+    return fail(B12X_ERR_INVALID_ARGUMENT, "NVFP4 activations need the activation scales (a13_global, a2_global)");
   if (T > 0) {
     if (!a || !ids || !tw || !out || !scratch) return fail(B12X_ERR_INVALID_ARGUMENT, "NULL device pointer");
     if (a_stride < p->H || out_stride < p->H) return fail(B12X_ERR_INVALID_ARGUMENT, "row stride smaller than H");
@@ -307,8 +323,8 @@ b12x_status b12x_moe_bind(b12x_moe_plan_t p, void* scratch, uint64_t scratch_byt
   b.path = (T > 0 && T * p->k <= p->decode_max_pairs) ? 2 : 1;
   b.E = p->E; b.H = p->H; b.I = p->I; b.k = p->k;
   b.gated = p->gated; b.wfmt = p->wfmt; b.afmt = p->afmt; b.act = p->act;
-  // grouped path, NVFP4 weights: GEMM1 reads a scaled f16 copy of a (of its MXFP8 round trips with MXFP8
-  // activations)
+  // grouped path, NVFP4 weights: GEMM1 reads a scaled f16 copy of a (of its MXFP8 or NVFP4 round trips with
+  // MXFP8 or NVFP4 activations)
   b.a_f16 = b.path == 1 && p->wfmt == B12X_WEIGHT_NVFP4;
   b.T = T; b.a_stride = a_stride; b.out_stride = out_stride;
   b.Hp = p->Hp; b.Ip = p->Ip; b.max_rows = p->max_rows; b.max_tiles = p->max_tiles;
@@ -324,6 +340,8 @@ b12x_status b12x_moe_bind(b12x_moe_plan_t p, void* scratch, uint64_t scratch_byt
   const bool nv = p->wfmt == B12X_WEIGHT_NVFP4;
   b.w13_global = nv ? (const float*)(wb + wp.w13_global_off) : nullptr;
   b.w2_global = nv ? (const float*)(wb + wp.w2_global_off) : nullptr;
+  b.a13_global = a4_nv(p->afmt) ? (const float*)(wb + wp.a13_global_off) : nullptr;
+  b.a2_global = a4_nv(p->afmt) ? (const float*)(wb + wp.a2_global_off) : nullptr;
   uint8_t* sb = (uint8_t*)scratch;
   b.counts = (int32_t*)(sb + p->off[R_COUNTS]);
   b.offsets = (int32_t*)(sb + p->off[R_OFFSETS]);
@@ -353,7 +371,7 @@ static b12x_status get_binding(const b12x_moe_binding* binding, BindingImpl* b) 
 }
 
 static bool stage_in_path(const BindingImpl& b, int stage) {
-  if (stage == B12X_STAGE_QUANT_X) return b.afmt == B12X_ACT_MXFP8 || b.a_f16;
+  if (stage == B12X_STAGE_QUANT_X) return b.afmt != B12X_ACT_BF16 || b.a_f16;
   if (b.path == 2)
     return stage == B12X_STAGE_DECODE1 || stage == B12X_STAGE_COMBINE ||
            (stage == B12X_STAGE_DECODE2 && !decode_fused(b));
@@ -370,7 +388,10 @@ static b12x_status run_stage(const BindingImpl& b, int stage, hipStream_t s) {
   switch (stage) {
     case B12X_STAGE_ROUTE: err = launch_route(b, s); break;
     case B12X_STAGE_QUANT_X:
-      if (b.a_f16)
+      if (a4_nv(b.afmt))  // exact NVFP4 round trips: f16 (grouped path, row exponents 0) or bf16
+        err = launch_nv_roundtrip_rows(b.a, b.T, b.H, b.a_stride, b.a13_global, (uint16_t*)b.xq, b.Hp,
+                                       (int32_t*)b.xs, b.a_f16, s);
+      else if (b.a_f16)
         err = launch_f16_rows(b.a, b.T, b.H, b.a_stride, (uint16_t*)b.xq, b.Hp, (int32_t*)b.xs,
                               a8_bf16(b.wfmt, b.afmt), s);
       else if (a8_bf16(b.wfmt, b.afmt))

@@ -44,6 +44,12 @@ struct DecodeParams {
   const uint8_t* bcodes;
   const uint8_t* bscales;
   const float* bglobal;
+  // NVFP4 activations: activation scale applied with bglobal (x: one value;
+  // h: one per expert, aglobal_per_expert = 1) and the scale of each expert's
+  // h for the gate/up epilogue's requantization
+  const float* aglobal;
+  int aglobal_per_expert;
+  const float* hglobal;
   int64_t b_codes_expert, b_scales_expert;
   int NF, KFS;
   int n_groups;  // fragment groups per expert
@@ -166,8 +172,9 @@ __device__ __forceinline__ void decode_items(const DecodeParams& p, DecodeLds& L
                                              uint64_t tag) {
   constexpr bool A8 = AF == B12X_ACT_MXFP8;
   constexpr bool RT = AF == kActRt;  // bf16 MXFP8 round trips: h stored as its own round trip
+  constexpr bool NVRT = AF == kActNvRt;  // bf16 NVFP4 round trips: h stored as its own NVFP4 round trip
   static_assert(FUSE == 0 || !A8, "the fused kernel runs 16-bit activations");
-  static_assert(FUSE == 0 || !RT, "the fused kernel stores plain bf16 h");
+  static_assert(FUSE == 0 || (!RT && !NVRT), "the fused kernel stores plain bf16 h");
   static_assert(FUSE != 1 || MODE != DMODE_DOWN, "phase 1 is gate/up");
   static_assert(FUSE != 2 || MODE == DMODE_DOWN, "phase 2 is down");
   int* const s_ids = L.ids;
@@ -246,7 +253,8 @@ __device__ __forceinline__ void decode_items(const DecodeParams& p, DecodeLds& L
   const int m = decode_expert(p, slot, s_ids, s_bits, s_wpre, s_rows, s_info, e);
   const uint8_t* bcodes = p.bcodes + (int64_t)e * p.b_codes_expert;
   const uint8_t* bscales = p.bscales + (int64_t)e * p.b_scales_expert;
-  const float gsc = p.bglobal ? p.bglobal[e] : 1.0f;
+  float gsc = p.bglobal ? p.bglobal[e] : 1.0f;
+  if (p.aglobal) gsc *= p.aglobal[p.aglobal_per_expert ? e : 0];
 
   // raw buffer loads: a fragment outside the wave's K range or the expert's
   // matrix (the resources end with the expert) reads zeros, so no load is
@@ -376,7 +384,21 @@ __device__ __forceinline__ void decode_items(const DecodeParams& p, DecodeLds& L
             }
             const int hcol0 = MODE == DMODE_SILU ? 16 * (f0 / 2) : 16 * f0;
             const int nh = MODE == DMODE_SILU ? max(0, min(NH, (p.NF - f0) / 2)) : max(0, min(NH, p.NF - f0));
-            if constexpr (RT) {
+            if constexpr (NVRT) {
+              // h as the bf16 value E2M1 * E4M3 of its NVFP4 round trip
+              // (blocks of 16 columns = one column block, the 16 lanes of a
+              // row); the down kernel applies the expert's activation scale
+              const float gh = p.hglobal[e];
+#pragma unroll
+              for (int q = 0; q < NH; ++q) {
+                if (q < nh) {
+                  float mx = fabsf(hv[q]);
+                  mx = row16_max(mx);
+                  const float sc = nv_block_scale(mx, gh);
+                  if (live) p.h16[pr * p.h_stride + hcol0 + 16 * q + r16] = (uint16_t)bf16_rne(nv_roundtrip(hv[q], sc, gh));
+                }
+              }
+            } else if constexpr (RT) {
               // h as the bf16 value of its MXFP8 round trip (blocks of 32
               // columns = column blocks (2b, 2b+1))
               static_assert(NH % 2 == 0, "whole MXFP8 blocks per group");
@@ -384,10 +406,7 @@ __device__ __forceinline__ void decode_items(const DecodeParams& p, DecodeLds& L
               for (int blk = 0; blk < NH / 2; ++blk) {
                 if (2 * blk < nh) {
                   float mx = fmaxf(fabsf(hv[2 * blk]), fabsf(hv[2 * blk + 1]));
-                  mx = fmaxf(mx, __shfl_xor(mx, 1));
-                  mx = fmaxf(mx, __shfl_xor(mx, 2));
-                  mx = fmaxf(mx, __shfl_xor(mx, 4));
-                  mx = fmaxf(mx, __shfl_xor(mx, 8));
+                  mx = row16_max(mx);
                   const int sx = mx_scale_exp(f32_bits(mx));
                   const int64_t col = hcol0 + 32 * blk + r16;
                   if (live) {
@@ -412,10 +431,7 @@ __device__ __forceinline__ void decode_items(const DecodeParams& p, DecodeLds& L
               for (int blk = 0; blk < NH / 2; ++blk) {
                 if (2 * blk < nh) {
                   float mx = fmaxf(fabsf(hv[2 * blk]), fabsf(hv[2 * blk + 1]));
-                  mx = fmaxf(mx, __shfl_xor(mx, 1));
-                  mx = fmaxf(mx, __shfl_xor(mx, 2));
-                  mx = fmaxf(mx, __shfl_xor(mx, 4));
-                  mx = fmaxf(mx, __shfl_xor(mx, 8));
+                  mx = row16_max(mx);
                   const int sx = mx_scale_exp(f32_bits(mx));
                   const int64_t col = hcol0 + 32 * blk + r16;
                   if (live) {
@@ -555,10 +571,15 @@ static DecodeParams gate_up_params(const BindingImpl& b) {
   p.as_stride = b.Hp / 32;
   p.a_bytes = a8 ? b.T * b.Hp : b.T * b.a_stride * 2;
   p.as_bytes = a8 ? b.T * (b.Hp / 32) : 0;
-  if (a8_bf16(b.wfmt, b.afmt)) {  // NVFP4 x MXFP8: the bf16 copy of a's MXFP8 round trip
+  if (a8_bf16(b.wfmt, b.afmt) || a4_nv(b.afmt)) {  // NVFP4 weights: the bf16 copy of a's MXFP8 / NVFP4 round trips
     p.a16 = (const uint16_t*)b.xq;
     p.a_stride = b.Hp;
     p.a_bytes = b.T * b.Hp * 2;
+  }
+  if (a4_nv(b.afmt)) {
+    p.aglobal = b.a13_global;  // x's activation scale, one value
+    p.aglobal_per_expert = 0;
+    p.hglobal = b.a2_global;   // h is requantized against its expert's scale
   }
   p.a_by_token = 1;
   p.K = b.H;
@@ -601,6 +622,10 @@ static DecodeParams down_params(const BindingImpl& b) {
   p.KFS = (int)b.kfs2;
   p.y = b.y;
   p.y_stride = b.H;
+  if (a4_nv(b.afmt)) {  // h's activation scale, one per expert
+    p.aglobal = b.a2_global;
+    p.aglobal_per_expert = 1;
+  }
   return p;
 }
 
@@ -664,6 +689,9 @@ int launch_decode1(const BindingImpl& b, hipStream_t s) {
   if (a8_bf16(b.wfmt, b.afmt))
     return b.gated ? launch_decode_t<B12X_WEIGHT_NVFP4, kActRt, DMODE_SILU, 4>(b, p, s)
                    : launch_decode_t<B12X_WEIGHT_NVFP4, kActRt, DMODE_RELU2, 2>(b, p, s);
+  if (a4_nv(b.afmt))  // an NVFP4 block of h (16 columns) = one gate/up pair
+    return b.gated ? launch_decode_t<B12X_WEIGHT_NVFP4, kActNvRt, DMODE_SILU, 2>(b, p, s)
+                   : launch_decode_t<B12X_WEIGHT_NVFP4, kActNvRt, DMODE_RELU2, 2>(b, p, s);
   if (b.gated) return launch_decode_fmt<DMODE_SILU, 2>(b, p, s);
   return launch_decode_fmt<DMODE_RELU2, 2>(b, p, s);
 }

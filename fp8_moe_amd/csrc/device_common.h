@@ -31,6 +31,14 @@ constexpr int kActRt = 4;
 // activations on the grouped path): the f16 operand path of kActF16 with the
 // round-trip epilogue of kActRt.
 constexpr int kActF16Rt = 5;
+// NVFP4 activations with NVFP4 weights (W4A4): the operands are the exact
+// values E2M1 * E4M3 of the NVFP4 round trips (at most 6 significant bits, so
+// exact in bf16 and in f16), the per-tensor activation scale is applied to
+// the fp32 accumulator with the weights' one, and the gate/up epilogue stores
+// h as its own NVFP4 round trip (against the expert's activation scale).
+// kActNvRt: bf16 operand path; kActF16NvRt: f16 operand path (grouped GEMM).
+constexpr int kActNvRt = 6;
+constexpr int kActF16NvRt = 7;
 
 // Raw buffer loads (CDNA buffer resource, stride 0).  A byte offset at or
 // past the record count returns zeros without a memory access, so a guarded
@@ -163,6 +171,48 @@ __device__ __forceinline__ float e4m3_value(uint32_t c) {
 // bf16 above its subnormal range, 2^-133).
 __device__ __forceinline__ uint32_t mx_roundtrip_bf16(float v, int s) {
   return bf16_rne(ldexpf(e4m3_value(e4m3_encode_scaled(f32_bits(v), s)), s));
+}
+
+// Largest value over the 16 lanes of this lane's DPP row (lanes 16r .. 16r+15),
+// in every lane of the row: max with the lane ^ 1 and ^ 2 (quad permutes),
+// then with the mirrored lane in the half row and in the row.  VALU only.
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, bits_f32((uint32_t)__builtin_amdgcn_update_dpp(0, (int)f32_bits(v), 0xB1, 0xF, 0xF, false)));
+  v = fmaxf(v, bits_f32((uint32_t)__builtin_amdgcn_update_dpp(0, (int)f32_bits(v), 0x4E, 0xF, 0xF, false)));
+  v = fmaxf(v, bits_f32((uint32_t)__builtin_amdgcn_update_dpp(0, (int)f32_bits(v), 0x141, 0xF, 0xF, false)));
+  v = fmaxf(v, bits_f32((uint32_t)__builtin_amdgcn_update_dpp(0, (int)f32_bits(v), 0x140, 0xF, 0xF, false)));
+  return v;
+}
+
+// NVFP4 block scale of a 16-block with largest magnitude amax against the
+// per-tensor scale g: the E4M3 value nearest to amax / (6 g) (ties to even,
+// saturating at 448), both quotients rounded once in fp32.
+__device__ __forceinline__ float nv_block_scale(float amax, float g) {
+  return e4m3_value(e4m3_encode_scaled(f32_bits(__fdiv_rn(amax, 6.0f * g)), 0));
+}
+
+// E2M1 value nearest to q, ties to even codes, saturating at +-6.
+__device__ __forceinline__ float e2m1_rne_sat(float q) {
+  const float a = fabsf(q);
+  float r;
+  if (a <= 0.25f) r = 0.0f;
+  else if (a < 0.75f) r = 0.5f;
+  else if (a <= 1.25f) r = 1.0f;
+  else if (a < 1.75f) r = 1.5f;
+  else if (a <= 2.5f) r = 2.0f;
+  else if (a < 3.5f) r = 3.0f;
+  else if (a <= 5.0f) r = 4.0f;
+  else r = 6.0f;
+  return copysignf(r, q);
+}
+
+// E2M1 * E4M3 value of the NVFP4 round trip of v in a block with scale s
+// (without the per-tensor scale g, which the GEMM applies): the E2M1 value
+// nearest to v / (s g), times s; exact in fp32, bf16 and f16.  A block whose
+// scale is 0 rounds to 0.
+__device__ __forceinline__ float nv_roundtrip(float v, float s, float g) {
+  const float u = s * g;
+  return u > 0.0f ? e2m1_rne_sat(__fdiv_rn(v, u)) * s : 0.0f;
 }
 
 // E8M0 scale code as the fp32 whose exponent field is the code; the gfx950

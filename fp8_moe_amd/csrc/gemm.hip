@@ -54,6 +54,12 @@ struct GemmParams {
   const uint8_t* bcodes;
   const uint8_t* bscales;
   const float* bglobal;
+  // NVFP4 activations: activation scale multiplied into the accumulator with
+  // bglobal (x: one value, aglobal_per_expert = 0; h: one per expert), and the
+  // scale of each expert's h for the gate/up epilogue's requantization
+  const float* aglobal;
+  int aglobal_per_expert;
+  const float* hglobal;
   int64_t b_codes_expert;
   int64_t b_scales_expert;
   int NF;
@@ -87,9 +93,11 @@ template <int WF, int AF, int MODE, int NFW>
 __global__ __launch_bounds__(kGemmThreads, 1) void moe_gemm_kernel(const GemmParams p) {
   constexpr bool A8 = AF == B12X_ACT_MXFP8;
   // f16 activations x NVFP4 weights dequantized to f16
-  constexpr bool F16 = AF == kActF16 || AF == kActF16Rt;
+  constexpr bool F16 = AF == kActF16 || AF == kActF16Rt || AF == kActF16NvRt;
   // MXFP8 round trips as activations (NVFP4 x MXFP8): h stored as its own round trip
   constexpr bool RT = AF == kActRt || AF == kActF16Rt;
+  // NVFP4 round trips as activations (W4A4): h stored as its own NVFP4 round trip
+  constexpr bool NVRT = AF == kActNvRt || AF == kActF16NvRt;
   static_assert(!F16 || WF == B12X_WEIGHT_NVFP4, "f16 activations run with NVFP4 weights");
   using OpT = std::conditional_t<F16, f16x8, bf16x8>;  // 16-bit MFMA operand type
   constexpr int ROWB = A8 ? 144 : 272;  // LDS bytes per A row: 128 K elements + 16 bytes of skew
@@ -141,7 +149,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void moe_gemm_kernel(const GemmPar
     const int nnf = max(0, min(NFW, p.NF - f0));
     const uint8_t* bcodes = p.bcodes + (int64_t)e * p.b_codes_expert;
     const uint8_t* bscales = p.bscales + (int64_t)e * p.b_scales_expert;
-    const float gsc = p.bglobal ? p.bglobal[e] : 1.0f;
+    float gsc = p.bglobal ? p.bglobal[e] : 1.0f;
+    if (p.aglobal) gsc *= p.aglobal[p.aglobal_per_expert ? e : 0];
 
     // ---- buffer resources: every load below is unconditional; a row, K chunk
     // or fragment outside the problem gets an out-of-range offset (zeros)
@@ -537,7 +546,21 @@ __global__ __launch_bounds__(kGemmThreads, 1) void moe_gemm_kernel(const GemmPar
                 hv[q] = z > 0.f ? z * z : 0.f;
               }
             }
-            if constexpr (RT) {
+            if constexpr (NVRT) {
+              // NVFP4 blocks of 16 columns = one column block (the 16 lanes of
+              // a row); h is the bf16 value E2M1 * E4M3 of its round trip, the
+              // expert's activation scale is applied by the down GEMM
+              const float gh = p.hglobal[e];
+#pragma unroll
+              for (int q = 0; q < NH; ++q) {
+                if (q < nh) {
+                  float m = fabsf(hv[q]);
+                  m = row16_max(m);
+                  const float sc = nv_block_scale(m, gh);
+                  p.h16[row * p.h_stride + hcol0 + 16 * q + r16] = (uint16_t)bf16_rne(nv_roundtrip(hv[q], sc, gh));
+                }
+              }
+            } else if constexpr (RT) {
               // MXFP8 blocks of 32 columns = column blocks (2b, 2b+1); h is the
               // bf16 value of its round trip
               static_assert(NH % 2 == 0, "whole MXFP8 blocks per wave");
@@ -545,10 +568,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void moe_gemm_kernel(const GemmPar
               for (int blk = 0; blk < NH / 2; ++blk) {
                 if (2 * blk < nh) {
                   float m = fmaxf(fabsf(hv[2 * blk]), fabsf(hv[2 * blk + 1]));
-                  m = fmaxf(m, __shfl_xor(m, 1));
-                  m = fmaxf(m, __shfl_xor(m, 2));
-                  m = fmaxf(m, __shfl_xor(m, 4));
-                  m = fmaxf(m, __shfl_xor(m, 8));
+                  m = row16_max(m);
                   const int sx = mx_scale_exp(f32_bits(m));
                   const int64_t col = hcol0 + 32 * blk + r16;
                   p.h16[row * p.h_stride + col] = (uint16_t)mx_roundtrip_bf16(hv[2 * blk], sx);
@@ -565,10 +585,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void moe_gemm_kernel(const GemmPar
               for (int blk = 0; blk < NH / 2; ++blk) {
                 if (2 * blk < nh) {
                   float m = fmaxf(fabsf(hv[2 * blk]), fabsf(hv[2 * blk + 1]));
-                  m = fmaxf(m, __shfl_xor(m, 1));
-                  m = fmaxf(m, __shfl_xor(m, 2));
-                  m = fmaxf(m, __shfl_xor(m, 4));
-                  m = fmaxf(m, __shfl_xor(m, 8));
+                  m = row16_max(m);
                   const int sx = mx_scale_exp(f32_bits(m));
                   const int64_t col = hcol0 + 32 * blk + r16;
                   p.h8[row * p.h_stride + col] = (uint8_t)e4m3_encode_scaled(f32_bits(hv[2 * blk]), sx);
@@ -620,6 +637,7 @@ static int dispatch(const BindingImpl& b, const GemmParams& p, int64_t max_work,
   if constexpr (MODE != MODE_DOWN) {
     // the scaled f16 copy of a (of its MXFP8 round trips with MXFP8 activations), else the
     // bf16 copy of the round trips
+    if (p.a_exp && a4_nv(b.afmt)) return launch_gemm_t<B12X_WEIGHT_NVFP4, kActF16NvRt, MODE>(p, max_work, s);
     if (p.a_exp && a8_bf16(b.wfmt, b.afmt)) return launch_gemm_t<B12X_WEIGHT_NVFP4, kActF16Rt, MODE>(p, max_work, s);
     if (p.a_exp) return launch_gemm_t<B12X_WEIGHT_NVFP4, kActF16, MODE>(p, max_work, s);
     if (a8_bf16(b.wfmt, b.afmt)) return launch_gemm_t<B12X_WEIGHT_NVFP4, kActRt, MODE>(p, max_work, s);
@@ -650,7 +668,12 @@ int launch_gemm1(const BindingImpl& b, hipStream_t s) {
     p.a_bytes = b.T * b.Hp * 2;
     p.a_exp = (const int32_t*)b.xs;
   }
-  // (NVFP4 x MXFP8 takes the same route: the copy then holds a's MXFP8 round trips)
+  // (NVFP4 x MXFP8 and NVFP4 x NVFP4 take the same route: the copy then holds a's round trips)
+  if (a4_nv(b.afmt)) {
+    p.aglobal = b.a13_global;  // x's activation scale, one value
+    p.aglobal_per_expert = 0;
+    p.hglobal = b.a2_global;   // h is requantized against its expert's scale
+  }
   p.sorted = b.sorted;
   p.k_top = b.k;
   p.n_pairs = b.T * b.k;
@@ -701,6 +724,10 @@ int launch_gemm2(const BindingImpl& b, hipStream_t s) {
   p.KFS = (int)b.kfs2;
   p.out16 = b.y16;
   p.out_stride = b.H;
+  if (a4_nv(b.afmt)) {  // h's activation scale, one per expert
+    p.aglobal = b.a2_global;
+    p.aglobal_per_expert = 1;
+  }
   const int64_t max_work = b.max_tiles * p.n_ntiles;
   return dispatch<MODE_DOWN>(b, p, max_work, s);
 }

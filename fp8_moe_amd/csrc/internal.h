@@ -44,6 +44,8 @@ constexpr int kDecodePairs = 256;     // T*k at or below which the decode path r
 // exact bf16 values multiply the NVFP4 weights on the bf16 MFMA.
 inline bool a8_native(int wfmt, int afmt) { return afmt == B12X_ACT_MXFP8 && wfmt == B12X_WEIGHT_MXFP4; }
 inline bool a8_bf16(int wfmt, int afmt) { return afmt == B12X_ACT_MXFP8 && wfmt == B12X_WEIGHT_NVFP4; }
+// NVFP4 activations (NVFP4 weights only): operands are the exact NVFP4 round trips
+inline bool a4_nv(int afmt) { return afmt == B12X_ACT_NVFP4; }
 // decode synchronization region: int32 call epoch, int32 status, then one
 // uint64 completion flag per (touched expert slot, gate/up group of 2 fragments)
 constexpr int kDecodeEpochOffset = 0;
@@ -113,6 +115,8 @@ struct BindingImpl {
   const uint8_t* w2_codes;
   const uint8_t* w2_scales;
   const float* w2_global;
+  const float* a13_global;  // NVFP4 activations: scale of x [1] and of each expert's h [E]
+  const float* a2_global;
   int32_t* counts;
   int32_t* offsets;
   int32_t* poff;
@@ -150,6 +154,8 @@ int launch_quant_rows(const uint16_t* x, int64_t rows, int64_t cols, int64_t str
                       int64_t code_stride, uint8_t* scales, int64_t scale_stride, hipStream_t s);
 int launch_mx_roundtrip_rows(const uint16_t* x, int64_t rows, int64_t cols, int64_t stride, uint16_t* out,
                              int64_t out_stride, hipStream_t s);
+int launch_nv_roundtrip_rows(const uint16_t* x, int64_t rows, int64_t cols, int64_t stride, const float* g,
+                             uint16_t* out, int64_t out_stride, int32_t* exps, bool f16, hipStream_t s);
 int launch_f16_rows(const uint16_t* x, int64_t rows, int64_t cols, int64_t stride, uint16_t* out,
                     int64_t out_stride, int32_t* exps, bool rt, hipStream_t s);
 int launch_gemm1(const BindingImpl& b, hipStream_t s);

@@ -62,6 +62,61 @@ int launch_mx_roundtrip_rows(const uint16_t* x, int64_t rows, int64_t cols, int6
   return (int)hipGetLastError();
 }
 
+// NVFP4 round trips of bf16 rows against the per-tensor activation scale
+// g[0] (NVFP4 activations with NVFP4 weights): per block of 16, the E4M3
+// scale s nearest to amax / (6 g) and each value's E2M1 code nearest to
+// v / (s g); out holds E2M1 * s (exact), the scale g is left to the GEMM.
+// Two threads per block of 16 (8 values each).  F16: f16 values plus a row
+// exponent of 0 for the f16 operand path of the grouped GEMM; else bf16.
+template <bool F16>
+__global__ __launch_bounds__(256) void nv_roundtrip_rows_kernel(const uint16_t* __restrict__ x, int64_t rows,
+                                                                int64_t blocks_per_row, int64_t stride,
+                                                                const float* __restrict__ g,
+                                                                uint16_t* __restrict__ out, int64_t out_stride,
+                                                                int32_t* __restrict__ exps) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t blk_all = idx >> 1;
+  if (blk_all >= rows * blocks_per_row) return;
+  const int part = (int)(idx & 1);
+  const int64_t r = blk_all / blocks_per_row, blk = blk_all % blocks_per_row;
+  const uint4 v = *(const uint4*)(x + r * stride + blk * 16 + 8 * part);
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  uint32_t amax = 0;  // bf16 magnitude bits compare like the values
+#pragma unroll
+  for (int i = 0; i < 4; ++i) amax = max(amax, max(w[i] & 0x7FFFu, (w[i] >> 16) & 0x7FFFu));
+  amax = max(amax, (uint32_t)__shfl_xor((int)amax, 1));
+  const float gs = g[0];
+  const float sc = nv_block_scale(bits_f32(amax << 16), gs);
+  uint32_t o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float lo = nv_roundtrip(bf16_to_f32(w[i] & 0xFFFFu), sc, gs);
+    const float hi = nv_roundtrip(bf16_to_f32(w[i] >> 16), sc, gs);
+    if constexpr (F16)
+      o[i] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)lo) |
+             ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)hi) << 16);
+    else
+      o[i] = bf16_rne(lo) | (bf16_rne(hi) << 16);
+  }
+  *(uint4*)(out + r * out_stride + blk * 16 + 8 * part) = make_uint4(o[0], o[1], o[2], o[3]);
+  if (F16 && blk == 0 && part == 0) exps[r] = 0;
+}
+
+int launch_nv_roundtrip_rows(const uint16_t* x, int64_t rows, int64_t cols, int64_t stride, const float* g,
+                             uint16_t* out, int64_t out_stride, int32_t* exps, bool f16, hipStream_t s) {
+  const int64_t bpr = cols / 16;
+  const int64_t total = rows * bpr;
+  if (total == 0) return 0;
+  const dim3 grid((unsigned)((2 * total + 255) / 256));
+  if (f16)
+    hipLaunchKernelGGL(nv_roundtrip_rows_kernel<true>, grid, dim3(256), 0, s, x, rows, bpr, stride, g, out,
+                       out_stride, exps);
+  else
+    hipLaunchKernelGGL(nv_roundtrip_rows_kernel<false>, grid, dim3(256), 0, s, x, rows, bpr, stride, g, out,
+                       out_stride, exps);
+  return (int)hipGetLastError();
+}
+
 int launch_quant_rows(const uint16_t* x, int64_t rows, int64_t cols, int64_t stride, uint8_t* codes,
                       int64_t code_stride, uint8_t* scales, int64_t scale_stride, hipStream_t s) {
   const int64_t bpr = cols / 32;

@@ -78,7 +78,7 @@ WORKLOADS = {
     "skew": Workload("skew", 256, 7168, 2048, 8, True, "nvfp4", "bf16", (8192,), routing="zipf"),
 }
 
-_STREAMS = {"x": 1, "w13": 2, "w2": 3, "ids": 4, "weights": 5}
+_STREAMS = {"x": 1, "w13": 2, "w2": 3, "ids": 4, "weights": 5, "act_scales": 6}
 
 
 def _gen(wl, stream, tokens, device, salt=0):
@@ -160,7 +160,8 @@ def _encode_nvfp4(w):
 def make_weights(wl, device="cpu", std=0.02):
     """Packed source-format weights as a dict of tensors on ``device``:
     w13_codes [E, N1, H/2], w13_scales [E, N1, H/G], w2_codes [E, H, I/2],
-    w2_scales [E, H, I/G], w13_global / w2_global [E] (NVFP4 only)."""
+    w2_scales [E, H, I/G], w13_global / w2_global [E] (NVFP4 only), and for NVFP4
+    weights the activation scales a13_global [1] and a2_global [E]."""
     out = {}
     for name, (n, k) in (("w13", (wl.n13, wl.H)), ("w2", (wl.H, wl.I))):
         g = _gen(wl, name, 0, device)
@@ -176,6 +177,15 @@ def make_weights(wl, device="cpu", std=0.02):
         out[name + "_codes"] = codes
         out[name + "_scales"] = scales
         out[name + "_global"] = glob if wl.weight_format == "nvfp4" else None
+    if wl.weight_format == "nvfp4":
+        # activation scales a checkpoint would carry for NVFP4 activations (its input
+        # scales): x ~ N(0, 1) rows, so a block maximum of about 8 maps to the largest
+        # block scale; h ~ (std^2 H) times O(1) factors, one scale per expert, spread
+        # by a seeded factor in [0.75, 1.25]
+        g = _gen(wl, "act_scales", 0, "cpu")
+        out["a13_global"] = torch.tensor([8.0 / (6 * 448)], dtype=torch.float32, device=device)
+        spread = 0.75 + 0.5 * torch.rand(wl.E, generator=g, dtype=torch.float32)
+        out["a2_global"] = (spread * (16.0 * std * std * wl.H / (6 * 448))).to(torch.float32).to(device)
     return out
 
 
@@ -208,6 +218,8 @@ def oracle_weights_kwargs(wdict, experts=None):
     for key, t in wdict.items():
         if t is None:
             res[key] = None
+        elif key == "a13_global":  # one value
+            res[key] = t.cpu().numpy()[0]
         elif experts is None or t.dim() == 1:
             res[key] = t.cpu().numpy()
         else:

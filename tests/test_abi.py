@@ -58,6 +58,8 @@ def test_support_matrix():
     assert fm.is_supported(mx_r, 2, 16, "mxfp8", "relu2")
     assert fm.is_supported(nv_g, 2, 16, "bf16", "silu")
     assert fm.is_supported(nv_g, 2, 16, "mxfp8", "silu")          # NVFP4 x MXFP8 through bf16 round trips
+    assert fm.is_supported(nv_g, 2, 16, "nvfp4", "silu")          # NVFP4 x NVFP4 (W4A4)
+    assert not fm.is_supported(mx_g, 2, 16, "nvfp4", "silu")      # NVFP4 activations need NVFP4 weights
     assert not fm.is_supported(mx_g, 2, 16, "bf16", "relu2")      # gated weights need SiLU
     assert not fm.is_supported(mx_g, 0, 16, "bf16", "silu")
 
@@ -123,6 +125,11 @@ def test_bind_validation_on_host():
     ex2 = fm.Experts(other, ctypes.c_void_p(0x7000000), other.prepared_bytes)
     assert _bind_status(p, ex2, 16)[0] == 6                                  # layout mismatch
     assert fm.lib().b12x_moe_run(None, None) == 1
+    # NVFP4 activations need the activation scales among the prepared weights
+    p4 = fm.plan(other, 2, 16, "nvfp4")
+    assert _bind_status(p4, ex2, 16)[0] == 1
+    ex3 = fm.Experts(other, ctypes.c_void_p(0x7000000), other.prepared_bytes, 1)
+    assert _bind_status(p4, ex3, 16)[0] == 0
 
 
 def test_status_strings():

@@ -72,6 +72,10 @@ SMALL = [
     ("nv_a8_gated", 4, 256, 128, 2, True, "nvfp4", "mxfp8", 200),
     ("nv_a8_relu2_ragged", 5, 160, 96, 3, False, "nvfp4", "mxfp8", 120),
     ("nv_a8_mid", 16, 1024, 512, 4, True, "nvfp4", "mxfp8", 256),
+    # NVFP4 weights x NVFP4 activations (W4A4), grouped path
+    ("nv_a4_gated", 4, 256, 128, 2, True, "nvfp4", "nvfp4", 200),
+    ("nv_a4_relu2_ragged", 5, 160, 96, 3, False, "nvfp4", "nvfp4", 120),
+    ("nv_a4_mid", 16, 1024, 512, 4, True, "nvfp4", "nvfp4", 256),
 ]
 
 
@@ -254,6 +258,9 @@ DECODE_EDGE = [
     # and 68 gate/up groups per expert
     ("nv_a8_gated_decode", 8, 256, 128, 2, True, "nvfp4", "mxfp8", 10, "uniform"),
     ("nv_a8_relu2_decode", 8, 288, 224, 4, False, "nvfp4", "mxfp8", 30, "one_expert"),
+    ("nv_a4_gated_decode", 8, 256, 128, 2, True, "nvfp4", "nvfp4", 10, "uniform"),
+    ("nv_a4_relu2_decode", 8, 288, 224, 4, False, "nvfp4", "nvfp4", 30, "one_expert"),
+    ("nv_a4_dups_dropped", 16, 256, 128, 4, True, "nvfp4", "nvfp4", 20, "bad_dups"),
     ("separate_long_k", 8, 2304, 128, 2, True, "mxfp4", "bf16", 6, "uniform"),
     ("separate_many_groups", 8, 256, 1088, 2, True, "nvfp4", "bf16", 5, "uniform"),
 ]
@@ -280,7 +287,7 @@ def test_decode_edge_cases(case):
     b, out = pr.model.bind(x, ids, tw)
     assert fm.binding_query(b, "path") == 2
     fused = afmt == "bf16" and not name.startswith("separate")
-    assert fm.binding_query(b, "num_stages") == (2 if fused else 3 + (afmt == "mxfp8"))
+    assert fm.binding_query(b, "num_stages") == (2 if fused else 3 + (afmt != "bf16"))
     out.fill_(1.0)
     fm.run(b)
     torch.cuda.synchronize()
@@ -290,6 +297,30 @@ def test_decode_edge_cases(case):
     assert ok, (rel_fro, rel_max)
     if kind == "all_bad":
         assert torch.all(out == 0)
+
+
+@pytest.mark.parametrize("T,rows", [(8, None), (4096, [0, 2047, 4095])])
+def test_w4a4_at_prefill_shape(T, rows):
+    """NVFP4 activations on the prefill layer's NVFP4 weights (E=128, H=4096,
+    I=1536, top-8): T=8 on the decode path (every row), T=4096 on the grouped
+    path (sampled rows)."""
+    import dataclasses
+    print(f"w4a4 prefill shape T={T} rows={rows}", flush=True)
+    wl = dataclasses.replace(synth.WORKLOADS["prefill"], act_format="nvfp4")
+    _PROBLEMS.clear()
+    torch.cuda.empty_cache()
+    pr = Problem(wl, 4096)
+    x, ids, tw = _inputs(wl, T)
+    out, b = pr.run(x, ids, tw)
+    torch.cuda.synchronize()
+    import fp8_moe_amd as fm
+    assert fm.binding_query(b, "path") == (2 if T * wl.k <= 256 else 1)
+    ref = pr.oracle(x, ids, tw, rows)
+    got = out if rows is None else out[rows]
+    rel_fro, rel_max, ok = compare(got, ref)
+    print(f"  rel_fro={rel_fro:.3e} rel_max={rel_max:.3e}", flush=True)
+    del pr
+    assert ok, (rel_fro, rel_max)
 
 
 def test_nvfp4_rows_of_extreme_magnitude():
