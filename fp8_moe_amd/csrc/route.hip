@@ -35,21 +35,36 @@ __global__ __launch_bounds__(kRouteThreads) void route_count_kernel(const int32_
   for (int e = threadIdx.x; e < E; e += kRouteThreads) chunk[(int64_t)blockIdx.x * E + e] = hist[e];
 }
 
-// Block-wide exclusive scan of one int per thread (blockDim.x = 1024).
-__device__ int block_exclusive_scan(int v, int* lds, int* total) {
-  const int tid = threadIdx.x;
-  lds[tid] = v;
-  __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {
-    const int add = tid >= off ? lds[tid - off] : 0;
-    __syncthreads();
-    lds[tid] += add;
-    __syncthreads();
+// Block-wide exclusive scans of three ints per thread (blockDim.x = 1024):
+// inclusive scans within each wave, then the wave totals in LDS (one
+// barrier).  ex and tot receive the exclusive prefixes and the block totals.
+__device__ void block_exclusive_scan3(const int (&v)[3], int (*wsum)[3], int (&ex)[3], int (&tot)[3]) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int incl[3] = {v[0], v[1], v[2]};
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+#pragma unroll
+    for (int q = 0; q < 3; ++q) {
+      const int t = __shfl_up(incl[q], off);
+      if (lane >= off) incl[q] += t;
+    }
   }
-  const int incl = lds[tid];
-  *total = lds[1023];
+  if (lane == 63) {
+#pragma unroll
+    for (int q = 0; q < 3; ++q) wsum[wave][q] = incl[q];
+  }
   __syncthreads();
-  return incl - v;
+#pragma unroll
+  for (int q = 0; q < 3; ++q) {
+    int before = 0, all = 0;
+    for (int w = 0; w < 16; ++w) {
+      const int x = wsum[w][q];
+      before += w < wave ? x : 0;
+      all += x;
+    }
+    ex[q] = before + incl[q] - v[q];
+    tot[q] = all;
+  }
 }
 
 // One workgroup of 1024 threads, thread e = expert e.
@@ -57,14 +72,20 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(int E, int n_chunks, i
                                                           int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
                                                           int32_t* __restrict__ poff, int32_t* __restrict__ sorted,
                                                           int32_t* __restrict__ tiles, int32_t* __restrict__ ntiles) {
-  __shared__ int lds[1024];
+  __shared__ int wsum[16][3];
   const int e = threadIdx.x;
   int cnt = 0;
   if (e < E) {
-    for (int c = 0; c < n_chunks; ++c) {  // chunk counts -> exclusive per-chunk bases
-      const int h = chunk[(int64_t)c * E + e];
-      chunk[(int64_t)c * E + e] = cnt;
-      cnt += h;
+    // chunk counts -> exclusive per-chunk bases, eight chunks' loads in flight at a time
+    for (int c0 = 0; c0 < n_chunks; c0 += 8) {
+      int h[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) h[u] = c0 + u < n_chunks ? chunk[(int64_t)(c0 + u) * E + e] : 0;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (c0 + u < n_chunks) chunk[(int64_t)(c0 + u) * E + e] = cnt;
+        cnt += h[u];
+      }
     }
   }
   const int padded = (cnt + kRowPad - 1) / kRowPad * kRowPad;
@@ -73,10 +94,11 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(int E, int n_chunks, i
   constexpr int kTileBlocks = kTileRows / kRowPad;
   const int nb = padded / kRowPad;
   const int n_t = (nb + kTileBlocks - 1) / kTileBlocks;
-  int tot_cnt, tot_pad, tot_tiles;
-  const int off = block_exclusive_scan(cnt, lds, &tot_cnt);
-  const int poffe = block_exclusive_scan(padded, lds, &tot_pad);
-  const int toff = block_exclusive_scan(n_t, lds, &tot_tiles);
+  const int vals[3] = {cnt, padded, n_t};
+  int ex[3], tot[3];
+  block_exclusive_scan3(vals, wsum, ex, tot);
+  const int off = ex[0], poffe = ex[1], toff = ex[2];
+  const int tot_cnt = tot[0], tot_pad = tot[1], tot_tiles = tot[2];
   if (e < E) {
     counts[e] = cnt;
     offsets[e] = off;
@@ -98,8 +120,8 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(int E, int n_chunks, i
 
 // Stable scatter: each wave takes 256 consecutive pairs of the chunk in four
 // rounds of 64; a lane's rank among equal experts of its round comes from
-// ballots (lanes below it with the same expert), and LDS counters carry the
-// count across rounds.  Waves are then ordered by a prefix over their counts.
+// ballots (the lanes below it with the same expert, found with one ballot per
+// bit of the expert id), and LDS counters carry the count across rounds.  Waves are then ordered by a prefix over their counts.
 __global__ __launch_bounds__(kRouteThreads) void route_scatter_kernel(const int32_t* __restrict__ ids, int64_t P,
                                                                        int E, const int32_t* __restrict__ chunk,
                                                                        const int32_t* __restrict__ poff,
@@ -112,6 +134,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_scatter_kernel(const int3
   const int64_t base = (int64_t)blockIdx.x * kRouteChunk + wave * 256;
   int my_e[4], my_rank[4];
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const int id_bits = E > 1 ? 32 - __builtin_clz((unsigned)(E - 1)) : 0;  // bits of the largest id
   for (int r = 0; r < 4; ++r) {
     const int64_t p = base + r * 64 + lane;
     int e = p < P ? ids[p] : -1;
@@ -119,16 +142,23 @@ __global__ __launch_bounds__(kRouteThreads) void route_scatter_kernel(const int3
     if (!v) e = -1;
     my_e[r] = e;
     my_rank[r] = -1;
-    uint64_t pending = __ballot(v);
-    while (pending) {
-      const int leader = __builtin_ctzll(pending);
-      const int le = __shfl(e, leader);
-      const uint64_t same = __ballot(e == le);
-      const int before = cnt[wave][le];
-      if (e == le) my_rank[r] = before + __builtin_popcountll(same & below);
-      if (lane == leader) cnt[wave][le] = before + __builtin_popcountll(same);
-      pending &= ~same;
+    // lanes with this lane's expert: the valid lanes that agree with it on
+    // every bit of the id (one ballot per bit)
+    uint64_t same = __ballot(v);
+    for (int b = 0; b < id_bits; ++b) {
+      const bool bit = (e >> b) & 1;
+      const uint64_t ones = __ballot(bit);
+      same &= bit ? ones : ~ones;
     }
+    if (v) {
+      // every lane of the group reads the counter, then the group's lowest
+      // lane advances it (the wave's LDS reads and writes run in program order)
+      const int before = cnt[wave][e];
+      my_rank[r] = before + __builtin_popcountll(same & below);
+      __builtin_amdgcn_wave_barrier();
+      if ((same & below) == 0) cnt[wave][e] = before + __builtin_popcountll(same);
+    }
+    __builtin_amdgcn_wave_barrier();
   }
   __syncthreads();
   for (int r = 0; r < 4; ++r) {
