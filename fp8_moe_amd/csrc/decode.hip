@@ -1,23 +1,31 @@
 // Small-batch decode path of the fused MoE (b12x README "What's in here": the
-// micro-kernel decode path of fused_moe).  For T*k <= kDecodePairs three
-// launches replace the routing buffers and the grouped GEMMs; every touched
+// micro-kernel decode path of fused_moe).  For T*k <= kDecodePairs these
+// kernels replace the routing buffers and the grouped GEMMs; every touched
 // expert's weights are read exactly once:
-//   D1 (gate/up) and D2 (down): a grid of as many workgroups as the chip
-//      holds at once.  Every workgroup reads topk_ids into LDS, finds the
-//      touched experts (a bitmap and its prefix popcounts) and takes an even,
-//      contiguous share of the items (touched expert in ascending id, group of
-//      FR weight fragments); for each expert of its share it builds that
-//      expert's pair list (stable by pair id).  Its 4 waves split K, keep
-//      their share of the activation rows in registers and take the groups
-//      one at a time (the other resident waves cover the load latency);
-//      partial sums are added in LDS in a fixed wave order.  D1
-//      applies SiLU-gated or ReLU^2 and writes h by pair id (bf16, or MXFP8
-//      codes and scales for W4A8); D2 writes y by pair id in fp32.
+//   D1 (gate/up) and D2 (down): a grid of at most as many workgroups as the
+//      chip holds at once.  Every workgroup reads topk_ids into LDS, finds the
+//      touched experts (a bitmap and its prefix popcounts) and takes its share
+//      of the items (touched expert in ascending id, group of FR weight
+//      fragments): one contiguous share, or chunks of items dealt round-robin
+//      when there are at least two per workgroup; for each expert of its share
+//      it builds that expert's pair list (stable by pair id).  Its 4 waves
+//      split K, keep their share of the activation rows in registers and take
+//      the groups one at a time (the other resident waves cover the load
+//      latency); wave 0 adds the other waves' partial sums from LDS to its own
+//      in a fixed wave order.  D1 applies SiLU-gated or ReLU^2 and writes h by
+//      pair id (bf16, MXFP8 codes and scales for W4A8, or the bf16 value of an
+//      MXFP8 / NVFP4 round trip with NVFP4 weights); D2 writes y by pair id in
+//      fp32.
+//   With 16-bit activations D1 and D2 run as one kernel: each workgroup does
+//      its gate/up share, publishes each finished group with a completion
+//      flag, then does its down share, waiting (bounded) for the flags of the
+//      gate/up groups of each expert it reaches.  Other formats launch D1 and
+//      D2 separately.
 //   D3 (combine): out[t] = sum_j w[t,j] * y[t*k+j] in ascending slot order,
 //      fp32, one bf16 rounding (the grouped path's combine kernel, reading y
 //      by pair id).
-// No atomics on data and no cross-workgroup synchronization: the result does
-// not depend on scheduling or on the grid size.
+// No atomics on data: every value is computed by one workgroup in a fixed
+// order, so the result does not depend on scheduling or on the grid size.
 #include "device_common.h"
 
 namespace b12x {
@@ -182,7 +190,10 @@ __device__ __forceinline__ void decode_items(const DecodeParams& p, DecodeLds& L
   uint32_t* const s_bits = L.bits;
   int* const s_wpre = L.wpre;
   int* const s_info = L.info;
-  auto s_red = [&](int par, int w, int j) -> f32x4& { return red[((par * 4 + w) * FR + j) * 64 + (threadIdx.x & 63)]; };
+  // split-K partials of waves 1..3 (wave 0 keeps its own in registers and sums)
+  auto s_red = [&](int par, int w, int j) -> f32x4& {
+    return red[((par * 3 + (w - 1)) * FR + j) * 64 + (threadIdx.x & 63)];
+  };
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -348,14 +359,16 @@ __device__ __forceinline__ void decode_items(const DecodeParams& p, DecodeLds& L
           }
         }
       }
+      if (wave != 0) {
 #pragma unroll
-      for (int j = 0; j < FR; ++j) s_red(par, wave, j) = acc[j];
+        for (int j = 0; j < FR; ++j) s_red(par, wave, j) = acc[j];
+      }
       __syncthreads();
       if (wave == 0) {
         f32x4 v[FR];
 #pragma unroll
         for (int j = 0; j < FR; ++j) {
-          v[j] = s_red(par, 0, j);
+          v[j] = acc[j];
 #pragma unroll
           for (int w = 1; w < 4; ++w) v[j] += s_red(par, w, j);
         }
@@ -480,7 +493,7 @@ __device__ __forceinline__ void decode_items(const DecodeParams& p, DecodeLds& L
 template <int WF, int AF, int MODE, int FR, int KW>
 __global__ __launch_bounds__(kDecThreads) void decode_kernel(const DecodeParams p) {
   __shared__ DecodeLds L;
-  __shared__ f32x4 s_red[2 * 4 * FR * 64];
+  __shared__ f32x4 s_red[2 * 3 * FR * 64];
   const int n_touched = decode_prep(p, L.ids, L.bits, L.wpre);
   decode_items<WF, AF, MODE, FR, KW, 0>(p, L, s_red, n_touched, 0);
 }
@@ -495,7 +508,7 @@ template <int WF, int MODE1, int FR1, int KW1, int FR2, int KW2>
 __global__ __launch_bounds__(kDecThreads) void decode_fused_kernel(const DecodeParams p1, const DecodeParams p2) {
   constexpr int FRM = FR1 > FR2 ? FR1 : FR2;
   __shared__ DecodeLds L;
-  __shared__ f32x4 s_red[2 * 4 * FRM * 64];
+  __shared__ f32x4 s_red[2 * 3 * FRM * 64];
   if (blockIdx.x == 0 && threadIdx.x == 0)
     __hip_atomic_store(p1.status, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const uint64_t tag = flag_tag(p1.epoch);
