@@ -222,8 +222,9 @@ def quantize_nvfp4(v, global_scale):
     E2M1_RNE_sat(v / (s g)); a block whose scale rounds to 0 takes codes 0.
     The quotients decide integer codes, so they are taken in fp32 as the
     kernels take them: d = fl32(6 * g), t = fl32(amax / d), u = fl32(s * g),
-    q = fl32(v / u), each one IEEE binary32 rounding of the exact result
-    (the inputs are binary32 values).
+    r = min(fl32(1 / u), the largest binary32) once per block, and
+    q = fl32(v * r) per element, each one IEEE binary32 rounding of the
+    exact result (the inputs are binary32 values).
     Returns (codes uint8 [..., K] unpacked, scales uint8 [..., K/16]).
     """
     v32 = _f32(v)
@@ -242,9 +243,10 @@ def quantize_nvfp4(v, global_scale):
     scodes = _e4m3_encode_sat(t.astype(_F64))
     s = e4m3_decode(scodes).astype(np.float32)
     u = (s * g).astype(np.float32)
-    with np.errstate(divide="ignore", invalid="ignore"):
-        q = (blocks / u[..., None]).astype(np.float32)
-    q = np.where(u[..., None] > 0, q, np.float32(0.0))
+    with np.errstate(divide="ignore", over="ignore"):
+        r = np.minimum((np.float32(1.0) / u).astype(np.float32), np.finfo(np.float32).max)
+    r = np.where(u > 0, r, np.float32(0.0)).astype(np.float32)
+    q = (blocks * r[..., None]).astype(np.float32)
     codes = _e2m1_encode_sat(q.astype(_F64)).reshape(v32.shape)
     return codes, scodes
 

@@ -26,7 +26,8 @@ def _nearest_even(table, q):
 
 
 def _brute_force(v, g):
-    """Codes and scales by exhaustive search, with the quotients in fp32."""
+    """Codes and scales by exhaustive search, with the quotients in fp32
+    (the element quotient as v times the rounded reciprocal of s g)."""
     v = np.asarray(v, dtype=np.float32)
     g = np.float32(g)
     e4m3_mag = e4m3_decode(np.arange(0x7F))           # codes 0x00..0x7E: every finite magnitude
@@ -41,7 +42,8 @@ def _brute_force(v, g):
         u = np.float32(s * g)
         if u == 0:
             continue
-        q = (blk / u).astype(np.float32).astype(np.float64)
+        r = np.float32(min(np.float32(np.float32(1.0) / u), np.finfo(np.float32).max))
+        q = (blk * r).astype(np.float32).astype(np.float64)
         mag = _nearest_even(E2M1_TABLE, np.minimum(np.abs(q), 6.0))
         codes[b] = mag | np.where(np.signbit(q), 8, 0)
     return codes.reshape(v.shape), scales.reshape(v.shape[:-1] + (v.shape[-1] // 16,))
