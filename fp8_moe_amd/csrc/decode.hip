@@ -407,8 +407,8 @@ __device__ __forceinline__ void decode_items(const DecodeParams& p, DecodeLds& L
                 if (q < nh) {
                   float mx = fabsf(hv[q]);
                   mx = row16_max(mx);
-                  const float sc = nv_block_scale(mx, gh);
-                  if (live) p.h16[pr * p.h_stride + hcol0 + 16 * q + r16] = (uint16_t)bf16_rne(nv_roundtrip(hv[q], sc, gh));
+                  const float sc = nv_block_scale(mx, gh), rc = nv_recip(sc, gh);
+                  if (live) p.h16[pr * p.h_stride + hcol0 + 16 * q + r16] = (uint16_t)bf16_rne(nv_roundtrip(hv[q], sc, rc));
                 }
               }
             } else if constexpr (RT) {

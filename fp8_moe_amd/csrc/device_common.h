@@ -206,13 +206,20 @@ __device__ __forceinline__ float e2m1_rne_sat(float q) {
   return copysignf(r, q);
 }
 
-// E2M1 * E4M3 value of the NVFP4 round trip of v in a block with scale s
-// (without the per-tensor scale g, which the GEMM applies): the E2M1 value
-// nearest to v / (s g), times s; exact in fp32, bf16 and f16.  A block whose
-// scale is 0 rounds to 0.
-__device__ __forceinline__ float nv_roundtrip(float v, float s, float g) {
+// Reciprocal of s g for the element quotients of an NVFP4 block with scale
+// s: the correctly rounded 1 / (s g), at most the largest finite fp32, and 0
+// for a block whose scale is 0 (its codes are then 0).
+__device__ __forceinline__ float nv_recip(float s, float g) {
   const float u = s * g;
-  return u > 0.0f ? e2m1_rne_sat(__fdiv_rn(v, u)) * s : 0.0f;
+  return u > 0.0f ? fminf(__fdiv_rn(1.0f, u), 3.40282347e38f) : 0.0f;
+}
+
+// E2M1 * E4M3 value of the NVFP4 round trip of v in a block with scale s and
+// reciprocal r = nv_recip(s, g) (without the per-tensor scale g, which the
+// GEMM applies): the E2M1 value nearest to v * r, times s; exact in fp32,
+// bf16 and f16.
+__device__ __forceinline__ float nv_roundtrip(float v, float s, float r) {
+  return e2m1_rne_sat(v * r) * s;
 }
 
 // E8M0 scale code as the fp32 whose exponent field is the code; the gfx950

@@ -556,8 +556,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void moe_gemm_kernel(const GemmPar
                 if (q < nh) {
                   float m = fabsf(hv[q]);
                   m = row16_max(m);
-                  const float sc = nv_block_scale(m, gh);
-                  p.h16[row * p.h_stride + hcol0 + 16 * q + r16] = (uint16_t)bf16_rne(nv_roundtrip(hv[q], sc, gh));
+                  const float sc = nv_block_scale(m, gh), rc = nv_recip(sc, gh);
+                  p.h16[row * p.h_stride + hcol0 + 16 * q + r16] = (uint16_t)bf16_rne(nv_roundtrip(hv[q], sc, rc));
                 }
               }
             } else if constexpr (RT) {

@@ -65,7 +65,8 @@ int launch_mx_roundtrip_rows(const uint16_t* x, int64_t rows, int64_t cols, int6
 // NVFP4 round trips of bf16 rows against the per-tensor activation scale
 // g[0] (NVFP4 activations with NVFP4 weights): per block of 16, the E4M3
 // scale s nearest to amax / (6 g) and each value's E2M1 code nearest to
-// v / (s g); out holds E2M1 * s (exact), the scale g is left to the GEMM.
+// v * RN(1 / (s g)); out holds E2M1 * s (exact), the scale g is left to the
+// GEMM.
 // Two threads per block of 16 (8 values each).  F16: f16 values plus a row
 // exponent of 0 for the f16 operand path of the grouped GEMM; else bf16.
 template <bool F16>
@@ -87,11 +88,12 @@ __global__ __launch_bounds__(256) void nv_roundtrip_rows_kernel(const uint16_t* 
   amax = max(amax, (uint32_t)__shfl_xor((int)amax, 1));
   const float gs = g[0];
   const float sc = nv_block_scale(bits_f32(amax << 16), gs);
+  const float rc = nv_recip(sc, gs);
   uint32_t o[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const float lo = nv_roundtrip(bf16_to_f32(w[i] & 0xFFFFu), sc, gs);
-    const float hi = nv_roundtrip(bf16_to_f32(w[i] >> 16), sc, gs);
+    const float lo = nv_roundtrip(bf16_to_f32(w[i] & 0xFFFFu), sc, rc);
+    const float hi = nv_roundtrip(bf16_to_f32(w[i] >> 16), sc, rc);
     if constexpr (F16)
       o[i] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)lo) |
              ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)hi) << 16);
