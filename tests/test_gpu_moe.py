@@ -176,6 +176,38 @@ def test_graph_replay_matches_eager():
         _ = (x.float() * 2).sum()      # unrelated eager work between replays
 
 
+@pytest.mark.parametrize("afmt,T", [("nvfp4", 8), ("nvfp4", 200), ("mxfp8", 8), ("mxfp8", 200)])
+def test_graph_replay_matches_eager_quantized(afmt, T):
+    """Graph replay of the paths with an activation-quantization stage
+    (NVFP4 weights with NVFP4 or MXFP8 activations), decode (T=8) and grouped
+    (T=200), bit-identical to the eager run on every replay."""
+    import fp8_moe_amd as fm
+    print(f"graph replay {afmt} T={T}", flush=True)
+    wl = small_workload(f"graph_{afmt}", 16, 512, 256, 4, True, "nvfp4", afmt)
+    pr = Problem(wl, 256, gen_device="cpu")
+    x, ids, tw = _inputs(wl, T)
+    out = torch.empty(T, wl.H, dtype=torch.bfloat16, device="cuda")
+    b, _ = pr.model.bind(x, ids, tw, out)
+    assert fm.binding_query(b, "path") == (2 if T * wl.k <= 256 else 1)
+    fm.run(b)
+    torch.cuda.synchronize()
+    eager = out.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        fm.run(b, stream=s)
+    for i in range(3):
+        out.fill_(0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), i
+        _ = (x.float() * 2).sum()      # unrelated eager work between replays
+    rel_fro, rel_max, ok = compare(out, pr.oracle(x, ids, tw))
+    assert ok, (rel_fro, rel_max)
+
+
 def test_decode_binding_reused_with_new_inputs():
     """One decode binding run again and again while its inputs change in place
     (x, then the routing): every output matches the oracle for the inputs of
