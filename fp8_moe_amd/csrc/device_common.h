@@ -186,24 +186,27 @@ __device__ __forceinline__ float row16_max(float v) {
 
 // NVFP4 block scale of a 16-block with largest magnitude amax against the
 // per-tensor scale g: the E4M3 value nearest to amax / (6 g) (ties to even,
-// saturating at 448), both quotients rounded once in fp32.
+// saturating at 448), both quotients rounded once in fp32.  The hardware
+// E4M3 conversion rounds to nearest even but does not saturate (checked on
+// the device against e4m3_encode_scaled over every fp32 value of 17-bit
+// mantissa in 2^-14 .. 2^13: equal up to 464, the tie that rounds to 448),
+// so the quotient is clamped to 448 first.
 __device__ __forceinline__ float nv_block_scale(float amax, float g) {
-  return e4m3_value(e4m3_encode_scaled(f32_bits(__fdiv_rn(amax, 6.0f * g)), 0));
+  typedef short s16x2 __attribute__((ext_vector_type(2)));
+  const float t = fminf(__fdiv_rn(amax, 6.0f * g), 448.0f);
+  s16x2 o = {0, 0};
+  o = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(o, t, t, 1.0f, false);
+  return e4m3_value((uint32_t)(uint16_t)o.x & 0xFFu);
 }
 
-// E2M1 value nearest to q, ties to even codes, saturating at +-6.
+// E2M1 value nearest to q, ties to even codes, saturating at +-6: the
+// hardware conversion to E2M1 and back (checked on the device against the
+// threshold rule over the same sweep, ties and saturation included: equal
+// everywhere); q is clamped to +-8 so that it stays inside that sweep.
 __device__ __forceinline__ float e2m1_rne_sat(float q) {
-  const float a = fabsf(q);
-  float r;
-  if (a <= 0.25f) r = 0.0f;
-  else if (a < 0.75f) r = 0.5f;
-  else if (a <= 1.25f) r = 1.0f;
-  else if (a < 1.75f) r = 1.5f;
-  else if (a <= 2.5f) r = 2.0f;
-  else if (a < 3.5f) r = 3.0f;
-  else if (a <= 5.0f) r = 4.0f;
-  else r = 6.0f;
-  return copysignf(r, q);
+  const float c = fminf(fmaxf(q, -8.0f), 8.0f);
+  const uint32_t code = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, c, c, 1.0f, 0);
+  return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(code, 1.0f, 0)[0];
 }
 
 // Reciprocal of s g for the element quotients of an NVFP4 block with scale
