@@ -190,24 +190,29 @@ def dequant_mxfp8(codes, scales):
     return vals * np.repeat(sc, 32, axis=-1)
 
 
-def _e2m1_encode_sat(q):
-    """fp64 -> E2M1 codes: round half to even onto {0, 0.5, 1, 1.5, 2, 3, 4, 6}
-    (1 mantissa bit, smallest normal 1, the subnormal 0.5), saturating at 6,
-    sign kept (-0 encodes as 0x8)."""
-    q = np.asarray(q, dtype=_F64)
-    neg = np.signbit(q)
-    r = np.minimum(_round_to_grid(np.minimum(np.abs(q), 6.0), 1, 0), 6.0)
-    # magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6 are codes 0..7
-    _, ex = np.frexp(r)
-    e = ex.astype(np.int64) - 1
-    normal = r >= 1.0
-    m = np.where(normal, np.ldexp(r, -np.where(normal, e, 0)) * 2.0 - 2.0, 0.0).astype(np.int64)
-    mag_code = np.where(normal, ((e + 1) << 1) + m, (r * 2.0).astype(np.int64))
-    return (mag_code | np.where(neg, 0x8, 0)).astype(np.uint8)
+# E2M1 magnitudes in code order (OCP MX v1.0) and the finite E4M3 magnitudes
+# in code order (codes 0x00 .. 0x7E), with the midpoints between neighbours
+_E2M1_MAGS = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+_E4M3_MAGS = e4m3_decode(np.arange(0x7F))
+_E2M1_MIDS = (_E2M1_MAGS[:-1] + _E2M1_MAGS[1:]) / 2.0
+_E4M3_MIDS = (_E4M3_MAGS[:-1] + _E4M3_MAGS[1:]) / 2.0
 
 
-def _f32(v):
-    return np.asarray(v, dtype=_F64).astype(np.float32)
+def _nearest_index(a, thresholds):
+    """Index i of the nearest grid value, given non-negative magnitudes ``a``
+    and the midpoints between consecutive grid values already multiplied by
+    the unit (``thresholds[..., i]`` lies between grid values i and i+1):
+    the number of thresholds below ``a``, plus one where ``a`` equals an odd
+    threshold (a tie goes to the even index).  Above the last threshold the
+    result is the last index (saturation).  Exact when every threshold is an
+    exact fp64 value."""
+    idx = np.zeros(np.shape(a), dtype=np.int64)
+    for i in range(thresholds.shape[-1]):
+        t = thresholds[..., i]
+        idx += (a > t).astype(np.int64)
+        if i % 2 == 1:
+            idx += (a == t).astype(np.int64)
+    return idx
 
 
 def quantize_nvfp4(v, global_scale):
@@ -215,40 +220,38 @@ def quantize_nvfp4(v, global_scale):
 
     The vLLM b12x page ("Supported Configurations") lists NVFP4 activations
     for NVFP4 MoE, and the README names an NVFP4 row quantizer
-    (quantization.nvfp4); neither gives the rule.  Reading, the NVFP4 recipe:
-    with g the fp32 per-tensor scale of the activations (the checkpoint's
-    input scale), each block of 16 takes the E4M3 scale
-    s = E4M3_RNE_sat(amax / (6 g)) and each element the E2M1 code
-    E2M1_RNE_sat(v / (s g)); a block whose scale rounds to 0 takes codes 0.
-    The quotients decide integer codes, so they are taken in fp32 as the
-    kernels take them: d = fl32(6 * g), t = fl32(amax / d), u = fl32(s * g),
-    r = min(fl32(1 / u), the largest binary32) once per block, and
-    q = fl32(v * r) per element, each one IEEE binary32 rounding of the
-    exact result (the inputs are binary32 values).
+    (quantization.nvfp4); neither gives the rule.  Reading, the NVFP4 format
+    written out: with g the fp32 per-tensor scale of the activations (the
+    checkpoint's input scale), each block of 16 takes the block scale s =
+    the E4M3 value nearest to amax / (6 g) (ties to the even code, saturating
+    at 448), and each element the E2M1 value nearest to v / (s g) (ties to the
+    even code, saturating at 6, sign kept); a block whose scale is 0 takes
+    codes 0.  Both nearest-value decisions are taken on the exact quotients:
+    a magnitude is compared with the midpoints of the grid multiplied by the
+    unit (6 g, or s g), and those products are exact in fp64 (a midpoint has at
+    most 5 significant bits, 6 two, an E4M3 value four and g 24, so at most 31
+    together).
     Returns (codes uint8 [..., K] unpacked, scales uint8 [..., K/16]).
     """
-    v32 = _f32(v)
-    if not np.isfinite(v32).all():
+    v = np.asarray(v, dtype=_F64)
+    if not np.isfinite(v).all():
         raise ValueError("NVFP4 quantization of a non-finite value")
-    g = np.float32(global_scale)
+    g = _F64(np.float32(global_scale))
     if not (np.isfinite(g) and g > 0):
         raise ValueError("NVFP4 activation scale must be finite and positive")
-    k = v32.shape[-1]
+    k = v.shape[-1]
     if k % 16:
         raise ValueError("NVFP4 rows must be a multiple of 16 long")
-    blocks = v32.reshape(v32.shape[:-1] + (k // 16, 16))
-    amax = np.abs(blocks).max(axis=-1)
-    d = np.float32(np.float32(6.0) * g)
-    t = (amax / d).astype(np.float32)
-    scodes = _e4m3_encode_sat(t.astype(_F64))
-    s = e4m3_decode(scodes).astype(np.float32)
-    u = (s * g).astype(np.float32)
-    with np.errstate(divide="ignore", over="ignore"):
-        r = np.minimum((np.float32(1.0) / u).astype(np.float32), np.finfo(np.float32).max)
-    r = np.where(u > 0, r, np.float32(0.0)).astype(np.float32)
-    q = (blocks * r[..., None]).astype(np.float32)
-    codes = _e2m1_encode_sat(q.astype(_F64)).reshape(v32.shape)
-    return codes, scodes
+    blocks = v.reshape(v.shape[:-1] + (k // 16, 16))
+    mag = np.abs(blocks)
+    amax = mag.max(axis=-1)
+    scodes = _nearest_index(amax, _E4M3_MIDS * (6.0 * g)).astype(np.uint8)
+    s = _E4M3_MAGS[scodes]
+    unit = s * g                                            # exact: at most 28 significant bits
+    mag_codes = _nearest_index(mag, _E2M1_MIDS * unit[..., None, None])
+    mag_codes = np.where(unit[..., None] > 0, mag_codes, 0)
+    codes = (mag_codes | np.where(np.signbit(blocks), 0x8, 0)).astype(np.uint8)
+    return codes.reshape(v.shape), scodes
 
 
 def nvfp4_values(codes, scales):

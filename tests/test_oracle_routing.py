@@ -1,10 +1,11 @@
 """Pins of the oracle's routing against a brute force built differently
 (per-expert filtering instead of one counting pass) and against the
-invariants any correct stable routing must satisfy."""
+invariants any correct stable routing must satisfy; the tile-list checker
+accepts two different valid tilings and rejects each kind of broken list."""
 import numpy as np
 import pytest
 
-from oracle.routing import route
+from oracle.routing import check_tiles, route
 
 
 def brute_force(ids, E, row_pad, tile_rows):
@@ -66,8 +67,11 @@ def test_route_matches_brute_force(kind, T, k, E, row_pad, tile_rows):
     assert r.counts.tolist() == counts
     assert r.sorted_ids.tolist() == rows
     assert r.pos.tolist() == pos
-    assert [tuple(t) for t in r.tiles.tolist()] == tiles
     assert r.offsets.tolist() == [0] + list(np.cumsum(counts))
+    # two different valid tilings: the oracle's greedy one and the brute force's balanced one
+    eff = tile_rows // row_pad * row_pad
+    assert check_tiles(r.tiles, len(r.tiles), r.padded_offsets, E, row_pad, eff) == []
+    assert check_tiles(np.array(tiles).reshape(-1, 3), len(tiles), r.padded_offsets, E, row_pad, eff) == []
 
 
 @pytest.mark.parametrize("seed", range(5))
@@ -92,3 +96,30 @@ def test_route_invariants(seed):
         assert np.all(np.diff(seg) > 0)
     assert r.tiles[:, 2].sum() == r.padded_offsets[-1] and np.all(r.tiles[:, 2] <= 24)
     assert np.all(r.tiles[:, 2] % 8 == 0)
+
+
+def test_check_tiles_rejects_broken_lists():
+    ids = np.array([[0, 2], [2, 0], [2, 2], [0, 0], [2, 2]], dtype=np.int32)
+    ids = np.concatenate([ids] * 7)                     # expert 0: 14 pairs, expert 2: 21, expert 1: none
+    r = route(ids, 3, 4, 8)
+    po = r.padded_offsets
+    good = r.tiles.tolist()
+    assert check_tiles(good, len(good), po, 3, 4, 8) == []
+    assert check_tiles(good, len(good) + 1, po, 3, 4, 8)                    # wrong count
+    bad = [list(t) for t in good]
+    bad[1][1] += 4                                                           # a gap
+    assert check_tiles(bad, len(bad), po, 3, 4, 8)
+    bad = [list(t) for t in good]
+    bad[0][2] += 4                                                           # too many rows / overlap
+    assert check_tiles(bad, len(bad), po, 3, 4, 8)
+    bad = [list(t) for t in good]
+    bad[-1][2] = 2                                                           # not a multiple of row_pad
+    assert check_tiles(bad, len(bad), po, 3, 4, 8)
+    assert check_tiles(good[::-1], len(good), po, 3, 4, 8)                  # experts descending
+    assert check_tiles(good[:-1], len(good) - 1, po, 3, 4, 8)               # last rows uncovered
+    assert check_tiles(good + [[1, int(po[1]), 4]], len(good) + 1, po, 3, 4, 8)   # tile for an empty expert
+    split = []
+    for e, r0, n in good:                                                    # a finer valid tiling
+        for k in range(0, n, 4):
+            split.append([e, r0 + k, 4])
+    assert check_tiles(split, len(split), po, 3, 4, 8) == []
