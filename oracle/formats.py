@@ -40,12 +40,13 @@ def e2m1_decode(codes):
     Closed form: s = c>>3, e = (c>>1)&3, m = c&1;
     value = (-1)^s * (0.5*m if e == 0 else (1 + m/2) * 2^(e-1)).
     """
-    c = _codes(codes) & 0xF
+    c = np.arange(16)
     s = c >> 3
     e = (c >> 1) & 3
     m = c & 1
     mag = np.where(e == 0, 0.5 * m, (1.0 + 0.5 * m) * np.exp2(e - 1.0))
-    return np.where(s == 1, -mag, mag).astype(_F64)
+    values = np.where(s == 1, -mag, mag).astype(_F64)   # the closed form at each of the 16 codes
+    return values[np.asarray(codes).astype(np.intp) & 0xF]
 
 
 def e4m3_decode(codes):
@@ -75,19 +76,34 @@ def unpack_fp4(packed):
     return out
 
 
+def _fp4_values(packed):
+    """E2M1 values of packed FP4 bytes [..., K/2] -> [..., K] (fp64): each byte
+    decodes to (E2M1 of its low nibble, E2M1 of its high nibble)."""
+    b = np.arange(256)
+    pairs = np.stack([e2m1_decode(b & 0xF), e2m1_decode(b >> 4)], axis=-1)   # [256, 2]
+    p = np.asarray(packed, dtype=np.uint8)
+    return np.take(pairs, p.astype(np.intp), axis=0).reshape(p.shape[:-1] + (p.shape[-1] * 2,))
+
+
+def _apply_block_scales(vals, sc, group):
+    """vals [..., K] times one scale per `group` consecutive elements of the last axis."""
+    k = vals.shape[-1]
+    if sc.shape[-1] * group != k:
+        raise ValueError(f"block scales must hold one code per {group} elements")
+    blocks = vals.reshape(vals.shape[:-1] + (k // group, group))
+    blocks *= sc[..., None]
+    return vals
+
+
 def dequant_mxfp4(packed, scales):
     """MXFP4 block [N, K]: E2M1(code[n,k]) * E8M0(scale[n, k//32]), exact in fp64.
 
     packed: uint8 [N, K/2]; scales: uint8 [N, K/32] along the contraction axis.
     """
-    vals = e2m1_decode(unpack_fp4(packed))
     sc = e8m0_decode(scales)
     if np.isnan(sc).any():
         raise ValueError("E8M0 scale 0xFF (NaN) in MXFP4 weights")
-    k = vals.shape[-1]
-    if sc.shape[-1] * 32 != k:
-        raise ValueError("MXFP4 scales must hold one code per 32 elements")
-    return vals * np.repeat(sc, 32, axis=-1)
+    return _apply_block_scales(_fp4_values(packed), sc, 32)
 
 
 def dequant_nvfp4(packed, scales, global_scale):
@@ -96,15 +112,11 @@ def dequant_nvfp4(packed, scales, global_scale):
     ``global_scale`` is the fp32 tensor scale of this matrix (one per expert
     and matrix here: the per-tensor scale broadcast).
     """
-    vals = e2m1_decode(unpack_fp4(packed))
     sc = e4m3_decode(scales)
     if np.isnan(sc).any():
         raise ValueError("E4M3 NaN block scale in NVFP4 weights")
-    k = vals.shape[-1]
-    if sc.shape[-1] * 16 != k:
-        raise ValueError("NVFP4 scales must hold one code per 16 elements")
     g = _F64(np.float32(global_scale))
-    return vals * np.repeat(sc, 16, axis=-1) * g
+    return _apply_block_scales(_fp4_values(packed), sc, 16) * g
 
 
 def bf16_decode(bits):
