@@ -28,7 +28,8 @@ ACT_FORMATS = {"bf16": 1, "mxfp8": 2, "nvfp4": 3}
 ACTIVATIONS = {"silu": 1, "relu2": 2}
 STAGES = {"route": 1, "quant_x": 2, "gemm1": 3, "gemm2": 4, "combine": 5, "decode1": 6, "decode2": 7}
 QUERIES = {"path": 1, "tile_rows": 2, "row_pad": 3, "T": 4, "num_stages": 5}
-REGIONS = {"counts": 1, "offsets": 2, "padded_offsets": 3, "sorted": 4, "pos": 5, "tiles": 6, "ntiles": 7}
+REGIONS = {"counts": 1, "offsets": 2, "padded_offsets": 3, "sorted": 4, "pos": 5, "tiles": 6, "ntiles": 7,
+           "xq": 9, "xs": 10, "h": 11, "hs": 12, "y": 13}
 
 STATUS_NAMES = {0: "OK", 1: "INVALID_ARGUMENT", 2: "UNSUPPORTED", 3: "CAPACITY", 4: "SCRATCH_TOO_SMALL",
                 5: "MISALIGNED", 6: "LAYOUT_MISMATCH", 7: "HIP"}
@@ -72,7 +73,7 @@ class Experts(ctypes.Structure):
 class Caps(ctypes.Structure):
     _fields_ = [("struct_size", ctypes.c_uint32), ("top_k", ctypes.c_int32), ("weights", WeightPlan),
                 ("act_format", ctypes.c_int32), ("activation", ctypes.c_int32), ("decode_max_pairs", ctypes.c_int32),
-                ("max_tokens", ctypes.c_int64)]
+                ("max_tokens", ctypes.c_int64), ("splitk_max_pairs", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 class ScratchSpec(ctypes.Structure):
@@ -194,11 +195,13 @@ def prepare_weights(wplan, w13_codes, w13_scales, w2_codes, w2_scales, w13_globa
 
 # ---------------------------------------------------------------- op plan
 
-def make_caps(wplan, top_k, max_tokens, act_format="bf16", activation="silu", decode_max_pairs=0):
+def make_caps(wplan, top_k, max_tokens, act_format="bf16", activation="silu", decode_max_pairs=0,
+              splitk_max_pairs=0):
     """decode_max_pairs: largest T*k routed to the decode path (0: library
-    default, negative: always use the grouped path)."""
+    default, negative: always use the grouped path); splitk_max_pairs: largest
+    T*k that runs the split-K decode kernel (0: default, negative: never)."""
     return Caps(ctypes.sizeof(Caps), top_k, wplan, ACT_FORMATS[act_format], ACTIVATIONS[activation],
-                decode_max_pairs, max_tokens)
+                decode_max_pairs, max_tokens, splitk_max_pairs, 0)
 
 
 def is_supported(wplan, top_k, max_tokens, act_format="bf16", activation="silu"):
@@ -233,8 +236,8 @@ class Plan:
             self._h = None
 
 
-def plan(wplan, top_k, max_tokens, act_format="bf16", activation="silu", decode_max_pairs=0):
-    caps = make_caps(wplan, top_k, max_tokens, act_format, activation, decode_max_pairs)
+def plan(wplan, top_k, max_tokens, act_format="bf16", activation="silu", decode_max_pairs=0, splitk_max_pairs=0):
+    caps = make_caps(wplan, top_k, max_tokens, act_format, activation, decode_max_pairs, splitk_max_pairs)
     h = ctypes.c_void_p()
     _check(_lib.b12x_moe_plan(ctypes.byref(caps), ctypes.byref(h)))
     return Plan(h, caps)
@@ -344,14 +347,14 @@ class FusedMoE:
     prepared experts and an op plan at a given capacity."""
 
     def __init__(self, E, H, I, top_k, weight_format, act_format, activation, max_tokens, weights, stream=None,
-                 decode_max_pairs=0):
+                 decode_max_pairs=0, splitk_max_pairs=0):
         gated = activation == "silu"
         self.wplan = plan_weights(E, H, I, gated, weight_format)
         self.experts = prepare_weights(self.wplan, weights["w13_codes"], weights["w13_scales"],
                                        weights["w2_codes"], weights["w2_scales"], weights.get("w13_global"),
                                        weights.get("w2_global"), stream=stream,
                                        a13_global=weights.get("a13_global"), a2_global=weights.get("a2_global"))
-        self.plan = plan(self.wplan, top_k, max_tokens, act_format, activation, decode_max_pairs)
+        self.plan = plan(self.wplan, top_k, max_tokens, act_format, activation, decode_max_pairs, splitk_max_pairs)
         self.scratch = alloc_scratch(self.plan, weights["w13_codes"].device)
         self.H = H
 

@@ -14,7 +14,9 @@ OUT = os.path.join(HERE, "libb12x_moe.so")
 BUILD = os.path.join(HERE, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["api.cpp", "pack.hip", "route.hip", "quant.hip", "gemm.hip", "combine.hip", "decode.hip", "probes.hip"]
+SOURCES = ["gemm_inst_silu_f16.hip", "gemm_inst_relu2_f16.hip", "gemm_inst_silu.hip", "gemm_inst_relu2.hip",
+           "gemm_inst_down.hip", "decode.hip", "decode_sk.hip", "api.cpp", "pack.hip", "route.hip", "quant.hip", "gemm.hip",
+           "combine.hip", "probes.hip"]
 
 # -packed-fp32-ops: keep hipcc from emitting packed fp32 VALU ops.
 FLAGS = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-function",
@@ -34,7 +36,7 @@ def _compile(src):
 
 def build(verbose=False):
     os.makedirs(BUILD, exist_ok=True)
-    jobs = min(len(SOURCES), max(1, int(os.environ.get("MAX_JOBS", "8"))))
+    jobs = min(len(SOURCES), max(1, int(os.environ.get("MAX_JOBS", str(os.cpu_count() or 8)))))
     with cf.ThreadPoolExecutor(jobs) as ex:
         results = list(ex.map(_compile, SOURCES))
     for _, errs in results:

@@ -222,6 +222,11 @@ b12x_status b12x_moe_plan(const b12x_moe_caps* caps, b12x_moe_plan_t* out) {
   int dmax = caps->decode_max_pairs == 0 ? kDecodePairs : caps->decode_max_pairs;
   if (dmax > kDecodePairs) dmax = kDecodePairs;
   p->decode_max_pairs = (decode_ok && dmax > 0) ? dmax : 0;
+  int smax = caps->splitk_max_pairs == 0 ? kSplitKPairs : caps->splitk_max_pairs;
+  if (smax > kSplitKMaxPairs) smax = kSplitKMaxPairs;
+  const bool splitk_ok = p->H <= kSplitKMaxH;
+  if (smax > p->decode_max_pairs) smax = p->decode_max_pairs;  // a part of the decode path
+  p->splitk_max_pairs = (splitk_ok && smax > 0) ? smax : 0;
   const bool a8 = a8_native(p->wfmt, p->afmt);
   // NVFP4 weights with bf16 activations: the grouped path's GEMM1 reads a
   // scaled f16 copy of a (2 bytes per element) and one exponent per row.
@@ -242,9 +247,12 @@ b12x_status b12x_moe_plan(const b12x_moe_caps* caps, b12x_moe_plan_t* out) {
   len[R_XS] = a8 ? (uint64_t)p->max_tokens * (p->Hp / 32) : (x16 || xrt ? 4ull * p->max_tokens : 0);
   len[R_H] = (uint64_t)p->max_rows * p->Ip * (a8 ? 1 : 2);
   len[R_HS] = a8 ? (uint64_t)p->max_rows * (p->Ip / 32) : 0;
-  {  // y: bf16 rows in routing order (grouped path) or fp32 rows by pair id (decode path)
+  {  // y: bf16 rows in routing order (grouped path), fp32 rows by pair id (decode path), or
+     // fp32 partial rows by (pair, 32-column slice of h) (split-K decode)
     const uint64_t grouped = 2ull * p->max_rows * p->H, decode = 4ull * p->decode_max_pairs * p->H;
+    const uint64_t splitk = 4ull * p->splitk_max_pairs * (p->I / 32) * ((p->H / 16 + 3) / 4 * 64 + kSplitKRowPad);
     len[R_Y] = grouped > decode ? grouped : decode;
+    if (splitk > len[R_Y]) len[R_Y] = splitk;
   }
   {  // decode path: epoch, status and one flag per (touched expert slot, gate/up group of 2 fragments)
     const int64_t slots = p->decode_max_pairs < p->E ? p->decode_max_pairs : p->E;
@@ -257,7 +265,8 @@ b12x_status b12x_moe_plan(const b12x_moe_caps* caps, b12x_moe_plan_t* out) {
     off = align_up(off + len[r], 256);
   }
   p->scratch_bytes = off;
-  if (len[R_XQ] >= (uint64_t)kMaxBufferBytes || len[R_H] >= (uint64_t)kMaxBufferBytes) {
+  if (len[R_XQ] >= (uint64_t)kMaxBufferBytes || len[R_H] >= (uint64_t)kMaxBufferBytes ||
+      4ull * p->splitk_max_pairs * (p->I / 32) * ((p->H / 16 + 3) / 4 * 64 + kSplitKRowPad) >= (uint64_t)kMaxBufferBytes) {
     delete p;
     return fail(B12X_ERR_UNSUPPORTED, "max_tokens too large: activation buffers would exceed 1 GiB");
   }
@@ -282,7 +291,8 @@ b12x_status b12x_moe_scratch_specs(b12x_moe_plan_t p, b12x_scratch_spec* specs, 
 
 b12x_status b12x_moe_scratch_region(b12x_moe_plan_t p, int32_t region, uint64_t* offset, uint64_t* bytes) {
   if (!p || !offset || !bytes) return fail(B12X_ERR_INVALID_ARGUMENT, "NULL argument");
-  if (region < R_COUNTS || region > R_NTILES) return fail(B12X_ERR_INVALID_ARGUMENT, "unknown region %d", region);
+  if (region < R_COUNTS || region > R_Y || region == R_CHUNK)
+    return fail(B12X_ERR_INVALID_ARGUMENT, "unknown region %d", region);
   *offset = p->off[region];
   *bytes = p->len[region];
   return B12X_OK;
@@ -321,6 +331,7 @@ b12x_status b12x_moe_bind(b12x_moe_plan_t p, void* scratch, uint64_t scratch_byt
   memset(&b, 0, sizeof(b));
   b.magic = kBindingMagic;
   b.path = (T > 0 && T * p->k <= p->decode_max_pairs) ? 2 : 1;
+  if (T > 0 && T * p->k <= p->splitk_max_pairs) b.path = 3;
   b.E = p->E; b.H = p->H; b.I = p->I; b.k = p->k;
   b.gated = p->gated; b.wfmt = p->wfmt; b.afmt = p->afmt; b.act = p->act;
   // grouped path, NVFP4 weights: GEMM1 reads a scaled f16 copy of a (of its MXFP8 or NVFP4 round trips with
@@ -371,6 +382,7 @@ static b12x_status get_binding(const b12x_moe_binding* binding, BindingImpl* b) 
 }
 
 static bool stage_in_path(const BindingImpl& b, int stage) {
+  if (b.path == 3) return stage == B12X_STAGE_DECODE1 || stage == B12X_STAGE_COMBINE;
   if (stage == B12X_STAGE_QUANT_X) return b.afmt != B12X_ACT_BF16 || b.a_f16;
   if (b.path == 2)
     return stage == B12X_STAGE_DECODE1 || stage == B12X_STAGE_COMBINE ||
@@ -383,7 +395,7 @@ static b12x_status run_stage(const BindingImpl& b, int stage, hipStream_t s) {
     return fail(B12X_ERR_INVALID_ARGUMENT, "unknown stage %d", stage);
   if (!stage_in_path(b, stage))
     return fail(B12X_ERR_UNSUPPORTED, "stage %d is not part of this binding's path (%s)", stage,
-                b.path == 2 ? "decode" : "grouped");
+                b.path == 3 ? "split-K decode" : b.path == 2 ? "decode" : "grouped");
   int err = 0;
   switch (stage) {
     case B12X_STAGE_ROUTE: err = launch_route(b, s); break;
@@ -400,8 +412,10 @@ static b12x_status run_stage(const BindingImpl& b, int stage, hipStream_t s) {
       break;
     case B12X_STAGE_GEMM1: err = launch_gemm1(b, s); break;
     case B12X_STAGE_GEMM2: err = launch_gemm2(b, s); break;
-    case B12X_STAGE_COMBINE: err = b.path == 2 ? launch_decode_combine(b, s) : launch_combine(b, s); break;
-    case B12X_STAGE_DECODE1: err = launch_decode1(b, s); break;
+    case B12X_STAGE_COMBINE:
+      err = b.path == 3 ? launch_decode_sk_combine(b, s) : b.path == 2 ? launch_decode_combine(b, s) : launch_combine(b, s);
+      break;
+    case B12X_STAGE_DECODE1: err = b.path == 3 ? launch_decode_sk(b, s) : launch_decode1(b, s); break;
     case B12X_STAGE_DECODE2: err = launch_decode2(b, s); break;
   }
   if (err) return hip_fail(err, "kernel launch");
@@ -425,8 +439,8 @@ b12x_status b12x_moe_run(const b12x_moe_binding* binding, void* stream) {
   static const int grouped[5] = {B12X_STAGE_ROUTE, B12X_STAGE_QUANT_X, B12X_STAGE_GEMM1, B12X_STAGE_GEMM2,
                                  B12X_STAGE_COMBINE};
   static const int decode[4] = {B12X_STAGE_QUANT_X, B12X_STAGE_DECODE1, B12X_STAGE_DECODE2, B12X_STAGE_COMBINE};
-  const int* stages = b.path == 2 ? decode : grouped;
-  const int n = b.path == 2 ? 4 : 5;
+  const int* stages = b.path == 1 ? grouped : decode;
+  const int n = b.path == 1 ? 5 : 4;
   for (int i = 0; i < n; ++i) {
     if (!stage_in_path(b, stages[i])) continue;
     st = run_stage(b, stages[i], s);
@@ -446,7 +460,7 @@ b12x_status b12x_moe_binding_query(const b12x_moe_binding* binding, int32_t what
     case B12X_QUERY_ROW_PAD: *value = kRowPad; break;
     case B12X_QUERY_T: *value = b.T; break;
     case B12X_QUERY_NUM_STAGES:
-      *value = (b.path == 2 ? (decode_fused(b) ? 2 : 3) : 4) + (stage_in_path(b, B12X_STAGE_QUANT_X) ? 1 : 0);
+      *value = b.path == 3 ? 2 : (b.path == 2 ? (decode_fused(b) ? 2 : 3) : 4) + (stage_in_path(b, B12X_STAGE_QUANT_X) ? 1 : 0);
       break;
     default: return fail(B12X_ERR_INVALID_ARGUMENT, "unknown query %d", what);
   }

@@ -26,13 +26,9 @@
 //      by pair id).
 // No atomics on data: every value is computed by one workgroup in a fixed
 // order, so the result does not depend on scheduling or on the grid size.
-#include "device_common.h"
+#include "decode_common.h"
 
 namespace b12x {
-
-constexpr int kDecThreads = 256;
-constexpr int kBitWords = kMaxExperts / 32;
-static_assert(kBitWords <= 64, "one wave scans the expert bitmap");
 
 struct DecodeParams {
   const int32_t* ids;
@@ -84,80 +80,6 @@ struct DecodeParams {
 };
 
 enum { DMODE_SILU = 1, DMODE_RELU2 = 2, DMODE_DOWN = 3 };
-
-// topk_ids -> LDS (invalid ids as -1), the bitmap of valid experts and the
-// exclusive prefix popcounts of its words; returns the number of distinct
-// valid experts.  All threads call it.
-__device__ int decode_prep(const DecodeParams& p, int* s_ids, uint32_t* s_bits, int* s_wpre) {
-  const int tid = threadIdx.x;
-  const int words = (p.E + 31) >> 5;
-  for (int i = tid; i < words; i += kDecThreads) s_bits[i] = 0;
-  __syncthreads();
-  for (int q = tid; q < p.P; q += kDecThreads) {
-    const int e = p.ids[q];
-    const bool v = e >= 0 && e < p.E;
-    s_ids[q] = v ? e : -1;
-    if (v) atomicOr(&s_bits[e >> 5], 1u << (e & 31));
-  }
-  __syncthreads();
-  if (tid < 64) {  // wave 0: words <= 64
-    const int c = tid < words ? __builtin_popcount(s_bits[tid]) : 0;
-    int incl = c;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int t = __shfl_up(incl, off);
-      if (tid >= off) incl += t;
-    }
-    if (tid < words) s_wpre[tid] = incl - c;
-    if (tid == 63) s_wpre[kBitWords] = incl;
-  }
-  __syncthreads();
-  return __builtin_amdgcn_readfirstlane(s_wpre[kBitWords]);
-}
-
-// Expert of touched slot `slot` (the slot-th smallest distinct valid id) and
-// its pairs in ascending pair order into s_rows; returns the pair count.
-// All threads call it; it starts with a barrier, so the caller may reuse
-// s_rows and s_info right after its own last reads.
-__device__ int decode_expert(const DecodeParams& p, int slot, const int* s_ids, const uint32_t* s_bits,
-                             const int* s_wpre, int* s_rows, int* s_info, int& e_out) {
-  const int tid = threadIdx.x;
-  const int words = (p.E + 31) >> 5;
-  __syncthreads();
-  if (tid < words && slot >= s_wpre[tid] && slot < s_wpre[tid] + __builtin_popcount(s_bits[tid])) {
-    uint32_t b = s_bits[tid];
-    for (int r = slot - s_wpre[tid]; r > 0; --r) b &= b - 1;  // drop the lower set bits
-    s_info[0] = tid * 32 + __builtin_ctz(b);
-  }
-  __syncthreads();
-  const int e = __builtin_amdgcn_readfirstlane(s_info[0]);
-  e_out = e;
-  // stable list of e's pairs: ballots per wave, waves ordered by a prefix
-  const int wave = tid >> 6, lane = tid & 63;
-  const uint64_t below = lane ? (~0ull >> (64 - lane)) : 0ull;
-  int total = 0;
-  for (int base = 0; base < p.P; base += kDecThreads) {
-    const int q = base + tid;
-    const bool hit = q < p.P && s_ids[q] == e;
-    const uint64_t bal = __ballot(hit);
-    if (lane == 0) s_info[4 + wave] = __builtin_popcountll(bal);
-    __syncthreads();
-    int off = total;
-    for (int w = 0; w < wave; ++w) off += s_info[4 + w];
-    if (hit) s_rows[off + __builtin_popcountll(bal & below)] = q;
-    total += s_info[4] + s_info[5] + s_info[6] + s_info[7];
-    __syncthreads();
-  }
-  return __builtin_amdgcn_readfirstlane(total);
-}
-
-struct DecodeLds {
-  int ids[kDecodePairs];
-  int rows[kDecodePairs];
-  uint32_t bits[kBitWords];
-  int wpre[kBitWords + 1];
-  int info[8];
-};
 
 // Tag of this call's completion flags: never 0 and never a previous call's.
 __device__ __forceinline__ uint64_t flag_tag(const int32_t* epoch) {
@@ -261,7 +183,7 @@ __device__ __forceinline__ void decode_items(const DecodeParams& p, DecodeLds& L
     }
   }
   int e;
-  const int m = decode_expert(p, slot, s_ids, s_bits, s_wpre, s_rows, s_info, e);
+  const int m = decode_expert(p.P, p.E, slot, s_ids, s_bits, s_wpre, s_rows, s_info, e);
   const uint8_t* bcodes = p.bcodes + (int64_t)e * p.b_codes_expert;
   const uint8_t* bscales = p.bscales + (int64_t)e * p.b_scales_expert;
   float gsc = p.bglobal ? p.bglobal[e] : 1.0f;
@@ -408,7 +330,7 @@ __device__ __forceinline__ void decode_items(const DecodeParams& p, DecodeLds& L
                   float mx = fabsf(hv[q]);
                   mx = row16_max(mx);
                   const float sc = nv_block_scale(mx, gh), rc = nv_recip(sc, gh);
-                  if (live) p.h16[pr * p.h_stride + hcol0 + 16 * q + r16] = (uint16_t)bf16_rne(nv_roundtrip(hv[q], sc, rc));
+                  if (live) p.h16[pr * p.h_stride + hcol0 + 16 * q + r16] = (uint16_t)bf16_rne(nv_roundtrip(hv[q], sc, gh, rc));
                 }
               }
             } else if constexpr (RT) {
@@ -494,7 +416,7 @@ template <int WF, int AF, int MODE, int FR, int KW>
 __global__ __launch_bounds__(kDecThreads) void decode_kernel(const DecodeParams p) {
   __shared__ DecodeLds L;
   __shared__ f32x4 s_red[2 * 3 * FR * 64];
-  const int n_touched = decode_prep(p, L.ids, L.bits, L.wpre);
+  const int n_touched = decode_prep(p.ids, p.P, p.E, L.ids, L.bits, L.wpre);
   decode_items<WF, AF, MODE, FR, KW, 0>(p, L, s_red, n_touched, 0);
 }
 
@@ -512,24 +434,9 @@ __global__ __launch_bounds__(kDecThreads) void decode_fused_kernel(const DecodeP
   if (blockIdx.x == 0 && threadIdx.x == 0)
     __hip_atomic_store(p1.status, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const uint64_t tag = flag_tag(p1.epoch);
-  const int n_touched = decode_prep(p1, L.ids, L.bits, L.wpre);
+  const int n_touched = decode_prep(p1.ids, p1.P, p1.E, L.ids, L.bits, L.wpre);
   decode_items<WF, B12X_ACT_BF16, MODE1, FR1, KW1, 1>(p1, L, s_red, n_touched, tag);
   decode_items<WF, B12X_ACT_BF16, DMODE_DOWN, FR2, KW2, 2>(p2, L, s_red, n_touched, tag);
-}
-
-// Workgroups the device holds at once for one kernel (per device, cached by
-// the caller: one cache per kernel).
-template <typename Kernel>
-static int resident_workgroups(Kernel kernel, int (&cache)[64]) {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-  if (!cache[dev]) {
-    int per_cu = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kDecThreads, 0) != hipSuccess || per_cu < 1)
-      per_cu = 1;
-    cache[dev] = per_cu * device_cu_count();
-  }
-  return cache[dev];
 }
 
 // One workgroup per resident slot, never more than the items of the largest

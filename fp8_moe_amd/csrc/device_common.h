@@ -194,45 +194,77 @@ __device__ __forceinline__ float row16_max(float v) {
   return v;
 }
 
-// NVFP4 block scale of a 16-block with largest magnitude amax against the
-// per-tensor scale g: the E4M3 value nearest to amax / (6 g) (ties to even,
-// saturating at 448), both quotients rounded once in fp32.  The hardware
-// E4M3 conversion rounds to nearest even but does not saturate (checked on
-// the device against e4m3_encode_scaled over every fp32 value of 17-bit
-// mantissa in 2^-14 .. 2^13: equal up to 464, the tie that rounds to 448),
-// so the quotient is clamped to 448 first.
+// NVFP4 activation quantization, exact rule: per block of 16 the E4M3 value s
+// nearest to amax / (6 g) (ties to the even code, saturating at 448), per
+// element the E2M1 value nearest to v / (s g) (ties to the even code,
+// saturating at 6); a block with s = 0 quantizes to zeros.  A candidate comes
+// from the binary32 quotient and the hardware conversions (round to nearest
+// even); it is at most one code from the exact answer (the quotient is within
+// 2^-22 relative of the exact one, and neighbouring codes are at least a
+// sixteenth apart).  It is then corrected by the exact comparisons of the
+// magnitude with the two midpoints next to it: a midpoint times the unit
+// (6 g or s g) is mid6 * g or (mid * s) * g, whose first factor is exact in
+// binary32 (at most 7 significant bits), and fma(first, g, -|v|) has the sign
+// of the exact difference.  Domain: g in [2^-64, 2^64] (every product and
+// nonzero difference then stays a normal binary32), finite v.
+typedef short nv_s16x2 __attribute__((ext_vector_type(2)));
+
+// Magnitude of the E4M3 code c in [0, 0x7E] and its distance to code c + 1.
+__device__ __forceinline__ float e4m3_mag(uint32_t c) { return e4m3_value(c & 0x7Fu); }
+__device__ __forceinline__ float e4m3_step(uint32_t c) {  // 2^(max(e, 1) - 10)
+  const uint32_t e = c >> 3;
+  return bits_f32((uint32_t)((e ? e : 1u) + 117u) << 23);
+}
+
 __device__ __forceinline__ float nv_block_scale(float amax, float g) {
-  typedef short s16x2 __attribute__((ext_vector_type(2)));
   const float t = fminf(__fdiv_rn(amax, 6.0f * g), 448.0f);
-  s16x2 o = {0, 0};
+  nv_s16x2 o = {0, 0};
   o = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(o, t, t, 1.0f, false);
-  return e4m3_value((uint32_t)(uint16_t)o.x & 0xFFu);
+  uint32_t c = (uint32_t)(uint16_t)o.x & 0x7Fu;
+  const float v = e4m3_mag(c);
+  if (c < 0x7Eu) {  // midpoint with the next code
+    const float d = fmaf((v + 0.5f * e4m3_step(c)) * 6.0f, g, -amax);
+    if (d < 0.0f || (d == 0.0f && (c & 1u))) return e4m3_mag(c + 1u);
+  }
+  if (c > 0u) {  // midpoint with the previous code
+    const float d = fmaf((v - 0.5f * e4m3_step(c - 1u)) * 6.0f, g, -amax);
+    if (d > 0.0f || (d == 0.0f && (c & 1u))) return e4m3_mag(c - 1u);
+  }
+  return v;
 }
 
-// E2M1 value nearest to q, ties to even codes, saturating at +-6: the
-// hardware conversion to E2M1 and back (checked on the device against the
-// threshold rule over the same sweep, ties and saturation included: equal
-// everywhere); q is clamped to +-8 so that it stays inside that sweep.
-__device__ __forceinline__ float e2m1_rne_sat(float q) {
-  const float c = fminf(fmaxf(q, -8.0f), 8.0f);
-  const uint32_t code = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, c, c, 1.0f, 0);
-  return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(code, 1.0f, 0)[0];
-}
-
-// Reciprocal of s g for the element quotients of an NVFP4 block with scale
-// s: the correctly rounded 1 / (s g), at most the largest finite fp32, and 0
-// for a block whose scale is 0 (its codes are then 0).
+// Reciprocal of s g for the candidate element quotients of a block with
+// scale s: 1 / (s g) rounded, at most the largest finite fp32, and 0 for a
+// block whose scale is 0.
 __device__ __forceinline__ float nv_recip(float s, float g) {
   const float u = s * g;
   return u > 0.0f ? fminf(__fdiv_rn(1.0f, u), 3.40282347e38f) : 0.0f;
 }
 
-// E2M1 * E4M3 value of the NVFP4 round trip of v in a block with scale s and
-// reciprocal r = nv_recip(s, g) (without the per-tensor scale g, which the
-// GEMM applies): the E2M1 value nearest to v * r, times s; exact in fp32,
-// bf16 and f16.
-__device__ __forceinline__ float nv_roundtrip(float v, float s, float r) {
-  return e2m1_rne_sat(v * r) * s;
+// E2M1 magnitude of the 3-bit code c (the hardware decode).
+__device__ __forceinline__ float e2m1_mag(uint32_t c) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c & 7u, 1.0f, 0)[0];
+}
+
+// E2M1 * s of the NVFP4 round trip of v in a block with scale s (g, the
+// per-tensor scale, is left to the GEMM; r = nv_recip(s, g)); sign of v kept.
+// Exact in fp32, bf16 and f16.
+__device__ __forceinline__ float nv_roundtrip(float v, float s, float g, float r) {
+  if (s == 0.0f) return v * 0.0f;
+  const float a = fabsf(v);
+  const float q = fminf(a * r, 8.0f);
+  uint32_t c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, q, q, 1.0f, 0) & 7u;
+  const float m = e2m1_mag(c);
+  float mag = m;
+  if (c < 7u) {
+    const float d = fmaf((0.5f * (m + e2m1_mag(c + 1u))) * s, g, -a);
+    if (d < 0.0f || (d == 0.0f && (c & 1u))) mag = e2m1_mag(c + 1u);
+  }
+  if (c > 0u) {
+    const float d = fmaf((0.5f * (m + e2m1_mag(c - 1u))) * s, g, -a);
+    if (d > 0.0f || (d == 0.0f && (c & 1u))) mag = e2m1_mag(c - 1u);
+  }
+  return copysignf(mag * s, v);
 }
 
 // E8M0 scale code as the fp32 whose exponent field is the code; the gfx950

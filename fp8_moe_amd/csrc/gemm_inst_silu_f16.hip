@@ -1,0 +1,11 @@
+// Instantiations of the grouped GEMM kernel (gemm_kernel.h), one translation
+// unit per group so that the build compiles them in parallel.
+#include "gemm_kernel.h"
+
+namespace b12x {
+
+B12X_GEMM_INST(B12X_WEIGHT_NVFP4, kActF16NvRt, MODE_SILU)
+B12X_GEMM_INST(B12X_WEIGHT_NVFP4, kActF16Rt, MODE_SILU)
+B12X_GEMM_INST(B12X_WEIGHT_NVFP4, kActF16, MODE_SILU)
+
+}  // namespace b12x

@@ -38,6 +38,10 @@ constexpr int kRouteChunk = 1024;  // routing pairs per workgroup
 constexpr int kMaxExperts = 1024;
 // ---- decode path -------------------------------------------------------------
 constexpr int kDecodePairs = 256;     // T*k at or below which the decode path runs
+constexpr int kSplitKPairs = 32;      // T*k at or below which the split-K decode kernel runs (default)
+constexpr int kSplitKMaxPairs = 64;   // its routing holds one pair per lane of a wave
+constexpr int kSplitKRowPad = 64;     // floats between its partial rows beyond H
+constexpr int kSplitKMaxH = 4096;     // its W2 slice (H / 16 fragments x 320 bytes) is staged in LDS
 // MXFP8 activations: with MXFP4 weights the scaled fp8 x fp4 MFMA multiplies
 // the codes (native); with NVFP4 weights (whose E4M3 block scales per 16 have
 // no place in that MFMA) x and h are round-tripped through MXFP8 and the
@@ -85,6 +89,7 @@ struct PlanImpl {
   int64_t Hp = 0, Ip = 0;  // H, I rounded up to 128
   int64_t max_pairs = 0, max_rows = 0, max_tiles = 0, max_chunks = 0;
   int decode_max_pairs = 0;  // largest T*k that takes the decode path (0: never)
+  int splitk_max_pairs = 0;  // largest T*k that takes the split-K decode kernel (0: never)
   uint64_t off[16] = {0};   // scratch region offsets, indexed by Region
   uint64_t len[16] = {0};   // scratch region sizes
   uint64_t scratch_bytes = 0;
@@ -98,7 +103,7 @@ enum Region {
 // Everything a run needs, resolved at bind time (trivially copyable).
 struct BindingImpl {
   uint32_t magic;
-  int32_t path;
+  int32_t path;  // 1 grouped, 2 decode (two-phase), 3 decode (split-K)
   int32_t E, H, I, k, gated, wfmt, afmt, act;
   int32_t a_f16;  // grouped path, NVFP4 weights: GEMM1 reads a scaled f16 copy of a (xq; of its MXFP8 round trips
                   // with MXFP8 activations) and row exponents (xs)
@@ -172,6 +177,10 @@ int device_cu_count();
 int launch_decode1(const BindingImpl& b, hipStream_t s);
 int launch_decode2(const BindingImpl& b, hipStream_t s);
 int launch_decode_combine(const BindingImpl& b, hipStream_t s);
+// split-K decode (path 3): one kernel for gate/up + activation + partial down
+// projections per 32-column slice of h, then the combine of the partials
+int launch_decode_sk(const BindingImpl& b, hipStream_t s);
+int launch_decode_sk_combine(const BindingImpl& b, hipStream_t s);
 // the decode path runs gate/up and down as one launch (DECODE1) for this binding
 bool decode_fused(const BindingImpl& b);
 const char* hip_error_name(int err);

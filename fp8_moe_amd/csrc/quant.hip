@@ -65,8 +65,8 @@ int launch_mx_roundtrip_rows(const uint16_t* x, int64_t rows, int64_t cols, int6
 // NVFP4 round trips of bf16 rows against the per-tensor activation scale
 // g[0] (NVFP4 activations with NVFP4 weights): per block of 16, the E4M3
 // scale s nearest to amax / (6 g) and each value's E2M1 code nearest to
-// v * RN(1 / (s g)); out holds E2M1 * s (exact), the scale g is left to the
-// GEMM.
+// v / (s g), both decided exactly (nv_block_scale, nv_roundtrip); out holds
+// E2M1 * s (exact), the scale g is left to the GEMM.
 // Two threads per block of 16 (8 values each).  F16: f16 values plus a row
 // exponent of 0 for the f16 operand path of the grouped GEMM; else bf16.
 template <bool F16>
@@ -92,8 +92,8 @@ __global__ __launch_bounds__(256) void nv_roundtrip_rows_kernel(const uint16_t* 
   uint32_t o[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const float lo = nv_roundtrip(bf16_to_f32(w[i] & 0xFFFFu), sc, rc);
-    const float hi = nv_roundtrip(bf16_to_f32(w[i] >> 16), sc, rc);
+    const float lo = nv_roundtrip(bf16_to_f32(w[i] & 0xFFFFu), sc, gs, rc);
+    const float hi = nv_roundtrip(bf16_to_f32(w[i] >> 16), sc, gs, rc);
     if constexpr (F16)
       o[i] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)lo) |
              ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)hi) << 16);
@@ -132,7 +132,8 @@ int launch_quant_rows(const uint16_t* x, int64_t rows, int64_t cols, int64_t str
 // Scaled f16 copy of bf16 rows for the NVFP4 weight GEMMs, which dequantize
 // the weights to f16 (half the conversion work of bf16 on gfx950, see the
 // grouped GEMM).  Row r is multiplied by 2^-e[r] with e[r] = floor(log2
-// max|x_r|) - 14 (clamped to [-110, 110]; 0 for an all-zero row), which puts
+// max|x_r|) - 14 (at least -126, so that 2^-e and 2^e are normal fp32
+// values; 0 for an all-zero row; bf16 maxima give at most 113), which puts
 // the row maximum in [2^14, 2^15): every bf16 value above 2^-31 of the row
 // maximum is then exact in f16, and the GEMM multiplies its fp32 results by
 // 2^e[r].  One workgroup per row.
@@ -160,7 +161,7 @@ __global__ __launch_bounds__(256) void f16_rows_kernel(const uint16_t* __restric
   __syncthreads();
   m = max(max(s_max[0], s_max[1]), max(s_max[2], s_max[3]));
   int e = m ? ilog2_mag(m << 16) - 14 : 0;
-  e = e < -110 ? -110 : (e > 110 ? 110 : e);
+  e = e < -126 ? -126 : e;
   const float mul = bits_f32((uint32_t)(127 - e) << 23);  // 2^-e, exact
   // cols is a multiple of 32: a whole 32-block is 4 threads of one pass, all active or all idle
   for (int64_t c0 = 0; c0 < cols; c0 += 256 * 8) {

@@ -35,7 +35,7 @@ def compare(gpu_out, ref):
 class Problem:
     """A workload instance on the GPU: source weights, prepared weights, plan."""
 
-    def __init__(self, wl, max_tokens, gen_device="cuda", weights=None, decode_max_pairs=0):
+    def __init__(self, wl, max_tokens, gen_device="cuda", weights=None, decode_max_pairs=0, splitk_max_pairs=0):
         import fp8_moe_amd as fm
         self.wl = wl
         self.fm = fm
@@ -43,7 +43,7 @@ class Problem:
         self.wd = {k: (None if v is None else v.cuda()) for k, v in self.w.items()}
         self.model = fm.FusedMoE(wl.E, wl.H, wl.I, wl.k, wl.weight_format, wl.act_format,
                                  "silu" if wl.gated else "relu2", max_tokens, self.wd,
-                                 decode_max_pairs=decode_max_pairs)
+                                 decode_max_pairs=decode_max_pairs, splitk_max_pairs=splitk_max_pairs)
 
     def run(self, x, ids, tw, out=None):
         binding, out = self.model.bind(x, ids, tw, out)
@@ -68,3 +68,28 @@ class Problem:
 def small_workload(name, E, H, I, k, gated=True, weight_format="mxfp4", act_format="bf16", routing="uniform",
                    x_lognormal=False):
     return synth.Workload(name, E, H, I, k, gated, weight_format, act_format, (1,), routing, x_lognormal)
+
+
+def scratch_ints(model, name, count):
+    """int32 [count] from one of the plan's scratch regions (after a run)."""
+    off, nbytes = model.plan.scratch_region(name)
+    assert 4 * count <= nbytes
+    return model.scratch[off:off + 4 * count].cpu().numpy().view(np.int32)
+
+
+def tile_edge_tokens(model, k):
+    """Tokens whose pairs sit in the first or the last real row of some GEMM
+    tile of the last grouped-path run: comparing their output rows reaches
+    every routed expert and every tile (both ends of each)."""
+    nt = scratch_ints(model, "ntiles", 4)
+    n_tiles, rows = int(nt[0]), int(nt[1])
+    tiles = scratch_ints(model, "tiles", 4 * n_tiles).reshape(-1, 4)
+    sorted_ids = scratch_ints(model, "sorted", rows)
+    tokens = set()
+    for e, r0, n, _ in tiles:
+        seg = sorted_ids[r0:r0 + n]
+        live = np.nonzero(seg >= 0)[0]
+        assert len(live) > 0, (e, r0, n)
+        tokens.add(int(seg[live[0]]) // k)
+        tokens.add(int(seg[live[-1]]) // k)
+    return sorted(tokens), n_tiles

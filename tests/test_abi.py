@@ -144,11 +144,18 @@ def test_path_selection_at_bind():
     wp = fm.plan_weights(128, 2048, 768, True, "mxfp4")
     ex = fm.Experts(wp, ctypes.c_void_p(0x7000000), wp.prepared_bytes)
     p = fm.plan(wp, 8, 64)
+    assert fm.binding_query(_bind_status(p, ex, 4, a_stride=2048)[1], "path") == 3      # 32 pairs: split-K decode
+    assert fm.binding_query(_bind_status(p, ex, 5, a_stride=2048)[1], "path") == 2      # 40 pairs: decode
     assert fm.binding_query(_bind_status(p, ex, 32, a_stride=2048)[1], "path") == 2     # 256 pairs: decode
     assert fm.binding_query(_bind_status(p, ex, 33, a_stride=2048)[1], "path") == 1     # 264 pairs: grouped
+    nosk = fm.plan(wp, 8, 64, splitk_max_pairs=-1)
+    assert fm.binding_query(_bind_status(nosk, ex, 1, a_stride=2048)[1], "path") == 2
+    wider = fm.plan(wp, 8, 64, splitk_max_pairs=64)
+    assert fm.binding_query(_bind_status(wider, ex, 8, a_stride=2048)[1], "path") == 3
+    assert fm.binding_query(_bind_status(wider, ex, 9, a_stride=2048)[1], "path") == 2
     never = fm.plan(wp, 8, 64, decode_max_pairs=-1)
     assert fm.binding_query(_bind_status(never, ex, 1, a_stride=2048)[1], "path") == 1
-    small = fm.plan(wp, 8, 64, decode_max_pairs=64)
+    small = fm.plan(wp, 8, 64, decode_max_pairs=64, splitk_max_pairs=-1)
     assert fm.binding_query(_bind_status(small, ex, 8, a_stride=2048)[1], "path") == 2
     assert fm.binding_query(_bind_status(small, ex, 9, a_stride=2048)[1], "path") == 1
     wide = fm.plan_weights(8, 7168, 256, True, "nvfp4")                                   # K too long per wave

@@ -7,7 +7,7 @@ import pytest
 import torch
 
 import synth
-from moe_cases import Problem, compare, small_workload
+from moe_cases import Problem, compare, small_workload, tile_edge_tokens
 
 pytestmark = pytest.mark.gpu
 
@@ -29,16 +29,17 @@ def _inputs(wl, T):
     return x, ids, tw
 
 
-# (workload, T, sampled token rows or None for all)
+# (workload, T, rows): "all" compares every output row; "tiles" every token that
+# owns the first or the last row of some GEMM tile (so every routed expert and
+# every tile of the grouped path is reached)
 FULL = [
-    ("tiny", 16, None),
-    # decode T=4: contiguous shares in both phases of the fused kernel; T=8: the down phase
-    # continues the gate/up deal; T=16 and 32: both phases deal from workgroup 0
-    ("decode", 1, None), ("decode", 4, None), ("decode", 8, None), ("decode", 16, [0, 7, 15]),
-    ("decode", 32, [0, 13, 31]),
-    ("mixed", 1, None), ("mixed", 64, [0, 40, 63]), ("mixed", 512, [3, 511]), ("mixed", 2048, [0, 2047]),
-    ("prefill", 4096, [0, 4095]),
-    ("skew", 8192, [1, 8191]),
+    ("tiny", 16, "all"),
+    # decode T=4: contiguous shares; T=8: short deals; T=16 and 32: several rounds
+    ("decode", 1, "all"), ("decode", 4, "all"), ("decode", 8, "all"), ("decode", 16, "all"),
+    ("decode", 32, "all"),
+    ("mixed", 1, "all"), ("mixed", 64, "all"), ("mixed", 512, "all"), ("mixed", 2048, "tiles"),
+    ("prefill", 4096, "tiles"),
+    ("skew", 8192, "tiles"),
 ]
 
 
@@ -48,14 +49,45 @@ def test_workload_parity(name, T, rows):
     wl = synth.WORKLOADS[name]
     pr = problem(name, max(wl.tokens))
     x, ids, tw = _inputs(wl, T)
-    out, _ = pr.run(x, ids, tw)
+    out, b = pr.run(x, ids, tw)
     torch.cuda.synchronize()
-    ref = pr.oracle(x, ids, tw, rows)
-    got = out if rows is None else out[rows]
+    assert torch.isfinite(out.float()).all()
+    sel = None
+    if rows == "tiles":
+        import fp8_moe_amd as fm
+        assert fm.binding_query(b, "path") == 1
+        sel, n_tiles = tile_edge_tokens(pr.model, wl.k)
+        print(f"  {len(sel)} tokens cover both ends of {n_tiles} tiles", flush=True)
+    ref = pr.oracle(x, ids, tw, sel)
+    got = out if sel is None else out[sel]
     rel_fro, rel_max, ok = compare(got, ref)
     print(f"  rel_fro={rel_fro:.3e} rel_max={rel_max:.3e}", flush=True)
     assert ok, (rel_fro, rel_max)
-    assert torch.isfinite(out.float()).all()
+
+
+@pytest.mark.parametrize("afmt", ["mxfp8", "nvfp4"])
+def test_prefill_layer_quantized_activations(afmt):
+    """The prefill layer's NVFP4 experts (E=128, H=4096, I=1536, top-8,
+    T=4096) with MXFP8 or NVFP4 activations, the shapes the benchmark times:
+    every token owning an end of a GEMM tile against the oracle."""
+    import dataclasses
+    import fp8_moe_amd as fm
+    print(f"prefill layer x {afmt}", flush=True)
+    wl = dataclasses.replace(synth.WORKLOADS["prefill"], act_format=afmt)
+    _PROBLEMS.clear()
+    torch.cuda.empty_cache()
+    pr = Problem(wl, 4096)
+    x, ids, tw = _inputs(wl, 4096)
+    out, b = pr.run(x, ids, tw)
+    torch.cuda.synchronize()
+    assert fm.binding_query(b, "path") == 1
+    sel, n_tiles = tile_edge_tokens(pr.model, wl.k)
+    print(f"  {len(sel)} tokens cover both ends of {n_tiles} tiles", flush=True)
+    ref = pr.oracle(x, ids, tw, sel)
+    rel_fro, rel_max, ok = compare(out[sel], ref)
+    print(f"  rel_fro={rel_fro:.3e} rel_max={rel_max:.3e}", flush=True)
+    del pr
+    assert ok, (rel_fro, rel_max)
 
 
 SMALL = [
@@ -152,12 +184,13 @@ def test_deterministic_and_permutation_invariant(name):
     assert torch.equal(a[perm].view(torch.int16), c.view(torch.int16))
 
 
-def test_graph_replay_matches_eager():
+@pytest.mark.parametrize("T", [1, 8])
+def test_graph_replay_matches_eager(T):
     import fp8_moe_amd as fm
     wl = synth.WORKLOADS["decode"]
     pr = problem("decode", 32)
-    x, ids, tw = _inputs(wl, 8)
-    out = torch.empty(8, wl.H, dtype=torch.bfloat16, device="cuda")
+    x, ids, tw = _inputs(wl, T)
+    out = torch.empty(T, wl.H, dtype=torch.bfloat16, device="cuda")
     b, _ = pr.model.bind(x, ids, tw, out)
     fm.run(b)
     torch.cuda.synchronize()
@@ -176,11 +209,12 @@ def test_graph_replay_matches_eager():
         _ = (x.float() * 2).sum()      # unrelated eager work between replays
 
 
-@pytest.mark.parametrize("afmt,T", [("nvfp4", 8), ("nvfp4", 200), ("mxfp8", 8), ("mxfp8", 200)])
+@pytest.mark.parametrize("afmt,T", [("nvfp4", 8), ("nvfp4", 20), ("nvfp4", 200), ("mxfp8", 8), ("mxfp8", 20),
+                                    ("mxfp8", 200)])
 def test_graph_replay_matches_eager_quantized(afmt, T):
-    """Graph replay of the paths with an activation-quantization stage
-    (NVFP4 weights with NVFP4 or MXFP8 activations), decode (T=8) and grouped
-    (T=200), bit-identical to the eager run on every replay."""
+    """Graph replay of the paths with activation quantization (NVFP4 weights
+    with NVFP4 or MXFP8 activations): split-K decode (T=8), two-phase decode
+    (T=20) and grouped (T=200), bit-identical to the eager run on every replay."""
     import fp8_moe_amd as fm
     print(f"graph replay {afmt} T={T}", flush=True)
     wl = small_workload(f"graph_{afmt}", 16, 512, 256, 4, True, "nvfp4", afmt)
@@ -188,7 +222,7 @@ def test_graph_replay_matches_eager_quantized(afmt, T):
     x, ids, tw = _inputs(wl, T)
     out = torch.empty(T, wl.H, dtype=torch.bfloat16, device="cuda")
     b, _ = pr.model.bind(x, ids, tw, out)
-    assert fm.binding_query(b, "path") == (2 if T * wl.k <= 256 else 1)
+    assert fm.binding_query(b, "path") == (3 if T * wl.k <= 32 else 2 if T * wl.k <= 256 else 1)
     fm.run(b)
     torch.cuda.synchronize()
     eager = out.clone()
@@ -263,11 +297,11 @@ def test_decode_and_grouped_paths_agree(name, T):
     x, ids, tw = _inputs(wl, T)
     b_dec, out_dec = pr.model.bind(x, ids, tw)
     b_grp, out_grp = grouped.bind(x, ids, tw)
-    assert fm.binding_query(b_dec, "path") == 2 and fm.binding_query(b_grp, "path") == 1
+    assert fm.binding_query(b_dec, "path") in (2, 3) and fm.binding_query(b_grp, "path") == 1
     fm.run(b_dec)
     fm.run(b_grp)
     torch.cuda.synchronize()
-    rows = None if T <= 8 else [0, T // 2, T - 1]
+    rows = None
     ref = pr.oracle(x, ids, tw, rows)
     for out in (out_dec, out_grp):
         got = out if rows is None else out[rows]
@@ -295,16 +329,27 @@ DECODE_EDGE = [
     ("nv_a4_dups_dropped", 16, 256, 128, 4, True, "nvfp4", "nvfp4", 20, "bad_dups"),
     ("separate_long_k", 8, 2304, 128, 2, True, "mxfp4", "bf16", 6, "uniform"),
     ("separate_many_groups", 8, 256, 1088, 2, True, "nvfp4", "bf16", 5, "uniform"),
+    # split-K decode (T*k <= 32): two 16-row blocks of one expert, ragged K, every
+    # activation format, K fragments in two rounds per wave, dropped and duplicate ids
+    ("sk_one_expert_two_blocks", 8, 256, 128, 8, True, "mxfp4", "bf16", 4, "one_expert"),
+    ("sk_ragged_k", 8, 160, 96, 3, False, "nvfp4", "bf16", 8, "uniform"),
+    ("sk_a8_relu2", 8, 288, 224, 4, False, "mxfp4", "mxfp8", 6, "uniform"),
+    ("sk_a8_gated_dups", 8, 256, 128, 4, True, "mxfp4", "mxfp8", 8, "bad_dups"),
+    ("sk_nv_a8", 8, 256, 128, 2, True, "nvfp4", "mxfp8", 10, "uniform"),
+    ("sk_nv_a4_relu2", 8, 288, 224, 4, False, "nvfp4", "nvfp4", 8, "one_expert"),
+    ("sk_long_k", 8, 2304, 128, 2, True, "mxfp4", "bf16", 6, "uniform"),
+    ("sk_k1", 4, 256, 128, 1, True, "nvfp4", "bf16", 1, "uniform"),
 ]
 
 
+@pytest.mark.parametrize("splitk", [True, False], ids=["splitk", "two_phase"])
 @pytest.mark.parametrize("case", DECODE_EDGE, ids=[c[0] for c in DECODE_EDGE])
-def test_decode_edge_cases(case):
+def test_decode_edge_cases(case, splitk):
     import fp8_moe_amd as fm
     name, E, H, I, k, gated, wfmt, afmt, T, kind = case
-    print(f"decode edge {case}", flush=True)
+    print(f"decode edge {case} splitk={splitk}", flush=True)
     wl = small_workload(name, E, H, I, k, gated, wfmt, afmt, x_lognormal=afmt == "mxfp8")
-    pr = Problem(wl, T, gen_device="cpu")
+    pr = Problem(wl, T, gen_device="cpu", splitk_max_pairs=0 if splitk else -1)
     x, ids, tw = _inputs(wl, T)
     ids = ids.clone()
     if kind == "one_expert":
@@ -317,9 +362,11 @@ def test_decode_edge_cases(case):
         ids[1, :] = 3
         ids[2, 2] = E + 7
     b, out = pr.model.bind(x, ids, tw)
-    assert fm.binding_query(b, "path") == 2
-    fused = afmt == "bf16" and not name.startswith("separate")
-    assert fm.binding_query(b, "num_stages") == (2 if fused else 3 + (afmt != "bf16"))
+    sk = splitk and T * k <= 32 and H <= 4096
+    assert fm.binding_query(b, "path") == (3 if sk else 2)
+    fused = afmt == "bf16" and not name.startswith("separate") and not name.startswith("sk_long")
+    expect_stages = 2 if sk else (2 if fused else 3 + (afmt != "bf16"))
+    assert fm.binding_query(b, "num_stages") == expect_stages
     out.fill_(1.0)
     fm.run(b)
     torch.cuda.synchronize()
@@ -331,11 +378,11 @@ def test_decode_edge_cases(case):
         assert torch.all(out == 0)
 
 
-@pytest.mark.parametrize("T,rows", [(8, None), (4096, [0, 2047, 4095])])
+@pytest.mark.parametrize("T,rows", [(8, None), (32, None)])
 def test_w4a4_at_prefill_shape(T, rows):
     """NVFP4 activations on the prefill layer's NVFP4 weights (E=128, H=4096,
-    I=1536, top-8): T=8 on the decode path (every row), T=4096 on the grouped
-    path (sampled rows)."""
+    I=1536, top-8) on the decode path, every row (T=4096 is covered with the
+    MXFP8 activations in test_prefill_layer_quantized_activations)."""
     import dataclasses
     print(f"w4a4 prefill shape T={T} rows={rows}", flush=True)
     wl = dataclasses.replace(synth.WORKLOADS["prefill"], act_format="nvfp4")

@@ -1,12 +1,13 @@
 """Routing stage on the GPU: counts, offsets, padded offsets, the stable
-permutation, pair positions and the tile list bit-exact with the oracle."""
+permutation and pair positions bit-exact with the oracle; the tile list
+(one of many valid ones) checked for validity by the oracle's checker."""
 import numpy as np
 import pytest
 import torch
 
 import synth
 from moe_cases import small_workload
-from oracle.routing import route
+from oracle.routing import check_tiles, route
 
 pytestmark = pytest.mark.gpu
 
@@ -62,8 +63,12 @@ def test_routing_bit_exact(kind, T, k, E):
     assert np.array_equal(region("offsets", E + 1), ref.offsets)
     assert np.array_equal(region("padded_offsets", E + 1), ref.padded_offsets)
     nt = region("ntiles", 4)
-    assert nt[0] == len(ref.tiles) and nt[1] == ref.padded_offsets[-1]
+    assert nt[1] == ref.padded_offsets[-1]
     assert np.array_equal(region("sorted", int(ref.padded_offsets[-1])), ref.sorted_ids)
     assert np.array_equal(region("pos", T * k), ref.pos)
-    tiles = region("tiles", 4 * len(ref.tiles)).reshape(-1, 4)
-    assert np.array_equal(tiles[:, :3], ref.tiles)
+    off, nbytes = model.plan.scratch_region("tiles")
+    assert 0 <= nt[0] <= nbytes // 16
+    tiles = region("tiles", 4 * int(nt[0])).reshape(-1, 4)
+    problems = check_tiles(tiles[:, :3], nt[0], ref.padded_offsets, E, fm.binding_query(b, "row_pad"),
+                           fm.binding_query(b, "tile_rows"))
+    assert problems == [], problems[:5]
