@@ -6,23 +6,26 @@
 // before the whole h of its expert exists.  Here the intermediate dimension
 // is cut into slices of 32 columns and one workgroup owns one (touched expert,
 // slice) item from start to end:
-//   1. it issues the DMA of the slice's W2 columns (one 32-wide lane group of
-//      every W2 fragment, codes and scales) into LDS, which runs while
-//   2. its 4 waves split K of the slice's gate/up (or w1) rows: weights,
-//      scales and activation rows go straight to registers, all of a wave's
-//      K fragments in flight at once; the activations are quantized in
-//      registers when the format asks for it (MXFP8 codes for the scaled
-//      fp8 x fp4 MFMA, or the exact MXFP8 / NVFP4 round trips as bf16);
+//   1. its 4 waves split K of the slice's gate/up (or w1) rows; each wave
+//      issues all of its weight loads at once, then the DMA of the slice's W2
+//      columns (one 32-wide lane group of every W2 fragment, codes and
+//      scales) into LDS, which lands while the rest runs;
+//   2. each wave stages the activation rows of the item's pairs over its own
+//      K range in its own LDS region, converted once per value: bf16, the
+//      exact MXFP8 / NVFP4 round trips as bf16, or MXFP8 codes and scales for
+//      the scaled fp8 x fp4 MFMA; the MFMAs read their activation operand
+//      from there;
 //   3. the split-K partial sums meet in LDS in a fixed wave order, wave 0
-//      applies the activation and the requantization of h (bf16, MXFP8 codes,
-//      or the MXFP8 / NVFP4 round trip) and leaves the h tile in LDS;
-//   4. the 4 waves multiply the h tile by the W2 slice from LDS (each wave a
-//      quarter of the output rows) and write fp32 partial rows
-//      part[pair][slice][H].
+//      applies the activation and the requantization of h (bf16, or the
+//      bf16 value of its MXFP8 / NVFP4 round trip) and leaves the h tile in
+//      LDS;
+//   4. the 4 waves multiply the h tile by the W2 slice from LDS, one bf16
+//      MFMA per W2 fragment (each wave a quarter of the output rows), and
+//      write fp32 partial rows part[pair][slice][H].
 // No workgroup waits for another, so the result does not depend on which
 // workgroups are resident.  The combine (decode_sk_combine_kernel) sums the
-// slices of each pair in ascending slice order and the pairs of each token
-// in ascending slot order, in fp32, and rounds once to bf16.
+// slices of each pair and the pairs of each token in a fixed order, in fp32,
+// and rounds once to bf16.
 #include "decode_common.h"
 
 namespace b12x {
@@ -60,19 +63,24 @@ struct SkParams {
                       // fragment q: position 64 G + 4 n + q
   int64_t part_bytes;
   int row_stride;     // 64 per fragment group + 64: consecutive rows start on different memory channels
+  int R;              // activation rows per tile (pairs of one expert processed together), <= kSkRows
+  int kper;           // W13 K fragments per wave
+  int xs;             // bytes per staged activation row
+  int xsc;            // offset of the staged E8M0 scales in a wave's region (MXFP8 codes)
+  int xwb;            // bytes of one wave's LDS region
+  int x_off;          // offset of the wave regions in the dynamic LDS
 };
 
-// LDS of one workgroup: routing, the split-K exchange, the h tile, and the
-// W2 slice (dynamic part after the static one).
+// Static LDS of one workgroup: routing and the h tile.  The dynamic part holds
+// the W2 slice (codes [NF2][256], scales [NF2][16] dwords, NF2 rounded up to
+// a multiple of 4) and one region per wave: that wave's staged activation
+// rows (row 0 all zeros for the rows outside the tile, rows 1..R the tile's
+// rows), which after its gate/up MFMAs holds its split-K partial sums.
 struct SkLds {
   uint32_t bits[4][32];         // each wave's copy of the touched-expert bitmap
-  f32x4 red[3][4][64];          // partial sums of waves 1..3, up to 4 fragments
-  uint16_t h16[16][kSkSlice];   // h tile, bf16 (16 rows x 32 columns)
-  uint8_t h8[16][kSkSlice];     // or MXFP8 codes
-  uint32_t hs[16];              // and their E8M0 scale codes
-  uint4 zero;                   // zeros for the lanes outside the slice
-  uint32_t neutral;             // a scale of 1 for those lanes
+  alignas(16) uint16_t h16[16][kSkSlice];  // h tile, bf16 (16 rows x 32 columns)
 };
+constexpr int kSkRows = 4;       // largest tile (rows staged per wave region)
 
 template <int WF>
 __device__ __forceinline__ float w_scale(uint32_t word, int kf, int s) {
@@ -83,67 +91,20 @@ __device__ __forceinline__ float w_scale(uint32_t word, int kf, int s) {
 // The bf16 operand of 8 activations from 4 dwords of bf16 values.
 __device__ __forceinline__ bf16x8 as_bf16x8(const uint4& v) { return __builtin_bit_cast(bf16x8, v); }
 
-// MXFP8 round trip of the lane's 32 consecutive bf16 values (one E8M0 block):
-// bf16 values of E4M3(v / 2^s) * 2^s.
-__device__ __forceinline__ void mx_roundtrip32(uint4 (&v)[4]) {
-  uint32_t amax = 0;
-#pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    const uint32_t w[4] = {v[s].x, v[s].y, v[s].z, v[s].w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) amax = max(amax, max(w[i] & 0x7FFFu, (w[i] >> 16) & 0x7FFFu));
-  }
-  const int sx = mx_scale_exp(amax << 16);
-#pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    uint32_t* w = (uint32_t*)&v[s];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      w[i] = mx_roundtrip_bf16(bf16_to_f32(w[i] & 0xFFFFu), sx) | (mx_roundtrip_bf16(bf16_to_f32(w[i] >> 16), sx) << 16);
-  }
-}
-
-// NVFP4 round trip (E2M1 * E4M3, exact in bf16) of the lane's 32 bf16 values
-// = two blocks of 16, against the per-tensor scale g.
-__device__ __forceinline__ void nv_roundtrip32(uint4 (&v)[4], float g) {
-#pragma unroll
-  for (int b = 0; b < 2; ++b) {
-    uint32_t amax = 0;
-#pragma unroll
-    for (int s = 2 * b; s < 2 * b + 2; ++s) {
-      const uint32_t w[4] = {v[s].x, v[s].y, v[s].z, v[s].w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) amax = max(amax, max(w[i] & 0x7FFFu, (w[i] >> 16) & 0x7FFFu));
-    }
-    const float sc = nv_block_scale(bits_f32(amax << 16), g), rc = nv_recip(sc, g);
-#pragma unroll
-    for (int s = 2 * b; s < 2 * b + 2; ++s) {
-      uint32_t* w = (uint32_t*)&v[s];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        w[i] = bf16_rne(nv_roundtrip(bf16_to_f32(w[i] & 0xFFFFu), sc, g, rc)) |
-               (bf16_rne(nv_roundtrip(bf16_to_f32(w[i] >> 16), sc, g, rc)) << 16);
-    }
-  }
-}
-
-// E4M3 codes of 8 bf16 values (one uint4) in a block with exponent s, as 2 dwords.
-__device__ __forceinline__ uint2 e4m3_codes8(const uint4& v, int s) {
+// Largest bf16 magnitude (bits) of the 8 values of a unit.
+__device__ __forceinline__ uint32_t unit_amax(const uint4& v) {
   const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-  uint32_t o[2];
-#pragma unroll
-  for (int h = 0; h < 2; ++h)
-    o[h] = e4m3_encode_scaled(w[2 * h] << 16, s) | (e4m3_encode_scaled(w[2 * h] & 0xFFFF0000u, s) << 8) |
-           (e4m3_encode_scaled(w[2 * h + 1] << 16, s) << 16) | (e4m3_encode_scaled(w[2 * h + 1] & 0xFFFF0000u, s) << 24);
-  return make_uint2(o[0], o[1]);
-}
-
-__device__ __forceinline__ uint32_t max_mag16(const uint4& a, const uint4& b) {
-  const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
   uint32_t m = 0;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) m = max(m, max(w[i] & 0x7FFFu, (w[i] >> 16) & 0x7FFFu));
+  for (int i = 0; i < 4; ++i) m = max(m, max(w[i] & 0x7FFFu, (w[i] >> 16) & 0x7FFFu));
   return m;
+}
+// max with lane ^ 1 (DPP quad permute [1, 0, 3, 2]) and with lane ^ 2 ([2, 3, 0, 1])
+__device__ __forceinline__ uint32_t max_lane_xor1(uint32_t v) {
+  return max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));
+}
+__device__ __forceinline__ uint32_t max_lane_xor2(uint32_t v) {
+  return max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));
 }
 
 // Routing of the split-K kernel, one wave at a time in registers (P <= 64: pair q
@@ -221,28 +182,27 @@ __global__ __launch_bounds__(kDecThreads) void decode_sk_kernel(const SkParams p
   constexpr bool NVRT = AF == kActNvRt;
   constexpr bool GATED = MODE == 1;
   constexpr int NF1 = GATED ? 4 : 2;  // W13 fragments of one slice (gate/up interleaved, or w1)
+  constexpr int GK = WF == B12X_WEIGHT_MXFP4 ? 4 : 2;  // K fragments per scale group
   __shared__ SkLds L;
-  extern __shared__ __attribute__((aligned(1024))) uint8_t dyn[];  // W2 slice: codes [NF2][256], scales [NF2][16]
+  extern __shared__ __attribute__((aligned(1024))) uint8_t dyn[];
+  const int nf2r = (p.NF2 + 3) / 4 * 4;
   uint8_t* const w2_lds = dyn;
-  uint32_t* const w2s_lds = (uint32_t*)(dyn + (size_t)((p.NF2 + 3) / 4 * 4) * 256);
+  uint32_t* const w2s_lds = (uint32_t*)(dyn + (size_t)nf2r * 256);
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int g = lane >> 4, r16 = lane & 15;
-  if (tid == 0) {
-    L.zero = make_uint4(0, 0, 0, 0);
-    L.neutral = WF == B12X_WEIGHT_MXFP4 ? 0x7F7F7F7Fu : 0x38383838u;
-  }
+  uint8_t* const xw = dyn + p.x_off + wave * p.xwb;  // this wave's region
   const SkRoute route = sk_route(p, L.bits[wave]);
-  const int64_t items = (int64_t)route.n_touched * p.n_slices;
-  const int kper = (p.KF1 + 3) / 4;
-  const int kb = wave * kper, ke = min(p.KF1, kb + kper);
+  const int items = route.n_touched * p.n_slices;
+  const int kb = wave * p.kper, ke = min(p.KF1, kb + p.kper);
+  const int nu = p.kper * 16;         // activation units per staged row
   const BufRsrc x_rsrc = make_rsrc(p.x, p.x_bytes);
   const BufRsrc part_rsrc = make_rsrc(p.part, p.part_bytes);
 
-  for (int64_t item = blockIdx.x; item < items; item += gridDim.x) {
-    const int slot = (int)(item / p.n_slices), j = (int)(item % p.n_slices);
+  for (int item = blockIdx.x; item < items; item += gridDim.x) {
+    const int slot = item / p.n_slices, j = item - slot * p.n_slices;
     const int e = sk_expert(route, slot);
     const uint64_t pairs = __ballot(route.id == e);  // the expert's pairs, ascending
     const int m = __builtin_popcountll(pairs);
@@ -257,7 +217,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_sk_kernel(const SkParams p
     const BufRsrc w2s_rsrc = make_rsrc(p.w2s + (int64_t)e * p.w2s_e, p.w2s_e);
     auto issue_w2_dma = [&]() {
       const int sgrp = WF == B12X_WEIGHT_MXFP4 ? kf2 >> 2 : kf2 >> 1;
-      const int n_dma = (p.NF2 + 3) / 4;  // each DMA instruction: 4 fragments x 16 lanes
+      const int n_dma = nf2r / 4;  // each DMA instruction: 4 fragments x 16 lanes
       for (int i = wave; i < n_dma; i += 4) {
         const int f2 = 4 * i + (lane >> 4);
         const bool v = f2 < p.NF2;
@@ -279,20 +239,25 @@ __global__ __launch_bounds__(kDecThreads) void decode_sk_kernel(const SkParams p
     const BufRsrc bs_rsrc = make_rsrc(p.w13s + (int64_t)e * p.w13s_e, p.w13s_e);
     const int f1 = NF1 * j;  // first W13 fragment of the slice
 
-    for (int r0 = 0; r0 < m; r0 += 16) {
-      // ---- 2. gate/up (or w1) over this wave's K range, KW fragments at a time
-      const int rr = r0 + r16;
-      const int tok = rr < m ? nth_set_bit(pairs, rr) / p.k : -1;
+    for (int r0 = 0; r0 < m; r0 += p.R) {
+      const int live = min(p.R, m - r0);  // rows of this tile
+      // tokens of the tile's rows (wave-uniform)
+      int pr[kSkRows], tok[kSkRows];
+#pragma unroll
+      for (int r = 0; r < kSkRows; ++r) {
+        pr[r] = r < live ? nth_set_bit(pairs, r0 + r) : 0;
+        tok[r] = pr[r] / p.k;
+      }
+      // this lane's staged row in the MFMA operand: r16 + 1, or the zero row 0
+      const int xrow = r16 < live ? r16 + 1 : 0;
+
+      // ---- 1./2. gate/up (or w1) over this wave's K range, KW fragments at a time
       f32x4 acc[NF1];
 #pragma unroll
       for (int f = 0; f < NF1; ++f) acc[f] = f32x4{0.f, 0.f, 0.f, 0.f};
       for (int c0 = kb; c0 < ke; c0 += KW) {
         uint4 q[KW][NF1];
-        uint32_t bs[KW][NF1];
-        uint4 xa[KW][4];
-        // scale words: one per fragment and scale group (4 K fragments for MXFP4, 2 for
-        // NVFP4); the chunk spans at most NG groups
-        constexpr int GK = WF == B12X_WEIGHT_MXFP4 ? 4 : 2;
+        // scale words: one per fragment and scale group; the chunk spans at most NG groups
         constexpr int NG = (KW + GK - 1) / GK + 1;
         const int sg0 = c0 / GK;
         uint32_t sw[NG][NF1];
@@ -308,69 +273,122 @@ __global__ __launch_bounds__(kDecThreads) void decode_sk_kernel(const SkParams p
         for (int i = 0; i < KW; ++i) {
           const int kf = c0 + i;
           const bool v = kf < ke;
-          const int su = kf / GK - sg0;  // 0 .. NG-1
 #pragma unroll
-          for (int f = 0; f < NF1; ++f) {
+          for (int f = 0; f < NF1; ++f)
             q[i][f] = buf_load16(b_rsrc, v ? (uint32_t)(((f1 + f) * p.KF1 + kf) * kFragBytes + lane * 16) : kBufOOB);
-            uint32_t word = sw[0][f];
+        }
+        __builtin_amdgcn_sched_barrier(0);  // the chunk's loads are all in flight before any MFMA waits
+        if (c0 == kb) {
+          // activation units of the tile over the wave's K range: lane unit (r, i) = row r,
+          // values 8 c .. 8 c + 7 of the wave's K range, c = lane + 64 i (nu <= 128);
+          // loaded after the weights, so the conversion below waits for everything
+          // issued so far
+          uint4 xv[kSkRows][2];
 #pragma unroll
-            for (int u = 1; u < NG; ++u) word = su == u ? sw[u][f] : word;
-            bs[i][f] = word;
+          for (int r = 0; r < kSkRows; ++r)
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+              const int c = lane + 64 * i;
+              const int kk = kb * kFragK + 8 * c;
+              const bool v = r < live && c < nu && kk < p.H;
+              xv[r][i] = buf_load16(x_rsrc, v ? (uint32_t)(((int64_t)tok[r] * p.x_stride + kk) * 2) : kBufOOB);
+            }
+          if (!dma_issued) {
+            issue_w2_dma();
+            dma_issued = true;
           }
-          // activations of row r16: bf16 operands hold K 32 g + [0, 32) of the fragment;
-          // the fp8 operand holds K 16 g + [0, 16) and 64 + 16 g + [0, 16)
-          const int64_t k0 = (int64_t)kf * kFragK;
-          const bool rv = v && tok >= 0;
+          __builtin_amdgcn_sched_barrier(0);
+          // zero row, then the tile's rows, converted once per value
+          if constexpr (!A8) {
+            for (int c = lane; c < nu; c += 64) *(uint4*)(xw + 16 * c) = make_uint4(0, 0, 0, 0);
+          } else {
+            for (int c = lane; c < nu / 2; c += 64) *(uint4*)(xw + 16 * c) = make_uint4(0, 0, 0, 0);
+            if (lane < p.kper) *(uint32_t*)(xw + p.xsc + 4 * lane) = 0u;
+          }
 #pragma unroll
-          for (int s = 0; s < 4; ++s) {
-            int64_t kk;
-            if constexpr (A8) kk = k0 + (s < 2 ? 16 * g + 8 * s : 64 + 16 * g + 8 * (s - 2));
-            else kk = k0 + 32 * g + 8 * s;
-            xa[i][s] = buf_load16(x_rsrc, rv && kk < p.H ? (uint32_t)((tok * p.x_stride + kk) * 2) : kBufOOB);
+          for (int r = 0; r < kSkRows; ++r) {
+            if (r >= p.R) break;  // wave-uniform
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+              if (64 * i >= nu) break;  // wave-uniform
+              const int c = lane + 64 * i;
+              const bool in = c < nu;
+              uint4 v = xv[r][i];
+              if constexpr (A8) {
+                // one E8M0 block = 4 units = 4 neighbouring lanes
+                const uint32_t amax = max_lane_xor2(max_lane_xor1(unit_amax(v)));
+                const int sx = mx_scale_exp(amax << 16);
+                const MxScale ms = mx_scale(sx);
+                const uint2 cw = make_uint2(e4m3_codes4_bf16(v.x, v.y, ms), e4m3_codes4_bf16(v.z, v.w, ms));
+                if (in) {
+                  *(uint2*)(xw + (r + 1) * p.xs + 8 * c) = cw;
+                  if ((c & 3) == 0) xw[p.xsc + (r + 1) * p.kper * 4 + (c >> 2)] = (uint8_t)(sx + 127);
+                }
+              } else {
+                if constexpr (RT) {
+                  const uint32_t amax = max_lane_xor2(max_lane_xor1(unit_amax(v)));
+                  const int sx = mx_scale_exp(amax << 16);
+                  uint32_t* w = (uint32_t*)&v;
+#pragma unroll
+                  for (int h = 0; h < 4; ++h)
+                    w[h] = mx_roundtrip_bf16(bf16_to_f32(w[h] & 0xFFFFu), sx) |
+                           (mx_roundtrip_bf16(bf16_to_f32(w[h] >> 16), sx) << 16);
+                }
+                if constexpr (NVRT) {  // one NVFP4 block = 2 units
+                  const float ga = p.ax[0];
+                  const uint32_t amax = max_lane_xor1(unit_amax(v));
+                  const float sc = nv_block_scale(bits_f32(amax << 16), ga), rc = nv_recip(sc, ga);
+                  uint32_t* w = (uint32_t*)&v;
+#pragma unroll
+                  for (int h = 0; h < 4; ++h)
+                    w[h] = bf16_rne(nv_roundtrip(bf16_to_f32(w[h] & 0xFFFFu), sc, ga, rc)) |
+                           (bf16_rne(nv_roundtrip(bf16_to_f32(w[h] >> 16), sc, ga, rc)) << 16);
+                }
+                if (in) *(uint4*)(xw + (r + 1) * p.xs + 16 * c) = v;
+              }
+            }
           }
         }
-        if (!dma_issued) {
-          issue_w2_dma();
-          dma_issued = true;
-        }
-        // every load of the chunk is in flight before the first MFMA waits
-        __builtin_amdgcn_sched_barrier(0);
+        // the chunk's MFMAs; a wave's LDS operations complete in order, so its staged
+        // rows are visible to its own reads
 #pragma unroll
         for (int i = 0; i < KW; ++i) {
           const int kf = c0 + i;
+          if (kf >= ke) break;  // wave-uniform
+          const int kl = kf - kb;
+          // scale words of this K fragment (selected here, where the loads are waited
+          // for anyway, not at issue time)
+          const int su = kf / GK - sg0;  // 0 .. NG-1, wave-uniform
+          uint32_t bs[NF1];
+#pragma unroll
+          for (int f = 0; f < NF1; ++f) {
+            bs[f] = sw[0][f];
+#pragma unroll
+            for (int u = 1; u < NG; ++u) bs[f] = su == u ? sw[u][f] : bs[f];
+          }
           if constexpr (!A8) {
-            if constexpr (RT) mx_roundtrip32(xa[i]);
-            if constexpr (NVRT) nv_roundtrip32(xa[i], p.ax[0]);
+            const uint8_t* xa = xw + xrow * p.xs + kl * 256 + g * 64;
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
+              const bf16x8 a = as_bf16x8(*(const uint4*)(xa + 16 * s));
 #pragma unroll
               for (int f = 0; f < NF1; ++f) {
                 const uint32_t dw = s == 0 ? q[i][f].x : s == 1 ? q[i][f].y : s == 2 ? q[i][f].z : q[i][f].w;
-                acc[f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xa[i][s]),
-                                                                 dequant8_bf16<WF>(dw, w_scale<WF>(bs[i][f], kf, s)),
+                acc[f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, dequant8_bf16<WF>(dw, w_scale<WF>(bs[f], kf, s)),
                                                                  acc[f], 0, 0, 0);
               }
             }
           } else {
-            // MXFP8 quantization of the activations: the first half (K 16 g ..) lies in
-            // block g / 2 and the second (K 64 + 16 g ..) in block 2 + g / 2; each block's
-            // other half sits in lane ^ 16
-            uint32_t m1 = max_mag16(xa[i][0], xa[i][1]), m2 = max_mag16(xa[i][2], xa[i][3]);
-            m1 = max(m1, (uint32_t)__shfl_xor((int)m1, 16));
-            m2 = max(m2, (uint32_t)__shfl_xor((int)m2, 16));
-            const int s1 = mx_scale_exp(m1 << 16), s2 = mx_scale_exp(m2 << 16);
-            const uint2 c0w = e4m3_codes8(xa[i][0], s1), c1w = e4m3_codes8(xa[i][1], s1);
-            const uint2 c2w = e4m3_codes8(xa[i][2], s2), c3w = e4m3_codes8(xa[i][3], s2);
-            const i32x8 afr = {(int)c0w.x, (int)c0w.y, (int)c1w.x, (int)c1w.y,
-                               (int)c2w.x, (int)c2w.y, (int)c3w.x, (int)c3w.y};
-            // the scale operand of lane group g is block g's: 0 <- own first half,
-            // 1 <- first half of lane group 2, 2 <- second half of lane group 1, 3 <- own second half
-            const int t1 = __shfl_xor(s1, 48), t2 = __shfl_xor(s2, 48);
-            const int sa = (g == 0 ? s1 : g == 1 ? t1 : g == 2 ? t2 : s2) + 127;
+            // fp8 operand of lane (r16, g): K 16 g + [0, 16) and 64 + 16 g + [0, 16) of the
+            // fragment; its scale operand is the E8M0 scale of K block g
+            const uint8_t* xa = xw + xrow * p.xs + kl * kFragK + 16 * g;
+            const uint4 lo = *(const uint4*)xa, hi = *(const uint4*)(xa + 64);
+            const int sa = xw[p.xsc + xrow * p.kper * 4 + kl * 4 + g];
+            const i32x8 afr = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
 #pragma unroll
             for (int f = 0; f < NF1; ++f) {
               const i32x8 bfr = {(int)q[i][f].x, (int)q[i][f].y, (int)q[i][f].z, (int)q[i][f].w, 0, 0, 0, 0};
-              const int sb = (int)((bs[i][f] >> (8 * (kf & 3))) & 0xFFu);
+              const int sb = (int)((bs[f] >> (8 * (kf & 3))) & 0xFFu);
               acc[f] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(afr, bfr, acc[f], 0, 4, 0, sa, 0, sb);
             }
           }
@@ -381,16 +399,21 @@ __global__ __launch_bounds__(kDecThreads) void decode_sk_kernel(const SkParams p
         issue_w2_dma();
         dma_issued = true;
       }
-      // ---- 3. split-K sums in wave order, activation and requantization of h by wave 0
+      // ---- 3. split-K sums in wave order (waves 1..3 leave theirs in their own regions),
+      // activation and requantization of h by wave 0
       if (wave != 0) {
 #pragma unroll
-        for (int f = 0; f < NF1; ++f) L.red[wave - 1][f][lane] = acc[f];
+        for (int f = 0; f < NF1; ++f) *(f32x4*)(xw + f * 1024 + lane * 16) = acc[f];
       }
       __syncthreads();
       if (wave == 0) {
         f32x4 v[NF1];
 #pragma unroll
-        for (int f = 0; f < NF1; ++f) v[f] = acc[f] + L.red[0][f][lane] + L.red[1][f][lane] + L.red[2][f][lane];
+        for (int f = 0; f < NF1; ++f) {
+          v[f] = acc[f];
+#pragma unroll
+          for (int w = 1; w < 4; ++w) v[f] += *(const f32x4*)(dyn + p.x_off + w * p.xwb + f * 1024 + lane * 16);
+        }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int row = 4 * g + i;
@@ -405,13 +428,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_sk_kernel(const SkParams p
               hv[qq] = z > 0.f ? z * z : 0.f;
             }
           }
-          if constexpr (A8) {
-            const float mx = row16_max(fmaxf(fabsf(hv[0]), fabsf(hv[1])));
-            const int sx = mx_scale_exp(f32_bits(mx));
-            L.h8[row][r16] = (uint8_t)e4m3_encode_scaled(f32_bits(hv[0]), sx);
-            L.h8[row][16 + r16] = (uint8_t)e4m3_encode_scaled(f32_bits(hv[1]), sx);
-            if (r16 == 0) L.hs[row] = (uint32_t)(sx + 127);
-          } else if constexpr (RT) {
+          if constexpr (A8 || RT) {  // bf16 value of the MXFP8 round trip (exact)
             const float mx = row16_max(fmaxf(fabsf(hv[0]), fabsf(hv[1])));
             const int sx = mx_scale_exp(f32_bits(mx));
             L.h16[row][r16] = (uint16_t)mx_roundtrip_bf16(hv[0], sx);
@@ -434,83 +451,49 @@ __global__ __launch_bounds__(kDecThreads) void decode_sk_kernel(const SkParams p
       wait_vmem();
       __syncthreads();
 
-      // ---- 4. partial down projection of the slice, a quarter of the W2 fragments per wave.
-      // One LDS read gives 4 fragments: lane group q holds the slice's K (32 values) of
-      // fragment f + q.  The MFMA with the h tile placed in lane group q only (zeros in
-      // the other lane groups) then yields fragment f + q's output rows.
-      uint4 hq[4];  // the h tile row r16: bf16 [8 s, 8 s + 8) for s = 0..3, or the codes
-      int hsc = 127;
-      if constexpr (!A8) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) hq[q] = *(const uint4*)&L.h16[r16][8 * q];
-      } else {
-        hq[0] = *(const uint4*)&L.h8[r16][0];
-        hq[1] = *(const uint4*)&L.h8[r16][16];
-        hsc = (int)L.hs[r16];
-      }
-      // output offsets of the lane's rows 4 g + i (column r16 of fragment 0), or out of range
+      // ---- 4. partial down projection of the slice, a quarter of the W2 fragments per
+      // wave: A = the h tile (lane (r16, g): row r16, K 8 g ..), B = fragment f's slice
+      // (lane (n, g): dword g of row n, K 8 g ..), one MFMA per fragment
+      const bf16x8 hA = as_bf16x8(*(const uint4*)&L.h16[r16][8 * g]);
+      // output offsets of the lane's rows 4 g + i (column r16 of fragment 0), or out of
+      // range: the tile's live rows (at most kSkRows = 4) are rows 0..3, in lane group 0
+      static_assert(kSkRows <= 4, "the live rows of a tile sit in lane group 0");
       uint32_t row_off[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = r0 + 4 * g + i;
-        row_off[i] = row < m ? (uint32_t)((((int64_t)nth_set_bit(pairs, row) * p.n_slices + j) * p.row_stride + 4 * r16) * 4)
-                             : kBufOOB;
-      }
-      // the 16 operands: h in lane group q, zeros in the others (bf16 path)
-      [[maybe_unused]] bf16x8 hvar[4][4];
-      if constexpr (!A8) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-#pragma unroll
-          for (int s2 = 0; s2 < 4; ++s2) hvar[q][s2] = as_bf16x8(g == q ? hq[s2] : L.zero);
-      }
+      for (int i = 0; i < 4; ++i)
+        row_off[i] = g == 0 && i < live ? (uint32_t)((((int64_t)pr[i] * p.n_slices + j) * p.row_stride + 4 * r16) * 4)
+                                        : kBufOOB;
       const int per = (p.NF2 + 15) / 16 * 4;  // fragments per wave, a multiple of 4
       const int fb = wave * per, fe = min(p.NF2, fb + per);
-      for (int f0 = fb; f0 < fe; f0 += 4) {
-        // lane (r16, g) reads fragment f0 + g (fragments past the end repeat the last one)
-        const int fq = min(f0 + g, p.NF2 - 1);
-        const uint4 bq = *(const uint4*)(w2_lds + fq * 256 + r16 * 16);
-        const uint32_t bsw = w2s_lds[fq * 16 + r16];
-        f32x4 y[4];
+      const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+      constexpr int FB = 16;  // fragments per batch: their LDS reads are all issued first
+      for (int f00 = fb; f00 < fe; f00 += FB) {
+        uint32_t dw[FB], bsw[FB];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) y[q] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if constexpr (!A8) {
-          bf16x8 wb[4];
-#pragma unroll
-          for (int s = 0; s < 4; ++s) {
-            const uint32_t dw = s == 0 ? bq.x : s == 1 ? bq.y : s == 2 ? bq.z : bq.w;
-            wb[s] = dequant8_bf16<WF>(dw, w_scale<WF>(bsw, kf2, s));
-          }
-#pragma unroll
-          for (int s = 0; s < 4; ++s) {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) y[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hvar[q][s], wb[s], y[q], 0, 0, 0);
-          }
-        } else {
-          // fp8 operand: K [32 q, 32 q + 32) sits in lane groups 2 (q & 1) and 2 (q & 1) + 1,
-          // first half for q < 2, second half otherwise
-          const i32x8 bfr = {(int)bq.x, (int)bq.y, (int)bq.z, (int)bq.w, 0, 0, 0, 0};
-          const int sb = (int)((bsw >> (8 * (kf2 & 3))) & 0xFFu);
-          const uint4 hv = hq[g & 1];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const bool act = (g >> 1) == (q & 1);
-            const uint4 lo = act && (q >> 1) == 0 ? hv : L.zero;
-            const uint4 hi = act && (q >> 1) == 1 ? hv : L.zero;
-            const i32x8 afr = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-            y[q] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(afr, bfr, y[q], 0, 4, 0, g == q ? hsc : 127, 0,
-                                                                    sb);
-          }
+        for (int qf = 0; qf < FB; ++qf) {
+          const int f = min(f00 + qf, p.NF2 - 1);  // fragments past the end repeat the last one
+          dw[qf] = *(const uint32_t*)(w2_lds + f * 256 + r16 * 16 + g * 4);
+          bsw[qf] = w2s_lds[f * 16 + r16];
         }
-        // lane (r16, g) holds rows 4 g + i of output columns 16 (f0 + q) + r16, q = 0..3:
-        // one 16-byte store per row (the partial rows keep the 4 fragments of a group
-        // side by side for each column; the combine reads them in that order)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          if (r0 + i >= m) continue;  // no lane holds a live row i (rows 4 g + i >= i)
-          const uint32_t off = row_off[i] != kBufOOB ? row_off[i] + (uint32_t)(64 * f0) : kBufOOB;
-          const float4 v = make_float4(y[0][i] * g2, y[1][i] * g2, y[2][i] * g2, y[3][i] * g2);
-          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, v), part_rsrc, off, 0, 0);
+        for (int b4 = 0; b4 < FB / 4; ++b4) {
+          const int f0 = f00 + 4 * b4;
+          if (f0 >= fe) break;  // wave-uniform
+          f32x4 y[4];
+#pragma unroll
+          for (int qf = 0; qf < 4; ++qf)
+            y[qf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                hA, dequant8_bf16<WF>(dw[4 * b4 + qf], w_scale<WF>(bsw[4 * b4 + qf], kf2, g)), zero4, 0, 0, 0);
+          // lane (r16, g) holds rows 4 g + i of output columns 16 (f0 + q) + r16, q = 0..3:
+          // one 16-byte store per row (the partial rows keep the 4 fragments of a group
+          // side by side for each column; the combine reads them in that order)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            if (i >= live) continue;  // no lane holds a live row i (rows 4 g + i >= i)
+            const uint32_t off = row_off[i] != kBufOOB ? row_off[i] + (uint32_t)(64 * f0) : kBufOOB;
+            const float4 v = make_float4(y[0][i] * g2, y[1][i] * g2, y[2][i] * g2, y[3][i] * g2);
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, v), part_rsrc, off, 0, 0);
+          }
         }
       }
     }
@@ -519,23 +502,27 @@ __global__ __launch_bounds__(kDecThreads) void decode_sk_kernel(const SkParams p
   wait_vmem();
 }
 
-// out[t] = sum_j w[t, j] * (sum_s part[t k + j][s]) over the valid pairs:
-// slices in ascending order, then slots in ascending order, fp32, one bf16
-// rounding.  One wave per workgroup; lane (g, j) covers 4 positions of the
-// partial rows (columns n of the 4 fragments of a group) for slot j: it loads
-// all of the slot's slices, 16 at a time in flight, and sums them.  The lanes
-// of the k slots of one position group then meet through lane exchanges, added
-// in slot order.  A call with a few tokens thus spreads its partial rows over
-// many compute units, with no LDS and no barrier.
+// out[t] = sum_j w[t, j] * (sum_s part[t k + j][s]) over the valid pairs, in
+// fp32 with one bf16 rounding.  One wave per workgroup; lane (g, j, u) covers
+// 4 positions of the partial rows (column n of the 4 fragments of a group G)
+// for slot j and part u of the slices: it loads the slices
+// [u c, u c + c) of its pair (c = ceil(slices / S)), 16 at a time in flight,
+// and sums them in ascending order.  The S parts of a slot are then added in
+// part order and the slots in slot order through lane exchanges, so the sum
+// order is fixed by (k, S, number of slices) alone.  A call with a few tokens
+// thus spreads its partial rows over many compute units, each lane with few
+// loads, and with no LDS and no barrier.
 constexpr int kSkCombineLoads = 16;
 __global__ __launch_bounds__(64) void decode_sk_combine_kernel(const float* __restrict__ part, int64_t part_bytes,
                                                                 const int32_t* __restrict__ ids, int E,
                                                                 const float* __restrict__ tw, int64_t T, int k,
-                                                                int H, int n_slices, int row_stride, int n_groups,
-                                                                uint16_t* __restrict__ out, int64_t out_stride) {
+                                                                int S, int H, int n_slices, int row_stride,
+                                                                int n_groups, uint16_t* __restrict__ out,
+                                                                int64_t out_stride) {
   const int lane = threadIdx.x;
-  const int PG = 64 / k;                     // position groups per wave (k <= 64)
-  const int pg = lane / k, j = lane % k;
+  const int KS = k * S;                      // lanes per position group (<= 64)
+  const int PG = 64 / KS;                    // position groups per wave
+  const int pg = lane / KS, j = (lane % KS) / S, u = lane % S;
   const int64_t t = blockIdx.y;
   const int grp = blockIdx.x * PG + pg;      // 4 positions: fragments 4 G .. 4 G + 3, column n
   const bool in = pg < PG && grp < n_groups;
@@ -547,35 +534,45 @@ __global__ __launch_bounds__(64) void decode_sk_combine_kernel(const float* __re
   // dropped pair are read but never added
   const int e = ids[t * k + j];
   const float w = tw[t * k + j];
+  const int c = (n_slices + S - 1) / S;
+  const int s_beg = u * c, s_end = min(n_slices, s_beg + c);
   const uint32_t base = in ? (uint32_t)((((t * k + j) * n_slices) * (int64_t)row_stride + pos) * 4) : kBufOOB;
   float4 y = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int s0 = 0; s0 < n_slices; s0 += kSkCombineLoads) {
+  for (int s0 = s_beg; s0 < s_end; s0 += kSkCombineLoads) {
     float4 v[kSkCombineLoads];
 #pragma unroll
-    for (int u = 0; u < kSkCombineLoads; ++u) {
-      const uint32_t off = s0 + u < n_slices ? base + (uint32_t)((s0 + u) * row_stride * 4) : kBufOOB;
-      v[u] = __builtin_bit_cast(float4, buf_load16(rsrc, off));
+    for (int q = 0; q < kSkCombineLoads; ++q) {
+      const uint32_t off = s0 + q < s_end ? base + (uint32_t)((s0 + q) * row_stride * 4) : kBufOOB;
+      v[q] = __builtin_bit_cast(float4, buf_load16(rsrc, off));
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int u = 0; u < kSkCombineLoads; ++u) {
-      y.x += v[u].x; y.y += v[u].y; y.z += v[u].z; y.w += v[u].w;
+    for (int q = 0; q < kSkCombineLoads; ++q) {
+      y.x += v[q].x; y.y += v[q].y; y.z += v[q].z; y.w += v[q].w;
     }
+  }
+  // parts of this lane's slot, in part order (every lane of the slot gets the sum)
+  const int src_j = pg * KS + j * S;
+  float4 ys = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int q = 0; q < S; ++q) {
+    ys.x += __shfl(y.x, src_j + q); ys.y += __shfl(y.y, src_j + q);
+    ys.z += __shfl(y.z, src_j + q); ys.w += __shfl(y.w, src_j + q);
   }
   const bool live = e >= 0 && e < E;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  const int src0 = pg * k;
-  for (int u = 0; u < k; ++u) {  // slot u of this position group, in slot order
-    const float yx = __shfl(y.x, src0 + u), yy = __shfl(y.y, src0 + u);
-    const float yz = __shfl(y.z, src0 + u), yw = __shfl(y.w, src0 + u);
-    const float wu = __shfl(w, src0 + u);
-    const int lu = __shfl((int)live, src0 + u);
-    if (lu) {
-      acc.x = fmaf(wu, yx, acc.x); acc.y = fmaf(wu, yy, acc.y);
-      acc.z = fmaf(wu, yz, acc.z); acc.w = fmaf(wu, yw, acc.w);
+  const int src0 = pg * KS;
+  for (int q = 0; q < k; ++q) {  // slot q of this position group, in slot order
+    const int src = src0 + q * S;
+    const float yx = __shfl(ys.x, src), yy = __shfl(ys.y, src);
+    const float yz = __shfl(ys.z, src), yw = __shfl(ys.w, src);
+    const float wq = __shfl(w, src);
+    const int lq = __shfl((int)live, src);
+    if (lq) {
+      acc.x = fmaf(wq, yx, acc.x); acc.y = fmaf(wq, yy, acc.y);
+      acc.z = fmaf(wq, yz, acc.z); acc.w = fmaf(wq, yw, acc.w);
     }
   }
-  if (in && j == 0) {  // columns 64 G + 16 q + n
+  if (in && j == 0 && u == 0) {  // columns 64 G + 16 q + n
     const float a4[4] = {acc.x, acc.y, acc.z, acc.w};
 #pragma unroll
     for (int q = 0; q < 4; ++q)
@@ -619,22 +616,38 @@ static SkParams sk_params(const BindingImpl& b) {
   p.part = b.y;
   p.row_stride = sk_row_stride(b.H);
   p.part_bytes = b.T * b.k * (int64_t)p.n_slices * p.row_stride * 4;
+  // LDS: the W2 slice, then one region per wave (staged activation rows: a zero row
+  // and R rows over the wave's K range, bf16 or MXFP8 codes plus their scales; at
+  // least the wave's split-K partial sums)
+  const bool codes = a8_native(b.wfmt, b.afmt);
+  p.R = (int)(b.T < kSkRows ? (b.T > 0 ? b.T : 1) : kSkRows);
+  p.kper = (p.KF1 + 3) / 4;
+  const int kw = p.kper * kFragK;
+  p.xs = codes ? kw + 32 : 2 * kw + 32;
+  p.xsc = (p.R + 1) * p.xs;
+  int bytes = p.xsc + (codes ? (p.R + 1) * p.kper * 4 : 0);
+  if (bytes < (b.gated ? 4 : 2) * 1024) bytes = (b.gated ? 4 : 2) * 1024;
+  p.xwb = (bytes + 15) / 16 * 16;
+  p.x_off = (p.NF2 + 3) / 4 * 4 * (256 + 64);
   return p;
 }
 
-size_t sk_dyn_lds(int nf2) { return (size_t)((nf2 + 3) / 4 * 4) * (256 + 64); }
+static size_t sk_dyn_lds(const SkParams& p) { return (size_t)p.x_off + 4 * (size_t)p.xwb; }
 
 template <int WF, int AF, int MODE, int KW>
 static int launch_sk_t(const BindingImpl& b, const SkParams& p, hipStream_t s) {
+  // resident workgroups per device, for the LDS size they were computed with
   static int cache[64];
+  static size_t cache_lds[64];
   auto kernel = decode_sk_kernel<WF, AF, MODE, KW>;
-  const size_t lds = sk_dyn_lds(p.NF2);
+  const size_t lds = sk_dyn_lds(p);
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-  if (!cache[dev]) {
+  if (!cache[dev] || cache_lds[dev] != lds) {
     int per_cu = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kDecThreads, lds) != hipSuccess || per_cu < 1)
       per_cu = 1;
+    cache_lds[dev] = lds;
     cache[dev] = per_cu * device_cu_count();
   }
   const int64_t max_slots = b.T * b.k < b.E ? b.T * b.k : b.E;
@@ -647,9 +660,13 @@ static int launch_sk_t(const BindingImpl& b, const SkParams& p, hipStream_t s) {
 
 template <int WF, int AF, int MODE>
 static int launch_sk_kw(const BindingImpl& b, const SkParams& p, hipStream_t s) {
-  const int kper = (p.KF1 + 3) / 4;
-  if (kper <= 2) return launch_sk_t<WF, AF, MODE, 2>(b, p, s);
-  return launch_sk_t<WF, AF, MODE, 4>(b, p, s);
+  // a wave holds up to 4 K fragments of the 4 gate/up fragment rows, or 8 of the 2 w1 rows
+  if constexpr (MODE == 1) {
+    return launch_sk_t<WF, AF, MODE, 4>(b, p, s);
+  } else {
+    if (p.kper <= 4) return launch_sk_t<WF, AF, MODE, 4>(b, p, s);
+    return launch_sk_t<WF, AF, MODE, 8>(b, p, s);
+  }
 }
 
 template <int MODE>
@@ -663,6 +680,8 @@ static int launch_sk_fmt(const BindingImpl& b, const SkParams& p, hipStream_t s)
 
 int launch_decode_sk(const BindingImpl& b, hipStream_t s) {
   const SkParams p = sk_params(b);
+  // the staging holds up to kSkRows rows of at most 128 units (8 K fragments) per wave
+  if (p.R > kSkRows || p.kper > 8) return (int)hipErrorInvalidValue;
   return b.gated ? launch_sk_fmt<1>(b, p, s) : launch_sk_fmt<2>(b, p, s);
 }
 
@@ -670,11 +689,16 @@ int launch_decode_sk_combine(const BindingImpl& b, hipStream_t s) {
   if (b.T == 0) return 0;
   const int row_stride = sk_row_stride(b.H);
   const int n_groups = (row_stride - kSkRowPad) / 4;
-  const int per_wave = 64 / b.k;
+  const int n_slices = b.I / kSkSlice;
+  // split the slices of a slot over S lanes while a lane would wait for more than one
+  // round of loads, keeping at least 2 position groups (32 contiguous bytes) per wave
+  int S = 1;
+  while (b.k * S * 4 <= 64 && (n_slices + S - 1) / S > kSkCombineLoads) S *= 2;
+  const int per_wave = 64 / (b.k * S);
   const dim3 grid((unsigned)((n_groups + per_wave - 1) / per_wave), (unsigned)b.T);
-  const int64_t part_bytes = b.T * b.k * (int64_t)(b.I / kSkSlice) * row_stride * 4;
+  const int64_t part_bytes = b.T * b.k * (int64_t)n_slices * row_stride * 4;
   hipLaunchKernelGGL(decode_sk_combine_kernel, grid, dim3(64), 0, s, (const float*)b.y, part_bytes, b.ids, b.E, b.tw,
-                     b.T, b.k, b.H, b.I / kSkSlice, row_stride, n_groups, b.out, b.out_stride);
+                     b.T, b.k, S, b.H, n_slices, row_stride, n_groups, b.out, b.out_stride);
   return (int)hipGetLastError();
 }
 

@@ -166,21 +166,44 @@ __device__ __forceinline__ float e4m3_value(uint32_t c) {
   return (c & 0x80u) ? -mag : mag;
 }
 
-// bf16 bits of the MXFP8 round trip of v (fp32) in a block with exponent s
-// (-127 .. 127): E4M3 code of v / 2^s, decoded and multiplied by 2^s (exact
-// in fp32; exact in bf16 above its subnormal range, 2^-133).  Done by the
-// hardware conversions with 2^s as their scale operand; they round to nearest
-// even but do not saturate, so v is clamped to 448 * 2^s first.  Checked on
-// the device against e4m3_encode_scaled + e4m3_value for every s and 12-bit
-// mantissas over 23 binades around it: equal up to the sign of a zero.
-__device__ __forceinline__ uint32_t mx_roundtrip_bf16(float v, int s) {
-  typedef short s16x2 __attribute__((ext_vector_type(2)));
-  const float scale = bits_f32((uint32_t)(s + 127) << 23);
-  const float lim = ldexpf(448.0f, s);
-  const float c = fminf(fmaxf(v, -lim), lim);
+typedef short s16x2 __attribute__((ext_vector_type(2)));
+
+// Operands of the scaled E4M3 conversions for a block with exponent s
+// (-127 .. 127): the scale 2^s (the conversions read only its exponent
+// field, so s = -127 gives 2^-127) and the saturation limit 448 * 2^s.
+struct MxScale {
+  float scale, lim;
+};
+__device__ __forceinline__ MxScale mx_scale(int s) { return {bits_f32((uint32_t)(s + 127) << 23), ldexpf(448.0f, s)}; }
+
+// E4M3 codes of a / 2^s and b / 2^s (finite a, b) into byte pair HI of o:
+// the hardware conversion rounds to nearest even but does not saturate, so
+// both are clamped to 448 * 2^s first.  Equal to e4m3_encode_scaled up to the
+// sign of a zero (mx_roundtrip_bf16, built on it, is compared element by
+// element with the integer encoder's round trip over every finite bf16 value
+// and every block exponent).
+template <bool HI>
+__device__ __forceinline__ s16x2 e4m3_pk_scaled(s16x2 o, float a, float b, MxScale m) {
+  return __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(o, __builtin_amdgcn_fmed3f(a, -m.lim, m.lim),
+                                                  __builtin_amdgcn_fmed3f(b, -m.lim, m.lim), m.scale, HI);
+}
+
+// E4M3 codes of the 4 bf16 values in w0, w1 (low half first) of a block: one dword.
+__device__ __forceinline__ uint32_t e4m3_codes4_bf16(uint32_t w0, uint32_t w1, MxScale m) {
   s16x2 o = {0, 0};
-  o = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(o, c, c, scale, false);
-  return bf16_rne(__builtin_amdgcn_cvt_scalef32_pk_f32_fp8((uint32_t)(uint16_t)o.x, scale, false)[0]);
+  o = e4m3_pk_scaled<false>(o, bits_f32(w0 << 16), bits_f32(w0 & 0xFFFF0000u), m);
+  o = e4m3_pk_scaled<true>(o, bits_f32(w1 << 16), bits_f32(w1 & 0xFFFF0000u), m);
+  return __builtin_bit_cast(uint32_t, o);
+}
+
+// bf16 bits of the MXFP8 round trip of v (fp32, finite) in a block with
+// exponent s (-127 .. 127): E4M3 code of v / 2^s, decoded and multiplied by
+// 2^s (exact in fp32; exact in bf16 above its subnormal range, 2^-133), by
+// the scaled hardware conversions both ways.
+__device__ __forceinline__ uint32_t mx_roundtrip_bf16(float v, int s) {
+  const MxScale m = mx_scale(s);
+  const s16x2 o = e4m3_pk_scaled<false>(s16x2{0, 0}, v, v, m);
+  return bf16_rne(__builtin_amdgcn_cvt_scalef32_pk_f32_fp8((uint32_t)(uint16_t)o.x, m.scale, false)[0]);
 }
 
 // Largest value over the 16 lanes of this lane's DPP row (lanes 16r .. 16r+15),
