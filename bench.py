@@ -14,9 +14,12 @@ timed for the roofline object, in the sequence it runs in: graphs of (fused
 kernel, combine) less graphs of the combines alone; its HBM traffic comes from
 the committed counter record in profiles/ when that record matches the kernel
 sources.  Extra lines report
-prefill (NVFP4, T=4096) TFLOP/s, the dense block-scaled GEMM (4096^3), the
-W4A8 (MXFP8 x MXFP4, ReLU^2) T=1 decode, and the CPU oracle's rate on a
-bounded sample.
+prefill (NVFP4, T=4096) TFLOP/s with bf16, MXFP8 and NVFP4 activations, the
+dense block-scaled GEMM (4096^3), and under "configs" every configuration
+(tiny T=16, decode T=1/8/32, mixed MXFP4 x MXFP8 ReLU^2 T=1/64/512/2048,
+prefill T=4096, large skewed T=8192): time per call, its roofline fraction
+(HBM on touched-expert weight bytes, or the bf16 MFMA peak), and the CPU
+oracle timed on a bounded sample of the same inputs.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extra] [--no-cpu]
        python bench.py --decode-t T [--steps K]   (one T only, for counter and trace runs)
@@ -369,27 +372,155 @@ def bench_dense_mm(fm, synth, torch, stream, m=4096, n=4096, k=4096, reps=20):
     return res
 
 
-def bench_mixed_t1(fm, synth, torch, stream, reps=50):
+def cpu_sample(wl, w_dev, x, ids, tw, max_experts=None, reps=1, seed=0):
+    """The fp64 oracle on the host for one call's inputs (device tensors).  With
+    max_experts, only the pairs of that many touched experts (a fixed-seed random
+    draw) are computed and the time is scaled by touched / sampled experts (the
+    oracle's cost is per expert: one dequantization plus the expert's rows).
+    Returns seconds per call (median of `reps`) and what was run."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    from oracle import Weights, fused_moe
+    import synth
+    import torch
+    cores = len(os.sched_getaffinity(0))
+    ids_h, tw_h = ids.cpu().numpy(), tw.cpu().numpy()
+    touched = sorted({int(e) for e in ids_h.reshape(-1) if 0 <= e < wl.E})
+    sample = touched
+    if max_experts is not None and len(touched) > max_experts:
+        rng = np.random.default_rng(seed)
+        sample = sorted(int(e) for e in rng.choice(touched, size=max_experts, replace=False))
+    ids_s = np.where(np.isin(ids_h, sample), ids_h, -1).astype(np.int32)
+    weights = Weights(wl.weight_format, wl.gated, num_experts=wl.E, **synth.oracle_weights_kwargs(w_dev, sample))
+    xb = x.cpu().view(torch.int16).numpy().view(np.uint16)
+    times = []
+    with threadpool_limits(limits=cores):
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            fused_moe(xb, ids_s, tw_h, weights, act_format=wl.act_format)
+            times.append(time.perf_counter() - t0)
+    med = sorted(times)[len(times) // 2]
+    sec = med * len(touched) / len(sample)
+    T = ids_h.shape[0]
+    what = (f"T={T}: all {len(touched)} touched experts, median of {reps}" if len(sample) == len(touched) else
+            f"T={T}: the pairs of {len(sample)} of {len(touched)} touched experts ({med:.2f} s), "
+            f"scaled by {len(touched)}/{len(sample)}")
+    return {"seconds_per_call": round(sec, 4), "tokens_per_s": round(T / sec, 2),
+            "gflops": round(6.0 * wl.H * wl.I * T * wl.k / sec / 1e9, 3) if wl.gated else
+                      round(4.0 * wl.H * wl.I * T * wl.k / sec / 1e9, 3),
+            "cores": cores, "kind": "oracle", "sample": what}
+
+
+def hbm_roofline(nbytes, sec):
+    ach = nbytes / sec / 1e9
+    return {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(ach / HBM_PEAK_GBS, 4), "scope": "whole call, touched-expert weight bytes"}
+
+
+def mfma_roofline(flops, sec):
+    ach = flops / sec / 1e12
+    return {"bound": "mfma", "achieved": round(ach, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(ach / BF16_PEAK_TFLOPS, 4), "scope": "whole call, bf16 dense peak"}
+
+
+def bench_mixed(fm, synth, torch, stream, reps=20, cpu=True):
+    """Mixed batch (MXFP4 weights x MXFP8 activations, ReLU^2, E=128, H=I=2880,
+    top_k=4) at each of its batch sizes: time per call over graphs of several
+    input sets (two weight copies rotate), HBM roofline on touched-expert bytes."""
     wl = synth.WORKLOADS["mixed"]
     w = synth.make_weights(wl, device="cuda")
     wp = fm.plan_weights(wl.E, wl.H, wl.I, wl.gated, wl.weight_format)
     copies = [fm.prepare_weights(wp, w["w13_codes"], w["w13_scales"], w["w2_codes"], w["w2_scales"])
               for _ in range(2)]   # 2 x 1.13 GB
-    del w
-    plan = fm.plan(wp, wl.k, 1, wl.act_format, "relu2")
+    res = {}
+    for T in wl.tokens:
+        plan = fm.plan(wp, wl.k, T, wl.act_format, "relu2")
+        scratch = fm.alloc_scratch(plan)
+        n_sets = 4 if T <= 64 else 2
+        bs, nbytes, nexp = [], 0, 0
+        for s in range(n_sets):
+            x = synth.make_x(wl, T, device="cuda", salt=s)
+            ids, tw = synth.make_routing(wl, T, device="cuda", salt=s)
+            out = torch.empty(T, wl.H, dtype=torch.bfloat16, device="cuda")
+            bs.append((fm.bind(plan, scratch, copies[s % 2], x, ids, tw, out), x, ids, tw, out))
+            ne = touched_experts(ids.cpu(), wl.E)
+            nexp += ne
+            nbytes += ne * wl.weight_bytes_per_expert()
+        g = capture(torch, fm, [t[0] for t in bs], stream)
+        g.replay()
+        sec = time_graph(torch, g, stream, reps) / (reps * n_sets)
+        path = fm.binding_query(bs[0][0], "path")
+        r = {"us": round(sec * 1e6, 3), "touched_experts": nexp / n_sets,
+             "path": {3: "decode, split-K", 2: "decode"}.get(path, "grouped"),
+             "roofline": hbm_roofline(nbytes / n_sets, sec)}
+        if cpu:
+            _, x, ids, tw, _ = bs[0]
+            r["cpu_baseline"] = cpu_sample(wl, w, x, ids, tw, max_experts=None if T == 1 else 4,
+                                           reps=3 if T == 1 else 1)
+        res[f"T{T}"] = r
+        del bs, g, scratch, plan
+    del copies, w
+    torch.cuda.empty_cache()
+    return res
+
+
+def bench_gemm_config(fm, synth, torch, stream, name, reps=10, cpu=True):
+    """A prefill-sized config (one batch): time per call, bf16 MFMA roofline on the
+    FFN FLOPs, stage times, and the oracle on a sample of its experts."""
+    wl = synth.WORKLOADS[name]
+    T = wl.tokens[0]
+    w = synth.make_weights(wl, device="cuda")
+    wp = fm.plan_weights(wl.E, wl.H, wl.I, wl.gated, wl.weight_format)
+    ex = fm.prepare_weights(wp, w["w13_codes"], w["w13_scales"], w["w2_codes"], w["w2_scales"],
+                            w["w13_global"], w["w2_global"])
+    plan = fm.plan(wp, wl.k, T, wl.act_format, "silu")
     scratch = fm.alloc_scratch(plan)
-    bs, nbytes = [], 0
-    for s in range(N_SETS):
-        x = synth.make_x(wl, 1, device="cuda", salt=s)
-        ids, tw = synth.make_routing(wl, 1, device="cuda", salt=s)
-        out = torch.empty(1, wl.H, dtype=torch.bfloat16, device="cuda")
-        bs.append((fm.bind(plan, scratch, copies[s % 2], x, ids, tw, out), x, ids, tw, out))
-        nbytes += touched_experts(ids.cpu(), wl.E) * wl.weight_bytes_per_expert()
-    g = capture(torch, fm, [t[0] for t in bs], stream)
+    x = synth.make_x(wl, T, device="cuda")
+    ids, tw = synth.make_routing(wl, T, device="cuda")
+    out = torch.empty(T, wl.H, dtype=torch.bfloat16, device="cuda")
+    b = fm.bind(plan, scratch, ex, x, ids, tw, out)
+    for _ in range(2):
+        fm.run(b, stream=stream)
+    g = capture(torch, fm, [b], stream)
     g.replay()
-    sec = time_graph(torch, g, stream, reps) / (reps * N_SETS)
-    gbs = nbytes / N_SETS / sec / 1e9
-    return {"T": 1, "us": sec * 1e6, "weight_GBs": gbs, "frac_hbm": gbs / HBM_PEAK_GBS}
+    samples = time_graph_samples(torch, g, stream, reps)
+    sec = sorted(samples)[len(samples) // 2]
+    flops = 6.0 * wl.H * wl.I * T * wl.k
+    stages = {st: round(time_stage_launches(torch, fm, [b], st, stream, repeats=2) * 1e6, 1)
+              for st in ("route", "quant_x", "gemm1", "gemm2", "combine")}
+    r = {"T": T, "us_p50": round(sec * 1e6, 1), "tflops": round(flops / sec / 1e12, 1),
+         "roofline": mfma_roofline(flops, sec), "stage_us": stages,
+         "weight_GB": round(wl.E * wl.weight_bytes_per_expert() / 1e9, 3)}
+    if cpu:
+        r["cpu_baseline"] = cpu_sample(wl, w, x, ids, tw, max_experts=4, reps=1)
+    del g, b, scratch, plan, ex, w
+    torch.cuda.empty_cache()
+    return r
+
+
+def bench_tiny(fm, synth, torch, stream, reps=50, cpu=True):
+    """Tiny reference config (E=8, H=256, I=128, top_k=2, T=16): launch-bound, time
+    per call over a graph of 10 calls; the oracle: median of 3 calls."""
+    wl = synth.WORKLOADS["tiny"]
+    T = wl.tokens[0]
+    w = synth.make_weights(wl, device="cuda")
+    wp = fm.plan_weights(wl.E, wl.H, wl.I, wl.gated, wl.weight_format)
+    ex = fm.prepare_weights(wp, w["w13_codes"], w["w13_scales"], w["w2_codes"], w["w2_scales"])
+    plan = fm.plan(wp, wl.k, T, wl.act_format, "silu")
+    scratch = fm.alloc_scratch(plan)
+    x = synth.make_x(wl, T, device="cuda")
+    ids, tw = synth.make_routing(wl, T, device="cuda")
+    out = torch.empty(T, wl.H, dtype=torch.bfloat16, device="cuda")
+    b = fm.bind(plan, scratch, ex, x, ids, tw, out)
+    g = capture(torch, fm, [b] * 10, stream)
+    g.replay()
+    sec = time_graph(torch, g, stream, reps) / (reps * 10)
+    r = {"T": T, "us": round(sec * 1e6, 3), "path": {3: "decode, split-K", 2: "decode"}.get(
+        fm.binding_query(b, "path"), "grouped"), "note": "launch-bound; correctness config"}
+    if cpu:
+        r["cpu_baseline"] = cpu_sample(wl, w, x, ids, tw, reps=3)
+    return r
 
 
 def main():
@@ -594,11 +725,31 @@ def main():
                                                             "stage_us")}
         log("dense mm line")
         result["dense_mm"] = bench_dense_mm(fm, synth, torch, stream)
-        log("w4a8 line")
-        result["w4a8_mixed_T1"] = bench_mixed_t1(fm, synth, torch, stream)
     if not args.no_cpu:
         log("cpu oracle baseline")
         result["cpu_baseline"] = cpu_baseline(wl, w_host, sets_host)
+    if not args.no_extra:
+        # every configuration: time per call, its roofline fraction, the oracle beside it
+        cpu = not args.no_cpu
+        configs = {}
+        log("config: tiny")
+        configs["tiny"] = bench_tiny(fm, synth, torch, stream, cpu=cpu)
+        configs["decode"] = {f"T{T}": {"us": round(per_t[f"T{T}"]["us"], 3), "path": per_t[f"T{T}"]["path"],
+                                       "roofline": hbm_roofline(per_t[f"T{T}"]["weight_MB"] * 1e6,
+                                                                per_t[f"T{T}"]["us"] * 1e-6)} for T in Ts}
+        if cpu:
+            row = sets[1][0]
+            configs["decode"]["T1"]["cpu_baseline"] = {
+                **{k: result["cpu_baseline"][k] for k in ("cores", "kind")},
+                "seconds_per_call": round(result["cpu_baseline"]["seconds_per_call"], 4),
+                "sample": "the decode line's baseline: " + result["cpu_baseline"]["sample"]}
+        log("config: mixed")
+        configs["mixed"] = bench_mixed(fm, synth, torch, stream, cpu=cpu)
+        log("config: prefill")
+        configs["prefill"] = bench_gemm_config(fm, synth, torch, stream, "prefill", cpu=cpu)
+        log("config: skew")
+        configs["skew"] = bench_gemm_config(fm, synth, torch, stream, "skew", reps=5, cpu=cpu)
+        result["configs"] = configs
     print(json.dumps(result))
 
 
