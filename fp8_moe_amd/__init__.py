@@ -27,6 +27,7 @@ WEIGHT_FORMATS = {"mxfp4": 1, "nvfp4": 2}
 ACT_FORMATS = {"bf16": 1, "mxfp8": 2, "nvfp4": 3}
 ACTIVATIONS = {"silu": 1, "relu2": 2}
 STAGES = {"route": 1, "quant_x": 2, "gemm1": 3, "gemm2": 4, "combine": 5, "decode1": 6, "decode2": 7}
+NOALLOC_SCRATCH_BYTES = 16 << 20   # B12X_NOALLOC_SCRATCH_BYTES: the static scratch of run_noalloc
 QUERIES = {"path": 1, "tile_rows": 2, "row_pad": 3, "T": 4, "num_stages": 5}
 REGIONS = {"counts": 1, "offsets": 2, "padded_offsets": 3, "sorted": 4, "pos": 5, "tiles": 6, "ntiles": 7,
            "xq": 9, "xs": 10, "h": 11, "hs": 12, "y": 13}
@@ -103,6 +104,7 @@ def _load():
         "b12x_moe_bind": (st, [vp, vp, ctypes.c_uint64, P(Experts), vp, i64, i64, vp, vp, vp, i64, P(Binding)]),
         "b12x_moe_run": (st, [P(Binding), vp]),
         "b12x_moe_run_stage": (st, [P(Binding), ctypes.c_int32, vp]),
+        "b12x_moe_run_noalloc": (st, [vp, P(Experts), vp, i64, i64, vp, vp, vp, i64, vp]),
         "b12x_moe_binding_query": (st, [P(Binding), ctypes.c_int32, P(i64)]),
         "b12x_moe_scratch_region": (st, [vp, ctypes.c_int32, P(ctypes.c_uint64), P(ctypes.c_uint64)]),
         "b12x_mxfp8_quantize_rows": (st, [vp, i64, i64, i64, vp, vp, vp]),
@@ -124,7 +126,7 @@ def _load():
 _lib = _load()
 EXPORTED = ("b12x_moe_plan_weights", "b12x_moe_prepare_weights", "b12x_moe_is_supported", "b12x_moe_plan",
             "b12x_moe_plan_destroy", "b12x_moe_scratch_specs", "b12x_moe_bind", "b12x_moe_run",
-            "b12x_moe_run_stage", "b12x_moe_binding_query", "b12x_moe_scratch_region",
+            "b12x_moe_run_stage", "b12x_moe_run_noalloc", "b12x_moe_binding_query", "b12x_moe_scratch_region",
             "b12x_mxfp8_quantize_rows", "b12x_gemm_packed_bytes", "b12x_gemm_pack_weight", "b12x_gemm_mm",
             "b12x_probe_stream_read", "b12x_probe_mfma", "b12x_status_string",
             "b12x_last_error")
@@ -269,6 +271,22 @@ def bind(p, scratch, experts, a, topk_ids, topk_weights, out):
 
 def run(binding, stream=None):
     _check(_lib.b12x_moe_run(ctypes.byref(binding), _stream(stream)))
+
+
+def run_noalloc(p, experts, a, topk_ids, topk_weights, out, stream=None):
+    """b12x_moe_run_noalloc: bind + run on the library's static scratch (split-K
+    decode path only); same arguments as bind() without the scratch."""
+    T = a.shape[0]
+    for t, dt in ((a, torch.bfloat16), (out, torch.bfloat16), (topk_ids, torch.int32),
+                  (topk_weights, torch.float32)):
+        if t.dtype != dt:
+            raise TypeError(f"expected {dt}, got {t.dtype}")
+    if topk_ids.shape != topk_weights.shape or topk_ids.shape[0] != T or out.shape[0] != T:
+        raise ValueError("shape mismatch between a, out, topk_ids and topk_weights")
+    if not (topk_ids.is_contiguous() and topk_weights.is_contiguous()):
+        raise ValueError("topk_ids / topk_weights must be contiguous")
+    _check(_lib.b12x_moe_run_noalloc(p.handle, ctypes.byref(experts.experts), _ptr(a), T, a.stride(0),
+                                     _ptr(topk_ids), _ptr(topk_weights), _ptr(out), out.stride(0), _stream(stream)))
 
 
 def run_stage(binding, stage, stream=None):

@@ -298,10 +298,14 @@ b12x_status b12x_moe_scratch_region(b12x_moe_plan_t p, int32_t region, uint64_t*
   return B12X_OK;
 }
 
-b12x_status b12x_moe_bind(b12x_moe_plan_t p, void* scratch, uint64_t scratch_bytes, const b12x_moe_experts* ex,
-                          const void* a, int64_t T, int64_t a_stride, const int32_t* ids, const float* tw, void* out,
-                          int64_t out_stride, b12x_moe_binding* binding) {
-  if (!p || !binding || !ex) return fail(B12X_ERR_INVALID_ARGUMENT, "NULL plan, experts or binding");
+}  // extern "C"
+
+// The binding of b12x_moe_bind; with no_scratch (the allocation-free call) the
+// scratch arguments are ignored and the scratch pointers left null.
+static b12x_status make_binding(b12x_moe_plan_t p, void* scratch, uint64_t scratch_bytes, bool no_scratch,
+                                const b12x_moe_experts* ex, const void* a, int64_t T, int64_t a_stride,
+                                const int32_t* ids, const float* tw, void* out, int64_t out_stride, BindingImpl& b) {
+  if (!p || !ex) return fail(B12X_ERR_INVALID_ARGUMENT, "NULL plan or experts");
   if (T < 0) return fail(B12X_ERR_INVALID_ARGUMENT, "T < 0");
   if (T > p->max_tokens)
     return fail(B12X_ERR_CAPACITY, "T = %lld exceeds max_tokens = %lld", (long long)T, (long long)p->max_tokens);
@@ -312,13 +316,13 @@ b12x_status b12x_moe_bind(b12x_moe_plan_t p, void* scratch, uint64_t scratch_byt
   if (a4_nv(p->afmt) && !ex->act_scales)
     return fail(B12X_ERR_INVALID_ARGUMENT, "NVFP4 activations need the activation scales (a13_global, a2_global)");
   if (T > 0) {
-    if (!a || !ids || !tw || !out || !scratch) return fail(B12X_ERR_INVALID_ARGUMENT, "NULL device pointer");
+    if (!a || !ids || !tw || !out || (!scratch && !no_scratch)) return fail(B12X_ERR_INVALID_ARGUMENT, "NULL device pointer");
     if (a_stride < p->H || out_stride < p->H) return fail(B12X_ERR_INVALID_ARGUMENT, "row stride smaller than H");
     if (a_stride % 8 || out_stride % 8) return fail(B12X_ERR_MISALIGNED, "row strides must be multiples of 8");
     if (!aligned(a, 16) || !aligned(out, 16) || !aligned(ids, 16) || !aligned(tw, 16))
       return fail(B12X_ERR_MISALIGNED, "a, out, topk_ids and topk_weights must be 16-byte aligned");
-    if (!aligned(scratch, 256)) return fail(B12X_ERR_MISALIGNED, "scratch must be 256-byte aligned");
-    if (scratch_bytes < p->scratch_bytes)
+    if (!no_scratch && !aligned(scratch, 256)) return fail(B12X_ERR_MISALIGNED, "scratch must be 256-byte aligned");
+    if (!no_scratch && scratch_bytes < p->scratch_bytes)
       return fail(B12X_ERR_SCRATCH_TOO_SMALL, "scratch %llu < %llu bytes", (unsigned long long)scratch_bytes,
                   (unsigned long long)p->scratch_bytes);
     const char* ab = (const char*)a;
@@ -327,7 +331,6 @@ b12x_status b12x_moe_bind(b12x_moe_plan_t p, void* scratch, uint64_t scratch_byt
     if (ab < ob + obytes && ob < ab + abytes) return fail(B12X_ERR_INVALID_ARGUMENT, "out aliases a");
     if (abytes >= kMaxBufferBytes) return fail(B12X_ERR_UNSUPPORTED, "a spans 1 GiB or more");
   }
-  BindingImpl b;
   memset(&b, 0, sizeof(b));
   b.magic = kBindingMagic;
   b.path = (T > 0 && T * p->k <= p->decode_max_pairs) ? 2 : 1;
@@ -353,6 +356,7 @@ b12x_status b12x_moe_bind(b12x_moe_plan_t p, void* scratch, uint64_t scratch_byt
   b.w2_global = nv ? (const float*)(wb + wp.w2_global_off) : nullptr;
   b.a13_global = a4_nv(p->afmt) ? (const float*)(wb + wp.a13_global_off) : nullptr;
   b.a2_global = a4_nv(p->afmt) ? (const float*)(wb + wp.a2_global_off) : nullptr;
+  if (no_scratch) return B12X_OK;
   uint8_t* sb = (uint8_t*)scratch;
   b.counts = (int32_t*)(sb + p->off[R_COUNTS]);
   b.offsets = (int32_t*)(sb + p->off[R_OFFSETS]);
@@ -369,6 +373,18 @@ b12x_status b12x_moe_bind(b12x_moe_plan_t p, void* scratch, uint64_t scratch_byt
   b.y = (float*)(sb + p->off[R_Y]);
   b.y16 = (uint16_t*)(sb + p->off[R_Y]);
   b.dsync = p->len[R_DSYNC] ? sb + p->off[R_DSYNC] : nullptr;
+  return B12X_OK;
+}
+
+extern "C" {
+
+b12x_status b12x_moe_bind(b12x_moe_plan_t p, void* scratch, uint64_t scratch_bytes, const b12x_moe_experts* ex,
+                          const void* a, int64_t T, int64_t a_stride, const int32_t* ids, const float* tw, void* out,
+                          int64_t out_stride, b12x_moe_binding* binding) {
+  if (!binding) return fail(B12X_ERR_INVALID_ARGUMENT, "NULL binding");
+  BindingImpl b;
+  const b12x_status st = make_binding(p, scratch, scratch_bytes, false, ex, a, T, a_stride, ids, tw, out, out_stride, b);
+  if (st) return st;
   memset(binding, 0, sizeof(*binding));
   memcpy(binding, &b, sizeof(b));
   return B12X_OK;
@@ -447,6 +463,33 @@ b12x_status b12x_moe_run(const b12x_moe_binding* binding, void* stream) {
     if (st) return st;
   }
   return B12X_OK;
+}
+
+b12x_status b12x_moe_run_noalloc(b12x_moe_plan_t p, const b12x_moe_experts* ex, const void* a, int64_t T,
+                                 int64_t a_stride, const int32_t* ids, const float* tw, void* out, int64_t out_stride,
+                                 void* stream) {
+  BindingImpl b;
+  b12x_status st = make_binding(p, nullptr, 0, true, ex, a, T, a_stride, ids, tw, out, out_stride, b);
+  if (st) return st;
+  if (T == 0) return B12X_OK;
+  if (b.path != 3)
+    return fail(B12X_ERR_UNSUPPORTED,
+                "b12x_moe_run_noalloc runs the split-K decode path only: T * top_k = %lld is above the plan's "
+                "split-K limit (%d pairs) or H = %d above %d",
+                (long long)(T * p->k), p->splitk_max_pairs, p->H, kSplitKMaxH);
+  const uint64_t need = sk_partial_bytes(b);
+  if (need > (uint64_t)B12X_NOALLOC_SCRATCH_BYTES)
+    return fail(B12X_ERR_CAPACITY, "the partial rows need %llu bytes, more than the static scratch (%llu bytes)",
+                (unsigned long long)need, (unsigned long long)B12X_NOALLOC_SCRATCH_BYTES);
+  void* ptr = nullptr;
+  const int err = sk_static_scratch(&ptr);
+  if (err) return hip_fail(err, "hipGetSymbolAddress of the static scratch");
+  b.y = (float*)ptr;
+  b.y16 = (uint16_t*)ptr;
+  hipStream_t s = (hipStream_t)stream;
+  st = run_stage(b, B12X_STAGE_DECODE1, s);
+  if (st) return st;
+  return run_stage(b, B12X_STAGE_COMBINE, s);
 }
 
 b12x_status b12x_moe_binding_query(const b12x_moe_binding* binding, int32_t what, int64_t* value) {

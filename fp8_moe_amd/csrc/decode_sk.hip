@@ -26,6 +26,8 @@
 // workgroups are resident.  The combine (decode_sk_combine_kernel) sums the
 // slices of each pair and the pairs of each token in a fixed order, in fp32,
 // and rounds once to bf16.
+#include <mutex>
+
 #include "decode_common.h"
 
 namespace b12x {
@@ -683,6 +685,36 @@ int launch_decode_sk(const BindingImpl& b, hipStream_t s) {
   // the staging holds up to kSkRows rows of at most 128 units (8 K fragments) per wave
   if (p.R > kSkRows || p.kper > 8) return (int)hipErrorInvalidValue;
   return b.gated ? launch_sk_fmt<1>(b, p, s) : launch_sk_fmt<2>(b, p, s);
+}
+
+uint64_t sk_partial_bytes(const BindingImpl& b) {
+  return (uint64_t)(b.T * b.k) * (uint64_t)(b.I / kSkSlice) * (uint64_t)sk_row_stride(b.H) * 4u;
+}
+
+// Scratch of the allocation-free call (b12x_moe_run_noalloc): the split-K partial
+// rows, in a static array that every device the library runs on holds until the
+// process ends.  In host code `scratch` only names the symbol: its device address
+// is looked up with hipGetSymbolAddress, once per device with that device current,
+// and that address (never the array's name) is what the kernels receive.
+static __device__ __align__(256) uint8_t scratch[B12X_NOALLOC_SCRATCH_BYTES];
+static void* g_scratch_ptr[64];
+static std::mutex g_scratch_mu;
+
+int sk_static_scratch(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return (int)e;
+  if (dev < 0 || dev >= 64) return (int)hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return (int)e;
+    if (!p) return (int)hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return 0;
 }
 
 int launch_decode_sk_combine(const BindingImpl& b, hipStream_t s) {

@@ -181,6 +181,11 @@ int launch_decode_combine(const BindingImpl& b, hipStream_t s);
 // projections per 32-column slice of h, then the combine of the partials
 int launch_decode_sk(const BindingImpl& b, hipStream_t s);
 int launch_decode_sk_combine(const BindingImpl& b, hipStream_t s);
+// Bytes of the split-K partial rows of a binding (its whole use of scratch).
+uint64_t sk_partial_bytes(const BindingImpl& b);
+// Device address of the static scratch array of the allocation-free call on the
+// current device (looked up once per device); 0 or the HIP error code.
+int sk_static_scratch(void** ptr);
 // the decode path runs gate/up and down as one launch (DECODE1) for this binding
 bool decode_fused(const BindingImpl& b);
 const char* hip_error_name(int err);
