@@ -5,6 +5,7 @@
 #include <stdarg.h>
 #include <stdint.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <new>
@@ -340,6 +341,9 @@ static b12x_status make_binding(b12x_moe_plan_t p, void* scratch, uint64_t scrat
   // grouped path, NVFP4 weights: GEMM1 reads a scaled f16 copy of a (of its MXFP8 or NVFP4 round trips with
   // MXFP8 or NVFP4 activations)
   b.a_f16 = b.path == 1 && p->wfmt == B12X_WEIGHT_NVFP4;
+  // test hook of the fused decode kernel's bounded waits (B12X_DEBUG_FORCE_GIVEUP=1 at bind)
+  const char* fg = getenv("B12X_DEBUG_FORCE_GIVEUP");
+  b.force_giveup = fg && fg[0] == '1';
   b.T = T; b.a_stride = a_stride; b.out_stride = out_stride;
   b.Hp = p->Hp; b.Ip = p->Ip; b.max_rows = p->max_rows; b.max_tiles = p->max_tiles;
   b.nf13 = p->l13.nf; b.kf13 = p->l13.kf; b.kfs13 = p->l13.kfs;

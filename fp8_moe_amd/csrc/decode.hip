@@ -67,13 +67,16 @@ struct DecodeParams {
   int64_t y_stride;
   // fused gate/up + down (one launch): completion flag of every (touched
   // expert slot, gate/up group), flags_per_slot of them per slot; a flag
-  // holds the call's tag once that group's h rows are stored.  epoch is
-  // advanced by the combine after every call; status is set when a wait
-  // gives up (the combine then writes NaN).
+  // holds the launch's tag once that group's h rows are stored.  Every
+  // workgroup reads the epoch when it starts and adds 1 to it when it is
+  // done, so each launch has a tag of its own; a wait that gives up stores
+  // the launch's tag in status (the combine then writes NaN).
   uint64_t* flags;
   int flags_per_slot;
-  const int32_t* epoch;
-  int32_t* status;
+  uint32_t* epoch;
+  uint64_t* status;
+  uint64_t expect_xor;  // 0; the test hook's waits expect tag ^ expect_xor, which no flag holds
+  int max_polls;
   int64_t h_bytes;  // extent of h16 (device-coherent stores and loads)
   int deal;         // 0: one contiguous share per workgroup; else chunks of this many items dealt round-robin
   int prev_groups;  // down phase of the fused kernel: the gate/up phase's groups per expert (same deal)
@@ -81,10 +84,9 @@ struct DecodeParams {
 
 enum { DMODE_SILU = 1, DMODE_RELU2 = 2, DMODE_DOWN = 3 };
 
-// Tag of this call's completion flags: never 0 and never a previous call's.
-__device__ __forceinline__ uint64_t flag_tag(const int32_t* epoch) {
-  const uint32_t e = (uint32_t)__hip_atomic_load(epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  return ((uint64_t)e << 32) | 0xB12DF1A9u;
+// Tag of this launch's completion flags (decode_tag of the epoch it starts with).
+__device__ __forceinline__ uint64_t flag_tag(const uint32_t* epoch) {
+  return decode_tag(__hip_atomic_load(epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
 }
 
 // Upper bound on the polls of one wait (each at least one round trip to
@@ -170,12 +172,13 @@ __device__ __forceinline__ void decode_items(const DecodeParams& p, DecodeLds& L
     // flag (the barrier that opens decode_expert holds the other waves)
     if (wave == 0) {
       const uint64_t* f = p.flags + (int64_t)slot * p.flags_per_slot;
+      const uint64_t expect = tag ^ p.expect_xor;
       for (int poll = 0;; ++poll) {
-        const bool ok =
-            lane >= p.flags_per_slot || __hip_atomic_load(f + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == tag;
+        const bool ok = lane >= p.flags_per_slot ||
+                        __hip_atomic_load(f + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == expect;
         if (__ballot(!ok) == 0) break;
-        if (poll >= kWaitPolls) {
-          if (lane == 0) __hip_atomic_store(p.status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (poll >= p.max_polls) {
+          if (lane == 0) __hip_atomic_store(p.status, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           break;
         }
         __builtin_amdgcn_s_sleep(8);
@@ -425,18 +428,26 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(const DecodeParams 
 // part waits only for the gate/up groups of its own expert.  The grid is at
 // most the resident capacity, and no workgroup waits before its gate/up
 // share is done, so every awaited group is being computed by a running
-// workgroup.
+// workgroup.  Should a workgroup not be resident (the device shared with
+// other work), the waits for its groups give up after kWaitPolls polls and
+// the call's output is NaN: a loud failure, never a stale result.
+//
+// The launch's tag: every workgroup reads the epoch first thing and adds 1
+// to it as its last action.  No workgroup can be done before all of them
+// have started (each down part waits for the gate/up groups of many
+// workgroups, and all are dispatched at once), so they all read the same
+// epoch, and the next launch (stream order) reads one grid size later.
 template <int WF, int MODE1, int FR1, int KW1, int FR2, int KW2>
 __global__ __launch_bounds__(kDecThreads) void decode_fused_kernel(const DecodeParams p1, const DecodeParams p2) {
   constexpr int FRM = FR1 > FR2 ? FR1 : FR2;
   __shared__ DecodeLds L;
   __shared__ f32x4 s_red[2 * 3 * FRM * 64];
-  if (blockIdx.x == 0 && threadIdx.x == 0)
-    __hip_atomic_store(p1.status, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const uint64_t tag = flag_tag(p1.epoch);
   const int n_touched = decode_prep(p1.ids, p1.P, p1.E, L.ids, L.bits, L.wpre);
   decode_items<WF, B12X_ACT_BF16, MODE1, FR1, KW1, 1>(p1, L, s_red, n_touched, tag);
   decode_items<WF, B12X_ACT_BF16, DMODE_DOWN, FR2, KW2, 2>(p2, L, s_red, n_touched, tag);
+  __syncthreads();
+  if (threadIdx.x == 0) __hip_atomic_fetch_add(p1.epoch, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // One workgroup per resident slot, never more than the items of the largest
@@ -558,8 +569,9 @@ bool decode_fused(const BindingImpl& b) {
 // Gate/up groups of FR1 = 2 fragments, down groups of FR2 = 4 (as the
 // separate launches use them at these K), grid as for one launch of the
 // larger item count.
+// With grid_out: the launch's grid only, nothing launched (the combine needs it).
 template <int WF, int MODE1, int KW1, int KW2>
-static int launch_fused_kw(const BindingImpl& b, DecodeParams& p1, DecodeParams& p2, hipStream_t s) {
+static int launch_fused_kw(const BindingImpl& b, DecodeParams& p1, DecodeParams& p2, hipStream_t s, int* grid_out) {
   static int cache[64];
   auto kernel = decode_fused_kernel<WF, MODE1, 2, KW1, 4, KW2>;
   p1.n_groups = (p1.NF + 1) / 2;
@@ -570,35 +582,48 @@ static int launch_fused_kw(const BindingImpl& b, DecodeParams& p1, DecodeParams&
   int64_t grid = resident_workgroups(kernel, cache);
   if (grid > items) grid = items;
   if (grid < 1) grid = 1;
+  if (grid_out) {
+    *grid_out = (int)grid;
+    return 0;
+  }
   hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kDecThreads), 0, s, p1, p2);
   return (int)hipGetLastError();
 }
 
 template <int WF, int MODE1>
-static int launch_fused_t(const BindingImpl& b, DecodeParams& p1, DecodeParams& p2, hipStream_t s) {
+static int launch_fused_t(const BindingImpl& b, DecodeParams& p1, DecodeParams& p2, hipStream_t s, int* grid_out) {
   const bool k1 = (p1.KF + 3) / 4 <= 2, k2 = (p2.KF + 3) / 4 <= 2;
-  if (k1 && k2) return launch_fused_kw<WF, MODE1, 2, 2>(b, p1, p2, s);
-  if (k1) return launch_fused_kw<WF, MODE1, 2, 4>(b, p1, p2, s);
-  if (k2) return launch_fused_kw<WF, MODE1, 4, 2>(b, p1, p2, s);
-  return launch_fused_kw<WF, MODE1, 4, 4>(b, p1, p2, s);
+  if (k1 && k2) return launch_fused_kw<WF, MODE1, 2, 2>(b, p1, p2, s, grid_out);
+  if (k1) return launch_fused_kw<WF, MODE1, 2, 4>(b, p1, p2, s, grid_out);
+  if (k2) return launch_fused_kw<WF, MODE1, 4, 2>(b, p1, p2, s, grid_out);
+  return launch_fused_kw<WF, MODE1, 4, 4>(b, p1, p2, s, grid_out);
 }
 
-static int launch_fused(const BindingImpl& b, hipStream_t s) {
+static int launch_fused(const BindingImpl& b, hipStream_t s, int* grid_out = nullptr) {
   DecodeParams p1 = gate_up_params(b), p2 = down_params(b);
   uint8_t* sync = b.dsync;
   for (DecodeParams* p : {&p1, &p2}) {
-    p->epoch = (const int32_t*)(sync + kDecodeEpochOffset);
-    p->status = (int32_t*)(sync + kDecodeStatusOffset);
+    p->epoch = (uint32_t*)(sync + kDecodeEpochOffset);
+    p->status = (uint64_t*)(sync + kDecodeStatusOffset);
     p->flags = (uint64_t*)(sync + kDecodeFlagsOffset);
     p->flags_per_slot = (int)((b.nf13 + 1) / 2);
     p->deal = 2;
+    // test hook: waits that cannot succeed, and give up after a few polls
+    p->expect_xor = b.force_giveup ? 0x80000000ull : 0ull;
+    p->max_polls = b.force_giveup ? 4 : kWaitPolls;
   }
   const bool nv = b.wfmt == B12X_WEIGHT_NVFP4;
   if (b.gated)
-    return nv ? launch_fused_t<B12X_WEIGHT_NVFP4, DMODE_SILU>(b, p1, p2, s)
-              : launch_fused_t<B12X_WEIGHT_MXFP4, DMODE_SILU>(b, p1, p2, s);
-  return nv ? launch_fused_t<B12X_WEIGHT_NVFP4, DMODE_RELU2>(b, p1, p2, s)
-            : launch_fused_t<B12X_WEIGHT_MXFP4, DMODE_RELU2>(b, p1, p2, s);
+    return nv ? launch_fused_t<B12X_WEIGHT_NVFP4, DMODE_SILU>(b, p1, p2, s, grid_out)
+              : launch_fused_t<B12X_WEIGHT_MXFP4, DMODE_SILU>(b, p1, p2, s, grid_out);
+  return nv ? launch_fused_t<B12X_WEIGHT_NVFP4, DMODE_RELU2>(b, p1, p2, s, grid_out)
+            : launch_fused_t<B12X_WEIGHT_MXFP4, DMODE_RELU2>(b, p1, p2, s, grid_out);
+}
+
+int decode_fused_grid(const BindingImpl& b) {
+  int grid = 0;
+  launch_fused(b, nullptr, &grid);
+  return grid;
 }
 
 int launch_decode1(const BindingImpl& b, hipStream_t s) {

@@ -52,9 +52,14 @@ inline bool a8_bf16(int wfmt, int afmt) { return afmt == B12X_ACT_MXFP8 && wfmt 
 inline bool a4_nv(int afmt) { return afmt == B12X_ACT_NVFP4; }
 // decode synchronization region: int32 call epoch, int32 status, then one
 // uint64 completion flag per (touched expert slot, gate/up group of 2 fragments)
-constexpr int kDecodeEpochOffset = 0;
-constexpr int kDecodeStatusOffset = 4;
-constexpr int kDecodeFlagsOffset = 64;
+constexpr int kDecodeEpochOffset = 0;   // uint32: every workgroup of the fused kernel adds 1 when done
+constexpr int kDecodeStatusOffset = 8;  // uint64: the tag of the last fused launch whose wait gave up
+constexpr int kDecodeFlagsOffset = 64;  // uint64 per (expert slot, gate/up group): the tag once its h is stored
+// Tag of the fused launch that read epoch e: never 0 (so zeroed memory never
+// matches) and different for every launch (the epoch advances by the grid
+// size per launch).
+constexpr uint32_t kDecodeTagMagic = 0xB12DF1A9u;
+__host__ __device__ inline uint64_t decode_tag(uint32_t e) { return ((uint64_t)e << 32) | kDecodeTagMagic; }
 // Kernels address each activation buffer and each expert's weights with
 // 32-bit buffer offsets; buffers are limited to 1 GiB (so that the sum of
 // two out-of-range markers is still out of range).
@@ -107,6 +112,7 @@ struct BindingImpl {
   int32_t E, H, I, k, gated, wfmt, afmt, act;
   int32_t a_f16;  // grouped path, NVFP4 weights: GEMM1 reads a scaled f16 copy of a (xq; of its MXFP8 round trips
                   // with MXFP8 activations) and row exponents (xs)
+  int32_t force_giveup;  // test hook (fused decode kernel): its waits expect a tag no one writes
   int64_t T, a_stride, out_stride;
   int64_t Hp, Ip, max_rows, max_tiles;
   int64_t nf13, kf13, kfs13, nf2, kf2, kfs2;
@@ -179,6 +185,7 @@ int launch_decode2(const BindingImpl& b, hipStream_t s);
 int launch_decode_combine(const BindingImpl& b, hipStream_t s);
 // split-K decode (path 3): one kernel for gate/up + activation + partial down
 // projections per 32-column slice of h, then the combine of the partials
+int decode_fused_grid(const BindingImpl& b);  // workgroups of the fused decode kernel's launch
 int launch_decode_sk(const BindingImpl& b, hipStream_t s);
 int launch_decode_sk_combine(const BindingImpl& b, hipStream_t s);
 // Bytes of the split-K partial rows of a binding (its whole use of scratch).

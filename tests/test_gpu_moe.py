@@ -280,6 +280,61 @@ def test_decode_binding_reused_with_new_inputs():
         assert ok, (i, rel_fro, rel_max)
 
 
+def test_fused_decode_stage_run_twice_with_new_inputs():
+    """The fused decode kernel run twice without the combine in between (a
+    stage-by-stage caller), the inputs changed between the two: every launch
+    tags its flags with a tag of its own, so the second launch's down phase
+    waits for its own gate/up results, and the combine gives the oracle's
+    output for the second inputs."""
+    import fp8_moe_amd as fm
+    wl = synth.WORKLOADS["decode"]
+    pr = problem("decode", 32)
+    T = 8
+    x, ids, tw = _inputs(wl, T)
+    b, out = pr.model.bind(x, ids, tw)
+    assert fm.binding_query(b, "path") == 2 and fm.binding_query(b, "num_stages") == 2
+    fm.run(b)
+    for salt in (201, 202):
+        fm.run_stage(b, "decode1")
+        x.copy_(synth.make_x(wl, T, device="cuda", salt=salt))
+        ids_s, tw_s = synth.make_routing(wl, T, device="cuda", salt=salt)
+        ids.copy_(ids_s)
+        tw.copy_(tw_s)
+        out.fill_(0)
+        fm.run_stage(b, "decode1")
+        fm.run_stage(b, "combine")
+        torch.cuda.synchronize()
+        rel_fro, rel_max, ok = compare(out, pr.oracle(x, ids, tw))
+        assert ok, (salt, rel_fro, rel_max)
+
+
+def test_fused_decode_wait_gives_up_then_recovers(monkeypatch):
+    """The fused decode kernel's bounded wait, forced from the host to give up
+    (the test hook makes every wait expect a tag that no flag holds; all
+    kernels still run to their end): the call's output is all NaN.  The next
+    call on an ordinary binding over the same scratch is correct again (the
+    failed launch's tag is not the next one's, so nothing needs clearing)."""
+    import fp8_moe_amd as fm
+    wl = synth.WORKLOADS["decode"]
+    pr = problem("decode", 32)
+    T = 8
+    x, ids, tw = _inputs(wl, T)
+    monkeypatch.setenv("B12X_DEBUG_FORCE_GIVEUP", "1")
+    bad, out_bad = pr.model.bind(x, ids, tw)
+    monkeypatch.delenv("B12X_DEBUG_FORCE_GIVEUP")
+    assert fm.binding_query(bad, "path") == 2 and fm.binding_query(bad, "num_stages") == 2
+    fm.run(bad)
+    torch.cuda.synchronize()
+    assert torch.isnan(out_bad.float()).all()
+    good, out = pr.model.bind(x, ids, tw)
+    for _ in range(2):
+        out.fill_(0)
+        fm.run(good)
+        torch.cuda.synchronize()
+        rel_fro, rel_max, ok = compare(out, pr.oracle(x, ids, tw))
+        assert ok, (rel_fro, rel_max)
+
+
 # decode path (T*k <= 256) against the grouped path and the oracle on the same inputs
 DECODE = [
     ("tiny", 16), ("decode", 1), ("decode", 8), ("decode", 32), ("mixed", 1), ("mixed", 64),
