@@ -44,6 +44,63 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+# ---- measurement probes (libb12x_probes.so, include/b12x_probes.h): the achieved
+# ceilings that the MoE kernels' rates are read against
+class ProbeError(RuntimeError):
+    pass
+
+
+_PROBES = None
+
+
+def _probes():
+    global _PROBES
+    if _PROBES is None:
+        import ctypes
+        path = os.path.join(ROOT, "fp8_moe_amd", "libb12x_probes.so")
+        if not os.path.exists(path):
+            raise ImportError(f"{path} is not built; run `python fp8_moe_amd/build.py`")
+        lib = ctypes.CDLL(path)
+        vp, i32 = ctypes.c_void_p, ctypes.c_int32
+        lib.b12x_probe_stream_read.restype = i32
+        lib.b12x_probe_stream_read.argtypes = [vp, ctypes.c_uint64, vp, i32, vp]
+        lib.b12x_probe_mfma.restype = i32
+        lib.b12x_probe_mfma.argtypes = [vp, i32, i32, i32, vp]
+        _PROBES = lib
+    return _PROBES
+
+
+def _probe_stream(stream):
+    import ctypes
+    import torch
+    return ctypes.c_void_p((stream if stream is not None else torch.cuda.current_stream()).cuda_stream)
+
+
+def probe_stream_read(src, sink, workgroups, stream=None):
+    """Stream `src` (contiguous device tensor, a multiple of 16 bytes) through
+    `workgroups` workgroups; sink: 32-bit tensor of workgroups * 256 elements."""
+    import ctypes
+    if sink.numel() < workgroups * 256:
+        raise ValueError("sink needs workgroups*256 elements")
+    st = _probes().b12x_probe_stream_read(ctypes.c_void_p(src.data_ptr()), src.numel() * src.element_size(),
+                                          ctypes.c_void_p(sink.data_ptr()), workgroups, _probe_stream(stream))
+    if st:
+        raise ProbeError(f"stream-read probe: status {st}")
+
+
+def probe_mfma(sink, workgroups, iterations, f16=False, stream=None):
+    """16 * iterations 16x16x32 MFMAs per wave, four waves per workgroup; sink:
+    float32 tensor of workgroups * 256 elements."""
+    import ctypes
+    import torch
+    if sink.dtype != torch.float32 or sink.numel() < workgroups * 256:
+        raise ValueError("sink must be float32 with workgroups*256 elements")
+    st = _probes().b12x_probe_mfma(ctypes.c_void_p(sink.data_ptr()), workgroups, iterations, int(bool(f16)),
+                                   _probe_stream(stream))
+    if st:
+        raise ProbeError(f"MFMA probe: status {st}")
+
+
 def _events():
     import torch
     return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -153,13 +210,13 @@ def measure_ceilings(fm, torch, stream):
         per = (nbytes // 16) // wg
         read = wg * (per // 1024) * 1024 * 16
         for _ in range(2):
-            fm.probe_stream_read(src, sink, wg, stream=stream)
+            probe_stream_read(src, sink, wg, stream=stream)
         e0, e1 = _events()
         torch.cuda.synchronize()
         with torch.cuda.stream(stream):
             e0.record(stream)
             for _ in range(10):
-                fm.probe_stream_read(src, sink, wg, stream=stream)
+                probe_stream_read(src, sink, wg, stream=stream)
             e1.record(stream)
         torch.cuda.synchronize()
         best = max(best, read * 10 / (e0.elapsed_time(e1) / 1e3) / 1e9)
@@ -168,13 +225,13 @@ def measure_ceilings(fm, torch, stream):
     wg, iters = cus * 2, 4000
     sink = torch.empty(wg * 256, dtype=torch.float32, device="cuda")
     for name, f16 in (("mfma_bf16_TFLOPs", False), ("mfma_f16_TFLOPs", True)):
-        fm.probe_mfma(sink, wg, 10, f16=f16, stream=stream)
+        probe_mfma(sink, wg, 10, f16=f16, stream=stream)
         e0, e1 = _events()
         torch.cuda.synchronize()
         with torch.cuda.stream(stream):
             e0.record(stream)
             for _ in range(3):
-                fm.probe_mfma(sink, wg, iters, f16=f16, stream=stream)
+                probe_mfma(sink, wg, iters, f16=f16, stream=stream)
             e1.record(stream)
         torch.cuda.synchronize()
         flops = 3.0 * wg * 4 * 16 * 16384 * iters
@@ -206,11 +263,11 @@ def measure_sized_reads(fm, torch, stream, sizes):
             sink = torch.empty(wg * 256, dtype=torch.int32, device="cuda")
             views = [src[(i % n_slices) * read // 4:(i % n_slices + 1) * read // 4] for i in range(10)]
             for v in views[:2]:
-                fm.probe_stream_read(v, sink, wg, stream=stream)
+                probe_stream_read(v, sink, wg, stream=stream)
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g, stream=stream):
                 for v in views:
-                    fm.probe_stream_read(v, sink, wg, stream=stream)
+                    probe_stream_read(v, sink, wg, stream=stream)
             g.replay()
             sec = time_graph(torch, g, stream, 20) / (20 * len(views))
             rate = read / sec / 1e9

@@ -111,8 +111,6 @@ def _load():
         "b12x_gemm_packed_bytes": (st, [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P(ctypes.c_uint64)]),
         "b12x_gemm_pack_weight": (st, [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, vp, vp, vp, ctypes.c_uint64, vp]),
         "b12x_gemm_mm": (st, [vp, i64, i64, vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, vp, vp, i64, vp]),
-        "b12x_probe_stream_read": (st, [vp, ctypes.c_uint64, vp, ctypes.c_int32, vp]),
-        "b12x_probe_mfma": (st, [vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, vp]),
         "b12x_status_string": (ctypes.c_char_p, [st]),
         "b12x_last_error": (ctypes.c_char_p, []),
     }
@@ -128,7 +126,7 @@ EXPORTED = ("b12x_moe_plan_weights", "b12x_moe_prepare_weights", "b12x_moe_is_su
             "b12x_moe_plan_destroy", "b12x_moe_scratch_specs", "b12x_moe_bind", "b12x_moe_run",
             "b12x_moe_run_stage", "b12x_moe_run_noalloc", "b12x_moe_binding_query", "b12x_moe_scratch_region",
             "b12x_mxfp8_quantize_rows", "b12x_gemm_packed_bytes", "b12x_gemm_pack_weight", "b12x_gemm_mm",
-            "b12x_probe_stream_read", "b12x_probe_mfma", "b12x_status_string",
+            "b12x_status_string",
             "b12x_last_error")
 
 
@@ -340,24 +338,6 @@ def gemm_mm(x, w_packed, n, weight_format, global_scale=None, out=None, stream=N
     _check(_lib.b12x_gemm_mm(_ptr(x), m, x.stride(0), _ptr(w_packed), n, k, _WFMT[weight_format], _ptr(global_scale),
                              _ptr(out), out.stride(0), _stream(stream)))
     return out
-
-
-def probe_stream_read(src, sink, workgroups, stream=None):
-    """Measurement probe: stream `src` (any contiguous device tensor, 16-byte
-    multiple) through `workgroups` workgroups; sink: int32/uint32 tensor of
-    workgroups*256 elements."""
-    if sink.numel() < workgroups * 256:
-        raise ValueError("sink needs workgroups*256 elements")
-    _check(_lib.b12x_probe_stream_read(_ptr(src), src.numel() * src.element_size(), _ptr(sink), workgroups,
-                                       _stream(stream)))
-
-
-def probe_mfma(sink, workgroups, iterations, f16=False, stream=None):
-    """Measurement probe: 16 * iterations 16x16x32 MFMAs per wave, four waves
-    per workgroup; sink: float32 tensor of workgroups*256 elements."""
-    if sink.dtype != torch.float32 or sink.numel() < workgroups * 256:
-        raise ValueError("sink must be float32 with workgroups*256 elements")
-    _check(_lib.b12x_probe_mfma(_ptr(sink), workgroups, iterations, int(bool(f16)), _stream(stream)))
 
 
 class FusedMoE:

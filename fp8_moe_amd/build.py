@@ -1,4 +1,5 @@
-"""Build ``libb12x_moe.so`` (all HIP kernels + the C ABI) for gfx950 in-tree.
+"""Build ``libb12x_moe.so`` (all HIP kernels + the C ABI) and the benchmark
+harness's ``libb12x_probes.so`` (measurement probes) for gfx950 in-tree.
 
 Usage: ``python fp8_moe_amd/build.py`` (or ``build()`` from Python).  Always
 recompiles every source; objects go to ``fp8_moe_amd/_build/``.
@@ -11,12 +12,14 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libb12x_moe.so")
+PROBES_OUT = os.path.join(HERE, "libb12x_probes.so")
 BUILD = os.path.join(HERE, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["gemm_inst_silu_f16.hip", "gemm_inst_relu2_f16.hip", "gemm_inst_silu.hip", "gemm_inst_relu2.hip",
            "gemm_inst_down.hip", "decode.hip", "decode_sk.hip", "api.cpp", "pack.hip", "route.hip", "quant.hip", "gemm.hip",
-           "combine.hip", "probes.hip"]
+           "combine.hip"]
+PROBE_SOURCES = ["probes.hip"]
 
 # -packed-fp32-ops: keep hipcc from emitting packed fp32 VALU ops.
 FLAGS = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-function",
@@ -34,20 +37,26 @@ def _compile(src):
     return obj, errs
 
 
-def build(verbose=False):
-    os.makedirs(BUILD, exist_ok=True)
-    jobs = min(len(SOURCES), max(1, int(os.environ.get("MAX_JOBS", str(os.cpu_count() or 8)))))
-    with cf.ThreadPoolExecutor(jobs) as ex:
-        results = list(ex.map(_compile, SOURCES))
-    for _, errs in results:
-        if verbose and errs.strip():
-            print(errs, file=sys.stderr)
-    tmp = OUT + ".tmp"
-    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *[o for o, _ in results], "-o", tmp]
+def _link(objs, out):
+    tmp = out + ".tmp"
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError("link failed:\n" + res.stderr)
-    os.replace(tmp, OUT)
+    os.replace(tmp, out)
+
+
+def build(verbose=False):
+    os.makedirs(BUILD, exist_ok=True)
+    sources = SOURCES + PROBE_SOURCES
+    jobs = min(len(sources), max(1, int(os.environ.get("MAX_JOBS", str(os.cpu_count() or 8)))))
+    with cf.ThreadPoolExecutor(jobs) as ex:
+        results = dict(zip(sources, ex.map(_compile, sources)))
+    for _, errs in results.values():
+        if verbose and errs.strip():
+            print(errs, file=sys.stderr)
+    _link([results[s][0] for s in SOURCES], OUT)
+    _link([results[s][0] for s in PROBE_SOURCES], PROBES_OUT)
     return OUT
 
 

@@ -598,23 +598,4 @@ b12x_status b12x_gemm_mm(const void* x, int64_t m, int64_t x_stride, const void*
   return B12X_OK;
 }
 
-b12x_status b12x_probe_stream_read(const void* src, uint64_t bytes, uint32_t* sink, int32_t workgroups,
-                                   void* stream) {
-  if (!src || !sink) return fail(B12X_ERR_INVALID_ARGUMENT, "NULL device pointer");
-  if (workgroups < 1) return fail(B12X_ERR_INVALID_ARGUMENT, "workgroups must be >= 1");
-  if (bytes % 16) return fail(B12X_ERR_INVALID_ARGUMENT, "bytes must be a multiple of 16");
-  if (!aligned(src, 16)) return fail(B12X_ERR_MISALIGNED, "src must be 16-byte aligned");
-  const int err = launch_probe_read(src, bytes, sink, workgroups, (hipStream_t)stream);
-  if (err) return hip_fail(err, "stream-read probe");
-  return B12X_OK;
-}
-
-b12x_status b12x_probe_mfma(float* sink, int32_t workgroups, int32_t iterations, int32_t f16, void* stream) {
-  if (!sink) return fail(B12X_ERR_INVALID_ARGUMENT, "NULL device pointer");
-  if (workgroups < 1 || iterations < 1) return fail(B12X_ERR_INVALID_ARGUMENT, "workgroups and iterations must be >= 1");
-  const int err = launch_probe_mfma(sink, workgroups, iterations, f16 != 0, (hipStream_t)stream);
-  if (err) return hip_fail(err, "MFMA probe");
-  return B12X_OK;
-}
-
 }  // extern "C"

@@ -176,8 +176,6 @@ int launch_combine(const BindingImpl& b, hipStream_t s);
 inline uint64_t dense_scales_offset(const MatrixLayout& l) { return (l.codes_per_expert + 255) / 256 * 256; }
 int launch_dense_mm(const uint16_t* x, int64_t m, int64_t x_stride, const uint8_t* w, const MatrixLayout& l,
                     int wfmt, const float* global_scale, uint16_t* out, int64_t out_stride, hipStream_t s);
-int launch_probe_read(const void* src, uint64_t bytes, uint32_t* sink, int workgroups, hipStream_t s);
-int launch_probe_mfma(float* sink, int workgroups, int iterations, bool f16, hipStream_t s);
 // compute units of the current device (cached per device)
 int device_cu_count();
 int launch_decode1(const BindingImpl& b, hipStream_t s);

@@ -4,6 +4,7 @@
 // memory traffic, at whatever clock the part holds under that load).
 #include <type_traits>
 
+#include "b12x_probes.h"
 #include "device_common.h"
 
 namespace b12x {
@@ -54,16 +55,28 @@ __global__ __launch_bounds__(256) void probe_mfma_kernel(float* __restrict__ sin
   sink[(uint64_t)blockIdx.x * 256 + threadIdx.x] = s;
 }
 
-int launch_probe_read(const void* src, uint64_t bytes, uint32_t* sink, int workgroups, hipStream_t s) {
-  hipLaunchKernelGGL(probe_read_kernel, dim3((unsigned)workgroups), dim3(256), 0, s, (const uint4*)src, bytes / 16,
-                     sink);
-  return (int)hipGetLastError();
-}
-
-int launch_probe_mfma(float* sink, int workgroups, int iterations, bool f16, hipStream_t s) {
-  if (f16) hipLaunchKernelGGL(probe_mfma_kernel<true>, dim3((unsigned)workgroups), dim3(256), 0, s, sink, iterations, 1.0f);
-  else hipLaunchKernelGGL(probe_mfma_kernel<false>, dim3((unsigned)workgroups), dim3(256), 0, s, sink, iterations, 1.0f);
-  return (int)hipGetLastError();
-}
-
 }  // namespace b12x
+
+extern "C" {
+
+int32_t b12x_probe_stream_read(const void* src, uint64_t bytes, uint32_t* sink, int32_t workgroups, void* stream) {
+  if (!src || !sink || workgroups < 1) return 1;
+  if (bytes % 16 || (uintptr_t)src % 16) return 5;
+  hipLaunchKernelGGL(b12x::probe_read_kernel, dim3((unsigned)workgroups), dim3(256), 0, (hipStream_t)stream,
+                     (const uint4*)src, bytes / 16, sink);
+  return hipGetLastError() == hipSuccess ? 0 : 7;
+}
+
+int32_t b12x_probe_mfma(float* sink, int32_t workgroups, int32_t iterations, int32_t f16, void* stream) {
+  if (!sink || workgroups < 1 || iterations < 1) return 1;
+  const hipStream_t s = (hipStream_t)stream;
+  if (f16)
+    hipLaunchKernelGGL(b12x::probe_mfma_kernel<true>, dim3((unsigned)workgroups), dim3(256), 0, s, sink, iterations,
+                       1.0f);
+  else
+    hipLaunchKernelGGL(b12x::probe_mfma_kernel<false>, dim3((unsigned)workgroups), dim3(256), 0, s, sink, iterations,
+                       1.0f);
+  return hipGetLastError() == hipSuccess ? 0 : 7;
+}
+
+}  // extern "C"

@@ -10,10 +10,21 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
-def _declared_functions():
-    text = open(os.path.join(ROOT, "include", "b12x_moe.h")).read()
+def _declared_functions(header="b12x_moe.h"):
+    text = open(os.path.join(ROOT, "include", header)).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(b12x_\w+)\s*\(", text)))
+
+
+def test_probe_library_is_separate():
+    # the harness's measurement probes live in their own library, not in the MoE ABI
+    import fp8_moe_amd as fm
+    names = _declared_functions("b12x_probes.h")
+    assert names == ["b12x_probe_mfma", "b12x_probe_stream_read"]
+    probes = ctypes.CDLL(os.path.join(ROOT, "fp8_moe_amd", "libb12x_probes.so"))
+    for n in names:
+        assert hasattr(probes, n), n
+        assert not hasattr(ctypes.CDLL(fm.LIB_PATH), n), n
 
 
 def test_library_exports_every_declared_function():

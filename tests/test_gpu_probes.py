@@ -1,13 +1,13 @@
-"""The measurement probes read what they claim to read and run the MFMAs they
-claim to run: the stream-read digest equals the XOR of each thread's words
-computed on the host, and the MFMA probe's result is linear in the number of
-rounds and the same for bf16 and f16 operands (its operands are exact in
-both)."""
+"""The benchmark harness's measurement probes (libb12x_probes.so) read what
+they claim to read and run the MFMAs they claim to run: the stream-read digest
+equals the XOR of each thread's words computed on the host, and the MFMA
+probe's result is linear in the number of rounds and the same for bf16 and f16
+operands (its operands are exact in both)."""
 import numpy as np
 import pytest
 import torch
 
-import fp8_moe_amd as fm
+from bench import ProbeError, probe_mfma, probe_stream_read
 
 pytestmark = pytest.mark.gpu
 
@@ -19,7 +19,7 @@ def test_stream_read_digest(workgroups, words_per_wg):
     host = torch.randint(-2**31, 2**31 - 1, (total * 4,), dtype=torch.int64, generator=g).to(torch.int32)
     src = host.cuda()
     sink = torch.zeros(workgroups * 256, dtype=torch.int32, device="cuda")
-    fm.probe_stream_read(src, sink, workgroups)
+    probe_stream_read(src, sink, workgroups)
     torch.cuda.synchronize()
     words = host.numpy().view(np.uint32).reshape(total, 4)
     per = total // workgroups
@@ -38,7 +38,7 @@ def test_mfma_probe_linear_and_dtype_independent():
     for f16 in (False, True):
         for it in (1, 3):
             sink = torch.full((wg * 256,), float("nan"), dtype=torch.float32, device="cuda")
-            fm.probe_mfma(sink, wg, it, f16=f16)
+            probe_mfma(sink, wg, it, f16=f16)
             torch.cuda.synchronize()
             out[f16, it] = sink.cpu()
     one = out[False, 1]
@@ -54,9 +54,9 @@ def test_mfma_probe_linear_and_dtype_independent():
 def test_probe_errors():
     sink = torch.zeros(256, dtype=torch.int32, device="cuda")
     src = torch.zeros(64, dtype=torch.int32, device="cuda")
-    with pytest.raises(fm.B12xError):
-        fm.probe_stream_read(src, sink, 0)
-    with pytest.raises(fm.B12xError):
-        fm.probe_stream_read(src[1:], sink, 1)  # 4-byte offset: misaligned, and not a multiple of 16
-    with pytest.raises(fm.B12xError):
-        fm.probe_mfma(torch.zeros(256, device="cuda"), 1, 0)
+    with pytest.raises(ProbeError):
+        probe_stream_read(src, sink, 0)
+    with pytest.raises(ProbeError):
+        probe_stream_read(src[1:], sink, 1)  # 4-byte offset: misaligned, and not a multiple of 16
+    with pytest.raises(ProbeError):
+        probe_mfma(torch.zeros(256, device="cuda"), 1, 0)
