@@ -21,7 +21,8 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libb12x_moe.so")
+# B12X_MOE_LIB: another build of the same library (the host-sanitized one for the sanitizer run)
+LIB_PATH = os.environ.get("B12X_MOE_LIB") or os.path.join(_HERE, "libb12x_moe.so")
 
 WEIGHT_FORMATS = {"mxfp4": 1, "nvfp4": 2}
 ACT_FORMATS = {"bf16": 1, "mxfp8": 2, "nvfp4": 3}

@@ -60,5 +60,47 @@ def build(verbose=False):
     return OUT
 
 
+# Host-sanitized variant of the MoE library for the CPU sanitizer run: api.cpp (the
+# host runtime: planning, validation, binding, dispatch) built with AddressSanitizer
+# and UndefinedBehaviorSanitizer on its host pass only, linked with the ordinary
+# kernel objects of build().  Load it with the sanitizer runtime preloaded
+# (HOSTSAN_RUNTIME) and B12X_MOE_LIB pointing at it.
+HOSTSAN_OUT = os.path.join(BUILD, "libb12x_moe_hostsan.so")
+HOSTSAN_RUNTIME = "/opt/rocm/llvm/lib/clang/{}/lib/linux/libclang_rt.asan-x86_64.so"
+
+
+def hostsan_runtime():
+    base = "/opt/rocm/llvm/lib/clang"
+    for v in sorted(os.listdir(base), reverse=True) if os.path.isdir(base) else []:
+        path = HOSTSAN_RUNTIME.format(v)
+        if os.path.exists(path):
+            return path
+    return None
+
+
+def build_hostsan():
+    san = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+           "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer"]
+    objs = [os.path.join(BUILD, s + ".o") for s in SOURCES if s != "api.cpp"]
+    missing = [o for o in objs if not os.path.exists(o)]
+    if missing:
+        raise RuntimeError(f"run build() first: {missing[0]} is missing")
+    api_o = os.path.join(BUILD, "api.cpp.hostsan.o")
+    flags = [f for f in FLAGS if f != "-O3"] + ["-O1", "-g"]
+    res = subprocess.run([HIPCC, "-x", "hip", *flags, *san, "-c", os.path.join(CSRC, "api.cpp"), "-o", api_o],
+                         capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError("hipcc failed for api.cpp (host-sanitized):\n" + res.stderr)
+    tmp = HOSTSAN_OUT + ".tmp"
+    res = subprocess.run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-shared-libsan", *san, api_o, *objs,
+                          "-o", tmp], capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError("link failed (host-sanitized):\n" + res.stderr)
+    os.replace(tmp, HOSTSAN_OUT)
+    return HOSTSAN_OUT
+
+
 if __name__ == "__main__":
     print(build(verbose=True))
+    if len(sys.argv) > 1 and sys.argv[1] == "--hostsan":
+        print(build_hostsan())
