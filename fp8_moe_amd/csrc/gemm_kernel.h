@@ -6,12 +6,18 @@
 //   GEMM1: h[row] = act(x[token(row)] . W13_e^T)   (SiLU-gated or ReLU^2)
 //   GEMM2: y[row] = h[row] . W2_e^T                (stored as bf16)
 // over the routing tiles (expert, first row, rows).  A workgroup of 4 waves
-// owns one routing tile (up to kTileRows = 144 rows) x 4*NFW weight fragments
-// (16 columns each).  The packed FP4 fragments stream from global memory
-// straight into registers.  The activation rows reach LDS by DMA
-// (buffer_load ... lds) for 16-bit activations, in a ring of four stages
-// loaded three K steps ahead, or through registers into two LDS buffers for
-// MXFP8 activations.  All loads are raw buffer loads whose out-of-range
+// owns one routing tile (up to kTileRows = 128 rows) x 4*NFW weight fragments
+// (16 columns each), and two workgroups share a CU: one wave per SIMD cannot
+// keep the matrix core busy with 16x16x32 MFMAs (a register-only loop of them
+// reaches ~53% of the datasheet rate at one wave per SIMD, ~82% at two), so
+// each wave holds at most 256 registers and each workgroup at most half of
+// the LDS, and the other workgroup's MFMAs run while one waits at its step
+// barrier.  Every wave covers all rows of the tile, so each dequantized
+// weight feeds 128 rows of MFMAs.  The packed FP4 fragments stream from
+// global memory straight into registers.  The activation rows reach LDS by
+// DMA (buffer_load ... lds) for 16-bit activations, in two stages loaded one
+// K step ahead, or through registers into two LDS buffers for MXFP8
+// activations.  All loads are raw buffer loads whose out-of-range
 // offsets read zeros, so none of them sits behind a branch.
 //   W4A16: each 1 KB fragment is four 16x16x32 MFMA operands; FP4 is turned
 //          into bf16 in registers (v_cvt_scalef32_pk_bf16_fp4 with the E8M0
@@ -91,7 +97,7 @@ enum { MODE_SILU = 1, MODE_RELU2 = 2, MODE_DOWN = 3, MODE_DENSE = 4 };
 // blocks.  Missing fragments (a partial N tile) load zeros and are dropped
 // in the epilogue.
 template <int WF, int AF, int MODE, int NFW>
-__global__ __launch_bounds__(kGemmThreads, 1) void moe_gemm_kernel(const GemmParams p) {
+__global__ __launch_bounds__(kGemmThreads, 2) void moe_gemm_kernel(const GemmParams p) {
   constexpr bool A8 = AF == B12X_ACT_MXFP8;
   // f16 activations x NVFP4 weights dequantized to f16
   constexpr bool F16 = AF == kActF16 || AF == kActF16Rt || AF == kActF16NvRt;
@@ -115,8 +121,6 @@ __global__ __launch_bounds__(kGemmThreads, 1) void moe_gemm_kernel(const GemmPar
   constexpr int kStageBytes = A8 ? 16 : kTileRows * 256;
   __shared__ __attribute__((aligned(1024))) uint8_t lds_st0[kStageBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t lds_st1[kStageBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t lds_st2[kStageBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t lds_st3[kStageBytes];
   __shared__ float lds_rs[F16 ? kTileRows : 1];  // f16: 2^exponent of each tile row
 
   const int tid = threadIdx.x;
@@ -229,23 +233,24 @@ __global__ __launch_bounds__(kGemmThreads, 1) void moe_gemm_kernel(const GemmPar
         if (tid < kTileRows) lds_s[buf][tid] = (rs & rk) | (0x7F7F7F7Fu & ~rk);
       }
     };
-    // weight fragments f0 + j: per-lane offsets (zeros past the matrix) and
-    // the K step as a scalar offset
-    uint32_t b_voff[NFW], bs_voff[NFW];
-#pragma unroll
-    for (int j = 0; j < NFW; ++j) {
-      const int f = f0 + j;
-      b_voff[j] = f < p.NF ? (uint32_t)(f * p.KF * kFragBytes + lane * 16) : kBufOOB;
-      bs_voff[j] = f < p.NF ? (uint32_t)(f * p.KFS * kScaleGroupBytes + lane * 4) : kBufOOB;
-    }
-    // scales first: a step needs them before its codes
+    // weight fragments f0 + j: the lane's offset in a fragment, and the fragment and
+    // K step as a scalar offset.  Fragments past the matrix (a partial N tile) reload
+    // the last one; their results are dropped in the epilogue.
+    const uint32_t b_voff = (uint32_t)(lane * 16), bs_voff = (uint32_t)(lane * 4);
     auto load_b = [&](uint4 (&q)[NFW], uint32_t (&sc)[NFW], int kf) {
       const int kfc = min(kf, p.KF - 1);
       const int sgrp = WF == B12X_WEIGHT_MXFP4 ? kfc >> 2 : kfc >> 1;
+      // scales first: a step needs them before its codes
 #pragma unroll
-      for (int j = 0; j < NFW; ++j) sc[j] = buf_load4s(bs_rsrc, bs_voff[j], (uint32_t)(sgrp * kScaleGroupBytes));
+      for (int j = 0; j < NFW; ++j) {
+        const int f = min(f0 + j, p.NF - 1);
+        sc[j] = buf_load4s(bs_rsrc, bs_voff, (uint32_t)((f * p.KFS + sgrp) * kScaleGroupBytes));
+      }
 #pragma unroll
-      for (int j = 0; j < NFW; ++j) q[j] = buf_load16s(b_rsrc, b_voff[j], (uint32_t)(kfc * kFragBytes));
+      for (int j = 0; j < NFW; ++j) {
+        const int f = min(f0 + j, p.NF - 1);
+        q[j] = buf_load16s(b_rsrc, b_voff, (uint32_t)((f * p.KF + kfc) * kFragBytes));
+      }
     };
 
     f32x4 acc[MF][NFW];
@@ -254,10 +259,10 @@ __global__ __launch_bounds__(kGemmThreads, 1) void moe_gemm_kernel(const GemmPar
 #pragma unroll
       for (int j = 0; j < NFW; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // MFMAs of one K fragment over the first NMF 16-row blocks.  W4A16: the
-    // bf16 operands of sub-step s+1 (dequantized weights, LDS activation
-    // reads) are produced while sub-step s runs on the MFMAs; the schedule
-    // interleaves them so the VALU works under the matrix core.
+    // MFMAs of one K fragment over the first NMF 16-row blocks.  W4A16: per
+    // sub-step the weights are dequantized in registers, then every 16-row
+    // block's activations are read from LDS; with two waves per SIMD the
+    // other wave's MFMAs run under this wave's VALU and LDS work.
     auto compute = [&](auto nmf_tag, auto par_tag, const uint8_t* la, const uint4 (&bq)[NFW],
                        const uint32_t (&bs)[NFW], int kf) {
       constexpr int NMF = decltype(nmf_tag)::value;
@@ -288,45 +293,22 @@ __global__ __launch_bounds__(kGemmThreads, 1) void moe_gemm_kernel(const GemmPar
             else out[j] = dequant8_bf16<WF>(dw, scl[j][s >> 1]);
           }
         };
-        // row 16 mf + r16, 16-byte chunk 4 g + s, stored at chunk position (4 g + s) ^ r16
-        auto ld = [&](uint4 (&out)[NMF], int s) {
-          const uint8_t* lp = la + r16 * 256 + 16 * ((4 * g + s) ^ r16);
+        // sub-step s: the 4 fragments' operands, then each 16-row block's LDS read and
+        // its NFW MFMAs
 #pragma unroll
-          for (int mf = 0; mf < NMF; ++mf) out[mf] = *(const uint4*)(lp + mf * 16 * 256);
-        };
-        OpT b0[NFW], b1[NFW];
-        uint4 a0[NMF], a1[NMF];
-        dq(b0, 0);
-        ld(a0, 0);
-        auto step = [&](const OpT (&bc)[NFW], const uint4 (&ac)[NMF], OpT (&bn)[NFW], uint4 (&an)[NMF], int s) {
-          if (s < 3) {
-            ld(an, s + 1);
-            dq(bn, s + 1);
-          }
+        for (int s = 0; s < 4; ++s) {
+          OpT b[NFW];
+          dq(b, s);
 #pragma unroll
           for (int mf = 0; mf < NMF; ++mf) {
-            const OpT afr = __builtin_bit_cast(OpT, ac[mf]);
+            const OpT afr = __builtin_bit_cast(OpT, *(const uint4*)(la + (16 * mf + r16) * 256 + 16 * ((4 * g + s) ^ r16)));
 #pragma unroll
             for (int j = 0; j < NFW; ++j) {
-              if constexpr (F16) acc[mf][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(afr, bc[j], acc[mf][j], 0, 0, 0);
-              else acc[mf][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr, bc[j], acc[mf][j], 0, 0, 0);
+              if constexpr (F16) acc[mf][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(afr, b[j], acc[mf][j], 0, 0, 0);
+              else acc[mf][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr, b[j], acc[mf][j], 0, 0, 0);
             }
           }
-          if (s < 3) {
-            // NMF*NFW MFMAs, each followed by a share of the next sub-step's VALU and LDS work
-            constexpr int kValu = (WF == B12X_WEIGHT_NVFP4 && !F16) ? 4 : 2;
-#pragma unroll
-            for (int i = 0; i < NMF * NFW; ++i) {
-              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);      // MFMA
-              __builtin_amdgcn_sched_group_barrier(0x002, kValu, 0);  // VALU
-              __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);      // DS read
-            }
-          }
-        };
-        step(b0, a0, b1, a1, 0);
-        step(b1, a1, b0, a0, 1);
-        step(b0, a0, b1, a1, 2);
-        step(b1, a1, b0, a0, 3);
+        }
       } else {
         i32x8 bfr[NFW];
         int sb[NFW];
@@ -386,27 +368,22 @@ __global__ __launch_bounds__(kGemmThreads, 1) void moe_gemm_kernel(const GemmPar
     };
 
     // ---- W4A16 main loop: activations global -> LDS by DMA (buffer_load ... lds) into
-    // kStages stages, weights into kStages register stages, both kAhead K steps ahead.
-    // DMA instruction j of wave w fills rows kRowsPerWave w + 4 j + lane/16 of a stage;
+    // two stages, weights into two register stages, both loaded one K step ahead.  DMA
+    // instruction j of wave w fills rows kRowsPerWave w + 4 j + lane/16 of a stage;
     // position lane%16 of a row holds its 16-byte chunk (lane%16) ^ (row & 15), so the
-    // MFMA operand reads of 16 rows hit 16 different bank groups.  Step kf waits for its
-    // own loads (the later steps' loads stay in flight), then a barrier makes every
-    // wave's DMA of the stage visible and frees the stage read at step kf - 1, which the
-    // loads of step kf + kAhead then refill.  Every step issues the same loads (steps
-    // past the end reload the last fragment and are not computed), so the wait counts
-    // are exact.
-    constexpr int kStages = 4;
-    constexpr int kAhead = kStages - 1;
+    // MFMA operand reads of 16 rows hit 16 different bank groups.  Step kf waits for
+    // its loads (issued during step kf - 1), then a barrier makes every wave's DMA of
+    // the stage visible and frees the other stage (read at step kf - 1), which the
+    // loads of step kf + 1 then refill while step kf computes.  Steps past the end
+    // reload the last fragment and are not computed.
+    constexpr int kStages = 2;
     constexpr int kRowsPerWave = kTileRows / 4;
-    constexpr int kDma = kRowsPerWave / 4;        // 1 KB DMA instructions per wave per step
-    constexpr int kLoadsPerStep = kDma + 2 * NFW;  // VMEM instructions a wave issues per step
-    static_assert(kRowsPerWave % 4 == 0 && (kAhead - 1) * kLoadsPerStep < 64, "DMA rows / wait count");
+    constexpr int kDma = kRowsPerWave / 4;  // 1 KB DMA instructions per wave per step
+    static_assert(kRowsPerWave % 4 == 0, "DMA rows");
     auto stage_lds = [&](auto st_tag) -> uint8_t* {
       constexpr int ST = decltype(st_tag)::value;
       if constexpr (ST == 0) return lds_st0;
-      else if constexpr (ST == 1) return lds_st1;
-      else if constexpr (ST == 2) return lds_st2;
-      else return lds_st3;
+      else return lds_st1;
     };
     auto fill_row_scales = [&]() {  // f16: 2^exponent of each row's token (read by the epilogue)
       if constexpr (F16) {
@@ -457,48 +434,40 @@ __global__ __launch_bounds__(kGemmThreads, 1) void moe_gemm_kernel(const GemmPar
                                                      16, dvoff[j], soff, 0, 0);
         }
       };
-      uint4 bq[kStages][NFW];
-      uint32_t bs[kStages][NFW];
-      auto issue = [&](auto st_tag, int kf) {
-        constexpr int ST = decltype(st_tag)::value;
-        dma_a(st_tag, kf);
-        load_b(bq[ST], bs[ST], kf);
-      };
+      uint4 bq[2][NFW];
+      uint32_t bs[2][NFW];
+      // step kf: stage ST = kf % 2 (LDS and registers; also the parity of kf)
       auto step = [&](auto st_tag, int kf) {
         constexpr int ST = decltype(st_tag)::value;
-        constexpr int NX = (ST + kAhead) % kStages;
-        constexpr int N = (kAhead - 1) * kLoadsPerStep;
         __builtin_amdgcn_sched_barrier(0);
-        // s_waitcnt vmcnt(N) (gfx9 encoding: vmcnt bits [3:0] and [15:14], expcnt 7, lgkmcnt 0)
-        __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (0 << 8));
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this step's loads
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
-        issue(std::integral_constant<int, NX>{}, kf + kAhead);
+        dma_a(std::integral_constant<int, ST ^ 1>{}, kf + 1);
+        load_b(bq[ST ^ 1], bs[ST ^ 1], kf + 1);
         __builtin_amdgcn_sched_barrier(0);
-        if (kf < p.KF && !idle) compute(nmf_tag, std::integral_constant<int, ST & 1>{}, stage_lds(st_tag), bq[ST], bs[ST], kf);
+        if (kf < p.KF && !idle)
+          compute(nmf_tag, std::integral_constant<int, ST>{}, stage_lds(st_tag), bq[ST], bs[ST], kf);
       };
       __syncthreads();  // the previous work item is done with LDS
       fill_row_scales();
-      issue(std::integral_constant<int, 0>{}, 0);
-      issue(std::integral_constant<int, 1>{}, 1);
-      issue(std::integral_constant<int, 2>{}, 2);
-      for (int kf = 0; kf < p.KF; kf += kStages) {
+      dma_a(std::integral_constant<int, 0>{}, 0);
+      load_b(bq[0], bs[0], 0);
+      for (int kf = 0; kf < p.KF; kf += 2) {
         step(std::integral_constant<int, 0>{}, kf);
+        if (kf + 1 >= p.KF) break;
         step(std::integral_constant<int, 1>{}, kf + 1);
-        step(std::integral_constant<int, 2>{}, kf + 2);
-        step(std::integral_constant<int, 3>{}, kf + 3);
       }
     };
+    static_assert(MF == 8, "the loops are instantiated for 8, 6, 4 and 2 row blocks");
     if constexpr (A8) {
-      if (nmf > 8) kloop(std::integral_constant<int, 9>{});
-      else if (nmf > 6) kloop(std::integral_constant<int, 8>{});
+      if (nmf > 6) kloop(std::integral_constant<int, 8>{});
       else if (nmf > 4) kloop(std::integral_constant<int, 6>{});
       else if (nmf > 2) kloop(std::integral_constant<int, 4>{});
       else kloop(std::integral_constant<int, 2>{});
     } else {
-      static_assert(kStages == 4, "the loop body is written for four stages");
-      if (nmf > 8) kloop_dma(std::integral_constant<int, 9>{});
-      else if (nmf > 6) kloop_dma(std::integral_constant<int, 8>{});
+      static_assert(kStages == 2, "the loop body is written for two stages");
+      if (nmf > 6) kloop_dma(std::integral_constant<int, 8>{});
       else if (nmf > 4) kloop_dma(std::integral_constant<int, 6>{});
       else if (nmf > 2) kloop_dma(std::integral_constant<int, 4>{});
       else kloop_dma(std::integral_constant<int, 2>{});
@@ -604,14 +573,14 @@ __global__ __launch_bounds__(kGemmThreads, 1) void moe_gemm_kernel(const GemmPar
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
 }
 
-constexpr int kGemmNFW = 4;  // weight fragments per wave: workgroup tile 144 rows x 256 columns
+constexpr int kGemmNFW = 4;  // weight fragments per wave: workgroup tile 128 rows x 256 columns
 
-// Persistent grid: one workgroup per CU, a multiple of 8 (one share per XCD).
+// Persistent grid: two workgroups per CU, a multiple of 8 (one share per XCD).
 // Defined here, instantiated for each (weight format, activation format,
 // mode) in the gemm_inst_*.hip sources so that they compile in parallel.
 template <int WF, int AF, int MODE>
 int launch_gemm_t(const GemmParams& p, int64_t max_work, hipStream_t s) {
-  int64_t grid = device_cu_count();
+  int64_t grid = 2 * (int64_t)device_cu_count();
   if (max_work < grid) grid = (max_work + 7) / 8 * 8;
   grid = grid / 8 * 8;
   if (grid <= 0) grid = 8;

@@ -32,7 +32,7 @@ constexpr int kScaleGroupBytes = 256;
 constexpr uint32_t kLayoutId = 0x4d4f4501u;  // "MOE", version 1
 
 // ---- grouped path ------------------------------------------------------------
-constexpr int kTileRows = 144;   // most rows per GEMM tile (multiple of kRowPad)
+constexpr int kTileRows = 128;   // most rows per GEMM tile (multiple of kRowPad)
 constexpr int kRowPad = 16;      // per-expert row padding = MFMA row block
 constexpr int kRouteChunk = 1024;  // routing pairs per workgroup
 constexpr int kMaxExperts = 1024;
