@@ -153,8 +153,10 @@ def bench_decode_t(fm, synth, torch, stream, T, reps):
     g.replay()
     sec = time_graph(torch, g, stream, reps) / (reps * len(bl))
     nb = sum(row["bytes"] for row in sets[T]) / len(bl)
+    kind, d, extra = time_decode_kernel(torch, fm, bl, stream)
     return {"decode_T": T, "calls": reps * len(bl), "us_per_call": sec * 1e6, "weight_GBs": nb / sec / 1e9,
-            "w13_bytes_per_call": sum(row["w13_bytes"] for row in sets[T]) / len(bl)}
+            "w13_bytes_per_call": sum(row["w13_bytes"] for row in sets[T]) / len(bl),
+            "kernel": kind, "kernel_launch_us": round(d * 1e6, 3), **extra}
 
 
 def capture(torch, fm, bindings, stream):
@@ -292,6 +294,28 @@ def time_stage_graph(torch, fm, bindings, stages, stream, reps=10):
                 fm.run_stage(b, stage, stream=stream)
     g.replay()
     return time_graph(torch, g, stream, reps) / (reps * len(bindings))
+
+
+def time_decode_kernel(torch, fm, bl, stream):
+    """The decode path's main kernel and its mean launch duration (s) over the
+    bindings `bl` (one T): (kind, seconds, per-T fields).
+
+    The split-K kernel and the fused gate/up + down kernel are timed alone:
+    a graph of that one kernel for every binding (each fused launch has a tag
+    of its own, so every launch waits for its own gate/up groups).  Without
+    either (unfused decode or grouped path) the gate/up kernel alone."""
+    path = fm.binding_query(bl[0], "path")
+    fused = path == 2 and fm.binding_query(bl[0], "num_stages") == 2
+    extra = {"path": {3: "decode, split-K", 2: "decode, fused" if fused else "decode"}.get(path, "grouped")}
+    if path == 3 or fused:
+        d = time_stage_graph(torch, fm, bl, ["decode1"], stream)
+        extra["decode_kernel_us"] = d * 1e6
+        return ("splitk" if path == 3 else "fused"), d, extra
+    st1, st2 = ("decode1", "decode2") if path == 2 else ("gemm1", "gemm2")
+    d = time_stage_graph(torch, fm, bl, [st1], stream)
+    extra["gate_up_kernel_us"] = d * 1e6
+    extra["down_kernel_us"] = time_stage_graph(torch, fm, bl, [st2], stream) * 1e6
+    return "gate_up", d, extra
 
 
 def time_stage_launches(torch, fm, bindings, stage, stream, repeats=3):
@@ -679,38 +703,15 @@ def main():
                           "us_p10_p50_p90": [round(percentile(samples, q) * 1e6, 2) for q in (0.1, 0.5, 0.9)],
                           "calls": reps * N_SETS}
 
-    # dominant kernel: the decode path's fused gate/up + down kernel (all touched weight
-    # bytes), timed in the sequence it runs in: a graph of (fused kernel, combine) per input
-    # set less a graph of the combines alone (the combine advances the call epoch that the
-    # fused kernel's waits compare against, so each launch really waits for its gate/up
-    # groups).  Without the fused kernel (unfused decode or grouped path) the gate/up
-    # kernel alone, with the W13 bytes.
     durs, kbytes, kinds = [], [], []
     for T in Ts:
         bl = [row["binding"] for row in sets[T]]
-        path = fm.binding_query(bl[0], "path")
-        fused = path == 2 and fm.binding_query(bl[0], "num_stages") == 2
-        nb = sum(row["bytes"] for row in sets[T]) / N_SETS
-        if path == 3:
-            # split-K decode kernel: all touched weight bytes, no dependency on the combine
-            d = time_stage_graph(torch, fm, bl, ["decode1"], stream)
-            per_t[f"T{T}"]["decode_kernel_us"] = d * 1e6
-            kinds.append("splitk")
-        elif fused:
-            d = (time_stage_graph(torch, fm, bl, ["decode1", "combine"], stream)
-                 - time_stage_graph(torch, fm, bl, ["combine"], stream))
-            per_t[f"T{T}"]["decode_kernel_us"] = d * 1e6
-            kinds.append("fused")
-        else:
-            st1, st2 = ("decode1", "decode2") if path == 2 else ("gemm1", "gemm2")
-            d = time_stage_graph(torch, fm, bl, [st1], stream)
-            nb = sum(row["w13_bytes"] for row in sets[T]) / N_SETS
-            per_t[f"T{T}"]["gate_up_kernel_us"] = d * 1e6
-            per_t[f"T{T}"]["down_kernel_us"] = time_stage_graph(torch, fm, bl, [st2], stream) * 1e6
-            kinds.append("gate_up")
+        kind, d, extra = time_decode_kernel(torch, fm, bl, stream)
+        nb = sum(row["w13_bytes" if kind == "gate_up" else "bytes"] for row in sets[T]) / N_SETS
+        per_t[f"T{T}"].update(extra)
         durs.append(d)
         kbytes.append(nb)
-        per_t[f"T{T}"]["path"] = {3: "decode, split-K", 2: "decode, fused" if fused else "decode"}.get(path, "grouped")
+        kinds.append(kind)
         per_t[f"T{T}"]["kernel_GBs"] = round(nb / d / 1e9, 1)
         per_t[f"T{T}"]["kernel_frac_hbm"] = round(nb / d / 1e9 / HBM_PEAK_GBS, 4)
     names = {"fused": "decode_fused_kernel<MXFP4, SILU> (gate/up + down, decode path)",

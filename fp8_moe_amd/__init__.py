@@ -102,6 +102,7 @@ def _load():
         "b12x_moe_plan": (st, [P(Caps), P(vp)]),
         "b12x_moe_plan_destroy": (None, [vp]),
         "b12x_moe_scratch_specs": (st, [vp, P(ScratchSpec), ctypes.c_int32, P(ctypes.c_int32)]),
+        "b12x_moe_prime": (st, [vp, vp, ctypes.c_uint64, vp]),
         "b12x_moe_bind": (st, [vp, vp, ctypes.c_uint64, P(Experts), vp, i64, i64, vp, vp, vp, i64, P(Binding)]),
         "b12x_moe_run": (st, [P(Binding), vp]),
         "b12x_moe_run_stage": (st, [P(Binding), ctypes.c_int32, vp]),
@@ -124,7 +125,7 @@ def _load():
 
 _lib = _load()
 EXPORTED = ("b12x_moe_plan_weights", "b12x_moe_prepare_weights", "b12x_moe_is_supported", "b12x_moe_plan",
-            "b12x_moe_plan_destroy", "b12x_moe_scratch_specs", "b12x_moe_bind", "b12x_moe_run",
+            "b12x_moe_plan_destroy", "b12x_moe_scratch_specs", "b12x_moe_prime", "b12x_moe_bind", "b12x_moe_run",
             "b12x_moe_run_stage", "b12x_moe_run_noalloc", "b12x_moe_binding_query", "b12x_moe_scratch_region",
             "b12x_mxfp8_quantize_rows", "b12x_gemm_packed_bytes", "b12x_gemm_pack_weight", "b12x_gemm_mm",
             "b12x_status_string",
@@ -244,9 +245,18 @@ def plan(wplan, top_k, max_tokens, act_format="bf16", activation="silu", decode_
     return Plan(h, caps)
 
 
-def alloc_scratch(p, device="cuda"):
+def alloc_scratch(p, device="cuda", stream=None):
+    """A scratch buffer for plan p, primed (b12x_moe_prime) on `stream`."""
     spec = p.scratch_specs()[0]
-    return torch.empty(spec.bytes, dtype=torch.uint8, device=device)
+    scratch = torch.empty(spec.bytes, dtype=torch.uint8, device=device)
+    prime(p, scratch, stream)
+    return scratch
+
+
+def prime(p, scratch, stream=None):
+    """b12x_moe_prime: zero the decode synchronization region of a scratch
+    buffer (once per buffer, before its first run)."""
+    _check(_lib.b12x_moe_prime(p.handle, _ptr(scratch), scratch.numel(), _stream(stream)))
 
 
 def bind(p, scratch, experts, a, topk_ids, topk_weights, out):

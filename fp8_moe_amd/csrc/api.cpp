@@ -255,7 +255,7 @@ b12x_status b12x_moe_plan(const b12x_moe_caps* caps, b12x_moe_plan_t* out) {
     len[R_Y] = grouped > decode ? grouped : decode;
     if (splitk > len[R_Y]) len[R_Y] = splitk;
   }
-  {  // decode path: epoch, status and one flag per (touched expert slot, gate/up group of 2 fragments)
+  {  // decode path: launch counter, status and one flag per (touched expert slot, gate/up group of 2 fragments)
     const int64_t slots = p->decode_max_pairs < p->E ? p->decode_max_pairs : p->E;
     len[R_DSYNC] = p->decode_max_pairs > 0 ? kDecodeFlagsOffset + 8ull * slots * ((p->l13.nf + 1) / 2) : 0;
   }
@@ -287,6 +287,18 @@ b12x_status b12x_moe_scratch_specs(b12x_moe_plan_t p, b12x_scratch_spec* specs, 
     specs[0].dtype = 0;
     specs[0].reserved = 0;
   }
+  return B12X_OK;
+}
+
+b12x_status b12x_moe_prime(b12x_moe_plan_t p, void* scratch, uint64_t scratch_bytes, void* stream) {
+  if (!p || !scratch) return fail(B12X_ERR_INVALID_ARGUMENT, "NULL plan or scratch");
+  if (!aligned(scratch, 256)) return fail(B12X_ERR_MISALIGNED, "scratch must be 256-byte aligned");
+  if (scratch_bytes < p->scratch_bytes)
+    return fail(B12X_ERR_SCRATCH_TOO_SMALL, "scratch %llu < %llu bytes", (unsigned long long)scratch_bytes,
+                (unsigned long long)p->scratch_bytes);
+  if (!p->len[R_DSYNC]) return B12X_OK;
+  const int err = launch_decode_prime((uint8_t*)scratch + p->off[R_DSYNC], p->len[R_DSYNC], (hipStream_t)stream);
+  if (err) return hip_fail(err, "kernel launch");
   return B12X_OK;
 }
 

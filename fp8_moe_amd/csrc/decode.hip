@@ -68,12 +68,13 @@ struct DecodeParams {
   // fused gate/up + down (one launch): completion flag of every (touched
   // expert slot, gate/up group), flags_per_slot of them per slot; a flag
   // holds the launch's tag once that group's h rows are stored.  Every
-  // workgroup reads the epoch when it starts and adds 1 to it when it is
-  // done, so each launch has a tag of its own; a wait that gives up stores
-  // the launch's tag in status (the combine then writes NaN).
+  // workgroup reads the launch counter when it starts and adds its share of
+  // kLaunchStep when it is done, so each launch has a tag of its own; a wait
+  // that gives up stores the launch's tag in status (the combine then
+  // writes NaN).
   uint64_t* flags;
   int flags_per_slot;
-  uint32_t* epoch;
+  uint64_t* counter;
   uint64_t* status;
   uint64_t expect_xor;  // 0; the test hook's waits expect tag ^ expect_xor, which no flag holds
   int max_polls;
@@ -84,9 +85,10 @@ struct DecodeParams {
 
 enum { DMODE_SILU = 1, DMODE_RELU2 = 2, DMODE_DOWN = 3 };
 
-// Tag of this launch's completion flags (decode_tag of the epoch it starts with).
-__device__ __forceinline__ uint64_t flag_tag(const uint32_t* epoch) {
-  return decode_tag(__hip_atomic_load(epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+// Tag of this launch's completion flags: decode_tag of the launch number,
+// the counter's value in units of kLaunchStep.
+__device__ __forceinline__ uint64_t flag_tag(const uint64_t* counter) {
+  return decode_tag((uint32_t)(__hip_atomic_load(counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >> kLaunchShift));
 }
 
 // Upper bound on the polls of one wait (each at least one round trip to
@@ -432,22 +434,28 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(const DecodeParams 
 // other work), the waits for its groups give up after kWaitPolls polls and
 // the call's output is NaN: a loud failure, never a stale result.
 //
-// The launch's tag: every workgroup reads the epoch first thing and adds 1
-// to it as its last action.  No workgroup can be done before all of them
-// have started (each down part waits for the gate/up groups of many
-// workgroups, and all are dispatched at once), so they all read the same
-// epoch, and the next launch (stream order) reads one grid size later.
+// The launch's tag: every workgroup reads the launch counter first thing and
+// adds its share of kLaunchStep (the shares of a grid sum to kLaunchStep, and
+// each is at least 1) as its last action.  So whenever a workgroup of launch
+// n starts, some of its own launch's shares are still missing (its own among
+// them) and none of the next launch's are there: it reads a value in
+// [n, n + 1) * kLaunchStep, whatever the order in which workgroups start and
+// end.  The counter must start at a multiple of kLaunchStep (b12x_moe_prime
+// zeroes it); the combine checks that it still is one.
 template <int WF, int MODE1, int FR1, int KW1, int FR2, int KW2>
 __global__ __launch_bounds__(kDecThreads) void decode_fused_kernel(const DecodeParams p1, const DecodeParams p2) {
   constexpr int FRM = FR1 > FR2 ? FR1 : FR2;
   __shared__ DecodeLds L;
   __shared__ f32x4 s_red[2 * 3 * FRM * 64];
-  const uint64_t tag = flag_tag(p1.epoch);
+  const uint64_t tag = flag_tag(p1.counter);
   const int n_touched = decode_prep(p1.ids, p1.P, p1.E, L.ids, L.bits, L.wpre);
   decode_items<WF, B12X_ACT_BF16, MODE1, FR1, KW1, 1>(p1, L, s_red, n_touched, tag);
   decode_items<WF, B12X_ACT_BF16, DMODE_DOWN, FR2, KW2, 2>(p2, L, s_red, n_touched, tag);
   __syncthreads();
-  if (threadIdx.x == 0) __hip_atomic_fetch_add(p1.epoch, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (threadIdx.x == 0) {
+    const uint64_t share = kLaunchStep / gridDim.x + (blockIdx.x < kLaunchStep % gridDim.x ? 1 : 0);
+    __hip_atomic_fetch_add(p1.counter, share, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
 }
 
 // One workgroup per resident slot, never more than the items of the largest
@@ -569,9 +577,8 @@ bool decode_fused(const BindingImpl& b) {
 // Gate/up groups of FR1 = 2 fragments, down groups of FR2 = 4 (as the
 // separate launches use them at these K), grid as for one launch of the
 // larger item count.
-// With grid_out: the launch's grid only, nothing launched (the combine needs it).
 template <int WF, int MODE1, int KW1, int KW2>
-static int launch_fused_kw(const BindingImpl& b, DecodeParams& p1, DecodeParams& p2, hipStream_t s, int* grid_out) {
+static int launch_fused_kw(const BindingImpl& b, DecodeParams& p1, DecodeParams& p2, hipStream_t s) {
   static int cache[64];
   auto kernel = decode_fused_kernel<WF, MODE1, 2, KW1, 4, KW2>;
   p1.n_groups = (p1.NF + 1) / 2;
@@ -582,28 +589,25 @@ static int launch_fused_kw(const BindingImpl& b, DecodeParams& p1, DecodeParams&
   int64_t grid = resident_workgroups(kernel, cache);
   if (grid > items) grid = items;
   if (grid < 1) grid = 1;
-  if (grid_out) {
-    *grid_out = (int)grid;
-    return 0;
-  }
+  if (grid > (int64_t)kLaunchStep) grid = (int64_t)kLaunchStep;  // every share of the launch counter >= 1
   hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kDecThreads), 0, s, p1, p2);
   return (int)hipGetLastError();
 }
 
 template <int WF, int MODE1>
-static int launch_fused_t(const BindingImpl& b, DecodeParams& p1, DecodeParams& p2, hipStream_t s, int* grid_out) {
+static int launch_fused_t(const BindingImpl& b, DecodeParams& p1, DecodeParams& p2, hipStream_t s) {
   const bool k1 = (p1.KF + 3) / 4 <= 2, k2 = (p2.KF + 3) / 4 <= 2;
-  if (k1 && k2) return launch_fused_kw<WF, MODE1, 2, 2>(b, p1, p2, s, grid_out);
-  if (k1) return launch_fused_kw<WF, MODE1, 2, 4>(b, p1, p2, s, grid_out);
-  if (k2) return launch_fused_kw<WF, MODE1, 4, 2>(b, p1, p2, s, grid_out);
-  return launch_fused_kw<WF, MODE1, 4, 4>(b, p1, p2, s, grid_out);
+  if (k1 && k2) return launch_fused_kw<WF, MODE1, 2, 2>(b, p1, p2, s);
+  if (k1) return launch_fused_kw<WF, MODE1, 2, 4>(b, p1, p2, s);
+  if (k2) return launch_fused_kw<WF, MODE1, 4, 2>(b, p1, p2, s);
+  return launch_fused_kw<WF, MODE1, 4, 4>(b, p1, p2, s);
 }
 
-static int launch_fused(const BindingImpl& b, hipStream_t s, int* grid_out = nullptr) {
+static int launch_fused(const BindingImpl& b, hipStream_t s) {
   DecodeParams p1 = gate_up_params(b), p2 = down_params(b);
   uint8_t* sync = b.dsync;
   for (DecodeParams* p : {&p1, &p2}) {
-    p->epoch = (uint32_t*)(sync + kDecodeEpochOffset);
+    p->counter = (uint64_t*)(sync + kDecodeCounterOffset);
     p->status = (uint64_t*)(sync + kDecodeStatusOffset);
     p->flags = (uint64_t*)(sync + kDecodeFlagsOffset);
     p->flags_per_slot = (int)((b.nf13 + 1) / 2);
@@ -614,16 +618,25 @@ static int launch_fused(const BindingImpl& b, hipStream_t s, int* grid_out = nul
   }
   const bool nv = b.wfmt == B12X_WEIGHT_NVFP4;
   if (b.gated)
-    return nv ? launch_fused_t<B12X_WEIGHT_NVFP4, DMODE_SILU>(b, p1, p2, s, grid_out)
-              : launch_fused_t<B12X_WEIGHT_MXFP4, DMODE_SILU>(b, p1, p2, s, grid_out);
-  return nv ? launch_fused_t<B12X_WEIGHT_NVFP4, DMODE_RELU2>(b, p1, p2, s, grid_out)
-            : launch_fused_t<B12X_WEIGHT_MXFP4, DMODE_RELU2>(b, p1, p2, s, grid_out);
+    return nv ? launch_fused_t<B12X_WEIGHT_NVFP4, DMODE_SILU>(b, p1, p2, s)
+              : launch_fused_t<B12X_WEIGHT_MXFP4, DMODE_SILU>(b, p1, p2, s);
+  return nv ? launch_fused_t<B12X_WEIGHT_NVFP4, DMODE_RELU2>(b, p1, p2, s)
+            : launch_fused_t<B12X_WEIGHT_MXFP4, DMODE_RELU2>(b, p1, p2, s);
 }
 
-int decode_fused_grid(const BindingImpl& b) {
-  int grid = 0;
-  launch_fused(b, nullptr, &grid);
-  return grid;
+// The decode synchronization region zeroed by a fill kernel (not a memset
+// node, so that a captured graph may hold it): counter 0, status 0, flags 0
+// (no flag then holds a launch's tag, which is never 0).
+__global__ __launch_bounds__(256) void zero_words_kernel(uint64_t* __restrict__ w, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) w[i] = 0;
+}
+
+int launch_decode_prime(uint8_t* dsync, uint64_t bytes, hipStream_t s) {
+  const int64_t n = (int64_t)(bytes / 8);
+  if (!dsync || n == 0) return 0;
+  hipLaunchKernelGGL(zero_words_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, (uint64_t*)dsync, n);
+  return (int)hipGetLastError();
 }
 
 int launch_decode1(const BindingImpl& b, hipStream_t s) {

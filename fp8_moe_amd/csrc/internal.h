@@ -50,14 +50,21 @@ inline bool a8_native(int wfmt, int afmt) { return afmt == B12X_ACT_MXFP8 && wfm
 inline bool a8_bf16(int wfmt, int afmt) { return afmt == B12X_ACT_MXFP8 && wfmt == B12X_WEIGHT_NVFP4; }
 // NVFP4 activations (NVFP4 weights only): operands are the exact NVFP4 round trips
 inline bool a4_nv(int afmt) { return afmt == B12X_ACT_NVFP4; }
-// decode synchronization region: int32 call epoch, int32 status, then one
-// uint64 completion flag per (touched expert slot, gate/up group of 2 fragments)
-constexpr int kDecodeEpochOffset = 0;   // uint32: every workgroup of the fused kernel adds 1 when done
-constexpr int kDecodeStatusOffset = 8;  // uint64: the tag of the last fused launch whose wait gave up
-constexpr int kDecodeFlagsOffset = 64;  // uint64 per (expert slot, gate/up group): the tag once its h is stored
-// Tag of the fused launch that read epoch e: never 0 (so zeroed memory never
-// matches) and different for every launch (the epoch advances by the grid
-// size per launch).
+// decode synchronization region: a uint64 launch counter, a uint64 status word,
+// then one uint64 completion flag per (touched expert slot, gate/up group of
+// 2 fragments).  b12x_moe_prime zeroes it once per scratch.
+constexpr int kDecodeCounterOffset = 0;  // uint64: kLaunchStep per completed fused launch
+constexpr int kDecodeStatusOffset = 8;   // uint64: the tag of the last fused launch whose wait gave up
+constexpr int kDecodeFlagsOffset = 64;   // uint64 per (expert slot, gate/up group): the tag once its h is stored
+// Every fused launch adds exactly kLaunchStep to the counter, split over its
+// workgroups (each adds its share when done), so between launches the
+// counter is n * kLaunchStep after n launches and every workgroup of launch
+// n reads a value in [n, n + 1) * kLaunchStep whenever it starts: launch n's
+// tag is decode_tag(n).  A grid holds at most kLaunchStep workgroups.
+constexpr int kLaunchShift = 16;
+constexpr uint64_t kLaunchStep = 1ull << kLaunchShift;
+// Tag of fused launch number e: never 0 (so zeroed memory never matches) and
+// different for every launch.
 constexpr uint32_t kDecodeTagMagic = 0xB12DF1A9u;
 __host__ __device__ inline uint64_t decode_tag(uint32_t e) { return ((uint64_t)e << 32) | kDecodeTagMagic; }
 // Kernels address each activation buffer and each expert's weights with
@@ -142,7 +149,7 @@ struct BindingImpl {
   uint8_t* hs;
   float* y;        // decode path: fp32 rows, one per pair id
   uint16_t* y16;   // grouped path: bf16 rows in routing order (same memory as y)
-  uint8_t* dsync;  // decode path: call epoch, status and the fused kernel's completion flags
+  uint8_t* dsync;  // decode path: launch counter, status and the fused kernel's completion flags
 };
 constexpr uint32_t kBindingMagic = 0xb12b1d01u;
 static_assert(sizeof(BindingImpl) <= sizeof(b12x_moe_binding), "binding does not fit the ABI struct");
@@ -183,7 +190,7 @@ int launch_decode2(const BindingImpl& b, hipStream_t s);
 int launch_decode_combine(const BindingImpl& b, hipStream_t s);
 // split-K decode (path 3): one kernel for gate/up + activation + partial down
 // projections per 32-column slice of h, then the combine of the partials
-int decode_fused_grid(const BindingImpl& b);  // workgroups of the fused decode kernel's launch
+int launch_decode_prime(uint8_t* dsync, uint64_t bytes, hipStream_t s);  // zero the decode synchronization region
 int launch_decode_sk(const BindingImpl& b, hipStream_t s);
 int launch_decode_sk_combine(const BindingImpl& b, hipStream_t s);
 // Bytes of the split-K partial rows of a binding (its whole use of scratch).

@@ -1,7 +1,8 @@
 """Summaries of rocprofv3 output for the measurement record in profiles/.
 
-  python profile_summary.py trace CSV TITLE COMMAND
-      kernel_trace.csv -> markdown table of kernel durations (per kernel and grid)
+  python profile_summary.py trace CSV TITLE COMMAND [--bench-json FILE]
+      kernel_trace.csv -> markdown table of kernel durations (per kernel and grid),
+      optionally followed by the JSON line bench.py printed in the traced run
   python profile_summary.py counters CSV [NAME_SUBSTRING]
       counter_collection.csv -> mean value per dispatch of each counter, per kernel
   python profile_summary.py mfma CSV [CSV ...] [--filter NAME]
@@ -125,6 +126,7 @@ def main():
     t.add_argument("title")
     t.add_argument("command")
     t.add_argument("--filter", default="b12x")
+    t.add_argument("--bench-json", help="the JSON line bench.py printed in the traced run, appended as is")
     c = sub.add_parser("counters")
     c.add_argument("csv")
     c.add_argument("name", nargs="?", default="")
@@ -143,6 +145,11 @@ def main():
     a = ap.parse_args()
     if a.cmd == "trace":
         sys.stdout.write(trace(a.csv, a.title, a.command, a.filter))
+        if a.bench_json:
+            with open(a.bench_json) as f:
+                line = [ln for ln in f.read().splitlines() if ln.startswith("{")][-1]
+            sys.stdout.write("\nThe line bench.py printed in the same run (its own HIP-event timings):\n\n"
+                             f"```json\n{line}\n```\n")
     elif a.cmd == "mfma":
         sys.stdout.write(mfma_table(a.csv, a.filter))
     elif a.cmd == "counters":

@@ -117,6 +117,21 @@ def _bind_status(p, ex, T, a_ptr=0x10000, a_stride=256, out_ptr=0x9000000, scrat
                                   ctypes.c_void_p(tw_ptr), ctypes.c_void_p(out_ptr), a_stride, ctypes.byref(b)), b
 
 
+def test_prime_validation_on_host():
+    """b12x_moe_prime checks its arguments before it enqueues anything; a
+    plan without a decode path has nothing to prime."""
+    import fp8_moe_amd as fm
+    wp = fm.plan_weights(8, 256, 128, True, "mxfp4")
+    p = fm.plan(wp, 2, 16)
+    nbytes = p.scratch_specs()[0].bytes
+    prime = fm.lib().b12x_moe_prime
+    assert prime(p.handle, None, nbytes, None) == 1                          # NULL scratch
+    assert prime(p.handle, ctypes.c_void_p(0x4000080), nbytes, None) == 5    # misaligned
+    assert prime(p.handle, ctypes.c_void_p(0x4000000), nbytes - 1, None) == 4   # too small
+    grouped_only = fm.plan(wp, 2, 16, decode_max_pairs=-1)
+    assert prime(grouped_only.handle, ctypes.c_void_p(0x4000000), grouped_only.scratch_specs()[0].bytes, None) == 0
+
+
 def test_bind_validation_on_host():
     import fp8_moe_amd as fm
     wp = fm.plan_weights(8, 256, 128, True, "mxfp4")

@@ -246,8 +246,8 @@ def test_decode_binding_reused_with_new_inputs():
     """One decode binding run again and again while its inputs change in place
     (x, then the routing): every output matches the oracle for the inputs of
     its own call, in eager runs and in replays of one captured graph.  The
-    fused decode kernel's down phase waits for flags tagged with a per-call
-    epoch, so it never consumes the h rows of an earlier call."""
+    fused decode kernel's down phase waits for flags tagged with its own
+    launch's number, so it never consumes the h rows of an earlier call."""
     import fp8_moe_amd as fm
     wl = synth.WORKLOADS["decode"]
     pr = problem("decode", 32)
@@ -333,6 +333,33 @@ def test_fused_decode_wait_gives_up_then_recovers(monkeypatch):
         torch.cuda.synchronize()
         rel_fro, rel_max, ok = compare(out, pr.oracle(x, ids, tw))
         assert ok, (rel_fro, rel_max)
+
+
+def test_fused_decode_needs_a_primed_scratch():
+    """A scratch that b12x_moe_prime never zeroed (filled with 0x01 bytes here:
+    its launch counter is not a multiple of the launch step) makes the fused
+    decode call write NaN rows, not a result that may be stale.  Primed, the
+    same scratch gives the output of a freshly allocated one, bit for bit."""
+    import fp8_moe_amd as fm
+    wl = synth.WORKLOADS["decode"]
+    pr = problem("decode", 32)
+    T = 8
+    x, ids, tw = _inputs(wl, T)
+    ref_b, ref_out = pr.model.bind(x, ids, tw)
+    fm.run(ref_b)
+    raw = torch.full_like(pr.model.scratch, 1)
+    out = torch.zeros_like(ref_out)
+    b = fm.bind(pr.model.plan, raw, pr.model.experts, x, ids, tw, out)
+    assert fm.binding_query(b, "path") == 2 and fm.binding_query(b, "num_stages") == 2
+    fm.run(b)
+    torch.cuda.synchronize()
+    assert torch.isnan(out.float()).all()
+    fm.prime(pr.model.plan, raw)
+    for _ in range(2):
+        out.fill_(0)
+        fm.run(b)
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_out)
 
 
 # decode path (T*k <= 256) against the grouped path and the oracle on the same inputs
