@@ -22,8 +22,13 @@ SOURCES = ["gemm_inst_silu_f16.hip", "gemm_inst_relu2_f16.hip", "gemm_inst_silu.
 PROBE_SOURCES = ["probes.hip"]
 
 # -packed-fp32-ops: keep hipcc from emitting packed fp32 VALU ops.
+# -pragma-unroll-threshold: loops marked `#pragma unroll` are unrolled whatever
+# their size.  Under LLVM's default limit the grouped GEMM's W4A4 epilogue (the
+# exact NVFP4 requantization of h, once per element of the tile) stayed a loop,
+# which indexed the accumulator array at run time and moved it to scratch
+# memory, inside the K loop too.
 FLAGS = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-function",
-         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-mllvm", "-pragma-unroll-threshold=1000000",
          "-I" + os.path.join(os.path.dirname(HERE), "include")]
 
 

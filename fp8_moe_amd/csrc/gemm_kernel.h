@@ -92,9 +92,9 @@ enum { MODE_SILU = 1, MODE_RELU2 = 2, MODE_DOWN = 3, MODE_DENSE = 4 };
 // an L2 work on the same row tiles (A reuse) and the same experts (B reuse).
 //
 // Wave w owns all rows of the tile and weight fragments [NFW w, NFW w +
-// NFW): every fragment is dequantized by exactly one wave.  A full tile (144
-// rows) runs a branch-free MFMA loop; a partial tile skips whole 16-row
-// blocks.  Missing fragments (a partial N tile) load zeros and are dropped
+// NFW): every fragment is dequantized by exactly one wave.  A full tile
+// (kTileRows rows) runs a branch-free MFMA loop; a partial tile skips whole
+// 16-row blocks.  Missing fragments (a partial N tile) load zeros and are dropped
 // in the epilogue.
 template <int WF, int AF, int MODE, int NFW>
 __global__ __launch_bounds__(kGemmThreads, 2) void moe_gemm_kernel(const GemmParams p) {
