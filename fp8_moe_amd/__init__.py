@@ -34,7 +34,7 @@ REGIONS = {"counts": 1, "offsets": 2, "padded_offsets": 3, "sorted": 4, "pos": 5
            "xq": 9, "xs": 10, "h": 11, "hs": 12, "y": 13}
 
 STATUS_NAMES = {0: "OK", 1: "INVALID_ARGUMENT", 2: "UNSUPPORTED", 3: "CAPACITY", 4: "SCRATCH_TOO_SMALL",
-                5: "MISALIGNED", 6: "LAYOUT_MISMATCH", 7: "HIP"}
+                5: "MISALIGNED", 6: "LAYOUT_MISMATCH", 7: "HIP", 8: "FROZEN"}
 
 
 class B12xError(RuntimeError):
@@ -104,6 +104,8 @@ def _load():
         "b12x_moe_scratch_specs": (st, [vp, P(ScratchSpec), ctypes.c_int32, P(ctypes.c_int32)]),
         "b12x_moe_prime": (st, [vp, vp, ctypes.c_uint64, vp]),
         "b12x_moe_bind": (st, [vp, vp, ctypes.c_uint64, P(Experts), vp, i64, i64, vp, vp, vp, i64, P(Binding)]),
+        "b12x_moe_bind_live": (st, [vp, vp, ctypes.c_uint64, P(Experts), vp, i64, vp, vp, vp, i64, vp, P(Binding)]),
+        "b12x_moe_freeze": (st, [vp]),
         "b12x_moe_run": (st, [P(Binding), vp]),
         "b12x_moe_run_stage": (st, [P(Binding), ctypes.c_int32, vp]),
         "b12x_moe_run_noalloc": (st, [vp, P(Experts), vp, i64, i64, vp, vp, vp, i64, vp]),
@@ -125,7 +127,8 @@ def _load():
 
 _lib = _load()
 EXPORTED = ("b12x_moe_plan_weights", "b12x_moe_prepare_weights", "b12x_moe_is_supported", "b12x_moe_plan",
-            "b12x_moe_plan_destroy", "b12x_moe_scratch_specs", "b12x_moe_prime", "b12x_moe_bind", "b12x_moe_run",
+            "b12x_moe_plan_destroy", "b12x_moe_scratch_specs", "b12x_moe_prime", "b12x_moe_bind",
+            "b12x_moe_bind_live", "b12x_moe_freeze", "b12x_moe_run",
             "b12x_moe_run_stage", "b12x_moe_run_noalloc", "b12x_moe_binding_query", "b12x_moe_scratch_region",
             "b12x_mxfp8_quantize_rows", "b12x_gemm_packed_bytes", "b12x_gemm_pack_weight", "b12x_gemm_mm",
             "b12x_status_string",
@@ -276,6 +279,32 @@ def bind(p, scratch, experts, a, topk_ids, topk_weights, out):
                               a.stride(0), _ptr(topk_ids), _ptr(topk_weights), _ptr(out), out.stride(0),
                               ctypes.byref(b)))
     return b
+
+
+def bind_live(p, scratch, experts, a, topk_ids, topk_weights, out, t_live):
+    """b12x_moe_bind_live: a, out bf16 [max_tokens, H]; topk_ids int32 and
+    topk_weights float32 [max_tokens, k]; t_live: int32 device tensor of one
+    element, the token count each run reads when its kernels run."""
+    for t, dt in ((a, torch.bfloat16), (out, torch.bfloat16), (topk_ids, torch.int32),
+                  (topk_weights, torch.float32), (t_live, torch.int32)):
+        if t.dtype != dt:
+            raise TypeError(f"expected {dt}, got {t.dtype}")
+    cap = p.caps.max_tokens
+    if (a.shape[0] < cap or out.shape[0] < cap or topk_ids.shape[0] < cap or topk_weights.shape != topk_ids.shape
+            or t_live.numel() != 1):
+        raise ValueError("a, out, topk_ids and topk_weights need max_tokens rows; t_live one element")
+    if not (topk_ids.is_contiguous() and topk_weights.is_contiguous()):
+        raise ValueError("topk_ids / topk_weights must be contiguous")
+    b = Binding()
+    _check(_lib.b12x_moe_bind_live(p.handle, _ptr(scratch), scratch.numel(), ctypes.byref(experts.experts), _ptr(a),
+                                   a.stride(0), _ptr(topk_ids), _ptr(topk_weights), _ptr(out), out.stride(0),
+                                   _ptr(t_live), ctypes.byref(b)))
+    return b
+
+
+def freeze(p):
+    """b12x_moe_freeze: bindings of paths not used before now fail."""
+    _check(_lib.b12x_moe_freeze(p.handle))
 
 
 def run(binding, stream=None):

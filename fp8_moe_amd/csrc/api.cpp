@@ -8,6 +8,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <algorithm>
 #include <new>
 
 #include "internal.h"
@@ -97,6 +98,7 @@ const char* b12x_status_string(b12x_status s) {
     case B12X_ERR_MISALIGNED: return "misaligned";
     case B12X_ERR_LAYOUT_MISMATCH: return "layout mismatch";
     case B12X_ERR_HIP: return "HIP error";
+    case B12X_ERR_FROZEN: return "kernel resolution frozen";
     default: return "unknown status";
   }
 }
@@ -317,7 +319,8 @@ b12x_status b12x_moe_scratch_region(b12x_moe_plan_t p, int32_t region, uint64_t*
 // scratch arguments are ignored and the scratch pointers left null.
 static b12x_status make_binding(b12x_moe_plan_t p, void* scratch, uint64_t scratch_bytes, bool no_scratch,
                                 const b12x_moe_experts* ex, const void* a, int64_t T, int64_t a_stride,
-                                const int32_t* ids, const float* tw, void* out, int64_t out_stride, BindingImpl& b) {
+                                const int32_t* ids, const float* tw, void* out, int64_t out_stride, BindingImpl& b,
+                                const int32_t* t_live = nullptr) {
   if (!p || !ex) return fail(B12X_ERR_INVALID_ARGUMENT, "NULL plan or experts");
   if (T < 0) return fail(B12X_ERR_INVALID_ARGUMENT, "T < 0");
   if (T > p->max_tokens)
@@ -348,6 +351,18 @@ static b12x_status make_binding(b12x_moe_plan_t p, void* scratch, uint64_t scrat
   b.magic = kBindingMagic;
   b.path = (T > 0 && T * p->k <= p->decode_max_pairs) ? 2 : 1;
   if (T > 0 && T * p->k <= p->splitk_max_pairs) b.path = 3;
+  if (t_live) b.path = 4;
+  // kernel resolution: a path first bound after b12x_moe_freeze is refused
+  const uint32_t bit = 1u << b.path;
+  if (!(p->resolved.load() & bit)) {
+    if (p->frozen.load())
+      return fail(B12X_ERR_FROZEN, "kernel resolution is frozen and this binding needs the %s path, not resolved before",
+                  b.path == 4 ? "live-token" : b.path == 3 ? "split-K decode" : b.path == 2 ? "decode" : "grouped");
+    p->resolved.fetch_or(bit);
+  }
+  b.t_live = t_live;
+  b.splitk_max = p->splitk_max_pairs;
+  b.decode_max = p->decode_max_pairs;
   b.E = p->E; b.H = p->H; b.I = p->I; b.k = p->k;
   b.gated = p->gated; b.wfmt = p->wfmt; b.afmt = p->afmt; b.act = p->act;
   // grouped path, NVFP4 weights: GEMM1 reads a scaled f16 copy of a (of its MXFP8 or NVFP4 round trips with
@@ -406,6 +421,29 @@ b12x_status b12x_moe_bind(b12x_moe_plan_t p, void* scratch, uint64_t scratch_byt
   return B12X_OK;
 }
 
+b12x_status b12x_moe_bind_live(b12x_moe_plan_t p, void* scratch, uint64_t scratch_bytes, const b12x_moe_experts* ex,
+                               const void* a, int64_t a_stride, const int32_t* ids, const float* tw, void* out,
+                               int64_t out_stride, const int32_t* t_live, b12x_moe_binding* binding) {
+  if (!binding) return fail(B12X_ERR_INVALID_ARGUMENT, "NULL binding");
+  if (!p) return fail(B12X_ERR_INVALID_ARGUMENT, "NULL plan");
+  if (!t_live) return fail(B12X_ERR_INVALID_ARGUMENT, "NULL live token count");
+  if (!aligned(t_live, 4)) return fail(B12X_ERR_MISALIGNED, "the live token count must be 4-byte aligned");
+  if (p->max_tokens < 1) return fail(B12X_ERR_CAPACITY, "a live binding needs max_tokens >= 1");
+  BindingImpl b;
+  const b12x_status st = make_binding(p, scratch, scratch_bytes, false, ex, a, p->max_tokens, a_stride, ids, tw, out,
+                                      out_stride, b, t_live);
+  if (st) return st;
+  memset(binding, 0, sizeof(*binding));
+  memcpy(binding, &b, sizeof(b));
+  return B12X_OK;
+}
+
+b12x_status b12x_moe_freeze(b12x_moe_plan_t p) {
+  if (!p) return fail(B12X_ERR_INVALID_ARGUMENT, "NULL plan");
+  p->frozen.store(1);
+  return B12X_OK;
+}
+
 static b12x_status get_binding(const b12x_moe_binding* binding, BindingImpl* b) {
   if (!binding) return fail(B12X_ERR_INVALID_ARGUMENT, "binding is NULL");
   memcpy(b, binding, sizeof(*b));
@@ -414,6 +452,7 @@ static b12x_status get_binding(const b12x_moe_binding* binding, BindingImpl* b) 
 }
 
 static bool stage_in_path(const BindingImpl& b, int stage) {
+  if (b.path == 4) return false;  // a live binding runs whole calls only
   if (b.path == 3) return stage == B12X_STAGE_DECODE1 || stage == B12X_STAGE_COMBINE;
   if (stage == B12X_STAGE_QUANT_X) return b.afmt != B12X_ACT_BF16 || b.a_f16;
   if (b.path == 2)
@@ -433,14 +472,14 @@ static b12x_status run_stage(const BindingImpl& b, int stage, hipStream_t s) {
     case B12X_STAGE_ROUTE: err = launch_route(b, s); break;
     case B12X_STAGE_QUANT_X:
       if (a4_nv(b.afmt))  // exact NVFP4 round trips: f16 (grouped path, row exponents 0) or bf16
-        err = launch_nv_roundtrip_rows(b.a, b.T, b.H, b.a_stride, b.a13_global, (uint16_t*)b.xq, b.Hp,
+        err = launch_nv_roundtrip_rows(b.a, b.live(), b.H, b.a_stride, b.a13_global, (uint16_t*)b.xq, b.Hp,
                                        (int32_t*)b.xs, b.a_f16, s);
       else if (b.a_f16)
-        err = launch_f16_rows(b.a, b.T, b.H, b.a_stride, (uint16_t*)b.xq, b.Hp, (int32_t*)b.xs,
+        err = launch_f16_rows(b.a, b.live(), b.H, b.a_stride, (uint16_t*)b.xq, b.Hp, (int32_t*)b.xs,
                               a8_bf16(b.wfmt, b.afmt), s);
       else if (a8_bf16(b.wfmt, b.afmt))
-        err = launch_mx_roundtrip_rows(b.a, b.T, b.H, b.a_stride, (uint16_t*)b.xq, b.Hp, s);
-      else err = launch_quant_rows(b.a, b.T, b.H, b.a_stride, b.xq, b.Hp, b.xs, b.Hp / 32, s);
+        err = launch_mx_roundtrip_rows(b.a, b.live(), b.H, b.a_stride, (uint16_t*)b.xq, b.Hp, s);
+      else err = launch_quant_rows(b.a, b.live(), b.H, b.a_stride, b.xq, b.Hp, b.xs, b.Hp / 32, s);
       break;
     case B12X_STAGE_GEMM1: err = launch_gemm1(b, s); break;
     case B12X_STAGE_GEMM2: err = launch_gemm2(b, s); break;
@@ -462,12 +501,46 @@ b12x_status b12x_moe_run_stage(const b12x_moe_binding* binding, int32_t stage, v
   return run_stage(b, stage, (hipStream_t)stream);
 }
 
+// A live binding: each path the plan has, launched for the token counts it
+// serves, as a copy of the binding whose T is the largest such count; the
+// kernels of every path but the one that serves the live count return at once.
+static b12x_status run_path(const BindingImpl& b, hipStream_t s);
+static b12x_status run_live(const BindingImpl& b, hipStream_t s) {
+  const int64_t cap = b.T, k = b.k;
+  const int32_t sk = b.splitk_max, dm = b.decode_max;
+  struct Leg {
+    int path;
+    int32_t lo, hi;
+  };
+  const Leg legs[3] = {{3, 0, sk}, {2, sk, dm}, {1, std::max(sk, dm), INT32_MAX}};
+  for (const Leg& l : legs) {
+    if (l.hi <= l.lo) continue;
+    const int64_t tcap = l.path == 1 ? cap : std::min<int64_t>(cap, l.hi / k);
+    if (tcap < 1 || tcap * k <= l.lo) continue;  // no token count reaches this path
+    BindingImpl r = b;
+    r.path = l.path;
+    r.T = tcap;
+    r.rlo = l.lo;
+    r.rhi = l.hi;
+    r.a_f16 = l.path == 1 && b.wfmt == B12X_WEIGHT_NVFP4;
+    const b12x_status st = run_path(r, s);
+    if (st) return st;
+  }
+  return B12X_OK;
+}
+
 b12x_status b12x_moe_run(const b12x_moe_binding* binding, void* stream) {
   BindingImpl b;
   b12x_status st = get_binding(binding, &b);
   if (st) return st;
   if (b.T == 0) return B12X_OK;
   hipStream_t s = (hipStream_t)stream;
+  if (b.path == 4) return run_live(b, s);
+  return run_path(b, s);
+}
+
+static b12x_status run_path(const BindingImpl& b, hipStream_t s) {
+  b12x_status st = B12X_OK;
   static const int grouped[5] = {B12X_STAGE_ROUTE, B12X_STAGE_QUANT_X, B12X_STAGE_GEMM1, B12X_STAGE_GEMM2,
                                  B12X_STAGE_COMBINE};
   static const int decode[4] = {B12X_STAGE_QUANT_X, B12X_STAGE_DECODE1, B12X_STAGE_DECODE2, B12X_STAGE_COMBINE};
@@ -519,7 +592,9 @@ b12x_status b12x_moe_binding_query(const b12x_moe_binding* binding, int32_t what
     case B12X_QUERY_ROW_PAD: *value = kRowPad; break;
     case B12X_QUERY_T: *value = b.T; break;
     case B12X_QUERY_NUM_STAGES:
-      *value = b.path == 3 ? 2 : (b.path == 2 ? (decode_fused(b) ? 2 : 3) : 4) + (stage_in_path(b, B12X_STAGE_QUANT_X) ? 1 : 0);
+      *value = b.path == 4 ? 0  // a live binding has no stages of its own
+               : b.path == 3 ? 2
+                             : (b.path == 2 ? (decode_fused(b) ? 2 : 3) : 4) + (stage_in_path(b, B12X_STAGE_QUANT_X) ? 1 : 0);
       break;
     default: return fail(B12X_ERR_INVALID_ARGUMENT, "unknown query %d", what);
   }
@@ -535,7 +610,7 @@ b12x_status b12x_mxfp8_quantize_rows(const void* x, int64_t rows, int64_t cols, 
   if (stride < cols) return fail(B12X_ERR_INVALID_ARGUMENT, "stride smaller than cols");
   if (stride % 8 || !aligned(x, 16) || !aligned(codes, 16))
     return fail(B12X_ERR_MISALIGNED, "x, codes and the row stride must be 16-byte aligned");
-  int err = launch_quant_rows((const uint16_t*)x, rows, cols, stride, codes, cols, scales, cols / 32,
+  int err = launch_quant_rows((const uint16_t*)x, LiveT{nullptr, rows, 1, 0, 0}, cols, stride, codes, cols, scales, cols / 32,
                               (hipStream_t)stream);
   if (err) return hip_fail(err, "quantize rows");
   return B12X_OK;

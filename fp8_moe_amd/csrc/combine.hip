@@ -30,14 +30,15 @@ template <typename YT>
 __global__ __launch_bounds__(256) void combine_kernel(const YT* __restrict__ y, int64_t y_stride,
                                                        const int32_t* __restrict__ pos,
                                                        const int32_t* __restrict__ ids, int E,
-                                                       const float* __restrict__ tw, int64_t T, int k, int H,
+                                                       const float* __restrict__ tw, LiveT lv, int k, int H,
                                                        int64_t max_rows, uint16_t* __restrict__ out,
                                                        int64_t out_stride, const uint64_t* counter,
                                                        const uint64_t* status) {
   constexpr int kChunk = 8;
   const int64_t groups = H / 8;
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= T * groups) return;
+  const int64_t T = lv.tokens();
+  if (!lv.on() || idx >= T * groups) return;
   // The fused decode launch before this combine is launch number c / kLaunchStep - 1
   // of its scratch.  The output is NaN, not stale, if one of its waits gave up
   // (status holds that launch's tag; nothing is cleared: a later launch has
@@ -99,7 +100,7 @@ static int launch_combine_rows(const BindingImpl& b, const YT* y, const int32_t*
   const int64_t total = b.T * (b.H / 8);
   if (total == 0) return 0;
   hipLaunchKernelGGL(combine_kernel<YT>, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, y, (int64_t)b.H,
-                     pos, b.ids, b.E, b.tw, b.T, b.k, b.H, b.max_rows, b.out, b.out_stride, counter, status);
+                     pos, b.ids, b.E, b.tw, b.live(), b.k, b.H, b.max_rows, b.out, b.out_stride, counter, status);
   return (int)hipGetLastError();
 }
 

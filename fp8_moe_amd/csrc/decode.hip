@@ -81,6 +81,7 @@ struct DecodeParams {
   int64_t h_bytes;  // extent of h16 (device-coherent stores and loads)
   int deal;         // 0: one contiguous share per workgroup; else chunks of this many items dealt round-robin
   int prev_groups;  // down phase of the fused kernel: the gate/up phase's groups per expert (same deal)
+  LiveT lv;         // token count (T; or the live one)
 };
 
 enum { DMODE_SILU = 1, DMODE_RELU2 = 2, DMODE_DOWN = 3 };
@@ -103,7 +104,7 @@ constexpr int kWaitPolls = 1 << 18;
 // raised its flag, and h is loaded device-coherent.
 template <int WF, int AF, int MODE, int FR, int KW, int FUSE>
 __device__ __forceinline__ void decode_items(const DecodeParams& p, DecodeLds& L, f32x4* red, int n_touched,
-                                             uint64_t tag) {
+                                             uint64_t tag, int P) {
   constexpr bool A8 = AF == B12X_ACT_MXFP8;
   constexpr bool RT = AF == kActRt;  // bf16 MXFP8 round trips: h stored as its own round trip
   constexpr bool NVRT = AF == kActNvRt;  // bf16 NVFP4 round trips: h stored as its own NVFP4 round trip
@@ -188,7 +189,7 @@ __device__ __forceinline__ void decode_items(const DecodeParams& p, DecodeLds& L
     }
   }
   int e;
-  const int m = decode_expert(p.P, p.E, slot, s_ids, s_bits, s_wpre, s_rows, s_info, e);
+  const int m = decode_expert(P, p.E, slot, s_ids, s_bits, s_wpre, s_rows, s_info, e);
   const uint8_t* bcodes = p.bcodes + (int64_t)e * p.b_codes_expert;
   const uint8_t* bscales = p.bscales + (int64_t)e * p.b_scales_expert;
   float gsc = p.bglobal ? p.bglobal[e] : 1.0f;
@@ -421,8 +422,10 @@ template <int WF, int AF, int MODE, int FR, int KW>
 __global__ __launch_bounds__(kDecThreads) void decode_kernel(const DecodeParams p) {
   __shared__ DecodeLds L;
   __shared__ f32x4 s_red[2 * 3 * FR * 64];
-  const int n_touched = decode_prep(p.ids, p.P, p.E, L.ids, L.bits, L.wpre);
-  decode_items<WF, AF, MODE, FR, KW, 0>(p, L, s_red, n_touched, 0);
+  if (!p.lv.on()) return;
+  const int P = (int)(p.lv.tokens() * p.k);
+  const int n_touched = decode_prep(p.ids, P, p.E, L.ids, L.bits, L.wpre);
+  decode_items<WF, AF, MODE, FR, KW, 0>(p, L, s_red, n_touched, 0, P);
 }
 
 // Gate/up and down in one launch (16-bit activations): every workgroup takes
@@ -448,9 +451,12 @@ __global__ __launch_bounds__(kDecThreads) void decode_fused_kernel(const DecodeP
   __shared__ DecodeLds L;
   __shared__ f32x4 s_red[2 * 3 * FRM * 64];
   const uint64_t tag = flag_tag(p1.counter);
-  const int n_touched = decode_prep(p1.ids, p1.P, p1.E, L.ids, L.bits, L.wpre);
-  decode_items<WF, B12X_ACT_BF16, MODE1, FR1, KW1, 1>(p1, L, s_red, n_touched, tag);
-  decode_items<WF, B12X_ACT_BF16, DMODE_DOWN, FR2, KW2, 2>(p2, L, s_red, n_touched, tag);
+  if (p1.lv.on()) {  // (a live token count that another path serves: nothing but the counter share)
+    const int P = (int)(p1.lv.tokens() * p1.k);
+    const int n_touched = decode_prep(p1.ids, P, p1.E, L.ids, L.bits, L.wpre);
+    decode_items<WF, B12X_ACT_BF16, MODE1, FR1, KW1, 1>(p1, L, s_red, n_touched, tag, P);
+    decode_items<WF, B12X_ACT_BF16, DMODE_DOWN, FR2, KW2, 2>(p2, L, s_red, n_touched, tag, P);
+  }
   __syncthreads();
   if (threadIdx.x == 0) {
     const uint64_t share = kLaunchStep / gridDim.x + (blockIdx.x < kLaunchStep % gridDim.x ? 1 : 0);
@@ -494,6 +500,7 @@ static DecodeParams common_params(const BindingImpl& b) {
   p.ids = b.ids;
   p.tw = b.tw;
   p.T = (int)b.T;
+  p.lv = b.live();
   p.k = b.k;
   p.E = b.E;
   p.P = (int)(b.T * b.k);

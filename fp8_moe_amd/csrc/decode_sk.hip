@@ -71,6 +71,7 @@ struct SkParams {
   int xsc;            // offset of the staged E8M0 scales in a wave's region (MXFP8 codes)
   int xwb;            // bytes of one wave's LDS region
   int x_off;          // offset of the wave regions in the dynamic LDS
+  LiveT lv;           // token count (T; or the live one)
 };
 
 // Static LDS of one workgroup: routing and the h tile.  The dynamic part holds
@@ -138,11 +139,11 @@ struct SkRoute {
   int n_touched;
 };
 
-__device__ __forceinline__ SkRoute sk_route(const SkParams& p, uint32_t* wbits) {
+__device__ __forceinline__ SkRoute sk_route(const SkParams& p, int P, uint32_t* wbits) {
   const int lane = threadIdx.x & 63;
   SkRoute r;
   int id = -1;
-  if (lane < p.P) {
+  if (lane < P) {
     const int e = p.ids[lane];
     id = (e >= 0 && e < p.E) ? e : -1;
   }
@@ -196,7 +197,8 @@ __global__ __launch_bounds__(kDecThreads) void decode_sk_kernel(const SkParams p
   const int lane = tid & 63;
   const int g = lane >> 4, r16 = lane & 15;
   uint8_t* const xw = dyn + p.x_off + wave * p.xwb;  // this wave's region
-  const SkRoute route = sk_route(p, L.bits[wave]);
+  if (!p.lv.on()) return;
+  const SkRoute route = sk_route(p, (int)(p.lv.tokens() * p.k), L.bits[wave]);
   const int items = route.n_touched * p.n_slices;
   const int kb = wave * p.kper, ke = min(p.KF1, kb + p.kper);
   const int nu = p.kper * 16;         // activation units per staged row
@@ -517,10 +519,11 @@ __global__ __launch_bounds__(kDecThreads) void decode_sk_kernel(const SkParams p
 constexpr int kSkCombineLoads = 16;
 __global__ __launch_bounds__(64) void decode_sk_combine_kernel(const float* __restrict__ part, int64_t part_bytes,
                                                                 const int32_t* __restrict__ ids, int E,
-                                                                const float* __restrict__ tw, int64_t T, int k,
+                                                                const float* __restrict__ tw, LiveT lv, int k,
                                                                 int S, int H, int n_slices, int row_stride,
                                                                 int n_groups, uint16_t* __restrict__ out,
                                                                 int64_t out_stride) {
+  if (!lv.on() || (int64_t)blockIdx.y >= lv.tokens()) return;
   const int lane = threadIdx.x;
   const int KS = k * S;                      // lanes per position group (<= 64)
   const int PG = 64 / KS;                    // position groups per wave
@@ -589,6 +592,7 @@ static SkParams sk_params(const BindingImpl& b) {
   p.ids = b.ids;
   p.tw = b.tw;
   p.T = (int)b.T;
+  p.lv = b.live();
   p.k = b.k;
   p.E = b.E;
   p.P = (int)(b.T * b.k);
@@ -730,7 +734,7 @@ int launch_decode_sk_combine(const BindingImpl& b, hipStream_t s) {
   const dim3 grid((unsigned)((n_groups + per_wave - 1) / per_wave), (unsigned)b.T);
   const int64_t part_bytes = b.T * b.k * (int64_t)n_slices * row_stride * 4;
   hipLaunchKernelGGL(decode_sk_combine_kernel, grid, dim3(64), 0, s, (const float*)b.y, part_bytes, b.ids, b.E, b.tw,
-                     b.T, b.k, S, b.H, n_slices, row_stride, n_groups, b.out, b.out_stride);
+                     b.live(), b.k, S, b.H, n_slices, row_stride, n_groups, b.out, b.out_stride);
   return (int)hipGetLastError();
 }
 

@@ -57,6 +57,7 @@ static int dispatch(const BindingImpl& b, const GemmParams& p, int64_t max_work,
 
 int launch_gemm1(const BindingImpl& b, hipStream_t s) {
   GemmParams p = {};
+  p.lv = b.live();
   const bool a8 = a8_native(b.wfmt, b.afmt);
   p.tiles = b.tiles;
   p.ntiles = b.ntiles;
@@ -106,6 +107,7 @@ int launch_gemm1(const BindingImpl& b, hipStream_t s) {
 
 int launch_gemm2(const BindingImpl& b, hipStream_t s) {
   GemmParams p = {};
+  p.lv = b.live();
   const bool a8 = a8_native(b.wfmt, b.afmt);  // else h is bf16
   p.tiles = b.tiles;
   p.ntiles = b.ntiles;

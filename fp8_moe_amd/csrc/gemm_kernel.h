@@ -83,6 +83,7 @@ struct GemmParams {
   uint16_t* out16;
   int64_t out_stride;
   int64_t dense_m;
+  LiveT lv;  // live token count: the whole grid returns unless the grouped path serves it
 };
 
 enum { MODE_SILU = 1, MODE_RELU2 = 2, MODE_DOWN = 3, MODE_DENSE = 4 };
@@ -129,6 +130,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void moe_gemm_kernel(const GemmPar
   const int g = lane >> 4, r16 = lane & 15;
   const int c = tid % CHUNKS;
 
+  if (!p.lv.on()) return;
   const int n_row_tiles =
       MODE == MODE_DENSE ? (int)((p.dense_m + kTileRows - 1) / kTileRows) : min(max(p.ntiles[0], 0), p.max_tiles);
   const int n_items = n_row_tiles * p.n_ntiles;

@@ -2,6 +2,7 @@
 // Not part of the C ABI.
 #pragma once
 
+#include <atomic>
 #include <stddef.h>
 #include <stdint.h>
 
@@ -105,6 +106,11 @@ struct PlanImpl {
   uint64_t off[16] = {0};   // scratch region offsets, indexed by Region
   uint64_t len[16] = {0};   // scratch region sizes
   uint64_t scratch_bytes = 0;
+  // kernel resolution (b12x_moe_freeze): bit `path` set once a binding of
+  // that path (1 grouped, 2 decode, 3 split-K decode, 4 live token count) was
+  // made; once frozen, a binding of a path not set is refused
+  std::atomic<uint32_t> resolved{0};
+  std::atomic<int> frozen{0};
 };
 
 enum Region {
@@ -112,10 +118,33 @@ enum Region {
   R_CHUNK = 8, R_XQ = 9, R_XS = 10, R_H = 11, R_HS = 12, R_Y = 13, R_DSYNC = 14, R_COUNT_ = 15
 };
 
+// Token count of a launch.  An ordinary binding passes t = nullptr and its
+// own T as cap.  A binding bound at capacity for a live token count
+// (b12x_moe_bind_live) passes the device int32 t, read by the kernel at run
+// time, the largest T this launch's path can serve as cap (its grids and
+// buffers are sized for it), and the pair counts the path serves: the kernel
+// works only while t is in [0, cap] and lo < t * k <= hi (each path of such a
+// binding is launched, and all but the one serving t return at once).
+struct LiveT {
+  const int32_t* t;
+  int64_t cap;
+  int32_t k, lo, hi;
+  __host__ __device__ int64_t tokens() const {
+    if (!t) return cap;
+    const int64_t v = *t;
+    return v < 0 ? 0 : (v > cap ? cap : v);
+  }
+  __host__ __device__ bool on() const {
+    if (!t) return true;
+    const int64_t v = *t;
+    return v >= 0 && v <= cap && v * k > lo && v * k <= hi;
+  }
+};
+
 // Everything a run needs, resolved at bind time (trivially copyable).
 struct BindingImpl {
   uint32_t magic;
-  int32_t path;  // 1 grouped, 2 decode (two-phase), 3 decode (split-K)
+  int32_t path;  // 1 grouped, 2 decode (two-phase), 3 decode (split-K), 4 live token count (all three)
   int32_t E, H, I, k, gated, wfmt, afmt, act;
   int32_t a_f16;  // grouped path, NVFP4 weights: GEMM1 reads a scaled f16 copy of a (xq; of its MXFP8 round trips
                   // with MXFP8 activations) and row exponents (xs)
@@ -150,6 +179,13 @@ struct BindingImpl {
   float* y;        // decode path: fp32 rows, one per pair id
   uint16_t* y16;   // grouped path: bf16 rows in routing order (same memory as y)
   uint8_t* dsync;  // decode path: launch counter, status and the fused kernel's completion flags
+  // live token count (b12x_moe_bind_live; null otherwise).  Such a binding
+  // holds its capacity in T; run() launches each path with a copy whose T is
+  // the largest that path serves and (rlo, rhi] its pair counts.
+  const int32_t* t_live;
+  int32_t rlo, rhi;
+  int32_t splitk_max, decode_max;  // the plan's path limits (pairs)
+  LiveT live() const { return LiveT{t_live, T, k, rlo, rhi}; }
 };
 constexpr uint32_t kBindingMagic = 0xb12b1d01u;
 static_assert(sizeof(BindingImpl) <= sizeof(b12x_moe_binding), "binding does not fit the ABI struct");
@@ -168,13 +204,13 @@ struct PackArgs {
 int launch_pack(const PackArgs& a, hipStream_t s);
 int launch_copy_f32(const float* src, float* dst, int n, hipStream_t s);
 int launch_route(const BindingImpl& b, hipStream_t s);
-int launch_quant_rows(const uint16_t* x, int64_t rows, int64_t cols, int64_t stride, uint8_t* codes,
+int launch_quant_rows(const uint16_t* x, LiveT lv, int64_t cols, int64_t stride, uint8_t* codes,
                       int64_t code_stride, uint8_t* scales, int64_t scale_stride, hipStream_t s);
-int launch_mx_roundtrip_rows(const uint16_t* x, int64_t rows, int64_t cols, int64_t stride, uint16_t* out,
+int launch_mx_roundtrip_rows(const uint16_t* x, LiveT lv, int64_t cols, int64_t stride, uint16_t* out,
                              int64_t out_stride, hipStream_t s);
-int launch_nv_roundtrip_rows(const uint16_t* x, int64_t rows, int64_t cols, int64_t stride, const float* g,
+int launch_nv_roundtrip_rows(const uint16_t* x, LiveT lv, int64_t cols, int64_t stride, const float* g,
                              uint16_t* out, int64_t out_stride, int32_t* exps, bool f16, hipStream_t s);
-int launch_f16_rows(const uint16_t* x, int64_t rows, int64_t cols, int64_t stride, uint16_t* out,
+int launch_f16_rows(const uint16_t* x, LiveT lv, int64_t cols, int64_t stride, uint16_t* out,
                     int64_t out_stride, int32_t* exps, bool rt, hipStream_t s);
 int launch_gemm1(const BindingImpl& b, hipStream_t s);
 int launch_gemm2(const BindingImpl& b, hipStream_t s);

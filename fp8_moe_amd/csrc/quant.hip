@@ -9,13 +9,15 @@ namespace b12x {
 // Eight lanes per 32-element block, four values each (an aligned group of 8
 // lanes of a wave, so a group is wholly in or out of range): the block's
 // largest magnitude by lane exchange, then each lane encodes its four values.
-__global__ __launch_bounds__(256) void quant_rows_kernel(const uint16_t* __restrict__ x, int64_t rows,
+// The row count is lv's (a binding's T, or the live token count).
+__global__ __launch_bounds__(256) void quant_rows_kernel(const uint16_t* __restrict__ x, LiveT lv,
                                                           int64_t blocks_per_row, int64_t stride,
                                                           uint8_t* __restrict__ codes, int64_t code_stride,
                                                           uint8_t* __restrict__ scales, int64_t scale_stride) {
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t blk_all = idx >> 3;
-  if (blk_all >= rows * blocks_per_row) return;
+  const int64_t rows = lv.tokens();
+  if (!lv.on() || blk_all >= rows * blocks_per_row) return;
   const int part = (int)(idx & 7);  // elements [4 part, 4 part + 4) of the block
   const int64_t r = blk_all / blocks_per_row, blk = blk_all % blocks_per_row;
   const uint2 v = *(const uint2*)(x + r * stride + blk * 32 + 4 * part);
@@ -33,12 +35,13 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const uint16_t* __restr
 
 // The same blocks, writing bf16 of each value's MXFP8 round trip instead of
 // codes and scales (NVFP4 weights x MXFP8 activations).
-__global__ __launch_bounds__(256) void mx_roundtrip_rows_kernel(const uint16_t* __restrict__ x, int64_t rows,
+__global__ __launch_bounds__(256) void mx_roundtrip_rows_kernel(const uint16_t* __restrict__ x, LiveT lv,
                                                                  int64_t blocks_per_row, int64_t stride,
                                                                  uint16_t* __restrict__ out, int64_t out_stride) {
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t blk_all = idx >> 3;
-  if (blk_all >= rows * blocks_per_row) return;
+  const int64_t rows = lv.tokens();
+  if (!lv.on() || blk_all >= rows * blocks_per_row) return;
   const int part = (int)(idx & 7);
   const int64_t r = blk_all / blocks_per_row, blk = blk_all % blocks_per_row;
   const uint2 v = *(const uint2*)(x + r * stride + blk * 32 + 4 * part);
@@ -52,12 +55,12 @@ __global__ __launch_bounds__(256) void mx_roundtrip_rows_kernel(const uint16_t* 
   *(uint2*)(out + r * out_stride + blk * 32 + 4 * part) = make_uint2(lo, hi);
 }
 
-int launch_mx_roundtrip_rows(const uint16_t* x, int64_t rows, int64_t cols, int64_t stride, uint16_t* out,
+int launch_mx_roundtrip_rows(const uint16_t* x, LiveT lv, int64_t cols, int64_t stride, uint16_t* out,
                              int64_t out_stride, hipStream_t s) {
   const int64_t bpr = cols / 32;
-  const int64_t total = rows * bpr;
+  const int64_t total = lv.cap * bpr;
   if (total == 0) return 0;
-  hipLaunchKernelGGL(mx_roundtrip_rows_kernel, dim3((unsigned)((8 * total + 255) / 256)), dim3(256), 0, s, x, rows,
+  hipLaunchKernelGGL(mx_roundtrip_rows_kernel, dim3((unsigned)((8 * total + 255) / 256)), dim3(256), 0, s, x, lv,
                      bpr, stride, out, out_stride);
   return (int)hipGetLastError();
 }
@@ -70,14 +73,15 @@ int launch_mx_roundtrip_rows(const uint16_t* x, int64_t rows, int64_t cols, int6
 // Two threads per block of 16 (8 values each).  F16: f16 values plus a row
 // exponent of 0 for the f16 operand path of the grouped GEMM; else bf16.
 template <bool F16>
-__global__ __launch_bounds__(256) void nv_roundtrip_rows_kernel(const uint16_t* __restrict__ x, int64_t rows,
+__global__ __launch_bounds__(256) void nv_roundtrip_rows_kernel(const uint16_t* __restrict__ x, LiveT lv,
                                                                 int64_t blocks_per_row, int64_t stride,
                                                                 const float* __restrict__ g,
                                                                 uint16_t* __restrict__ out, int64_t out_stride,
                                                                 int32_t* __restrict__ exps) {
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t blk_all = idx >> 1;
-  if (blk_all >= rows * blocks_per_row) return;
+  const int64_t rows = lv.tokens();
+  if (!lv.on() || blk_all >= rows * blocks_per_row) return;
   const int part = (int)(idx & 1);
   const int64_t r = blk_all / blocks_per_row, blk = blk_all % blocks_per_row;
   const uint4 v = *(const uint4*)(x + r * stride + blk * 16 + 8 * part);
@@ -104,27 +108,27 @@ __global__ __launch_bounds__(256) void nv_roundtrip_rows_kernel(const uint16_t* 
   if (F16 && blk == 0 && part == 0) exps[r] = 0;
 }
 
-int launch_nv_roundtrip_rows(const uint16_t* x, int64_t rows, int64_t cols, int64_t stride, const float* g,
+int launch_nv_roundtrip_rows(const uint16_t* x, LiveT lv, int64_t cols, int64_t stride, const float* g,
                              uint16_t* out, int64_t out_stride, int32_t* exps, bool f16, hipStream_t s) {
   const int64_t bpr = cols / 16;
-  const int64_t total = rows * bpr;
+  const int64_t total = lv.cap * bpr;
   if (total == 0) return 0;
   const dim3 grid((unsigned)((2 * total + 255) / 256));
   if (f16)
-    hipLaunchKernelGGL(nv_roundtrip_rows_kernel<true>, grid, dim3(256), 0, s, x, rows, bpr, stride, g, out,
+    hipLaunchKernelGGL(nv_roundtrip_rows_kernel<true>, grid, dim3(256), 0, s, x, lv, bpr, stride, g, out,
                        out_stride, exps);
   else
-    hipLaunchKernelGGL(nv_roundtrip_rows_kernel<false>, grid, dim3(256), 0, s, x, rows, bpr, stride, g, out,
+    hipLaunchKernelGGL(nv_roundtrip_rows_kernel<false>, grid, dim3(256), 0, s, x, lv, bpr, stride, g, out,
                        out_stride, exps);
   return (int)hipGetLastError();
 }
 
-int launch_quant_rows(const uint16_t* x, int64_t rows, int64_t cols, int64_t stride, uint8_t* codes,
+int launch_quant_rows(const uint16_t* x, LiveT lv, int64_t cols, int64_t stride, uint8_t* codes,
                       int64_t code_stride, uint8_t* scales, int64_t scale_stride, hipStream_t s) {
   const int64_t bpr = cols / 32;
-  const int64_t total = rows * bpr;
+  const int64_t total = lv.cap * bpr;
   if (total == 0) return 0;
-  hipLaunchKernelGGL(quant_rows_kernel, dim3((unsigned)((8 * total + 255) / 256)), dim3(256), 0, s, x, rows, bpr,
+  hipLaunchKernelGGL(quant_rows_kernel, dim3((unsigned)((8 * total + 255) / 256)), dim3(256), 0, s, x, lv, bpr,
                      stride, codes, code_stride, scales, scale_stride);
   return (int)hipGetLastError();
 }
@@ -144,9 +148,11 @@ int launch_quant_rows(const uint16_t* x, int64_t rows, int64_t cols, int64_t str
 template <bool RT>
 __global__ __launch_bounds__(256) void f16_rows_kernel(const uint16_t* __restrict__ x, int64_t cols, int64_t stride,
                                                         uint16_t* __restrict__ out, int64_t out_stride,
-                                                        int32_t* __restrict__ exps) {
+                                                        int32_t* __restrict__ exps, LiveT lv) {
   __shared__ uint32_t s_max[4];
   const int64_t r = blockIdx.x;
+  const int64_t rows = lv.tokens();
+  if (!lv.on() || r >= rows) return;
   const uint16_t* src = x + r * stride;
   uint32_t m = 0;  // bf16 magnitude bits compare like the values
   for (int64_t c = threadIdx.x * 8; c < cols; c += 256 * 8) {
@@ -193,15 +199,15 @@ __global__ __launch_bounds__(256) void f16_rows_kernel(const uint16_t* __restric
   if (threadIdx.x == 0) exps[r] = e;
 }
 
-int launch_f16_rows(const uint16_t* x, int64_t rows, int64_t cols, int64_t stride, uint16_t* out,
+int launch_f16_rows(const uint16_t* x, LiveT lv, int64_t cols, int64_t stride, uint16_t* out,
                     int64_t out_stride, int32_t* exps, bool rt, hipStream_t s) {
-  if (rows == 0) return 0;
+  if (lv.cap == 0) return 0;
   if (rt)
-    hipLaunchKernelGGL(f16_rows_kernel<true>, dim3((unsigned)rows), dim3(256), 0, s, x, cols, stride, out, out_stride,
-                       exps);
+    hipLaunchKernelGGL(f16_rows_kernel<true>, dim3((unsigned)lv.cap), dim3(256), 0, s, x, cols, stride, out,
+                       out_stride, exps, lv);
   else
-    hipLaunchKernelGGL(f16_rows_kernel<false>, dim3((unsigned)rows), dim3(256), 0, s, x, cols, stride, out, out_stride,
-                       exps);
+    hipLaunchKernelGGL(f16_rows_kernel<false>, dim3((unsigned)lv.cap), dim3(256), 0, s, x, cols, stride, out,
+                       out_stride, exps, lv);
   return (int)hipGetLastError();
 }
 

@@ -18,8 +18,11 @@ constexpr int kPairsPerThread = kRouteChunk / kRouteThreads;
 __device__ __forceinline__ int valid_expert(int e, int E) { return e >= 0 && e < E; }
 
 // chunk[c * E + e] = number of valid pairs of chunk c routed to e.
-__global__ __launch_bounds__(kRouteThreads) void route_count_kernel(const int32_t* __restrict__ ids, int64_t P,
+__global__ __launch_bounds__(kRouteThreads) void route_count_kernel(const int32_t* __restrict__ ids, LiveT lv,
                                                                      int E, int32_t* __restrict__ chunk) {
+  const int64_t T = lv.tokens();
+  if (!lv.on()) return;
+  const int64_t P = T * lv.k;
   __shared__ int hist[kMaxExperts];
   for (int e = threadIdx.x; e < E; e += kRouteThreads) hist[e] = 0;
   __syncthreads();
@@ -71,7 +74,9 @@ __device__ void block_exclusive_scan3(const int (&v)[3], int (*wsum)[3], int (&e
 __global__ __launch_bounds__(1024) void route_scan_kernel(int E, int n_chunks, int32_t* __restrict__ chunk,
                                                           int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
                                                           int32_t* __restrict__ poff, int32_t* __restrict__ sorted,
-                                                          int32_t* __restrict__ tiles, int32_t* __restrict__ ntiles) {
+                                                          int32_t* __restrict__ tiles, int32_t* __restrict__ ntiles,
+                                                          LiveT lv) {
+  if (!lv.on()) return;
   __shared__ int wsum[16][3];
   const int e = threadIdx.x;
   int cnt = 0;
@@ -122,11 +127,14 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(int E, int n_chunks, i
 // rounds of 64; a lane's rank among equal experts of its round comes from
 // ballots (the lanes below it with the same expert, found with one ballot per
 // bit of the expert id), and LDS counters carry the count across rounds.  Waves are then ordered by a prefix over their counts.
-__global__ __launch_bounds__(kRouteThreads) void route_scatter_kernel(const int32_t* __restrict__ ids, int64_t P,
+__global__ __launch_bounds__(kRouteThreads) void route_scatter_kernel(const int32_t* __restrict__ ids, LiveT lv,
                                                                        int E, const int32_t* __restrict__ chunk,
                                                                        const int32_t* __restrict__ poff,
                                                                        int32_t* __restrict__ sorted,
                                                                        int32_t* __restrict__ pos) {
+  const int64_t T = lv.tokens();
+  if (!lv.on()) return;
+  const int64_t P = T * lv.k;
   __shared__ int cnt[4][kMaxExperts];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   for (int i = threadIdx.x; i < 4 * kMaxExperts; i += kRouteThreads) (&cnt[0][0])[i] = 0;
@@ -177,17 +185,20 @@ __global__ __launch_bounds__(kRouteThreads) void route_scatter_kernel(const int3
   }
 }
 
+// Grids cover the binding's capacity (its T, or the live binding's largest T);
+// with a live token count the chunks past the live pairs count nothing.
 int launch_route(const BindingImpl& b, hipStream_t s) {
   const int64_t P = b.T * b.k;
   const int n_chunks = (int)((P + kRouteChunk - 1) / kRouteChunk);
-  hipLaunchKernelGGL(route_count_kernel, dim3(n_chunks), dim3(kRouteThreads), 0, s, b.ids, P, b.E, b.chunk);
+  const LiveT lv = b.live();
+  hipLaunchKernelGGL(route_count_kernel, dim3(n_chunks), dim3(kRouteThreads), 0, s, b.ids, lv, b.E, b.chunk);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return (int)e;
   hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(1024), 0, s, b.E, n_chunks, b.chunk, b.counts, b.offsets,
-                     b.poff, b.sorted, b.tiles, b.ntiles);
+                     b.poff, b.sorted, b.tiles, b.ntiles, lv);
   e = hipGetLastError();
   if (e != hipSuccess) return (int)e;
-  hipLaunchKernelGGL(route_scatter_kernel, dim3(n_chunks), dim3(kRouteThreads), 0, s, b.ids, P, b.E, b.chunk,
+  hipLaunchKernelGGL(route_scatter_kernel, dim3(n_chunks), dim3(kRouteThreads), 0, s, b.ids, lv, b.E, b.chunk,
                      b.poff, b.sorted, b.pos);
   return (int)hipGetLastError();
 }

@@ -132,6 +132,53 @@ def test_prime_validation_on_host():
     assert prime(grouped_only.handle, ctypes.c_void_p(0x4000000), grouped_only.scratch_specs()[0].bytes, None) == 0
 
 
+def test_freeze_refuses_unresolved_paths():
+    """b12x_moe_freeze: a binding of a path that no binding of the plan used
+    before is refused (status 8); paths used before keep binding."""
+    import fp8_moe_amd as fm
+    wp = fm.plan_weights(8, 256, 128, True, "mxfp4")
+    p = fm.plan(wp, 2, 512)   # T*k: <= 32 split-K, <= 256 decode, beyond grouped
+    ex = fm.Experts(wp, ctypes.c_void_p(0x7000000), wp.prepared_bytes)
+    assert _bind_status(p, ex, 1)[0] == 0
+    assert fm.binding_query(_bind_status(p, ex, 1)[1], "path") == 3
+    assert _bind_status(p, ex, 300)[0] == 0                                  # grouped, resolved
+    assert fm.lib().b12x_moe_freeze(p.handle) == 0
+    assert _bind_status(p, ex, 16)[0] == 0                                   # split-K again
+    assert _bind_status(p, ex, 400)[0] == 0                                  # grouped again
+    assert _bind_status(p, ex, 64)[0] == 8                                   # decode: never resolved
+    b = fm.Binding()
+    live = fm.lib().b12x_moe_bind_live(p.handle, ctypes.c_void_p(0x4000000), p.scratch_specs()[0].bytes,
+                                       ctypes.byref(ex), ctypes.c_void_p(0x10000), 256, ctypes.c_void_p(0x200000),
+                                       ctypes.c_void_p(0x300000), ctypes.c_void_p(0x9000000), 256,
+                                       ctypes.c_void_p(0x500000), ctypes.byref(b))
+    assert live == 8                                                         # live: never resolved
+    assert fm.lib().b12x_moe_freeze(None) == 1
+
+
+def test_bind_live_validation_on_host():
+    import fp8_moe_amd as fm
+    wp = fm.plan_weights(8, 256, 128, True, "mxfp4")
+    p = fm.plan(wp, 2, 64)
+    ex = fm.Experts(wp, ctypes.c_void_p(0x7000000), wp.prepared_bytes)
+    nbytes = p.scratch_specs()[0].bytes
+
+    def live(t_ptr, out_ptr=0x9000000):
+        b = fm.Binding()
+        st = fm.lib().b12x_moe_bind_live(p.handle, ctypes.c_void_p(0x4000000), nbytes, ctypes.byref(ex),
+                                         ctypes.c_void_p(0x10000), 256, ctypes.c_void_p(0x200000),
+                                         ctypes.c_void_p(0x300000), ctypes.c_void_p(out_ptr), 256,
+                                         ctypes.c_void_p(t_ptr) if t_ptr else None, ctypes.byref(b))
+        return st, b
+    st, b = live(0x500000)
+    assert st == 0
+    assert fm.binding_query(b, "path") == 4 and fm.binding_query(b, "T") == 64
+    assert fm.binding_query(b, "num_stages") == 0
+    assert fm.lib().b12x_moe_run_stage(ctypes.byref(b), 6, None) == 2      # whole calls only
+    assert live(0)[0] == 1                                                   # no live count
+    assert live(0x500002)[0] == 5                                            # misaligned count
+    assert live(0x500000, out_ptr=0x10000 + 512)[0] == 1                     # out aliases a (at capacity)
+
+
 def test_bind_validation_on_host():
     import fp8_moe_amd as fm
     wp = fm.plan_weights(8, 256, 128, True, "mxfp4")
