@@ -18,7 +18,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["gemm_inst_silu_f16.hip", "gemm_inst_relu2_f16.hip", "gemm_inst_silu.hip", "gemm_inst_relu2.hip",
            "gemm_inst_down.hip", "decode.hip", "decode_sk.hip", "api.cpp", "pack.hip", "route.hip", "quant.hip", "gemm.hip",
-           "combine.hip"]
+           "combine.hip", "debug.hip"]
 PROBE_SOURCES = ["probes.hip"]
 
 # -packed-fp32-ops: keep hipcc from emitting packed fp32 VALU ops.

@@ -298,6 +298,14 @@ b12x_status b12x_moe_prime(b12x_moe_plan_t p, void* scratch, uint64_t scratch_by
   if (scratch_bytes < p->scratch_bytes)
     return fail(B12X_ERR_SCRATCH_TOO_SMALL, "scratch %llu < %llu bytes", (unsigned long long)scratch_bytes,
                 (unsigned long long)p->scratch_bytes);
+  // debug aid (B12X_DEBUG_SCRATCH_FILL=1): every byte of the plan's scratch set to 0xFF before the
+  // synchronization region is zeroed, so a kernel that reads scratch it has not written reads NaNs and
+  // out-of-range codes instead of stale values that happen to be right
+  const char* fill = getenv("B12X_DEBUG_SCRATCH_FILL");
+  if (fill && fill[0] == '1') {
+    const int err = launch_fill_words(scratch, p->scratch_bytes, ~0ull, (hipStream_t)stream);
+    if (err) return hip_fail(err, "kernel launch");
+  }
   if (!p->len[R_DSYNC]) return B12X_OK;
   const int err = launch_decode_prime((uint8_t*)scratch + p->off[R_DSYNC], p->len[R_DSYNC], (hipStream_t)stream);
   if (err) return hip_fail(err, "kernel launch");
@@ -371,6 +379,8 @@ static b12x_status make_binding(b12x_moe_plan_t p, void* scratch, uint64_t scrat
   // test hook of the fused decode kernel's bounded waits (B12X_DEBUG_FORCE_GIVEUP=1 at bind)
   const char* fg = getenv("B12X_DEBUG_FORCE_GIVEUP");
   b.force_giveup = fg && fg[0] == '1';
+  const char* tm = getenv("B12X_TIMING");
+  b.timing = tm && tm[0] == '1';
   b.T = T; b.a_stride = a_stride; b.out_stride = out_stride;
   b.Hp = p->Hp; b.Ip = p->Ip; b.max_rows = p->max_rows; b.max_tiles = p->max_tiles;
   b.nf13 = p->l13.nf; b.kf13 = p->l13.kf; b.kfs13 = p->l13.kfs;
@@ -539,6 +549,19 @@ b12x_status b12x_moe_run(const b12x_moe_binding* binding, void* stream) {
   return run_path(b, s);
 }
 
+static const char* stage_name(int stage) {
+  switch (stage) {
+    case B12X_STAGE_ROUTE: return "route";
+    case B12X_STAGE_QUANT_X: return "quant_x";
+    case B12X_STAGE_GEMM1: return "gemm1";
+    case B12X_STAGE_GEMM2: return "gemm2";
+    case B12X_STAGE_COMBINE: return "combine";
+    case B12X_STAGE_DECODE1: return "decode1";
+    case B12X_STAGE_DECODE2: return "decode2";
+  }
+  return "?";
+}
+
 static b12x_status run_path(const BindingImpl& b, hipStream_t s) {
   b12x_status st = B12X_OK;
   static const int grouped[5] = {B12X_STAGE_ROUTE, B12X_STAGE_QUANT_X, B12X_STAGE_GEMM1, B12X_STAGE_GEMM2,
@@ -546,12 +569,29 @@ static b12x_status run_path(const BindingImpl& b, hipStream_t s) {
   static const int decode[4] = {B12X_STAGE_QUANT_X, B12X_STAGE_DECODE1, B12X_STAGE_DECODE2, B12X_STAGE_COMBINE};
   const int* stages = b.path == 1 ? grouped : decode;
   const int n = b.path == 1 ? 5 : 4;
+  // debug aid (B12X_TIMING=1 at bind): an event before and after every stage, then one line per stage on
+  // stderr; the call waits for its kernels.  Skipped while the stream is being captured.
+  const bool timed = b.timing && !stream_capturing(s);
+  void* marks[6] = {};
+  int ran[5] = {};
+  int m = 0;
+  if (timed) marks[m] = timing_mark(s);
   for (int i = 0; i < n; ++i) {
     if (!stage_in_path(b, stages[i])) continue;
     st = run_stage(b, stages[i], s);
-    if (st) return st;
+    if (st) break;
+    if (timed) {
+      ran[m] = stages[i];
+      marks[++m] = timing_mark(s);
+    }
   }
-  return B12X_OK;
+  if (timed) {
+    for (int i = 0; i < m && !st; ++i)
+      fprintf(stderr, "b12x_moe_run: path %d T %lld %-8s %9.2f us\n", b.path, (long long)b.T, stage_name(ran[i]),
+              1e3 * timing_ms(marks[i], marks[i + 1]));
+    for (int i = 0; i <= m; ++i) timing_free(marks[i]);
+  }
+  return st;
 }
 
 b12x_status b12x_moe_run_noalloc(b12x_moe_plan_t p, const b12x_moe_experts* ex, const void* a, int64_t T,

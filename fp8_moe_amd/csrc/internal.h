@@ -149,6 +149,7 @@ struct BindingImpl {
   int32_t a_f16;  // grouped path, NVFP4 weights: GEMM1 reads a scaled f16 copy of a (xq; of its MXFP8 round trips
                   // with MXFP8 activations) and row exponents (xs)
   int32_t force_giveup;  // test hook (fused decode kernel): its waits expect a tag no one writes
+  int32_t timing;        // B12X_TIMING=1 at bind: run() times each stage and prints the times
   int64_t T, a_stride, out_stride;
   int64_t Hp, Ip, max_rows, max_tiles;
   int64_t nf13, kf13, kfs13, nf2, kf2, kfs2;
@@ -227,6 +228,12 @@ int launch_decode_combine(const BindingImpl& b, hipStream_t s);
 // split-K decode (path 3): one kernel for gate/up + activation + partial down
 // projections per 32-column slice of h, then the combine of the partials
 int launch_decode_prime(uint8_t* dsync, uint64_t bytes, hipStream_t s);  // zero the decode synchronization region
+// debug aids (debug.hip)
+int launch_fill_words(void* p, uint64_t bytes, uint64_t value, hipStream_t s);
+bool stream_capturing(hipStream_t s);
+void* timing_mark(hipStream_t s);     // a new event recorded on s, or null
+double timing_ms(void* a, void* b);   // waits for b; milliseconds from a to b (< 0 on failure)
+void timing_free(void* e);
 int launch_decode_sk(const BindingImpl& b, hipStream_t s);
 int launch_decode_sk_combine(const BindingImpl& b, hipStream_t s);
 // Bytes of the split-K partial rows of a binding (its whole use of scratch).
