@@ -14,8 +14,9 @@ What it computes (plain, slow, fp64, NumPy):
   scale).
 * ``routing``  - the integer routing stage: expert histogram, prefix scan,
   stable token permutation, per-expert padded row tiles, inverse positions.
-* ``ffn``      - the routed-expert FFN: gather, gate/up projection, SiLU-gated
-  or ReLU^2 activation, down projection and the top-k-weighted combine.
+* ``ffn``      - the routed-expert FFN: gather, gate/up projection, SiLU-gated,
+  SwiGLU-OAI or ReLU^2 activation, down projection and the top-k-weighted
+  combine.
 * ``gemm``     - the dense block-scaled FP4 GEMM (gemm.blockscaled mm).
 
 Sources are the b12x pages: the README ("What's in here" and "Using it": the
@@ -34,5 +35,5 @@ from .formats import (  # noqa: F401
     quantize_nvfp4, nvfp4_values, nvfp4_roundtrip,
 )
 from .routing import route  # noqa: F401
-from .ffn import fused_moe, Weights  # noqa: F401
+from .ffn import fused_moe, Weights, swiglu_oai  # noqa: F401
 from .gemm import blockscaled_mm  # noqa: F401

@@ -20,6 +20,12 @@ Readings where the pages are silent:
   rows ``[I, 2I)`` the up projection; ``h = silu(gate) * up`` with
   ``silu(z) = z / (1 + exp(-z))``; no clamp, no bias.
 * non-gated weights ``w1[E, I, H]``: ``h = max(w1 x, 0)^2``.
+* SwiGLU-OAI (named by b12x README "What's in here", defined nowhere on the
+  pages): the published definition of the open-weight gpt-oss models, taken
+  as the reading.  Gated weights as for SiLU; the gate is clamped from above
+  at ``limit``, the up projection to ``[-limit, limit]``, and
+  ``h = gate * sigmoid(alpha * gate) * (up + 1)`` with ``alpha = 1.702`` and
+  ``limit = 7``; bias-free like the other activations.
 * the expert's intermediate ``h`` is rounded to the precision of the down
   projection's operand before it: bf16 (round to nearest even) for BF16
   activations, MXFP8 (per 32 along I, the same rule as the activations) for
@@ -92,13 +98,39 @@ def _silu(z):
         return z / (1.0 + np.exp(-z))
 
 
-def expert_ffn(xa, w13, w2, gated, intermediate, h_global=None):
+OAI_ALPHA = 1.702
+OAI_LIMIT = 7.0
+
+
+def swiglu_oai(gate, up):
+    """SwiGLU-OAI of gate and up projections (fp64): the gate clamped from
+    above at the limit, up clamped to [-limit, limit], then
+    gate * sigmoid(alpha * gate) * (up + 1)."""
+    g = np.minimum(gate, OAI_LIMIT)
+    u = np.clip(up, -OAI_LIMIT, OAI_LIMIT)
+    with np.errstate(over="ignore"):
+        return g / (1.0 + np.exp(-OAI_ALPHA * g)) * (u + 1.0)
+
+
+ACTIVATIONS = ("silu", "relu2", "swiglu_oai")
+
+
+def expert_ffn(xa, w13, w2, gated, intermediate, h_global=None, activation=None):
     """One expert on the rows ``xa`` [m, H]: returns y [m, H] (fp64).
-    ``h_global``: the expert's NVFP4 activation scale (intermediate "nvfp4")."""
+    ``h_global``: the expert's NVFP4 activation scale (intermediate "nvfp4").
+    ``activation``: "silu" or "swiglu_oai" (gated weights), "relu2"
+    (non-gated); None picks "silu" or "relu2" from ``gated``."""
+    if activation is None:
+        activation = "silu" if gated else "relu2"
+    if activation not in ACTIVATIONS or (activation == "relu2") == gated:
+        raise ValueError(f"activation {activation!r} with gated={gated}")
     z = xa @ w13.T
     if gated:
         inter = w13.shape[0] // 2
-        h = _silu(z[:, :inter]) * z[:, inter:]
+        if activation == "silu":
+            h = _silu(z[:, :inter]) * z[:, inter:]
+        else:
+            h = swiglu_oai(z[:, :inter], z[:, inter:])
     else:
         h = np.maximum(z, 0.0) ** 2
     if intermediate == "bf16":
@@ -113,7 +145,7 @@ def expert_ffn(xa, w13, w2, gated, intermediate, h_global=None):
 
 
 def fused_moe(x_bits, topk_ids, topk_weights, weights, act_format="bf16",
-              intermediate=None):
+              intermediate=None, activation=None):
     """Reference fused MoE.  Returns the fp64 output [T, H] before the final
     bf16 rounding.
 
@@ -125,6 +157,8 @@ def fused_moe(x_bits, topk_ids, topk_weights, weights, act_format="bf16",
     ``weights.a13_global``, h against ``weights.a2_global[e]``).
     intermediate: rounding of h before the down projection; defaults to the
     activation format ("bf16", "mxfp8" or "nvfp4"; "none" keeps fp64).
+    activation: "silu", "relu2" or "swiglu_oai"; None picks "silu" for gated
+    weights and "relu2" for non-gated ones.
     """
     x = bf16_decode(x_bits)
     ids = np.asarray(topk_ids).astype(np.int64)
@@ -150,7 +184,8 @@ def fused_moe(x_bits, topk_ids, topk_weights, weights, act_format="bf16",
     for e in np.unique(ids[valid]):
         tt, jj = np.nonzero(ids == e)
         hg = None if weights.a2_global is None else weights.a2_global[e]
-        y[tt, jj] = expert_ffn(xa[tt], weights.w13(e), weights.w2(e), weights.gated, intermediate, hg)
+        y[tt, jj] = expert_ffn(xa[tt], weights.w13(e), weights.w2(e), weights.gated, intermediate, hg,
+                               activation)
 
     out = np.zeros((T, x.shape[1]), dtype=np.float64)
     for j in range(k):

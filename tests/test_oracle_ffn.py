@@ -1,7 +1,10 @@
 """Pins of the oracle FFN: a hand-derived worked example, a scalar brute force
 (table decode, explicit loops, torch for the roundings), the E=1/top_k=1
 dense special case, and invariances (token and slot permutation, linearity in
-topk_weights, dropped ids, duplicate ids, power-of-two global scales)."""
+topk_weights, dropped ids, duplicate ids, power-of-two global scales).
+SwiGLU-OAI is pinned by identities of the logistic function (its odd part is
+the identity map, its even part is g tanh(alpha g / 2)), by its clamps and by
+its zero at up = -1."""
 import math
 import os
 
@@ -9,7 +12,7 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import fused_moe, Weights
+from oracle import fused_moe, swiglu_oai, Weights
 from oracle import formats as F
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -74,6 +77,61 @@ def test_worked_example_relu2():
     assert out[0, 0] == 0.5 * 0.5 * 9.0 and np.count_nonzero(out) == 1
 
 
+# ---------------------------------------------------------------- SwiGLU-OAI
+
+def test_swiglu_oai_odd_part_is_the_gate():
+    # sigmoid(z) + sigmoid(-z) = 1, so below the clamp f(g) - f(-g) = g (up + 1)
+    g = np.linspace(-6.9, 6.9, 139)
+    for u in (-3.0, 0.0, 0.5, 6.0):
+        d = swiglu_oai(g, np.full_like(g, u)) - swiglu_oai(-g, np.full_like(g, u))
+        assert np.allclose(d, g * (u + 1.0), rtol=0, atol=1e-13)
+
+
+def test_swiglu_oai_even_part_fixes_alpha():
+    # sigmoid(z) - sigmoid(-z) = tanh(z / 2): f(g) + f(-g) = g tanh(1.702 g / 2) at up = 0
+    for g in (1e-3, 0.25, 1.0, 3.0, 6.5):
+        got = swiglu_oai(np.float64(g), 0.0) + swiglu_oai(np.float64(-g), 0.0)
+        assert math.isclose(got, g * math.tanh(0.851 * g), rel_tol=1e-12)
+
+
+def test_swiglu_oai_clamps():
+    g = np.array([-3.0, 0.3, 2.0, 6.99])
+    u = np.array([-2.0, 0.0, 1.5, 6.0])
+    # the gate is clamped from above at 7 only
+    assert np.array_equal(swiglu_oai(np.full(4, 7.0), u), swiglu_oai(np.full(4, 100.0), u))
+    assert swiglu_oai(np.float64(-100.0), 1.0) < 0 and swiglu_oai(np.float64(-100.0), 1.0) > -1e-60
+    # up is clamped to [-7, 7]
+    assert np.array_equal(swiglu_oai(g, np.full(4, 7.0)), swiglu_oai(g, np.full(4, 1e6)))
+    assert np.array_equal(swiglu_oai(g, np.full(4, -7.0)), swiglu_oai(g, np.full(4, -1e6)))
+    # and h vanishes at up = -1 and at gate = 0
+    assert np.all(swiglu_oai(g, np.full(4, -1.0)) == 0)
+    assert np.all(swiglu_oai(np.zeros(4), u) == 0)
+    # below the clamps: gate 2, up 1.5 -> 2 (1 + tanh(1.702)) / 2 * 2.5
+    assert math.isclose(float(swiglu_oai(np.float64(2.0), 1.5)), 2.5 * (1.0 + math.tanh(1.702)), rel_tol=1e-13)
+
+
+def test_worked_example_swiglu_oai():
+    # the SiLU worked example's weights: gate 1, up 2 -> h = sigmoid(1.702) * 3, rounded to bf16
+    E, H, I = 1, 32, 32
+    w13 = np.zeros((E, 2 * I, H // 2), np.uint8)
+    w13[0, 0, 0] = 0x02
+    w13[0, I, 0] = 0x04
+    w2 = np.zeros((E, H, I // 2), np.uint8)
+    w2[0, 0, 0] = 0x02
+    wts = Weights("mxfp4", True, w13, np.full((E, 2 * I, 1), 127, np.uint8),
+                  w2, np.full((E, H, 1), 127, np.uint8))
+    x = np.zeros((1, H), np.float32)
+    x[0, 0] = 1.0
+    out = fused_moe(x_bits(x), np.zeros((1, 1), np.int32), np.ones((1, 1), np.float32), wts,
+                    activation="swiglu_oai")
+    h = 3.0 * (1.0 + math.tanh(0.851)) / 2.0
+    assert out[0, 0] == float(bf16([h])[0]) and np.count_nonzero(out) == 1
+    with pytest.raises(ValueError):
+        fused_moe(x_bits(x), np.zeros((1, 1), np.int32), np.ones((1, 1), np.float32),
+                  Weights("mxfp4", False, w13[:, :I], np.full((E, I, 1), 127, np.uint8),
+                          w2, np.full((E, H, 1), 127, np.uint8)), activation="swiglu_oai")
+
+
 # ---------------------------------------------------------------- random tiny problems
 
 def random_weights(rng, fmt, gated, E, H, I):
@@ -113,7 +171,7 @@ def torch_mxfp8(v):
     return out
 
 
-def brute_force(xb, ids, tw, w, act):
+def brute_force(xb, ids, tw, w, act, activation=None):
     x = torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
     T, H = x.shape
     E = w.E
@@ -128,7 +186,11 @@ def brute_force(xb, ids, tw, w, act):
                 continue
             z = [sum(xa[kk] * scalar_weight(w.w13_codes, w.w13_scales, w.w13_global, w.weight_format, e, n, kk)
                      for kk in range(H)) for n in range(n1)]
-            if w.gated:
+            if activation == "swiglu_oai":
+                # logistic through tanh: sigmoid(a g) = (1 + tanh(a g / 2)) / 2
+                h = [min(z[i], 7.0) * (1.0 + math.tanh(0.851 * min(z[i], 7.0))) / 2.0
+                     * (min(max(z[inter + i], -7.0), 7.0) + 1.0) for i in range(inter)]
+            elif w.gated:
                 h = [z[i] / (1.0 + math.exp(-z[i])) * z[inter + i] for i in range(inter)]
             else:
                 h = [max(z[i], 0.0) ** 2 for i in range(inter)]
@@ -152,6 +214,23 @@ def test_matches_scalar_brute_force(fmt, gated, act):
     tw = rng.uniform(0.1, 1.0, size=(T, k)).astype(np.float32)
     got = fused_moe(xb, ids, tw, w, act_format=act)
     want = brute_force(xb, ids, tw, w, act)
+    scale = np.abs(want).max()
+    assert scale > 0
+    assert np.abs(got - want).max() <= 1e-12 * scale
+
+
+@pytest.mark.parametrize("fmt", ["mxfp4", "nvfp4"])
+@pytest.mark.parametrize("act", ["bf16", "mxfp8"])
+def test_swiglu_oai_matches_scalar_brute_force(fmt, act):
+    rng = np.random.default_rng([len(fmt), 7, len(act)])
+    E, H, I, T, k = 3, 64, 32, 3, 2
+    w = random_weights(rng, fmt, True, E, H, I)
+    # wide inputs so that both clamps are reached
+    xb = x_bits(4.0 * rng.standard_normal((T, H)).astype(np.float32))
+    ids = np.array([[0, 2], [1, 1], [2, -1]], np.int32)
+    tw = rng.uniform(0.1, 1.0, size=(T, k)).astype(np.float32)
+    got = fused_moe(xb, ids, tw, w, act_format=act, activation="swiglu_oai")
+    want = brute_force(xb, ids, tw, w, act, activation="swiglu_oai")
     scale = np.abs(want).max()
     assert scale > 0
     assert np.abs(got - want).max() <= 1e-12 * scale
