@@ -26,7 +26,7 @@ LIB_PATH = os.environ.get("B12X_MOE_LIB") or os.path.join(_HERE, "libb12x_moe.so
 
 WEIGHT_FORMATS = {"mxfp4": 1, "nvfp4": 2}
 ACT_FORMATS = {"bf16": 1, "mxfp8": 2, "nvfp4": 3}
-ACTIVATIONS = {"silu": 1, "relu2": 2}
+ACTIVATIONS = {"silu": 1, "relu2": 2, "swiglu_oai": 3}
 STAGES = {"route": 1, "quant_x": 2, "gemm1": 3, "gemm2": 4, "combine": 5, "decode1": 6, "decode2": 7}
 NOALLOC_SCRATCH_BYTES = 16 << 20   # B12X_NOALLOC_SCRATCH_BYTES: the static scratch of run_noalloc
 QUERIES = {"path": 1, "tile_rows": 2, "row_pad": 3, "T": 4, "num_stages": 5}
@@ -386,7 +386,7 @@ class FusedMoE:
 
     def __init__(self, E, H, I, top_k, weight_format, act_format, activation, max_tokens, weights, stream=None,
                  decode_max_pairs=0, splitk_max_pairs=0):
-        gated = activation == "silu"
+        gated = activation != "relu2"
         self.wplan = plan_weights(E, H, I, gated, weight_format)
         self.experts = prepare_weights(self.wplan, weights["w13_codes"], weights["w13_scales"],
                                        weights["w2_codes"], weights["w2_scales"], weights.get("w13_global"),

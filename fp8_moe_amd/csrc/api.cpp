@@ -77,10 +77,12 @@ b12x_status check_caps(const b12x_moe_caps* c) {
     return fail(B12X_ERR_INVALID_ARGUMENT, "unknown activation format %d", c->act_format);
   if (c->act_format == B12X_ACT_NVFP4 && c->weights.desc.weight_format != B12X_WEIGHT_NVFP4)
     return fail(B12X_ERR_UNSUPPORTED, "NVFP4 activations run with NVFP4 weights only");
-  if (c->activation != B12X_ACTIVATION_SILU_GATED && c->activation != B12X_ACTIVATION_RELU2)
+  if (c->activation != B12X_ACTIVATION_SILU_GATED && c->activation != B12X_ACTIVATION_RELU2 &&
+      c->activation != B12X_ACTIVATION_SWIGLU_OAI)
     return fail(B12X_ERR_INVALID_ARGUMENT, "unknown activation %d", c->activation);
-  if ((c->activation == B12X_ACTIVATION_SILU_GATED) != (c->weights.desc.gated == 1))
-    return fail(B12X_ERR_UNSUPPORTED, "SiLU-gated experts need gated weights and ReLU^2 needs non-gated ones");
+  if ((c->activation != B12X_ACTIVATION_RELU2) != (c->weights.desc.gated == 1))
+    return fail(B12X_ERR_UNSUPPORTED,
+                "SiLU-gated and SwiGLU-OAI experts need gated weights and ReLU^2 needs non-gated ones");
   return B12X_OK;
 }
 
@@ -373,6 +375,7 @@ static b12x_status make_binding(b12x_moe_plan_t p, void* scratch, uint64_t scrat
   b.decode_max = p->decode_max_pairs;
   b.E = p->E; b.H = p->H; b.I = p->I; b.k = p->k;
   b.gated = p->gated; b.wfmt = p->wfmt; b.afmt = p->afmt; b.act = p->act;
+  b.oai = p->act == B12X_ACTIVATION_SWIGLU_OAI;
   // grouped path, NVFP4 weights: GEMM1 reads a scaled f16 copy of a (of its MXFP8 or NVFP4 round trips with
   // MXFP8 or NVFP4 activations)
   b.a_f16 = b.path == 1 && p->wfmt == B12X_WEIGHT_NVFP4;

@@ -54,6 +54,7 @@ struct DecodeParams {
   const float* aglobal;
   int aglobal_per_expert;
   const float* hglobal;
+  int oai;  // gated: SwiGLU-OAI instead of SiLU
   int64_t b_codes_expert, b_scales_expert;
   int NF, KFS;
   int n_groups;  // fragment groups per expert
@@ -317,7 +318,7 @@ __device__ __forceinline__ void decode_items(const DecodeParams& p, DecodeLds& L
             for (int q = 0; q < NH; ++q) {
               if constexpr (MODE == DMODE_SILU) {
                 const float gt = v[2 * q][i] * gsc, up = v[2 * q + 1][i] * gsc;
-                hv[q] = gt / (1.0f + __expf(-gt)) * up;
+                hv[q] = p.oai ? swiglu_oai(gt, up) : gt / (1.0f + __expf(-gt)) * up;
               } else {
                 const float z = v[q][i] * gsc;
                 hv[q] = z > 0.f ? z * z : 0.f;
@@ -509,6 +510,7 @@ static DecodeParams common_params(const BindingImpl& b) {
 
 static DecodeParams gate_up_params(const BindingImpl& b) {
   DecodeParams p = common_params(b);
+  p.oai = b.oai;
   const bool a8 = a8_native(b.wfmt, b.afmt);
   p.a16 = b.a;
   p.a8 = b.xq;

@@ -61,6 +61,7 @@ struct SkParams {
   int64_t w2c_e, w2s_e;
   const float* ax;    // NVFP4 activations: scale of x [1]
   const float* ah;    // and of each expert's h [E]
+  int oai;            // gated: SwiGLU-OAI instead of SiLU
   float* part;        // [P][n_slices][row_stride]: per fragment group G (4 fragments), column n,
                       // fragment q: position 64 G + 4 n + q
   int64_t part_bytes;
@@ -426,7 +427,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_sk_kernel(const SkParams p
           for (int qq = 0; qq < 2; ++qq) {
             if constexpr (GATED) {
               const float gt = v[2 * qq][i] * g1, up = v[2 * qq + 1][i] * g1;
-              hv[qq] = gt / (1.0f + __expf(-gt)) * up;
+              hv[qq] = p.oai ? swiglu_oai(gt, up) : gt / (1.0f + __expf(-gt)) * up;
             } else {
               const float z = v[qq][i] * g1;
               hv[qq] = z > 0.f ? z * z : 0.f;
@@ -593,6 +594,7 @@ static SkParams sk_params(const BindingImpl& b) {
   p.tw = b.tw;
   p.T = (int)b.T;
   p.lv = b.live();
+  p.oai = b.oai;
   p.k = b.k;
   p.E = b.E;
   p.P = (int)(b.T * b.k);

@@ -206,6 +206,17 @@ __device__ __forceinline__ uint32_t mx_roundtrip_bf16(float v, int s) {
   return bf16_rne(__builtin_amdgcn_cvt_scalef32_pk_f32_fp8((uint32_t)(uint16_t)o.x, m.scale, false)[0]);
 }
 
+// SwiGLU-OAI (b12x README "What's in here" names it; the definition is the one
+// published with the gpt-oss models): the gate clamped from above at 7, up to
+// [-7, 7], h = gate * sigmoid(1.702 gate) * (up + 1).  A gate far below zero
+// makes the exponential infinite and h a signed zero.
+constexpr float kOaiAlpha = 1.702f, kOaiLimit = 7.0f;
+__device__ __forceinline__ float swiglu_oai(float gt, float up) {
+  gt = fminf(gt, kOaiLimit);
+  up = fminf(fmaxf(up, -kOaiLimit), kOaiLimit);
+  return gt * __builtin_amdgcn_rcpf(1.0f + __expf(-kOaiAlpha * gt)) * (up + 1.0f);
+}
+
 // Largest value over the 16 lanes of this lane's DPP row (lanes 16r .. 16r+15),
 // in every lane of the row: max with the lane ^ 1 and ^ 2 (quad permutes),
 // then with the mirrored lane in the half row and in the row.  VALU only.

@@ -58,6 +58,7 @@ static int dispatch(const BindingImpl& b, const GemmParams& p, int64_t max_work,
 int launch_gemm1(const BindingImpl& b, hipStream_t s) {
   GemmParams p = {};
   p.lv = b.live();
+  p.oai = b.oai;
   const bool a8 = a8_native(b.wfmt, b.afmt);
   p.tiles = b.tiles;
   p.ntiles = b.ntiles;

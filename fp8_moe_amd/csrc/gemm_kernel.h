@@ -67,6 +67,7 @@ struct GemmParams {
   const float* aglobal;
   int aglobal_per_expert;
   const float* hglobal;
+  int oai;  // gated: SwiGLU-OAI instead of SiLU
   int64_t b_codes_expert;
   int64_t b_scales_expert;
   int NF;
@@ -512,7 +513,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void moe_gemm_kernel(const GemmPar
             for (int q = 0; q < NH; ++q) {
               if constexpr (MODE == MODE_SILU) {
                 const float gt = acc[mf][2 * q][i] * rsc, up = acc[mf][2 * q + 1][i] * rsc;
-                hv[q] = gt * __builtin_amdgcn_rcpf(1.0f + __expf(-gt)) * up;
+                hv[q] = p.oai ? swiglu_oai(gt, up) : gt * __builtin_amdgcn_rcpf(1.0f + __expf(-gt)) * up;
               } else {
                 const float z = acc[mf][q][i] * rsc;
                 hv[q] = z > 0.f ? z * z : 0.f;

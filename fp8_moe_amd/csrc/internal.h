@@ -146,6 +146,7 @@ struct BindingImpl {
   uint32_t magic;
   int32_t path;  // 1 grouped, 2 decode (two-phase), 3 decode (split-K), 4 live token count (all three)
   int32_t E, H, I, k, gated, wfmt, afmt, act;
+  int32_t oai;  // gated with SwiGLU-OAI instead of SiLU
   int32_t a_f16;  // grouped path, NVFP4 weights: GEMM1 reads a scaled f16 copy of a (xq; of its MXFP8 round trips
                   // with MXFP8 activations) and row exponents (xs)
   int32_t force_giveup;  // test hook (fused decode kernel): its waits expect a tag no one writes

@@ -35,14 +35,16 @@ def compare(gpu_out, ref):
 class Problem:
     """A workload instance on the GPU: source weights, prepared weights, plan."""
 
-    def __init__(self, wl, max_tokens, gen_device="cuda", weights=None, decode_max_pairs=0, splitk_max_pairs=0):
+    def __init__(self, wl, max_tokens, gen_device="cuda", weights=None, decode_max_pairs=0, splitk_max_pairs=0,
+                 activation=None):
         import fp8_moe_amd as fm
         self.wl = wl
         self.fm = fm
+        self.activation = activation or ("silu" if wl.gated else "relu2")
         self.w = weights if weights is not None else synth.make_weights(wl, device=gen_device)
         self.wd = {k: (None if v is None else v.cuda()) for k, v in self.w.items()}
         self.model = fm.FusedMoE(wl.E, wl.H, wl.I, wl.k, wl.weight_format, wl.act_format,
-                                 "silu" if wl.gated else "relu2", max_tokens, self.wd,
+                                 self.activation, max_tokens, self.wd,
                                  decode_max_pairs=decode_max_pairs, splitk_max_pairs=splitk_max_pairs)
 
     def run(self, x, ids, tw, out=None):
@@ -62,7 +64,8 @@ class Problem:
         ids_np = ids.numpy()
         touched = sorted({int(e) for e in ids_np.reshape(-1) if 0 <= e < self.wl.E})
         w = self.oracle_weights(touched)
-        return fused_moe(bits(x), ids_np, tw.numpy(), w, act_format=self.wl.act_format)
+        return fused_moe(bits(x), ids_np, tw.numpy(), w, act_format=self.wl.act_format,
+                         activation=self.activation)
 
 
 def small_workload(name, E, H, I, k, gated=True, weight_format="mxfp4", act_format="bf16", routing="uniform",

@@ -71,7 +71,12 @@ def test_support_matrix():
     assert fm.is_supported(nv_g, 2, 16, "mxfp8", "silu")          # NVFP4 x MXFP8 through bf16 round trips
     assert fm.is_supported(nv_g, 2, 16, "nvfp4", "silu")          # NVFP4 x NVFP4 (W4A4)
     assert not fm.is_supported(mx_g, 2, 16, "nvfp4", "silu")      # NVFP4 activations need NVFP4 weights
-    assert not fm.is_supported(mx_g, 2, 16, "bf16", "relu2")      # gated weights need SiLU
+    assert not fm.is_supported(mx_g, 2, 16, "bf16", "relu2")      # gated weights need SiLU or SwiGLU-OAI
+    for af in ("bf16", "mxfp8"):
+        assert fm.is_supported(mx_g, 2, 16, af, "swiglu_oai")
+        assert fm.is_supported(nv_g, 2, 16, af, "swiglu_oai")
+        assert not fm.is_supported(mx_r, 2, 16, af, "swiglu_oai")  # SwiGLU-OAI needs gated weights
+    assert fm.is_supported(nv_g, 2, 16, "nvfp4", "swiglu_oai")
     assert not fm.is_supported(mx_g, 0, 16, "bf16", "silu")
 
 
