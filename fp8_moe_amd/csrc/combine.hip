@@ -32,24 +32,19 @@ __global__ __launch_bounds__(256) void combine_kernel(const YT* __restrict__ y, 
                                                        const int32_t* __restrict__ ids, int E,
                                                        const float* __restrict__ tw, LiveT lv, int k, int H,
                                                        int64_t max_rows, uint16_t* __restrict__ out,
-                                                       int64_t out_stride, const uint64_t* counter,
-                                                       const uint64_t* status) {
+                                                       int64_t out_stride, const uint64_t* counter) {
   constexpr int kChunk = 8;
   const int64_t groups = H / 8;
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t T = lv.tokens();
   if (!lv.on() || idx >= T * groups) return;
-  // The fused decode launch before this combine is launch number c / kLaunchStep - 1
-  // of its scratch.  The output is NaN, not stale, if one of its waits gave up
-  // (status holds that launch's tag; nothing is cleared: a later launch has
-  // another tag) or if the counter is not a multiple of kLaunchStep (a
-  // scratch never primed, whose launches' workgroups may not share one tag).
+  // After a fused decode launch the launch counter is a multiple of kLaunchStep.
+  // The output is NaN, not stale, if it is not: a scratch never primed, whose
+  // launches' workgroups may not share one tag.
   bool failed = false;
-  if (status) {
+  if (counter) {
     const uint64_t c = __hip_atomic_load(counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    failed = (c & (kLaunchStep - 1)) != 0 ||
-             __hip_atomic_load(status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-                 decode_tag((uint32_t)(c >> kLaunchShift) - 1u);
+    failed = (c & (kLaunchStep - 1)) != 0;
   }
   const int64_t t = idx / groups, c = (idx % groups) * 8;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
@@ -96,24 +91,23 @@ __global__ __launch_bounds__(256) void combine_kernel(const YT* __restrict__ y, 
 
 template <typename YT>
 static int launch_combine_rows(const BindingImpl& b, const YT* y, const int32_t* pos, const uint64_t* counter,
-                               const uint64_t* status, hipStream_t s) {
+                               hipStream_t s) {
   const int64_t total = b.T * (b.H / 8);
   if (total == 0) return 0;
   hipLaunchKernelGGL(combine_kernel<YT>, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, y, (int64_t)b.H,
-                     pos, b.ids, b.E, b.tw, b.live(), b.k, b.H, b.max_rows, b.out, b.out_stride, counter, status);
+                     pos, b.ids, b.E, b.tw, b.live(), b.k, b.H, b.max_rows, b.out, b.out_stride, counter);
   return (int)hipGetLastError();
 }
 
 // grouped path: bf16 y rows in routing order, located through pos
 int launch_combine(const BindingImpl& b, hipStream_t s) {
-  return launch_combine_rows(b, (const uint16_t*)b.y16, b.pos, nullptr, nullptr, s);
+  return launch_combine_rows(b, (const uint16_t*)b.y16, b.pos, nullptr, s);
 }
 
 // decode path: fp32 y rows indexed by pair id
 int launch_decode_combine(const BindingImpl& b, hipStream_t s) {
-  if (!decode_fused(b)) return launch_combine_rows(b, (const float*)b.y, nullptr, nullptr, nullptr, s);
-  return launch_combine_rows(b, (const float*)b.y, nullptr, (const uint64_t*)(b.dsync + kDecodeCounterOffset),
-                             (const uint64_t*)(b.dsync + kDecodeStatusOffset), s);
+  if (!decode_fused(b)) return launch_combine_rows(b, (const float*)b.y, nullptr, nullptr, s);
+  return launch_combine_rows(b, (const float*)b.y, nullptr, (const uint64_t*)(b.dsync + kDecodeCounterOffset), s);
 }
 
 }  // namespace b12x

@@ -70,13 +70,12 @@ struct DecodeParams {
   // expert slot, gate/up group), flags_per_slot of them per slot; a flag
   // holds the launch's tag once that group's h rows are stored.  Every
   // workgroup reads the launch counter when it starts and adds its share of
-  // kLaunchStep when it is done, so each launch has a tag of its own; a wait
-  // that gives up stores the launch's tag in status (the combine then
-  // writes NaN).
+  // kLaunchStep when it is done, so each launch has a tag of its own.  A
+  // wait that has polled max_polls times computes the groups still missing
+  // itself.
   uint64_t* flags;
   int flags_per_slot;
   uint64_t* counter;
-  uint64_t* status;
   uint64_t expect_xor;  // 0; the test hook's waits expect tag ^ expect_xor, which no flag holds
   int max_polls;
   int64_t h_bytes;  // extent of h16 (device-coherent stores and loads)
@@ -93,25 +92,38 @@ __device__ __forceinline__ uint64_t flag_tag(const uint64_t* counter) {
   return decode_tag((uint32_t)(__hip_atomic_load(counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >> kLaunchShift));
 }
 
-// Upper bound on the polls of one wait (each at least one round trip to
-// memory plus a sleep: far beyond any wait that can end).
-constexpr int kWaitPolls = 1 << 18;
+// Polls of one wait before the waiting workgroup computes the missing groups
+// itself (each poll is a round trip to memory plus a sleep, about a
+// microsecond: some hundred times the longest wait measured with the whole
+// grid resident).
+constexpr int kWaitPolls = 1 << 11;
+
+// No fallback: the plain decode kernels and the fused kernel's own gate/up phase.
+struct NoFallback {
+  __device__ void operator()(int, uint64_t) const {}
+};
 
 // This workgroup's share of the (touched expert slot, group of FR weight
 // fragments) items of one GEMV.  FUSE = 0: a launch of its own.  FUSE = 1:
 // the gate/up phase of the fused kernel: h is stored device-coherent and
 // each finished group raises its flag.  FUSE = 2: the down phase: before an
 // expert's part, wave 0 waits until every gate/up group of that expert has
-// raised its flag, and h is loaded device-coherent.
-template <int WF, int AF, int MODE, int FR, int KW, int FUSE>
+// raised its flag, and h is loaded device-coherent; a wait that runs out of
+// polls hands the groups still missing to fallback(slot, mask), which
+// computes them in this workgroup.  FUSE = 3: that fallback, gate/up items
+// [lo_in, hi_in) of one slot computed as in FUSE = 1.  A group computed
+// twice (by its owner and by a waiter that gave up on it) is stored twice
+// with the same bytes: the computation does not depend on who runs it.
+template <int WF, int AF, int MODE, int FR, int KW, int FUSE, typename Fallback>
 __device__ __forceinline__ void decode_items(const DecodeParams& p, DecodeLds& L, f32x4* red, int n_touched,
-                                             uint64_t tag, int P) {
+                                             uint64_t tag, int P, int lo_in, int hi_in, const Fallback& fallback) {
+  constexpr bool GU = FUSE == 1 || FUSE == 3;  // a gate/up phase of the fused kernel
   constexpr bool A8 = AF == B12X_ACT_MXFP8;
   constexpr bool RT = AF == kActRt;  // bf16 MXFP8 round trips: h stored as its own round trip
   constexpr bool NVRT = AF == kActNvRt;  // bf16 NVFP4 round trips: h stored as its own NVFP4 round trip
   static_assert(FUSE == 0 || !A8, "the fused kernel runs 16-bit activations");
   static_assert(FUSE == 0 || (!RT && !NVRT), "the fused kernel stores plain bf16 h");
-  static_assert(FUSE != 1 || MODE != DMODE_DOWN, "phase 1 is gate/up");
+  static_assert(!GU || MODE != DMODE_DOWN, "phase 1 is gate/up");
   static_assert(FUSE != 2 || MODE == DMODE_DOWN, "phase 2 is down");
   int* const s_ids = L.ids;
   int* const s_rows = L.rows;
@@ -134,7 +146,7 @@ __device__ __forceinline__ void decode_items(const DecodeParams& p, DecodeLds& L
   // With at least p.deal items per workgroup: chunks of p.deal consecutive
   // items dealt round-robin (chunk c to workgroup c % grid).  Otherwise (and
   // with p.deal = 0) one contiguous share per workgroup.
-  const int deal = p.deal && items >= (int64_t)p.deal * gridDim.x ? p.deal : 0;
+  const int deal = FUSE != 3 && p.deal && items >= (int64_t)p.deal * gridDim.x ? p.deal : 0;
   // When the gate/up phase dealt between one and two rounds of chunks, its
   // first C1 % grid workgroups took two chunks and the others one.  The down
   // phase then continues that deal (its chunk c goes to workgroup
@@ -151,7 +163,10 @@ __device__ __forceinline__ void decode_items(const DecodeParams& p, DecodeLds& L
       chunk_id = ((int)blockIdx.x - start + (int)gridDim.x) % (int)gridDim.x;
     }
   }
-  if (deal) {
+  if (FUSE == 3) {
+    lo = lo_in;
+    hi = hi_in;
+  } else if (deal) {
     lo = chunk_id * deal;
     hi = (int)min(items, (int64_t)lo + deal);
   } else {  // one contiguous share
@@ -173,24 +188,37 @@ __device__ __forceinline__ void decode_items(const DecodeParams& p, DecodeLds& L
   item += g_end - g_begin;
   if constexpr (FUSE == 2) {
     // wave 0 waits until every gate/up group of this expert has raised its
-    // flag (the barrier that opens decode_expert holds the other waves)
+    // flag; should its polls run out (a producer not resident, the device
+    // shared with other work), the groups still missing are computed here
     if (wave == 0) {
       const uint64_t* f = p.flags + (int64_t)slot * p.flags_per_slot;
       const uint64_t expect = tag ^ p.expect_xor;
+      uint64_t miss = 0;
       for (int poll = 0;; ++poll) {
         const bool ok = lane >= p.flags_per_slot ||
                         __hip_atomic_load(f + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == expect;
-        if (__ballot(!ok) == 0) break;
-        if (poll >= p.max_polls) {
-          if (lane == 0) __hip_atomic_store(p.status, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          break;
-        }
+        miss = __ballot(!ok);
+        if (miss == 0 || poll >= p.max_polls) break;
         __builtin_amdgcn_s_sleep(8);
+      }
+      if (lane == 0) {  // published by the barrier that opens decode_expert
+        s_info[2] = (int)(uint32_t)miss;
+        s_info[3] = (int)(uint32_t)(miss >> 32);
       }
     }
   }
   int e;
   const int m = decode_expert(P, p.E, slot, s_ids, s_bits, s_wpre, s_rows, s_info, e);
+  if constexpr (FUSE == 2) {
+    const uint64_t miss = (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane(s_info[2]) |
+                          ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane(s_info[3]) << 32);
+    if (miss) {
+      // (it rebuilds this slot's pair list in LDS, the same one, and ends with wave 0
+      // waiting for its h stores, which the barrier then orders before this part's h loads)
+      fallback(slot, miss);
+      __syncthreads();
+    }
+  }
   const uint8_t* bcodes = p.bcodes + (int64_t)e * p.b_codes_expert;
   const uint8_t* bscales = p.bscales + (int64_t)e * p.b_scales_expert;
   float gsc = p.bglobal ? p.bglobal[e] : 1.0f;
@@ -217,7 +245,7 @@ __device__ __forceinline__ void decode_items(const DecodeParams& p, DecodeLds& L
     }
   };
   const BufRsrc a_rsrc = make_rsrc(A8 ? (const void*)p.a8 : (const void*)p.a16, p.a_bytes);
-  [[maybe_unused]] const BufRsrc h_rsrc = make_rsrc(p.h16, FUSE == 1 ? p.h_bytes : 0);
+  [[maybe_unused]] const BufRsrc h_rsrc = make_rsrc(p.h16, GU ? p.h_bytes : 0);
   const BufRsrc as_rsrc = make_rsrc(p.as, p.as_bytes);
 
   for (int r0 = 0; r0 < m; r0 += 16) {
@@ -361,7 +389,7 @@ __device__ __forceinline__ void decode_items(const DecodeParams& p, DecodeLds& L
 #pragma unroll
               for (int q = 0; q < NH; ++q) {
                 if (live && q < nh) {
-                  if constexpr (FUSE == 1)
+                  if constexpr (GU)
                     buf_store2_dev(h_rsrc, (uint32_t)((pr * p.h_stride + hcol0 + 16 * q + r16) * 2),
                                    (uint16_t)bf16_rne(hv[q]));
                   else
@@ -399,7 +427,7 @@ __device__ __forceinline__ void decode_items(const DecodeParams& p, DecodeLds& L
       group(bq, bs, gi);
     }
   }
-  if constexpr (FUSE == 1) {
+  if constexpr (GU) {
     // wave 0 stored this part's h rows; once they are visible device-wide,
     // raise the groups' flags
     if (wave == 0) {
@@ -426,7 +454,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(const DecodeParams 
   if (!p.lv.on()) return;
   const int P = (int)(p.lv.tokens() * p.k);
   const int n_touched = decode_prep(p.ids, P, p.E, L.ids, L.bits, L.wpre);
-  decode_items<WF, AF, MODE, FR, KW, 0>(p, L, s_red, n_touched, 0, P);
+  decode_items<WF, AF, MODE, FR, KW, 0>(p, L, s_red, n_touched, 0, P, 0, 0, NoFallback{});
 }
 
 // Gate/up and down in one launch (16-bit activations): every workgroup takes
@@ -434,9 +462,10 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(const DecodeParams 
 // part waits only for the gate/up groups of its own expert.  The grid is at
 // most the resident capacity, and no workgroup waits before its gate/up
 // share is done, so every awaited group is being computed by a running
-// workgroup.  Should a workgroup not be resident (the device shared with
-// other work), the waits for its groups give up after kWaitPolls polls and
-// the call's output is NaN: a loud failure, never a stale result.
+// workgroup as long as the whole grid is resident.  Should a workgroup not
+// be (the device shared with other work), a wait for its groups runs out
+// after kWaitPolls polls and the waiting workgroup computes them itself:
+// slower, with the same result.
 //
 // The launch's tag: every workgroup reads the launch counter first thing and
 // adds its share of kLaunchStep (the shares of a grid sum to kLaunchStep, and
@@ -455,8 +484,21 @@ __global__ __launch_bounds__(kDecThreads) void decode_fused_kernel(const DecodeP
   if (p1.lv.on()) {  // (a live token count that another path serves: nothing but the counter share)
     const int P = (int)(p1.lv.tokens() * p1.k);
     const int n_touched = decode_prep(p1.ids, P, p1.E, L.ids, L.bits, L.wpre);
-    decode_items<WF, B12X_ACT_BF16, MODE1, FR1, KW1, 1>(p1, L, s_red, n_touched, tag, P);
-    decode_items<WF, B12X_ACT_BF16, DMODE_DOWN, FR2, KW2, 2>(p2, L, s_red, n_touched, tag, P);
+    decode_items<WF, B12X_ACT_BF16, MODE1, FR1, KW1, 1>(p1, L, s_red, n_touched, tag, P, 0, 0, NoFallback{});
+    // a down part whose wait ran out computes the gate/up groups still missing: each
+    // run of consecutive missing groups as one part of the gate/up phase
+    auto fallback = [&](int slot, uint64_t miss) {
+      const int base = slot * p1.n_groups;
+      while (miss) {
+        const int g0 = __builtin_ctzll(miss);
+        const uint64_t above = miss >> g0;
+        const int len = ~above ? __builtin_ctzll(~above) : 64 - g0;
+        decode_items<WF, B12X_ACT_BF16, MODE1, FR1, KW1, 3>(p1, L, s_red, n_touched, tag, P, base + g0,
+                                                            base + g0 + len, NoFallback{});
+        miss = g0 + len >= 64 ? 0ull : miss & (~0ull << (g0 + len));
+      }
+    };
+    decode_items<WF, B12X_ACT_BF16, DMODE_DOWN, FR2, KW2, 2>(p2, L, s_red, n_touched, tag, P, 0, 0, fallback);
   }
   __syncthreads();
   if (threadIdx.x == 0) {
@@ -617,11 +659,11 @@ static int launch_fused(const BindingImpl& b, hipStream_t s) {
   uint8_t* sync = b.dsync;
   for (DecodeParams* p : {&p1, &p2}) {
     p->counter = (uint64_t*)(sync + kDecodeCounterOffset);
-    p->status = (uint64_t*)(sync + kDecodeStatusOffset);
     p->flags = (uint64_t*)(sync + kDecodeFlagsOffset);
     p->flags_per_slot = (int)((b.nf13 + 1) / 2);
     p->deal = 2;
-    // test hook: waits that cannot succeed, and give up after a few polls
+    // test hook: waits that cannot succeed and run out after a few polls, so that every
+    // down part computes its expert's gate/up groups itself
     p->expect_xor = b.force_giveup ? 0x80000000ull : 0ull;
     p->max_polls = b.force_giveup ? 4 : kWaitPolls;
   }

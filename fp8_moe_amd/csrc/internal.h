@@ -51,11 +51,10 @@ inline bool a8_native(int wfmt, int afmt) { return afmt == B12X_ACT_MXFP8 && wfm
 inline bool a8_bf16(int wfmt, int afmt) { return afmt == B12X_ACT_MXFP8 && wfmt == B12X_WEIGHT_NVFP4; }
 // NVFP4 activations (NVFP4 weights only): operands are the exact NVFP4 round trips
 inline bool a4_nv(int afmt) { return afmt == B12X_ACT_NVFP4; }
-// decode synchronization region: a uint64 launch counter, a uint64 status word,
-// then one uint64 completion flag per (touched expert slot, gate/up group of
-// 2 fragments).  b12x_moe_prime zeroes it once per scratch.
+// decode synchronization region: a uint64 launch counter, then (from byte 64)
+// one uint64 completion flag per (touched expert slot, gate/up group of 2
+// fragments).  b12x_moe_prime zeroes it once per scratch.
 constexpr int kDecodeCounterOffset = 0;  // uint64: kLaunchStep per completed fused launch
-constexpr int kDecodeStatusOffset = 8;   // uint64: the tag of the last fused launch whose wait gave up
 constexpr int kDecodeFlagsOffset = 64;   // uint64 per (expert slot, gate/up group): the tag once its h is stored
 // Every fused launch adds exactly kLaunchStep to the counter, split over its
 // workgroups (each adds its share when done), so between launches the
@@ -149,7 +148,7 @@ struct BindingImpl {
   int32_t oai;  // gated with SwiGLU-OAI instead of SiLU
   int32_t a_f16;  // grouped path, NVFP4 weights: GEMM1 reads a scaled f16 copy of a (xq; of its MXFP8 round trips
                   // with MXFP8 activations) and row exponents (xs)
-  int32_t force_giveup;  // test hook (fused decode kernel): its waits expect a tag no one writes
+  int32_t force_giveup;  // test hook (fused decode kernel): its waits expect a tag no one writes and run out
   int32_t timing;        // B12X_TIMING=1 at bind: run() times each stage and prints the times
   int64_t T, a_stride, out_stride;
   int64_t Hp, Ip, max_rows, max_tiles;

@@ -308,31 +308,50 @@ def test_fused_decode_stage_run_twice_with_new_inputs():
         assert ok, (salt, rel_fro, rel_max)
 
 
-def test_fused_decode_wait_gives_up_then_recovers(monkeypatch):
-    """The fused decode kernel's bounded wait, forced from the host to give up
-    (the test hook makes every wait expect a tag that no flag holds; all
-    kernels still run to their end): the call's output is all NaN.  The next
-    call on an ordinary binding over the same scratch is correct again (the
-    failed launch's tag is not the next one's, so nothing needs clearing)."""
+def test_fused_decode_wait_runs_out_and_computes_the_missing_groups(monkeypatch):
+    """The fused decode kernel's bounded wait, forced from the host to run out
+    (the test hook makes every wait expect a tag that no flag holds, with a
+    few polls; all kernels still run to their end): every down part then
+    computes its expert's gate/up groups itself, which is what a workgroup
+    does when the groups' producer is not resident.  The output is
+    bit-identical to an ordinary call's, eager and replayed from a graph, and
+    an ordinary binding over the same scratch is unaffected afterwards."""
     import fp8_moe_amd as fm
     wl = synth.WORKLOADS["decode"]
     pr = problem("decode", 32)
-    T = 8
-    x, ids, tw = _inputs(wl, T)
-    monkeypatch.setenv("B12X_DEBUG_FORCE_GIVEUP", "1")
-    bad, out_bad = pr.model.bind(x, ids, tw)
-    monkeypatch.delenv("B12X_DEBUG_FORCE_GIVEUP")
-    assert fm.binding_query(bad, "path") == 2 and fm.binding_query(bad, "num_stages") == 2
-    fm.run(bad)
-    torch.cuda.synchronize()
-    assert torch.isnan(out_bad.float()).all()
-    good, out = pr.model.bind(x, ids, tw)
-    for _ in range(2):
-        out.fill_(0)
+    for T in (8, 32):  # (T = 1 runs the split-K kernel, which has no waits)
+        x, ids, tw = _inputs(wl, T)
+        good, ref = pr.model.bind(x, ids, tw)
+        assert fm.binding_query(good, "path") == 2 and fm.binding_query(good, "num_stages") == 2
         fm.run(good)
+        monkeypatch.setenv("B12X_DEBUG_FORCE_GIVEUP", "1")
+        forced, out = pr.model.bind(x, ids, tw)
+        monkeypatch.delenv("B12X_DEBUG_FORCE_GIVEUP")
+        for _ in range(2):
+            out.fill_(0)
+            fm.run(forced)
+            torch.cuda.synchronize()
+            assert torch.equal(out, ref), T
+        s = torch.cuda.Stream()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(g, stream=s):
+                fm.run(forced, s)
         torch.cuda.synchronize()
-        rel_fro, rel_max, ok = compare(out, pr.oracle(x, ids, tw))
-        assert ok, (rel_fro, rel_max)
+        for _ in range(3):
+            out.fill_(0)
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(out, ref), T
+        del g
+        again = torch.zeros_like(ref)
+        b2, _ = pr.model.bind(x, ids, tw, again)
+        fm.run(b2)
+        torch.cuda.synchronize()
+        assert torch.equal(again, ref), T
+        rel_fro, rel_max, ok = compare(ref, pr.oracle(x, ids, tw))
+        assert ok, (T, rel_fro, rel_max)
 
 
 def test_fused_decode_needs_a_primed_scratch():
