@@ -13,19 +13,19 @@ from moe_cases import Problem, compare, small_workload
 pytestmark = pytest.mark.gpu
 
 CAP = 4096
-# (weights, activations, gated): bf16 activations with the fused decode kernel;
-# MXFP8 activations with the quantization stage and the two-launch decode
-CASES = [("mxfp4", "bf16", True), ("nvfp4", "mxfp8", False)]
+# (weights, activations, gated, activation): bf16 activations with the fused decode
+# kernel; MXFP8 activations with the quantization stage and the two-launch decode
+CASES = [("mxfp4", "bf16", True, "silu"), ("nvfp4", "mxfp8", False, "relu2"), ("mxfp4", "bf16", True, "swiglu_oai")]
 # T*k with k = 4: 4 and 28 (split-K), 160 (decode), 1200 and 16384 (grouped)
 TS = [1, 7, 40, 300, 4096, 7]
 
 
-@pytest.mark.parametrize("wfmt,afmt,gated", CASES, ids=[f"{c[0]}_{c[1]}" for c in CASES])
-def test_one_graph_serves_every_token_count(wfmt, afmt, gated):
+@pytest.mark.parametrize("wfmt,afmt,gated,act", CASES, ids=[f"{c[0]}_{c[1]}_{c[3]}" for c in CASES])
+def test_one_graph_serves_every_token_count(wfmt, afmt, gated, act):
     import fp8_moe_amd as fm
     wl = small_workload("live", 16, 256, 128, 4, gated=gated, weight_format=wfmt, act_format=afmt)
-    print(f"live binding {wfmt} x {afmt}", flush=True)
-    pr = Problem(wl, CAP)
+    print(f"live binding {wfmt} x {afmt} {act}", flush=True)
+    pr = Problem(wl, CAP, activation=act)
     model = pr.model
     full_x = synth.make_x(wl, CAP, device="cuda", salt=7)
     full_ids, full_tw = synth.make_routing(wl, CAP, device="cuda", salt=7)

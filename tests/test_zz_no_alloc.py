@@ -34,11 +34,12 @@ def test_noalloc_refusals_on_host():
     assert _noalloc_status(pb, exb, 1, 4096) == 3                # partial rows beyond the static array
 
 
-CASES = [("tiny", "silu", (16, 5)), ("decode", "silu", (4, 1)), ("mixed", "relu2", (3, 1))]
+CASES = [("tiny", "silu", (16, 5)), ("decode", "silu", (4, 1)), ("mixed", "relu2", (3, 1)),
+         ("decode", "swiglu_oai", (4, 1))]
 
 
 @pytest.mark.gpu
-@pytest.mark.parametrize("name,act,Ts", CASES, ids=[c[0] for c in CASES])
+@pytest.mark.parametrize("name,act,Ts", CASES, ids=[f"{c[0]}-{c[1]}" for c in CASES])
 def test_noalloc_matches_bind_run(name, act, Ts):
     import fp8_moe_amd as fm
     import synth
