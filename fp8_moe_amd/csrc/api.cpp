@@ -259,7 +259,7 @@ b12x_status b12x_moe_plan(const b12x_moe_caps* caps, b12x_moe_plan_t* out) {
     len[R_Y] = grouped > decode ? grouped : decode;
     if (splitk > len[R_Y]) len[R_Y] = splitk;
   }
-  {  // decode path: launch counter, status and one flag per (touched expert slot, gate/up group of 2 fragments)
+  {  // decode path: launch counter and one flag per (touched expert slot, gate/up group of 2 fragments)
     const int64_t slots = p->decode_max_pairs < p->E ? p->decode_max_pairs : p->E;
     len[R_DSYNC] = p->decode_max_pairs > 0 ? kDecodeFlagsOffset + 8ull * slots * ((p->l13.nf + 1) / 2) : 0;
   }

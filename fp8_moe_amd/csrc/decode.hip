@@ -676,7 +676,7 @@ static int launch_fused(const BindingImpl& b, hipStream_t s) {
 }
 
 // The decode synchronization region zeroed by a fill kernel (not a memset
-// node, so that a captured graph may hold it): counter 0, status 0, flags 0
+// node, so that a captured graph may hold it): counter 0, flags 0
 // (no flag then holds a launch's tag, which is never 0).
 __global__ __launch_bounds__(256) void zero_words_kernel(uint64_t* __restrict__ w, int64_t n) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
