@@ -728,10 +728,13 @@ int launch_decode_sk_combine(const BindingImpl& b, hipStream_t s) {
   const int row_stride = sk_row_stride(b.H);
   const int n_groups = (row_stride - kSkRowPad) / 4;
   const int n_slices = b.I / kSkSlice;
-  // split the slices of a slot over S lanes while a lane would wait for more than one
-  // round of loads, keeping at least 2 position groups (32 contiguous bytes) per wave
+  // split the slices of a slot over S lanes: k * S = 16 lanes per position group where
+  // the slices allow (4 position groups, 64 contiguous bytes of each row per wave, the
+  // fastest measured at top-4 and top-8), more while a lane would wait for more than
+  // two rounds of loads
   int S = 1;
-  while (b.k * S * 4 <= 64 && (n_slices + S - 1) / S > kSkCombineLoads) S *= 2;
+  while (b.k * S < 16 && S < n_slices) S *= 2;
+  while (b.k * S * 2 <= 64 && (n_slices + S - 1) / S > 2 * kSkCombineLoads) S *= 2;
   const int per_wave = 64 / (b.k * S);
   const dim3 grid((unsigned)((n_groups + per_wave - 1) / per_wave), (unsigned)b.T);
   const int64_t part_bytes = b.T * b.k * (int64_t)n_slices * row_stride * 4;
