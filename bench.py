@@ -337,8 +337,8 @@ def time_stage_launches(torch, fm, bindings, stage, stream, repeats=3):
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_kernel_traffic.json")
-TRAFFIC_SOURCES = ["fp8_moe_amd/csrc/decode.hip", "fp8_moe_amd/csrc/device_common.h",
-                   "fp8_moe_amd/csrc/internal.h"]
+TRAFFIC_SOURCES = ["fp8_moe_amd/csrc/decode.hip", "fp8_moe_amd/csrc/decode_common.h",
+                   "fp8_moe_amd/csrc/device_common.h", "fp8_moe_amd/csrc/internal.h"]
 
 
 def kernel_source_hash():
