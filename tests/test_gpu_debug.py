@@ -84,3 +84,61 @@ def test_timing_prints_every_stage(monkeypatch, capfd):
             torch.cuda.synchronize()
             assert torch.equal(out, ref)
         del g
+
+
+@pytest.mark.parametrize("wf,af,gated", FORMATS[:2])
+def test_forced_fallback_on_a_filled_scratch_with_a_live_count(monkeypatch, wf, af, gated):
+    """Everything at once: a scratch filled with 0xFF bytes before priming, a
+    binding at capacity with the token count in device memory, and (bf16
+    activations) fused-decode waits forced to run out so that every down part
+    computes its gate/up groups itself.  Each token count gives the ordinary
+    binding's output bit for bit."""
+    import fp8_moe_amd as fm
+    wl = small_workload("all", 16, 256, 192, 4, gated=gated, weight_format=wf, act_format=af)
+    pr = Problem(wl, 256)
+    filled = torch.empty_like(pr.model.scratch)
+    monkeypatch.setenv("B12X_DEBUG_SCRATCH_FILL", "1")
+    fm.prime(pr.model.plan, filled)
+    monkeypatch.delenv("B12X_DEBUG_SCRATCH_FILL")
+    cap = 256
+    x = torch.zeros(cap, wl.H, dtype=torch.bfloat16, device="cuda")
+    ids = torch.zeros(cap, wl.k, dtype=torch.int32, device="cuda")
+    tw = torch.zeros(cap, wl.k, dtype=torch.float32, device="cuda")
+    out = torch.empty(cap, wl.H, dtype=torch.bfloat16, device="cuda")
+    t_live = torch.zeros(1, dtype=torch.int32, device="cuda")
+    monkeypatch.setenv("B12X_DEBUG_FORCE_GIVEUP", "1")
+    b = fm.bind_live(pr.model.plan, filled, pr.model.experts, x, ids, tw, out, t_live)
+    monkeypatch.delenv("B12X_DEBUG_FORCE_GIVEUP")
+    for T in (1, 16, 200, 16):
+        print(f"all-at-once {wf}/{af} T={T}", flush=True)
+        xs = synth.make_x(wl, T, device="cuda", salt=T)
+        ids_s, tw_s = synth.make_routing(wl, T, device="cuda", salt=T)
+        x[:T].copy_(xs)
+        ids[:T].copy_(ids_s)
+        tw[:T].copy_(tw_s)
+        t_live.fill_(T)
+        fm.run(b)
+        ref, _ = pr.run(xs, ids_s, tw_s)
+        torch.cuda.synchronize()
+        assert torch.equal(out[:T], ref), (wf, af, T)
+
+
+def test_two_scratch_buffers_give_the_same_bits():
+    """No state outside the scratch: two bindings of one plan over two scratch
+    buffers, run alternately on the same inputs, agree bit for bit on every path."""
+    import fp8_moe_amd as fm
+    wl = small_workload("two", 16, 256, 192, 4)
+    pr = Problem(wl, 256)
+    other = fm.alloc_scratch(pr.model.plan)
+    for T in (1, 16, 200):
+        x = synth.make_x(wl, T, device="cuda")
+        ids, tw = synth.make_routing(wl, T, device="cuda")
+        a = torch.empty(T, wl.H, dtype=torch.bfloat16, device="cuda")
+        c = torch.empty_like(a)
+        ba = fm.bind(pr.model.plan, pr.model.scratch, pr.model.experts, x, ids, tw, a)
+        bc = fm.bind(pr.model.plan, other, pr.model.experts, x, ids, tw, c)
+        for _ in range(2):
+            fm.run(ba)
+            fm.run(bc)
+        torch.cuda.synchronize()
+        assert torch.equal(a, c), T
